@@ -1,0 +1,143 @@
+/*
+ * ibp.h -- C ABI of libibp, an MI355X (gfx950) implementation of Invariant
+ * Bit Packing (IBP), a lossless codec for ML tensors.
+ *
+ * Sources cited below:
+ *   FR summary = gist.science French technical summary of arXiv 2605.30728,
+ *     "Résumé Technique : Réduire le goulot d'étranglement de la mémoire GPU
+ *     par la compression sans perte pour le ML";
+ *   KO summary = its Korean counterpart, "Reducing the GPU Memory
+ *     Bottleneck with Lossless Compression for ML -- Extended".
+ * Both describe the method in section "Algorithme central" / "핵심 알고리즘"
+ * (1 preprocessing, 2 compression, 3 decompression) and its use in section
+ * "Intégration au système" / "시스템 통합" (fixed-size slots, GPU bitmask).
+ *
+ * Format (the pages fix no bit layout; this is the layout every call uses):
+ *   - a tensor of L bytes is a bit string, bit i = bit (i mod 32) of
+ *     little-endian 32-bit word i/32; chunk c = bits [c*W, c*W + W);
+ *   - Mask/Bitval are M-bit strings (M/32 words, same bit order); chunk c
+ *     is tested against their bits (c*W .. c*W+W-1) mod M;
+ *   - a record = n = 8L/W participation bits (1 = the chunk matched and lost
+ *     its masked bits), zero padded to H = 32*ceil(n/32) bits, then each
+ *     chunk's kept bits in chunk order and ascending bit position, then zero
+ *     bits up to a multiple of 32 (R bits before padding);
+ *   - slot t (L bytes at slots + t*L) holds the record when
+ *     4*ceil(R/32) < L and bitmask bit t is 1; otherwise the slot holds the
+ *     tensor unchanged and the bit is 0.  Bitmask bit t is bit t%32 of word
+ *     t/32.  Slot bytes after a record are unspecified.
+ *
+ * Memory kinds.  "device" = hipMalloc'd memory of the handle's GPU.
+ * "device or pinned" = device memory or page-locked host memory
+ * (hipHostMalloc / torch pin_memory), which kernels read or write directly
+ * over the host link (zero copy).  Pageable host memory is rejected with
+ * IBP_ERR_INVALID_ARG.  The caller owns and frees every buffer passed in;
+ * the library owns only what an ibp_meta_t holds.
+ *
+ * Calls are asynchronous on `stream` unless stated; argument checks happen
+ * on the host before any launch and leave outputs untouched on error.  Errors
+ * found by kernels (an id out of range, a corrupt record) are latched in the
+ * handle and reported by ibp_check().  Calls on one handle may run on
+ * different streams at once; calls on the same stream run in order.
+ */
+#ifndef IBP_H
+#define IBP_H
+
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum ibp_status {
+    IBP_OK = 0,
+    IBP_ERR_INVALID_ARG = -1, /* bad size, pointer kind or parameter */
+    IBP_ERR_UNSUPPORTED = -2, /* valid format this GPU path does not implement */
+    IBP_ERR_DEVICE = -3,      /* a HIP call failed */
+    IBP_ERR_NOMEM = -4,       /* device or host allocation failed */
+    IBP_ERR_CORRUPT = -5,     /* a compressed slot holds no valid record */
+    IBP_ERR_RANGE = -6        /* a gather id lies outside [0, n_slots) */
+} ibp_status;
+
+typedef struct ibp_meta_s* ibp_meta_t; /* opaque, owned by the library */
+
+typedef struct ibp_params {
+    uint64_t tensor_bytes; /* L: multiple of 4; multiple of W/8 and of M/8        */
+    uint32_t chunk_bits;   /* W: 32, 64, 128, 256, 512 or 1024                    */
+    uint32_t period_bits;  /* M: multiple of W that divides 8L, at most 2^20      */
+    double threshold;      /* T in (0.5, 1]; read by ibp_build_metadata only      */
+} ibp_params;
+
+/* Derived facts about a handle's metadata. */
+typedef struct ibp_meta_info {
+    uint64_t invariant_bits;    /* popcount(Mask) over the M-bit period            */
+    uint64_t min_record_bytes;  /* record bytes when every chunk matches           */
+    uint32_t max_runs;          /* most runs of kept (unmasked) bits in one word   */
+    uint32_t uniform;           /* 1 when every 32-bit Mask/Bitval word is equal   */
+} ibp_meta_info;
+
+/* Step 1, preprocessing (FR/KO summary, "Algorithme central" step 1).
+ * sample: n_sample tensors of L bytes, contiguous, device or pinned.  Every
+ * M-bit block of the sample is one observation; bit position j (0 <= j < M)
+ * is invariant when at least K = ceil(T * n_obs) observations agree on it
+ * (product rounded to nearest in IEEE double, then ceiling), and Bitval
+ * keeps the agreed value there (0 elsewhere).  The histogram runs on the GPU;
+ * the call then waits for `stream` and keeps a host copy of Mask/Bitval, so
+ * it is synchronous.  n_sample * 8L / M must lie in [1, 2^32).  *out
+ * receives a new handle bound to the current HIP device. */
+ibp_status ibp_build_metadata(const ibp_params* params, const void* sample, uint64_t n_sample,
+                              ibp_meta_t* out, hipStream_t stream);
+
+/* A handle from Mask/Bitval given in host memory (M/32 words each; Bitval
+ * bits outside Mask must be 0).  Lets metadata be saved and reused for a
+ * whole dataset (FR/KO summary, step 1, last bullet).  Synchronous. */
+ibp_status ibp_meta_create(const ibp_params* params, const uint32_t* mask, const uint32_t* bitval,
+                           ibp_meta_t* out, hipStream_t stream);
+
+/* Copies the parameters and Mask/Bitval (M/32 words each) to host memory;
+ * any output pointer may be NULL. */
+ibp_status ibp_meta_get(ibp_meta_t meta, ibp_params* params, uint32_t* mask, uint32_t* bitval);
+
+ibp_status ibp_meta_get_info(ibp_meta_t meta, ibp_meta_info* info);
+
+/* Waits for all work on the handle's GPU, then frees the handle. */
+ibp_status ibp_meta_destroy(ibp_meta_t meta);
+
+/* Step 2, compression (FR/KO summary, "Algorithme central" step 2, and
+ * "Intégration au système": fixed slots and a bitmask in GPU memory).
+ * src: n_tensors tensors of L bytes (device or pinned).  dst_slots:
+ * n_tensors slots of L bytes (device or pinned), must not overlap src.
+ * bitmask: device, ceil(n_tensors/32) words; bits 0..n_tensors-1 are
+ * written, later bits of the last word are left as they were.
+ * stored_bytes: device or NULL; entry t = 4*ceil(R/32) for a compressed
+ * slot, L for a raw one. */
+ibp_status ibp_compress(ibp_meta_t meta, const void* src, uint64_t n_tensors, void* dst_slots,
+                        uint32_t* bitmask, uint64_t* stored_bytes, hipStream_t stream);
+
+/* Step 3, decompression (FR/KO summary, "Algorithme central" step 3):
+ * tensor t of dst (device, n_tensors * L bytes) <- slot t of slots (device
+ * or pinned).  Only the record prefix of a compressed slot is read.  A
+ * compressed slot whose header has non-zero padding bits or implies
+ * 4*ceil(R/32) >= L latches IBP_ERR_CORRUPT; its output bytes are then
+ * unspecified. */
+ibp_status ibp_decompress(ibp_meta_t meta, const void* slots, const uint32_t* bitmask,
+                          uint64_t n_tensors, void* dst, hipStream_t stream);
+
+/* Gather on decode: row i of dst (device, n_ids * L bytes) <- slot ids[i]
+ * of slots (n_slots slots, device or pinned).  ids: device int64, repeats
+ * allowed.  An id outside [0, n_slots) latches IBP_ERR_RANGE and leaves that
+ * row unspecified; corrupt records as for ibp_decompress. */
+ibp_status ibp_gather_decompress(ibp_meta_t meta, const void* slots, uint64_t n_slots,
+                                 const uint32_t* bitmask, const int64_t* ids, uint64_t n_ids,
+                                 void* dst, hipStream_t stream);
+
+/* Waits for `stream`, returns the first error latched by a kernel of this
+ * handle since the last ibp_check (IBP_OK if none) and clears it. */
+ibp_status ibp_check(ibp_meta_t meta, hipStream_t stream);
+
+const char* ibp_status_string(ibp_status status);
+
+#ifdef __cplusplus
+}
+#endif
+#endif

@@ -1,0 +1,474 @@
+// ibp_api.hip -- host side of libibp: argument checks, the metadata handle,
+// per-stream look-back scratch, and kernel dispatch.  The C ABI is declared
+// in include/ibp.h; every step of the codec runs in ibp_kernels.hip.
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdint.h>
+#include <string.h>
+
+#include <map>
+#include <mutex>
+#include <new>
+#include <vector>
+
+#include "../../include/ibp.h"
+#include "ibp_internal.hpp"
+
+using namespace ibp;
+
+namespace {
+
+constexpr uint32_t kLongTileWords = 1024;  // tile of a tensor longer than kMaxTileWords
+constexpr uint32_t kMaxPeriodBits = 1u << 20;
+
+struct Scratch {
+    unsigned long long* status = nullptr;
+    uint64_t status_cap = 0;
+    uint64_t* totals = nullptr;
+    uint64_t totals_cap = 0;
+    uint32_t* ticket = nullptr;
+    uint32_t ticket_base = 0;
+    uint32_t epoch = 0;
+};
+
+}  // namespace
+
+struct ibp_meta_s {
+    int device = 0;
+    ibp_params params{};
+    uint32_t Mw = 0, Pc = 0, g = 0, log2g = 0, G = 0, Ne = 0;
+    std::vector<uint32_t> mask_h, bitval_h;
+    void* dmem = nullptr;
+    uint32_t* d_mask = nullptr;
+    uint32_t* d_bitval = nullptr;
+    Summary* d_summary = nullptr;
+    uint32_t* d_err = nullptr;
+    Tables tabs{};
+    Summary sum{};
+    std::mutex mu;
+    std::map<hipStream_t, Scratch> scratch;
+};
+
+namespace {
+
+struct DeviceGuard {
+    int prev = -1;
+    bool ok = true;
+    explicit DeviceGuard(int dev) {
+        if (hipGetDevice(&prev) != hipSuccess) {
+            ok = false;
+            return;
+        }
+        if (prev != dev && hipSetDevice(dev) != hipSuccess) ok = false;
+    }
+    ~DeviceGuard() {
+        int cur = -1;
+        if (prev >= 0 && hipGetDevice(&cur) == hipSuccess && cur != prev) (void)hipSetDevice(prev);
+    }
+};
+
+uint32_t gcd32(uint32_t a, uint32_t b) {
+    while (b) {
+        uint32_t t = a % b;
+        a = b;
+        b = t;
+    }
+    return a;
+}
+
+uint32_t bit_length(uint32_t v) {
+    uint32_t n = 0;
+    while (v) {
+        ++n;
+        v >>= 1;
+    }
+    return n;
+}
+
+ibp_status check_params(const ibp_params* p, bool need_threshold) {
+    if (!p) return IBP_ERR_INVALID_ARG;
+    const uint64_t L = p->tensor_bytes;
+    const uint64_t W = p->chunk_bits, M = p->period_bits;
+    if (L == 0 || L % 4 != 0 || W == 0 || M == 0) return IBP_ERR_INVALID_ARG;
+    if ((8 * L) % W != 0 || M % W != 0 || (8 * L) % M != 0) return IBP_ERR_INVALID_ARG;
+    if (need_threshold && !(p->threshold > 0.5 && p->threshold <= 1.0)) return IBP_ERR_INVALID_ARG;
+    if (W < 32 || W > 1024 || (W & (W - 1)) != 0) return IBP_ERR_UNSUPPORTED;
+    if (M > kMaxPeriodBits) return IBP_ERR_UNSUPPORTED;
+    return IBP_OK;
+}
+
+enum class Kind { Device, Host, Bad };
+
+Kind pointer_kind(const void* ptr, int device) {
+    if (!ptr) return Kind::Bad;
+    hipPointerAttribute_t a;
+    memset(&a, 0, sizeof(a));
+    if (hipPointerGetAttributes(&a, ptr) != hipSuccess) {
+        (void)hipGetLastError();
+        return Kind::Bad;
+    }
+    switch (a.type) {
+        case hipMemoryTypeDevice:
+            return a.device == device ? Kind::Device : Kind::Bad;
+        case hipMemoryTypeManaged:
+            return Kind::Device;
+        case hipMemoryTypeHost:
+            return Kind::Host;
+        default:
+            return Kind::Bad;
+    }
+}
+
+bool device_or_pinned(const void* p, int dev) { return pointer_kind(p, dev) != Kind::Bad; }
+bool device_only(const void* p, int dev) { return pointer_kind(p, dev) == Kind::Device; }
+
+ibp_status from_hip(hipError_t e) {
+    if (e == hipSuccess) return IBP_OK;
+    (void)hipGetLastError();
+    return e == hipErrorOutOfMemory ? IBP_ERR_NOMEM : IBP_ERR_DEVICE;
+}
+
+#define IBP_TRY(expr)                        \
+    do {                                     \
+        ibp_status st_ = from_hip(expr);     \
+        if (st_ != IBP_OK) return st_;       \
+    } while (0)
+
+// Allocates the handle's device tables and fills in its shape fields.
+ibp_status new_handle(const ibp_params* p, ibp_meta_s** out) {
+    ibp_meta_s* h = new (std::nothrow) ibp_meta_s();
+    if (!h) return IBP_ERR_NOMEM;
+    if (hipGetDevice(&h->device) != hipSuccess) {
+        delete h;
+        return IBP_ERR_DEVICE;
+    }
+    h->params = *p;
+    h->Mw = p->period_bits / 32;
+    h->Pc = p->period_bits / p->chunk_bits;
+    h->g = p->chunk_bits / 32;
+    h->log2g = bit_length(h->g) - 1;
+    h->G = gcd32(32, h->Pc);
+    h->Ne = h->Pc / h->G;
+    const uint64_t Mw = h->Mw;
+    // layout (words): mask, bitval, kd, dx[4], r[16], planes[Ne*11], summary, err
+    const uint64_t words = Mw * (3 + 4 + kMaxRuns) + (uint64_t)h->Ne * kPlanes;
+    const uint64_t bytes = words * 4 + 256 + sizeof(Summary) + 64;
+    hipError_t e = hipMalloc(&h->dmem, bytes);
+    if (e != hipSuccess) {
+        (void)hipGetLastError();
+        delete h;
+        return IBP_ERR_NOMEM;
+    }
+    uint32_t* w = static_cast<uint32_t*>(h->dmem);
+    h->d_mask = w;
+    h->d_bitval = w + Mw;
+    uint32_t* kd = w + 2 * Mw;
+    uint32_t* dx = w + 3 * Mw;
+    uint32_t* r = w + 7 * Mw;
+    uint32_t* planes = w + (7 + kMaxRuns) * Mw;
+    uintptr_t tail = reinterpret_cast<uintptr_t>(planes + (uint64_t)h->Ne * kPlanes);
+    tail = (tail + 255) & ~uintptr_t(255);
+    h->d_summary = reinterpret_cast<Summary*>(tail);
+    h->d_err = reinterpret_cast<uint32_t*>(tail + ((sizeof(Summary) + 63) & ~size_t(63)));
+    h->tabs = Tables{h->d_mask, h->d_bitval, kd, dx, r, planes};
+    *out = h;
+    return IBP_OK;
+}
+
+// Derived tables from the device Mask/Bitval, then the host copies.
+ibp_status finish_handle(ibp_meta_s* h, hipStream_t s) {
+    Summary init{};
+    init.uniform = 1;
+    IBP_TRY(hipMemcpyAsync(h->d_summary, &init, sizeof(init), hipMemcpyHostToDevice, s));
+    IBP_TRY(launch_fill_u32(h->d_err, 1, 0, s));
+    uint32_t* kd = const_cast<uint32_t*>(h->tabs.kd);
+    uint32_t* dx = const_cast<uint32_t*>(h->tabs.dx);
+    uint32_t* r = const_cast<uint32_t*>(h->tabs.r);
+    uint32_t* pl = const_cast<uint32_t*>(h->tabs.planes);
+    IBP_TRY(launch_tables(h->d_mask, h->d_bitval, h->Mw, h->Pc, h->g, h->G, kd, dx, r, pl, h->d_summary, s));
+    h->mask_h.resize(h->Mw);
+    h->bitval_h.resize(h->Mw);
+    IBP_TRY(hipMemcpyAsync(h->mask_h.data(), h->d_mask, 4ull * h->Mw, hipMemcpyDeviceToHost, s));
+    IBP_TRY(hipMemcpyAsync(h->bitval_h.data(), h->d_bitval, 4ull * h->Mw, hipMemcpyDeviceToHost, s));
+    IBP_TRY(hipMemcpyAsync(&h->sum, h->d_summary, sizeof(Summary), hipMemcpyDeviceToHost, s));
+    IBP_TRY(hipStreamSynchronize(s));
+    return IBP_OK;
+}
+
+void free_handle(ibp_meta_s* h) {
+    if (!h) return;
+    (void)hipDeviceSynchronize();
+    for (auto& kv : h->scratch) {
+        if (kv.second.status) (void)hipFree(kv.second.status);
+        if (kv.second.totals) (void)hipFree(kv.second.totals);
+        if (kv.second.ticket) (void)hipFree(kv.second.ticket);
+    }
+    if (h->dmem) (void)hipFree(h->dmem);
+    delete h;
+}
+
+uint64_t min_record_bits(const ibp_meta_s* h) {
+    const uint64_t L = h->params.tensor_bytes;
+    const uint64_t n_chunks = 8 * L / h->params.chunk_bits;
+    const uint64_t H = 32 * ((n_chunks + 31) / 32);
+    const uint64_t periods = 8 * L / h->params.period_bits;
+    return H + 8 * L - periods * h->sum.invariant_bits;
+}
+
+Geo make_geo(const ibp_meta_s* h, bool aligned16) {
+    Geo g{};
+    const uint64_t L = h->params.tensor_bytes;
+    g.L = L;
+    g.n_words = L / 4;
+    g.n_chunks = 8 * L / h->params.chunk_bits;
+    g.hdr_words = (g.n_chunks + 31) / 32;
+    g.Mw = h->Mw;
+    g.Pc = h->Pc;
+    g.log2g = h->log2g;
+    g.G = h->G;
+    g.np = bit_length(h->sum.max_chunk_k);
+    if (g.np > (uint32_t)kPlanes) g.np = kPlanes;
+    g.aligned16 = aligned16 ? 1u : 0u;
+    if (g.n_words <= kMaxTileWords) {
+        g.tile_words = (uint32_t)g.n_words;
+        g.tiles_per_tensor = 1;
+    } else {
+        g.tile_words = kLongTileWords;
+        g.tiles_per_tensor = (g.n_words + kLongTileWords - 1) / kLongTileWords;
+    }
+    uint64_t spec = (min_record_bits(h) + 31) / 32;
+    if (spec < g.hdr_words) spec = g.hdr_words;
+    if (aligned16) spec = (spec + 3) & ~3ull;
+    if (spec > g.n_words) spec = g.n_words;
+    g.spec_words = (uint32_t)spec;
+    return g;
+}
+
+bool aligned16(uint64_t L, std::initializer_list<const void*> ptrs) {
+    if (L % 16 != 0) return false;
+    for (const void* p : ptrs)
+        if (reinterpret_cast<uintptr_t>(p) % 16 != 0) return false;
+    return true;
+}
+
+// Look-back state for one launch of `waves` waves over `tiles` tiles on
+// stream s.  Grows the per-stream buffers when needed.
+ibp_status lookback_for(ibp_meta_s* h, hipStream_t s, uint64_t tiles, uint64_t waves, uint64_t tensors,
+                        LookBack* lb) {
+    std::lock_guard<std::mutex> lock(h->mu);
+    Scratch& sc = h->scratch[s];
+    if (!sc.ticket) {
+        IBP_TRY(hipMalloc(&sc.ticket, 256));
+        IBP_TRY(launch_fill_u32(sc.ticket, 1, 0, s));
+        sc.ticket_base = 0;
+    }
+    if (sc.status_cap < tiles) {
+        IBP_TRY(hipStreamSynchronize(s));
+        if (sc.status) IBP_TRY(hipFree(sc.status));
+        sc.status = nullptr;
+        IBP_TRY(hipMalloc(&sc.status, tiles * sizeof(unsigned long long)));
+        IBP_TRY(launch_fill_u32(reinterpret_cast<uint32_t*>(sc.status), 2 * tiles, 0, s));
+        sc.status_cap = tiles;
+        sc.epoch = 0;
+    }
+    if (sc.totals_cap < tensors) {
+        IBP_TRY(hipStreamSynchronize(s));
+        if (sc.totals) IBP_TRY(hipFree(sc.totals));
+        sc.totals = nullptr;
+        IBP_TRY(hipMalloc(&sc.totals, tensors * sizeof(uint64_t)));
+        sc.totals_cap = tensors;
+    }
+    sc.epoch += 1;
+    if (sc.epoch >= (1u << 20)) {
+        IBP_TRY(launch_fill_u32(reinterpret_cast<uint32_t*>(sc.status), 2 * sc.status_cap, 0, s));
+        sc.epoch = 1;
+    }
+    lb->status = sc.status;
+    lb->ticket = sc.ticket;
+    lb->ticket_base = sc.ticket_base;
+    lb->epoch = sc.epoch;
+    lb->totals = sc.totals;
+    sc.ticket_base += (uint32_t)waves;
+    return IBP_OK;
+}
+
+uint64_t launched_waves(uint64_t tiles) {
+    return ((tiles + kWavesPerBlock - 1) / kWavesPerBlock) * kWavesPerBlock;
+}
+
+bool overlaps(const void* a, uint64_t na, const void* b, uint64_t nb) {
+    const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
+    return x < y + nb && y < x + na;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* ibp_status_string(ibp_status s) {
+    switch (s) {
+        case IBP_OK: return "ok";
+        case IBP_ERR_INVALID_ARG: return "invalid argument";
+        case IBP_ERR_UNSUPPORTED: return "unsupported format";
+        case IBP_ERR_DEVICE: return "HIP error";
+        case IBP_ERR_NOMEM: return "out of memory";
+        case IBP_ERR_CORRUPT: return "corrupt record";
+        case IBP_ERR_RANGE: return "id out of range";
+    }
+    return "unknown status";
+}
+
+ibp_status ibp_build_metadata(const ibp_params* params, const void* sample, uint64_t n_sample,
+                              ibp_meta_t* out, hipStream_t stream) {
+    if (!out) return IBP_ERR_INVALID_ARG;
+    ibp_status st = check_params(params, true);
+    if (st != IBP_OK) return st;
+    int dev = 0;
+    IBP_TRY(hipGetDevice(&dev));
+    if (n_sample == 0 || !device_or_pinned(sample, dev)) return IBP_ERR_INVALID_ARG;
+    const uint64_t L = params->tensor_bytes;
+    const uint64_t per = 8 * L / params->period_bits;
+    if (n_sample > (1ull << 40) / per) return IBP_ERR_INVALID_ARG;
+    const uint64_t n_obs = n_sample * per;
+    if (n_obs >= (1ull << 32)) return IBP_ERR_INVALID_ARG;
+    // K = ceil(T * n_obs), product rounded to nearest in IEEE double.
+    const double prod = params->threshold * (double)n_obs;
+    const uint64_t K = (uint64_t)ceil(prod);
+
+    ibp_meta_s* h = nullptr;
+    st = new_handle(params, &h);
+    if (st != IBP_OK) return st;
+    uint32_t* counts = nullptr;
+    hipError_t e = hipMalloc(&counts, 4ull * params->period_bits);
+    if (e == hipSuccess) e = launch_fill_u32(counts, params->period_bits, 0, stream);
+    if (e == hipSuccess)
+        e = launch_meta_hist(static_cast<const uint32_t*>(sample), n_sample * (L / 4), h->Mw, counts, stream);
+    if (e == hipSuccess) e = launch_meta_finalize(counts, h->Mw, n_obs, K, h->d_mask, h->d_bitval, stream);
+    st = from_hip(e);
+    if (st == IBP_OK) st = finish_handle(h, stream);
+    if (counts) (void)hipFree(counts);
+    if (st != IBP_OK) {
+        free_handle(h);
+        return st;
+    }
+    *out = h;
+    return IBP_OK;
+}
+
+ibp_status ibp_meta_create(const ibp_params* params, const uint32_t* mask, const uint32_t* bitval,
+                           ibp_meta_t* out, hipStream_t stream) {
+    if (!out || !mask || !bitval) return IBP_ERR_INVALID_ARG;
+    ibp_status st = check_params(params, false);
+    if (st != IBP_OK) return st;
+    const uint32_t Mw = params->period_bits / 32;
+    for (uint32_t i = 0; i < Mw; ++i)
+        if (bitval[i] & ~mask[i]) return IBP_ERR_INVALID_ARG;
+    ibp_meta_s* h = nullptr;
+    st = new_handle(params, &h);
+    if (st != IBP_OK) return st;
+    hipError_t e = hipMemcpyAsync(h->d_mask, mask, 4ull * Mw, hipMemcpyHostToDevice, stream);
+    if (e == hipSuccess) e = hipMemcpyAsync(h->d_bitval, bitval, 4ull * Mw, hipMemcpyHostToDevice, stream);
+    st = from_hip(e);
+    if (st == IBP_OK) st = finish_handle(h, stream);
+    if (st != IBP_OK) {
+        free_handle(h);
+        return st;
+    }
+    *out = h;
+    return IBP_OK;
+}
+
+ibp_status ibp_meta_get(ibp_meta_t h, ibp_params* params, uint32_t* mask, uint32_t* bitval) {
+    if (!h) return IBP_ERR_INVALID_ARG;
+    if (params) *params = h->params;
+    if (mask) memcpy(mask, h->mask_h.data(), 4ull * h->Mw);
+    if (bitval) memcpy(bitval, h->bitval_h.data(), 4ull * h->Mw);
+    return IBP_OK;
+}
+
+ibp_status ibp_meta_get_info(ibp_meta_t h, ibp_meta_info* info) {
+    if (!h || !info) return IBP_ERR_INVALID_ARG;
+    info->invariant_bits = h->sum.invariant_bits;
+    info->min_record_bytes = 4 * ((min_record_bits(h) + 31) / 32);
+    info->max_runs = h->sum.max_runs;
+    info->uniform = h->sum.uniform;
+    return IBP_OK;
+}
+
+ibp_status ibp_meta_destroy(ibp_meta_t h) {
+    if (!h) return IBP_ERR_INVALID_ARG;
+    DeviceGuard guard(h->device);
+    free_handle(h);
+    return IBP_OK;
+}
+
+ibp_status ibp_compress(ibp_meta_t h, const void* src, uint64_t n_tensors, void* dst_slots,
+                        uint32_t* bitmask, uint64_t* stored_bytes, hipStream_t stream) {
+    if (!h) return IBP_ERR_INVALID_ARG;
+    if (n_tensors == 0) return IBP_OK;
+    DeviceGuard guard(h->device);
+    if (!guard.ok) return IBP_ERR_DEVICE;
+    const uint64_t L = h->params.tensor_bytes;
+    if (n_tensors > (~0ull) / L) return IBP_ERR_INVALID_ARG;
+    if (!device_or_pinned(src, h->device) || !device_or_pinned(dst_slots, h->device)) return IBP_ERR_INVALID_ARG;
+    if (!device_only(bitmask, h->device)) return IBP_ERR_INVALID_ARG;
+    if (stored_bytes && !device_only(stored_bytes, h->device)) return IBP_ERR_INVALID_ARG;
+    if (overlaps(src, n_tensors * L, dst_slots, n_tensors * L)) return IBP_ERR_INVALID_ARG;
+    const Geo geo = make_geo(h, aligned16(L, {src, dst_slots}));
+    LookBack lb{};
+    if (geo.tiles_per_tensor > 1) {
+        const uint64_t tiles = n_tensors * geo.tiles_per_tensor;
+        ibp_status st = lookback_for(h, stream, tiles, launched_waves(tiles), n_tensors, &lb);
+        if (st != IBP_OK) return st;
+    }
+    return from_hip(launch_encode(h->tabs, geo, h->sum.max_runs, src, n_tensors, dst_slots, bitmask,
+                                  stored_bytes, &lb, stream));
+}
+
+static ibp_status decode_common(ibp_meta_t h, const void* slots, uint64_t n_slots, const uint32_t* bitmask,
+                                const int64_t* ids, uint64_t n_out, void* dst, hipStream_t stream) {
+    if (!h) return IBP_ERR_INVALID_ARG;
+    if (n_out == 0) return IBP_OK;
+    DeviceGuard guard(h->device);
+    if (!guard.ok) return IBP_ERR_DEVICE;
+    const uint64_t L = h->params.tensor_bytes;
+    if (n_out > (~0ull) / L || n_slots > (~0ull) / L) return IBP_ERR_INVALID_ARG;
+    if (!device_or_pinned(slots, h->device)) return IBP_ERR_INVALID_ARG;
+    if (!device_only(bitmask, h->device) || !device_only(dst, h->device)) return IBP_ERR_INVALID_ARG;
+    if (ids && !device_only(ids, h->device)) return IBP_ERR_INVALID_ARG;
+    if (overlaps(slots, n_slots * L, dst, n_out * L)) return IBP_ERR_INVALID_ARG;
+    const Geo geo = make_geo(h, aligned16(L, {slots, dst}));
+    LookBack lb{};
+    if (geo.tiles_per_tensor > 1) {
+        const uint64_t tiles = n_out * geo.tiles_per_tensor;
+        ibp_status st = lookback_for(h, stream, tiles, launched_waves(tiles), n_out, &lb);
+        if (st != IBP_OK) return st;
+    }
+    return from_hip(launch_decode(h->tabs, geo, h->sum.max_runs, slots, n_slots, bitmask, ids, n_out, dst,
+                                  h->d_err, &lb, stream));
+}
+
+ibp_status ibp_decompress(ibp_meta_t h, const void* slots, const uint32_t* bitmask, uint64_t n_tensors,
+                          void* dst, hipStream_t stream) {
+    return decode_common(h, slots, n_tensors, bitmask, nullptr, n_tensors, dst, stream);
+}
+
+ibp_status ibp_gather_decompress(ibp_meta_t h, const void* slots, uint64_t n_slots, const uint32_t* bitmask,
+                                 const int64_t* ids, uint64_t n_ids, void* dst, hipStream_t stream) {
+    if (n_ids && !ids) return IBP_ERR_INVALID_ARG;
+    return decode_common(h, slots, n_slots, bitmask, ids, n_ids, dst, stream);
+}
+
+ibp_status ibp_check(ibp_meta_t h, hipStream_t stream) {
+    if (!h) return IBP_ERR_INVALID_ARG;
+    DeviceGuard guard(h->device);
+    IBP_TRY(hipStreamSynchronize(stream));
+    uint32_t v = 0;
+    IBP_TRY(hipMemcpy(&v, h->d_err, 4, hipMemcpyDeviceToHost));
+    if (v == kErrNone) return IBP_OK;
+    IBP_TRY(launch_fill_u32(h->d_err, 1, 0, stream));
+    IBP_TRY(hipStreamSynchronize(stream));
+    return v == kErrRange ? IBP_ERR_RANGE : IBP_ERR_CORRUPT;
+}
+
+}  // extern "C"

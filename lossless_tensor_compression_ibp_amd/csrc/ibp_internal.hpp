@@ -1,0 +1,84 @@
+// ibp_internal.hpp -- structures shared by the host side of libibp and its
+// gfx950 kernels.  Not part of the public ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace ibp {
+
+constexpr int kWave = 64;           // CDNA wavefront width
+constexpr int kWavesPerBlock = 4;   // independent waves per workgroup
+constexpr int kMaxRuns = 16;        // a 32-bit word has at most 16 runs of ones
+constexpr int kPlanes = 11;         // bit planes of a per-chunk k (k <= 1024)
+constexpr uint32_t kMaxTileWords = 2048;  // largest tile one wave owns
+
+// Derived per-position tables in device memory (structure of arrays; every
+// array has Mw entries unless stated).  Position i of the metadata period is
+// 32-bit word i of Mask/Bitval.
+struct Tables {
+    const uint32_t* m;       // Mask word
+    const uint32_t* b;       // Bitval word
+    const uint32_t* kd;      // k | d0 << 8 | d1 << 16 | d2 << 24
+    const uint32_t* dx;      // [4][Mw]: run shifts d3.. packed 4 per word
+    const uint32_t* r;       // [kMaxRuns][Mw]: run masks, output positions
+    const uint32_t* planes;  // [Ne][kPlanes]: bit planes of per-chunk k
+};
+
+// Shape of one launch: the tensor geometry plus how it is cut into tiles.
+struct Geo {
+    uint64_t L;              // tensor (and slot) bytes
+    uint64_t n_words;        // L / 4
+    uint64_t n_chunks;       // 8L / W
+    uint64_t hdr_words;      // ceil(n_chunks / 32)
+    uint32_t Mw;             // period in words (M / 32)
+    uint32_t Pc;             // period in chunks (M / W)
+    uint32_t log2g;          // log2(W / 32)
+    uint32_t G;              // gcd(32, Pc)
+    uint32_t np;             // bit planes worth scanning (<= kPlanes)
+    uint32_t tile_words;     // words per tile (multiple of 64 * 32 >> ... see host)
+    uint64_t tiles_per_tensor;
+    uint32_t spec_words;     // first-read words of a single-tile record (multiple of 4)
+    uint32_t aligned16;      // slot base and L allow 16-byte vector access
+};
+
+// Decoupled look-back state for multi-tile tensors.  A status word packs
+// flag (2 bits) | epoch (20 bits) | value (42 bits).
+struct LookBack {
+    unsigned long long* status;  // one per tile of the launch
+    uint32_t* ticket;            // dynamic tile counter
+    uint32_t ticket_base;        // counter value at launch
+    uint32_t epoch;              // 1 .. 2^20-1, distinct from stale entries
+    uint64_t* totals;            // per output tensor: record bits (encode)
+};
+
+enum DeviceError : uint32_t { kErrNone = 0, kErrCorrupt = 5, kErrRange = 6 };
+
+// Summary written by the table builder, read back by the host.
+struct Summary {
+    uint32_t max_runs;
+    uint32_t max_chunk_k;
+    uint32_t uniform;
+    uint32_t pad;
+    unsigned long long invariant_bits;
+    unsigned long long removed_per_period;  // sum of k over the period
+};
+
+// Kernel launchers (ibp_kernels.hip).  All return hipError_t of the launch.
+hipError_t launch_fill_u32(uint32_t* p, uint64_t n, uint32_t v, hipStream_t s);
+hipError_t launch_meta_hist(const uint32_t* sample, uint64_t n_words, uint32_t Mw, uint32_t* counts,
+                            hipStream_t s);
+hipError_t launch_meta_finalize(const uint32_t* counts, uint32_t Mw, uint64_t n_obs, uint64_t K,
+                                uint32_t* mask, uint32_t* bitval, hipStream_t s);
+hipError_t launch_tables(const uint32_t* mask, const uint32_t* bitval, uint32_t Mw, uint32_t Pc,
+                         uint32_t g, uint32_t G, uint32_t* kd, uint32_t* dx, uint32_t* r,
+                         uint32_t* planes, Summary* summary, hipStream_t s);
+hipError_t launch_encode(const Tables& t, const Geo& geo, uint32_t runs, const void* src,
+                         uint64_t n_tensors, void* slots, uint32_t* bitmask, uint64_t* stored,
+                         const LookBack* lb, hipStream_t s);
+hipError_t launch_decode(const Tables& t, const Geo& geo, uint32_t runs, const void* slots,
+                         uint64_t n_slots, const uint32_t* bitmask, const int64_t* ids,
+                         uint64_t n_out, void* dst, uint32_t* err, const LookBack* lb,
+                         hipStream_t s);
+
+}  // namespace ibp

@@ -1,0 +1,198 @@
+"""Python binding of libibp (include/ibp.h): argument marshalling only.
+
+Every function forwards torch tensors (device memory, or pinned host memory
+where the C ABI allows it) as raw pointers together with the HIP stream of
+torch's current stream.  All codec work runs in the gfx950 kernels of
+libibp.so; if the library is missing this module raises on first use.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libibp.so")
+
+IBP_OK = 0
+IBP_ERR_INVALID_ARG = -1
+IBP_ERR_UNSUPPORTED = -2
+IBP_ERR_DEVICE = -3
+IBP_ERR_NOMEM = -4
+IBP_ERR_CORRUPT = -5
+IBP_ERR_RANGE = -6
+
+# every function the header declares (checked by the tests)
+ABI_FUNCTIONS = (
+    "ibp_build_metadata", "ibp_meta_create", "ibp_meta_get", "ibp_meta_get_info",
+    "ibp_meta_destroy", "ibp_compress", "ibp_decompress", "ibp_gather_decompress",
+    "ibp_check", "ibp_status_string",
+)
+
+
+class ibp_params(ctypes.Structure):
+    _fields_ = [("tensor_bytes", ctypes.c_uint64), ("chunk_bits", ctypes.c_uint32),
+                ("period_bits", ctypes.c_uint32), ("threshold", ctypes.c_double)]
+
+
+class ibp_meta_info(ctypes.Structure):
+    _fields_ = [("invariant_bits", ctypes.c_uint64), ("min_record_bytes", ctypes.c_uint64),
+                ("max_runs", ctypes.c_uint32), ("uniform", ctypes.c_uint32)]
+
+
+class IBPError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        super().__init__(f"{what}: {status_string(status)} ({status})")
+        self.status = status
+
+
+_lib = None
+
+
+def lib():
+    """Load libibp.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                               "python -m lossless_tensor_compression_ibp_amd.build_lib")
+        L = ctypes.CDLL(LIB_PATH)
+        p, u64, st = ctypes.c_void_p, ctypes.c_uint64, ctypes.c_int
+        P = ctypes.POINTER
+        L.ibp_build_metadata.argtypes = [P(ibp_params), p, u64, P(p), p]
+        L.ibp_meta_create.argtypes = [P(ibp_params), p, p, P(p), p]
+        L.ibp_meta_get.argtypes = [p, P(ibp_params), p, p]
+        L.ibp_meta_get_info.argtypes = [p, P(ibp_meta_info)]
+        L.ibp_meta_destroy.argtypes = [p]
+        L.ibp_compress.argtypes = [p, p, u64, p, p, p, p]
+        L.ibp_decompress.argtypes = [p, p, p, u64, p, p]
+        L.ibp_gather_decompress.argtypes = [p, p, u64, p, p, u64, p, p]
+        L.ibp_check.argtypes = [p, p]
+        L.ibp_status_string.argtypes = [st]
+        L.ibp_status_string.restype = ctypes.c_char_p
+        for f in ABI_FUNCTIONS:
+            if f != "ibp_status_string":
+                getattr(L, f).restype = st
+        _lib = L
+    return _lib
+
+
+def status_string(status: int) -> str:
+    return lib().ibp_status_string(int(status)).decode()
+
+
+def _check(status: int, what: str):
+    if status != IBP_OK:
+        raise IBPError(status, what)
+
+
+def _ptr(t: torch.Tensor | None):
+    if t is None:
+        return None
+    if not t.is_contiguous():
+        raise ValueError("tensors passed to libibp must be contiguous")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream) -> ctypes.c_void_p:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+class Meta:
+    """Owns an ibp_meta_t handle."""
+
+    def __init__(self, handle: ctypes.c_void_p):
+        self.handle = handle
+
+    @property
+    def _as_parameter_(self):
+        return self.handle
+
+    def close(self):
+        if self.handle:
+            _check(lib().ibp_meta_destroy(self.handle), "ibp_meta_destroy")
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+def _params(tensor_bytes, chunk_bits, period_bits, threshold=0.0):
+    return ibp_params(int(tensor_bytes), int(chunk_bits), int(period_bits), float(threshold))
+
+
+def ibp_build_metadata(sample: torch.Tensor, n_sample: int, tensor_bytes: int, chunk_bits: int,
+                       period_bits: int, threshold: float, stream=None) -> Meta:
+    prm = _params(tensor_bytes, chunk_bits, period_bits, threshold)
+    out = ctypes.c_void_p()
+    _check(lib().ibp_build_metadata(ctypes.byref(prm), _ptr(sample), int(n_sample), ctypes.byref(out),
+                                    _stream(stream)), "ibp_build_metadata")
+    return Meta(out)
+
+
+def ibp_meta_create(tensor_bytes: int, chunk_bits: int, period_bits: int, mask, bitval, stream=None) -> Meta:
+    mask = np.ascontiguousarray(mask, dtype=np.uint32)
+    bitval = np.ascontiguousarray(bitval, dtype=np.uint32)
+    prm = _params(tensor_bytes, chunk_bits, period_bits)
+    out = ctypes.c_void_p()
+    _check(lib().ibp_meta_create(ctypes.byref(prm), ctypes.c_void_p(mask.ctypes.data),
+                                 ctypes.c_void_p(bitval.ctypes.data), ctypes.byref(out), _stream(stream)),
+           "ibp_meta_create")
+    return Meta(out)
+
+
+def ibp_meta_get(meta: Meta):
+    prm = ibp_params()
+    _check(lib().ibp_meta_get(meta, ctypes.byref(prm), None, None), "ibp_meta_get")
+    mw = prm.period_bits // 32
+    mask = np.zeros(mw, np.uint32)
+    bitval = np.zeros(mw, np.uint32)
+    _check(lib().ibp_meta_get(meta, None, ctypes.c_void_p(mask.ctypes.data),
+                              ctypes.c_void_p(bitval.ctypes.data)), "ibp_meta_get")
+    params = dict(tensor_bytes=prm.tensor_bytes, chunk_bits=prm.chunk_bits,
+                  period_bits=prm.period_bits, threshold=prm.threshold)
+    return params, mask, bitval
+
+
+def ibp_meta_get_info(meta: Meta) -> dict:
+    info = ibp_meta_info()
+    _check(lib().ibp_meta_get_info(meta, ctypes.byref(info)), "ibp_meta_get_info")
+    return dict(invariant_bits=info.invariant_bits, min_record_bytes=info.min_record_bytes,
+                max_runs=info.max_runs, uniform=info.uniform)
+
+
+def ibp_meta_destroy(meta: Meta):
+    meta.close()
+
+
+def ibp_compress(meta: Meta, src: torch.Tensor, n_tensors: int, dst_slots: torch.Tensor,
+                 bitmask: torch.Tensor, stored_bytes: torch.Tensor | None = None, stream=None):
+    _check(lib().ibp_compress(meta, _ptr(src), int(n_tensors), _ptr(dst_slots), _ptr(bitmask),
+                              _ptr(stored_bytes), _stream(stream)), "ibp_compress")
+
+
+def ibp_decompress(meta: Meta, slots: torch.Tensor, bitmask: torch.Tensor, n_tensors: int,
+                   dst: torch.Tensor, stream=None):
+    _check(lib().ibp_decompress(meta, _ptr(slots), _ptr(bitmask), int(n_tensors), _ptr(dst),
+                                _stream(stream)), "ibp_decompress")
+
+
+def ibp_gather_decompress(meta: Meta, slots: torch.Tensor, n_slots: int, bitmask: torch.Tensor,
+                          ids: torch.Tensor, dst: torch.Tensor, stream=None):
+    if ids.dtype != torch.int64:
+        raise ValueError("ids must be int64")
+    _check(lib().ibp_gather_decompress(meta, _ptr(slots), int(n_slots), _ptr(bitmask), _ptr(ids),
+                                       int(ids.numel()), _ptr(dst), _stream(stream)),
+           "ibp_gather_decompress")
+
+
+def ibp_check(meta: Meta, stream=None) -> int:
+    """Synchronises the stream; returns the latched device status (0 = ok)."""
+    return int(lib().ibp_check(meta, _stream(stream)))

@@ -1,0 +1,114 @@
+"""Helpers shared by the GPU parity tests: run the HIP path through the C ABI
+and the oracle on the same bytes, then compare element by element."""
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+import torch
+
+from lossless_tensor_compression_ibp_amd import ibp
+from oracle import oracle
+
+
+def say(msg: str):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def device():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    return torch.device("cuda:0")
+
+
+def as_rows(x: np.ndarray) -> np.ndarray:
+    x = np.ascontiguousarray(x)
+    return x.view(np.uint8).reshape(x.shape[0], -1)
+
+
+def to_gpu(a: np.ndarray, pinned: bool = False) -> torch.Tensor:
+    t = torch.from_numpy(np.ascontiguousarray(a))
+    if pinned:
+        p = torch.empty(t.shape, dtype=t.dtype, pin_memory=True)
+        p.copy_(t)
+        return p
+    return t.to(device())
+
+
+def empty_like_loc(shape, dtype, pinned: bool):
+    if pinned:
+        return torch.empty(shape, dtype=dtype, pin_memory=True)
+    return torch.empty(shape, dtype=dtype, device=device())
+
+
+def bitmask_bits(bm_words: np.ndarray, n: int) -> np.ndarray:
+    b = np.unpackbits(np.ascontiguousarray(bm_words).view(np.uint8), bitorder="little")
+    return b[:n]
+
+
+class Result:
+    pass
+
+
+def compare_codec(raw: np.ndarray, W: int, M: int, T: float, n_sample: int, *, sample: np.ndarray | None = None,
+                  src_pinned: bool = False, slots_pinned: bool = False, ids: np.ndarray | None = None,
+                  check_slots: bool = True, label: str = "") -> Result:
+    """Metadata, compress, decompress (and gather when ids is given) on the
+    GPU and in the oracle; asserts bit-exact agreement."""
+    n, L = raw.shape
+    say(f"[parity] {label} n={n} L={L} W={W} M={M} T={T} src_pinned={src_pinned} slots_pinned={slots_pinned}")
+    if sample is None:
+        sample = raw[:n_sample]
+    dev = device()
+    # metadata
+    g_sample = to_gpu(sample)
+    meta = ibp.ibp_build_metadata(g_sample, n_sample, L, W, M, T)
+    _, g_mask, g_bitval = ibp.ibp_meta_get(meta)
+    o_mask, o_bitval = oracle.build_metadata(sample, 8 * L, W, M, T, n_sample)
+    np.testing.assert_array_equal(g_mask.view(np.uint8), o_mask, err_msg="Mask differs")
+    np.testing.assert_array_equal(g_bitval.view(np.uint8), o_bitval, err_msg="Bitval differs")
+    # compress
+    src = to_gpu(raw, pinned=src_pinned)
+    slots = empty_like_loc((n, L), torch.uint8, slots_pinned)
+    bm = torch.zeros((n + 31) // 32, dtype=torch.int32, device=dev)
+    stored = torch.zeros(n, dtype=torch.int64, device=dev)
+    ibp.ibp_compress(meta, src, n, slots, bm, stored)
+    torch.cuda.synchronize()
+    o_slots, o_bm, o_stored = oracle.compress(raw, L, W, M, o_mask, o_bitval, n)
+    g_bm = bm.cpu().numpy().view(np.uint32)
+    np.testing.assert_array_equal(bitmask_bits(g_bm, n), bitmask_bits(o_bm, n), err_msg="bitmask differs")
+    g_stored = stored.cpu().numpy().astype(np.uint64)
+    np.testing.assert_array_equal(g_stored, o_stored, err_msg="stored bytes differ")
+    g_slots = slots.cpu().numpy()
+    if check_slots:
+        comp = bitmask_bits(o_bm, n).astype(bool)
+        for t in np.flatnonzero(comp):
+            k = int(o_stored[t])
+            if not np.array_equal(g_slots[t, :k], o_slots[t, :k]):
+                diff = np.flatnonzero(g_slots[t, :k] != o_slots[t, :k])
+                raise AssertionError(f"record of slot {t} differs at bytes {diff[:8]} (of {k})")
+        raw_rows = np.flatnonzero(~comp)
+        np.testing.assert_array_equal(g_slots[raw_rows], raw[raw_rows], err_msg="raw slots differ")
+    # decompress
+    out = torch.empty((n, L), dtype=torch.uint8, device=dev)
+    ibp.ibp_decompress(meta, slots, bm, n, out)
+    assert ibp.ibp_check(meta) == ibp.IBP_OK
+    np.testing.assert_array_equal(out.cpu().numpy(), raw, err_msg="decompress differs")
+    # the GPU decodes what the oracle encoded
+    o_slots_g = to_gpu(o_slots, pinned=slots_pinned)
+    o_bm_g = torch.from_numpy(o_bm.view(np.int32).copy()).to(dev)
+    out2 = torch.empty((n, L), dtype=torch.uint8, device=dev)
+    ibp.ibp_decompress(meta, o_slots_g, o_bm_g, n, out2)
+    assert ibp.ibp_check(meta) == ibp.IBP_OK
+    np.testing.assert_array_equal(out2.cpu().numpy(), raw, err_msg="decode of oracle slots differs")
+    if ids is not None:
+        g_ids = torch.from_numpy(np.ascontiguousarray(ids, dtype=np.int64)).to(dev)
+        gout = torch.empty((ids.size, L), dtype=torch.uint8, device=dev)
+        ibp.ibp_gather_decompress(meta, slots, n, bm, g_ids, gout)
+        assert ibp.ibp_check(meta) == ibp.IBP_OK
+        np.testing.assert_array_equal(gout.cpu().numpy(), raw[ids], err_msg="gather differs")
+    r = Result()
+    r.meta, r.slots, r.bm, r.stored, r.o_slots, r.o_bm, r.o_stored = meta, slots, bm, stored, o_slots, o_bm, o_stored
+    r.savings = 1.0 - float(o_stored.sum()) / raw.size
+    say(f"[parity] {label} ok savings={r.savings:.4f}")
+    return r
