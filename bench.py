@@ -180,7 +180,10 @@ def run_sparse_gnn(args) -> dict:
     def raw_step(i):
         ibp.ibp_gather_decompress(meta, host, n, zero_bm, ids_dev[i], out[i & 1])
 
-    raw_wall, raw_durs = timed(raw_step, args.steps, args.warmup)
+    if args.no_raw:
+        raw_wall = float("nan")
+    else:
+        raw_wall, _ = timed(raw_step, args.steps, args.warmup)
     h2d = h2d_ceiling()
     achieved = float(link_bytes.mean() / durs.mean() / GB)
     res = {
@@ -290,6 +293,7 @@ def main():
     ap.add_argument("--workload", default="sparse_gnn", choices=sorted(WORKLOADS))
     ap.add_argument("--small", action="store_true", help="scaled-down table (quick check)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--no-raw", action="store_true", help="skip the raw zero-copy gather comparison")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle decode")
     args = ap.parse_args()
     if args.gpus != 1:

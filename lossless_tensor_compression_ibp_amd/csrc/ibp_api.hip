@@ -20,6 +20,7 @@ namespace {
 
 constexpr uint32_t kLongTileWords = 1024;  // tile of a tensor longer than kMaxTileWords
 constexpr uint32_t kMaxPeriodBits = 1u << 20;
+constexpr uint64_t kLineWords = 16;  // 64-byte memory transaction
 
 struct Scratch {
     unsigned long long* status = nullptr;
@@ -236,8 +237,20 @@ Geo make_geo(const ibp_meta_s* h, bool aligned16) {
         g.tile_words = kLongTileWords;
         g.tiles_per_tensor = (g.n_words + kLongTileWords - 1) / kLongTileWords;
     }
-    uint64_t spec = (min_record_bits(h) + 31) / 32;
-    if (spec < g.hdr_words) spec = g.hdr_words;
+    // First read of a single-tile record: every record is at least min_words
+    // long, so the read is cut at the last 64-byte line boundary inside that
+    // prefix (the second read then starts on a line and no line travels
+    // twice).  When no record can be shorter than 15/16 of the slot, the whole
+    // slot is read at once instead of paying a second round trip.
+    const uint64_t min_words = (min_record_bits(h) + 31) / 32;
+    uint64_t spec;
+    if ((g.n_words - min_words) * 16 <= g.n_words) {
+        spec = g.n_words;
+    } else {
+        spec = (min_words / kLineWords) * kLineWords;
+        if (spec < kLineWords) spec = kLineWords;
+        if (spec < g.hdr_words) spec = g.hdr_words;
+    }
     if (aligned16) spec = (spec + 3) & ~3ull;
     if (spec > g.n_words) spec = g.n_words;
     g.spec_words = (uint32_t)spec;
