@@ -12,7 +12,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libibp.so")
-SOURCES = ["ibp_kernels.hip", "ibp_api.hip"]
+SOURCES = ["ibp_meta.hip", "ibp_encode.hip", "ibp_decode.hip", "ibp_api.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 FLAGS = [

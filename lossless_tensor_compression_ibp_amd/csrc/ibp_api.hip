@@ -36,6 +36,7 @@ struct Scratch {
 
 struct ibp_meta_s {
     int device = 0;
+    uint32_t cu_count = 0;
     ibp_params params{};
     uint32_t Mw = 0, Pc = 0, g = 0, log2g = 0, G = 0, Ne = 0;
     std::vector<uint32_t> mask_h, bitval_h;
@@ -139,10 +140,14 @@ ibp_status from_hip(hipError_t e) {
 ibp_status new_handle(const ibp_params* p, ibp_meta_s** out) {
     ibp_meta_s* h = new (std::nothrow) ibp_meta_s();
     if (!h) return IBP_ERR_NOMEM;
-    if (hipGetDevice(&h->device) != hipSuccess) {
+    int cus = 0;
+    if (hipGetDevice(&h->device) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, h->device) != hipSuccess) {
+        (void)hipGetLastError();
         delete h;
         return IBP_ERR_DEVICE;
     }
+    h->cu_count = cus > 0 ? (uint32_t)cus : 1u;
     h->params = *p;
     h->Mw = p->period_bits / 32;
     h->Pc = p->period_bits / p->chunk_bits;
@@ -457,8 +462,8 @@ static ibp_status decode_common(ibp_meta_t h, const void* slots, uint64_t n_slot
         ibp_status st = lookback_for(h, stream, tiles, launched_waves(tiles), n_out, &lb);
         if (st != IBP_OK) return st;
     }
-    return from_hip(launch_decode(h->tabs, geo, h->sum.max_runs, slots, n_slots, bitmask, ids, n_out, dst,
-                                  h->d_err, &lb, stream));
+    return from_hip(launch_decode(h->tabs, geo, h->sum.max_runs, h->sum.uniform != 0, slots, n_slots, bitmask,
+                                  ids, n_out, dst, h->d_err, &lb, h->cu_count, stream));
 }
 
 ibp_status ibp_decompress(ibp_meta_t h, const void* slots, const uint32_t* bitmask, uint64_t n_tensors,

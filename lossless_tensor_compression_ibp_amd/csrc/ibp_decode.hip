@@ -1,0 +1,488 @@
+// ibp_decode.hip -- step 3 of Invariant Bit Packing on gfx950: decompression.
+//
+// Method: FR summary ("Résumé Technique : Réduire le goulot d'étranglement de
+// la mémoire GPU par la compression sans perte pour le ML") and KO summary
+// ("Reducing the GPU Memory Bottleneck with Lossless Compression for ML --
+// Extended"), section "Algorithme central" / "핵심 알고리즘", step 3: the
+// lanes of a wave load a contiguous compressed segment together into a
+// shared workspace, scan the chunk sizes for each chunk's start bit, and
+// rebuild their chunks by putting Bitval's invariant bits back; loads are
+// issued ahead of the decode to hide link latency.  Section "Intégration au
+// système": a bitmask in GPU memory says which fixed-size slots hold a record,
+// and only the record prefix of a slot is read.
+//
+// Layout of the work: one wave64 decodes one tile (all of a tensor of at most
+// 2048 words, or a 1024-word tile of a longer one).  A lane rebuilds four
+// consecutive 32-bit words per step (256 words per wave step), so a step
+// costs one DPP scan and one dwordx4 store per lane.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "ibp_device.hpp"
+#include "ibp_internal.hpp"
+
+namespace ibp {
+
+// Rebuild words [w0, w0 + nw) of a tensor into out.  hdr: participation bits
+// of the tile (bit 0 = the tile's first chunk); pay: LDS words holding the
+// tile's kept bits, the first at bit `bit0` of pay[0].  Lanes past the end
+// contribute size 0.  With `vec`, out + w0 is 16-byte aligned.  MW4: the
+// period Mw is a multiple of 4 (and w0 too), so a lane's four positions are
+// consecutive and their table entries are read as one 16-byte vector.
+template <int RUNS, bool MW4, class Tab>
+__device__ __forceinline__ uint32_t decode_tile(const Tab& tab, const Geo& geo, const uint32_t* hdr,
+                                                const uint32_t* pay, uint32_t bit0, uint64_t w0,
+                                                uint32_t nw, uint32_t* __restrict__ out, bool vec) {
+    constexpr bool UNI = IsUniformTab<Tab>::value;
+    const uint32_t lane = lane_id();
+    const uint32_t Mw = geo.Mw;
+    const uint32_t lg = geo.log2g;
+    const uint32_t step_inc = (uint32_t)(4 * kWave) % Mw;
+    uint32_t pos0 = UNI ? 0u : (uint32_t)((w0 + 4ull * lane) % Mw);
+    uint32_t carry = bit0;
+    const uint32_t steps = (nw + 4 * kWave - 1) / (4 * kWave);
+    for (uint32_t s = 0; s < steps; ++s) {
+        const uint32_t lw0 = s * (4 * kWave) + 4 * lane;
+        const bool full = (s + 1) * (4 * kWave) <= nw;  // wave-uniform: no lane runs past the end
+        uint32_t pos[4], kd[4], bv[4];
+        uint32_t rr[RUNS > 0 ? RUNS : 1][4];
+        if constexpr (UNI) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                pos[j] = 0;
+                kd[j] = tab.kdw(0);
+                bv[j] = tab.bw(0);
+            }
+        } else if constexpr (MW4) {
+            const u32x4 k4 = tab.kdw4(pos0), b4 = tab.bw4(pos0);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                pos[j] = pos0 + j;
+                kd[j] = k4[j];
+                bv[j] = b4[j];
+            }
+        } else {
+            pos[0] = pos0;
+#pragma unroll
+            for (int j = 1; j < 4; ++j) pos[j] = (pos[j - 1] + 1 == Mw) ? 0u : pos[j - 1] + 1;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                kd[j] = tab.kdw(pos[j]);
+                bv[j] = tab.bw(pos[j]);
+            }
+        }
+        const uint32_t c0 = lw0 >> lg;
+        const uint32_t hsh = hdr[c0 >> 5] >> (c0 & 31u);
+        uint32_t p[4], size[4];
+        uint32_t tot = 0;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            p[j] = (hsh >> ((uint32_t)j >> lg)) & 1u;
+            const uint32_t sz = p[j] ? 32u - (kd[j] & 63u) : 32u;
+            size[j] = (full || lw0 + j < nw) ? sz : 0u;
+            tot += size[j];
+        }
+        const uint32_t incl = wave_incl_scan(tot);
+        uint32_t off = carry + incl - tot;
+        carry += lane_value(incl, kWave - 1);
+        // run masks (and shifts of runs past the third) of the lane's four positions
+        if constexpr (MW4 && !UNI) {
+#pragma unroll
+            for (int r = 0; r < RUNS; ++r) {
+                const u32x4 v = tab.rw4(r, pos0);
+#pragma unroll
+                for (int j = 0; j < 4; ++j) rr[r][j] = v[j];
+            }
+        } else {
+#pragma unroll
+            for (int r = 0; r < RUNS; ++r)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) rr[r][j] = tab.rw(r, pos[j]);
+        }
+        uint32_t x[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const uint32_t q = off >> 5;
+            const uint32_t f = funnel(pay[q + 1], pay[q], off);
+            uint32_t dep = bv[j];
+#pragma unroll
+            for (int r = 0; r < RUNS; ++r) dep |= (f << (tab.dw(r, pos[j], kd[j]) & 31u)) & rr[r][j];
+            x[j] = p[j] ? dep : f;
+            off += size[j];
+        }
+        if (vec && (full || lw0 + 3 < nw)) {
+            __builtin_nontemporal_store(u32x4{x[0], x[1], x[2], x[3]}, reinterpret_cast<u32x4*>(out + w0 + lw0));
+        } else {
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                if (lw0 + j < nw) out[w0 + lw0 + j] = x[j];
+        }
+        if constexpr (!UNI) {
+            pos0 += step_inc;
+            if (pos0 >= Mw) pos0 -= Mw;
+        }
+    }
+    return carry;
+}
+
+// LDS image of the tables: b, kd, dx rows, r rows (stride Mw), then the
+// header bit planes.  Copied once per workgroup.
+template <int RUNS>
+__device__ __forceinline__ void stage_tables(const Tables& t, uint32_t Mw, uint32_t n_planes_words,
+                                             bool per_position, uint32_t* lds) {
+    const uint32_t rows = per_position ? tab_rows(RUNS) : 0u;
+    for (uint32_t i = threadIdx.x; i < rows * Mw; i += blockDim.x) {
+        const uint32_t row = i / Mw, pos = i - row * Mw;
+        uint32_t v;
+        if (row == 0)
+            v = t.b[pos];
+        else if (row == 1)
+            v = t.kd[pos];
+        else if (row < 2 + dx_rows(RUNS))
+            v = t.dx[(row - 2) * Mw + pos];
+        else
+            v = t.r[(row - 2 - dx_rows(RUNS)) * Mw + pos];
+        lds[i] = v;
+    }
+    uint32_t* pl = lds + rows * Mw;
+    for (uint32_t i = threadIdx.x; i < n_planes_words; i += blockDim.x) pl[i] = t.planes[i];
+}
+
+// ---------------------------------------------------------------------------
+// Tensors of at most kMaxTileWords words with 16-byte aligned slots and
+// output: persistent workgroups, tables staged once in LDS, and per wave a
+// software pipeline over its tiles.  All ids and bitmask bits of a wave's
+// next 64 tiles are fetched first (one lane per tile); then the first read of
+// tile k+1 (the whole slot of a raw tensor, the first spec_words of a record)
+// is in flight in registers while tile k is decoded.
+// ---------------------------------------------------------------------------
+template <int RUNS, bool UNI, bool MW4, int STAGE>
+__global__ __launch_bounds__(256) void k_decode_small(Tables t, Geo geo, const uint8_t* __restrict__ slots,
+                                                      uint64_t n_slots, const uint32_t* __restrict__ bitmask,
+                                                      const int64_t* __restrict__ ids, uint64_t n_out,
+                                                      uint8_t* __restrict__ dst, uint32_t* err,
+                                                      uint32_t buf_words) {
+    extern __shared__ uint32_t smem[];
+    const uint32_t lane = lane_id();
+    const uint32_t wib = uniform(threadIdx.x / kWave);
+    const uint32_t Mw = geo.Mw;
+    // LDS: [per-position tables (not for uniform metadata)][bit planes][wave buffers]
+    const uint32_t tab_words = UNI ? 0u : tab_rows(RUNS) * Mw;
+    const uint32_t planes_words = (geo.Pc / geo.G) * (uint32_t)kPlanes;
+    stage_tables<RUNS>(t, Mw, planes_words, !UNI, smem);
+    __syncthreads();
+    const uint32_t* planes = smem + tab_words;
+    uint32_t* buf = smem + ((tab_words + planes_words + 3u) & ~3u) + wib * buf_words;
+    const TabArrays ta{smem, smem + Mw, smem + 2 * Mw, smem + (2 + dx_rows(RUNS)) * Mw, Mw};
+    TabUniform<RUNS> tu;
+    if (UNI) tu = load_uniform<RUNS>(t, Mw);
+
+    const uint32_t nwords = (uint32_t)geo.n_words;
+    const uint32_t n4_raw = nwords >> 2;
+    const uint32_t n4_spec = geo.spec_words >> 2;
+    const uint32_t hw = (uint32_t)geo.hdr_words;
+    const uint64_t stride = (uint64_t)gridDim.x * kWavesPerBlock;
+    const uint64_t first = (uint64_t)blockIdx.x * kWavesPerBlock + wib;
+    if (first >= n_out) return;
+    const uint64_t my_tiles = (n_out - first + stride - 1) / stride;
+
+    u32x4 st[STAGE];
+    for (uint64_t base = 0; base < my_tiles; base += kWave) {
+        const uint32_t cnt = (uint32_t)min((uint64_t)kWave, my_tiles - base);
+        // lane k: id and bitmask bit of tile base + k
+        int64_t my_tensor = -1;
+        uint32_t my_comp = 0;
+        if (lane < cnt) {
+            const uint64_t oi = first + (base + lane) * stride;
+            const int64_t id = ids ? ids[oi] : (int64_t)oi;
+            if (id >= 0 && (uint64_t)id < n_slots) {
+                my_tensor = id;
+                my_comp = (bitmask[(uint64_t)id >> 5] >> ((uint64_t)id & 31)) & 1u;
+            }
+        }
+        if (ballot(lane < cnt && my_tensor < 0)) latch_error(err, kErrRange);
+        const uint32_t t_lo = (uint32_t)my_tensor, t_hi = (uint32_t)((uint64_t)my_tensor >> 32);
+
+        auto tensor_of = [&](uint32_t k) __attribute__((always_inline)) -> int64_t {
+            return (int64_t)(((uint64_t)lane_value(t_hi, k) << 32) | lane_value(t_lo, k));
+        };
+        auto issue = [&](uint32_t k) __attribute__((always_inline)) {
+            const int64_t tn = tensor_of(k);
+            if (tn < 0) return;
+            const u32x4* s4 = reinterpret_cast<const u32x4*>(slots + (uint64_t)tn * geo.L);
+            const uint32_t n4 = lane_value(my_comp, k) ? n4_spec : n4_raw;
+#pragma unroll
+            for (int r = 0; r < STAGE; ++r) {
+                const uint32_t i = lane + (uint32_t)r * kWave;
+                if (i < n4) st[r] = __builtin_nontemporal_load(s4 + i);
+            }
+        };
+
+        issue(0);
+        for (uint32_t k = 0; k < cnt; ++k) {
+            const int64_t tn = tensor_of(k);
+            const uint32_t comp = lane_value(my_comp, k);
+            const uint64_t oi = first + (base + k) * stride;
+            uint32_t* out = reinterpret_cast<uint32_t*>(dst + oi * geo.L);
+            const uint32_t n4 = comp ? n4_spec : n4_raw;
+            if (tn >= 0) {
+                if (comp) {
+#pragma unroll
+                    for (int r = 0; r < STAGE; ++r) {
+                        const uint32_t i = lane + (uint32_t)r * kWave;
+                        if (i < n4) reinterpret_cast<u32x4*>(buf)[i] = st[r];
+                    }
+                } else {
+#pragma unroll
+                    for (int r = 0; r < STAGE; ++r) {
+                        const uint32_t i = lane + (uint32_t)r * kWave;
+                        if (i < n4) __builtin_nontemporal_store(st[r], reinterpret_cast<u32x4*>(out) + i);
+                    }
+                }
+            }
+            if (k + 1 < cnt) issue(k + 1);
+            if (tn < 0 || !comp) continue;
+
+            __builtin_amdgcn_wave_barrier();
+            bool bad_pad;
+            const uint32_t rem = header_removed_bits(planes, geo, buf, 0, hw, &bad_pad);
+            const uint64_t R = 32ull * hw + 32ull * nwords - rem;
+            const uint32_t words = (uint32_t)((R + 31) / 32);
+            if (bad_pad || 4ull * words >= geo.L) {
+                latch_error(err, kErrCorrupt);
+                continue;
+            }
+            uint32_t have = geo.spec_words;
+            if (words > have) {
+                const uint32_t upto = min((words + 3u) & ~3u, nwords);
+                load_words_to_lds(reinterpret_cast<const uint32_t*>(slots + (uint64_t)tn * geo.L), have, upto,
+                                  buf + have, true);
+                have = upto;
+            }
+            if (lane == 0) buf[have] = 0;
+            __builtin_amdgcn_wave_barrier();
+            if (UNI)
+                decode_tile<RUNS, MW4>(tu, geo, buf, buf + hw, 0, 0, nwords, out, true);
+            else
+                decode_tile<RUNS, MW4>(ta, geo, buf, buf + hw, 0, 0, nwords, out, true);
+            __builtin_amdgcn_wave_barrier();
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// General tiles: tensors longer than one tile (decoupled look-back between
+// the tiles of a tensor) and single-tile tensors whose slots or output are
+// not 16-byte aligned.  One wave per tile, tables read from global memory.
+// ---------------------------------------------------------------------------
+template <int RUNS, bool UNI, bool MULTI>
+__global__ __launch_bounds__(256) void k_decode_tiles(Tables t, Geo geo, const uint8_t* __restrict__ slots,
+                                                      uint64_t n_slots, const uint32_t* __restrict__ bitmask,
+                                                      const int64_t* __restrict__ ids, uint64_t n_out,
+                                                      uint8_t* __restrict__ dst, uint32_t* err, LookBack lb,
+                                                      uint32_t lds_words) {
+    extern __shared__ uint32_t smem[];
+    const uint32_t lane = lane_id();
+    uint32_t* lds = smem + (threadIdx.x / kWave) * lds_words;
+
+    uint64_t tile;
+    if (MULTI) {
+        uint32_t tk = 0;
+        if (lane == 0) tk = atomicAdd(lb.ticket, 1u);
+        tile = (uint32_t)(uniform(tk) - lb.ticket_base);
+    } else {
+        tile = (uint64_t)blockIdx.x * kWavesPerBlock + threadIdx.x / kWave;
+    }
+    const uint64_t tpt = MULTI ? geo.tiles_per_tensor : 1;
+    if (tile >= n_out * tpt) return;
+    const uint64_t oi = MULTI ? tile / tpt : tile;
+    const uint64_t local = MULTI ? tile - oi * tpt : 0;
+
+    const int64_t tensor = ids ? (int64_t)uniform64((uint64_t)ids[oi]) : (int64_t)oi;
+    if (tensor < 0 || (uint64_t)tensor >= n_slots) {
+        latch_error(err, kErrRange);
+        return;
+    }
+    const uint32_t* src = reinterpret_cast<const uint32_t*>(slots + (uint64_t)tensor * geo.L);
+    uint32_t* out = reinterpret_cast<uint32_t*>(dst + oi * geo.L);
+    const uint64_t w0 = local * geo.tile_words;
+    const uint32_t nw = (uint32_t)min((uint64_t)geo.tile_words, geo.n_words - w0);
+    const bool vec = geo.aligned16 != 0;
+    const bool comp = (uniform(bitmask[(uint64_t)tensor >> 5]) >> ((uint64_t)tensor & 31)) & 1u;
+    if (!comp) {
+        copy_words(src, out, w0, nw, vec);
+        return;
+    }
+    TabArrays ta{t.b, t.kd, t.dx, t.r, geo.Mw};
+    TabUniform<RUNS> tu;
+    if (UNI) tu = load_uniform<RUNS>(t, geo.Mw);
+
+    if (!MULTI) {
+        const uint32_t hw = (uint32_t)geo.hdr_words;
+        const uint32_t cap = (uint32_t)geo.n_words;
+        uint32_t have = geo.spec_words;
+        load_words_to_lds(src, 0, have, lds, vec);
+        __builtin_amdgcn_wave_barrier();
+        bool bad_pad;
+        const uint32_t rem = header_removed_bits(t.planes, geo, lds, 0, hw, &bad_pad);
+        const uint64_t R = 32ull * hw + 32ull * geo.n_words - rem;
+        const uint64_t words = (R + 31) / 32;
+        if (bad_pad || 4 * words >= geo.L) {
+            latch_error(err, kErrCorrupt);
+            return;
+        }
+        if (words > have) {
+            const uint32_t need = vec ? (uint32_t)((words + 3) & ~3ull) : (uint32_t)words;
+            const uint32_t upto = min(need, cap);
+            load_words_to_lds(src, have, upto, lds + have, vec);
+            have = upto;
+        }
+        if (lane == 0) lds[have] = 0;
+        __builtin_amdgcn_wave_barrier();
+        if (UNI)
+            decode_tile<RUNS, false>(tu, geo, lds, lds + hw, 0, 0, nw, out, vec);
+        else
+            decode_tile<RUNS, false>(ta, geo, lds, lds + hw, 0, 0, nw, out, vec);
+        return;
+    }
+
+    // Tile of a long tensor: header slice, look-back, then the payload slice.
+    const uint64_t c0 = w0 >> geo.log2g;
+    const uint32_t nch = nw >> geo.log2g;
+    const uint32_t hw_t = (nch + 31) / 32;
+    const uint64_t hw0 = c0 >> 5;
+    uint32_t* hdr = lds;
+    uint32_t* pay = lds + 64;
+    for (uint32_t j = lane; j < hw_t; j += kWave) hdr[j] = src[hw0 + j];
+    __builtin_amdgcn_wave_barrier();
+    bool bad_pad;
+    const uint32_t rem = header_removed_bits(t.planes, geo, hdr, hw0, hw_t, &bad_pad);
+    const uint64_t agg = 32ull * nw - rem;
+    const uint64_t S = lookback_exclusive(lb.status, oi * tpt, local, agg, 32ull * geo.hdr_words, lb.epoch);
+    const uint64_t E = S + agg;
+    const bool last = local == tpt - 1;
+    if (bad_pad || E > 8ull * geo.L || (last && 4 * ((E + 31) / 32) >= geo.L)) {
+        latch_error(err, kErrCorrupt);
+        return;
+    }
+    uint64_t a = S >> 5, b = (E + 31) >> 5;
+    if (vec) {
+        a &= ~3ull;
+        b = (b + 3) & ~3ull;
+    }
+    b = min(b, geo.n_words);
+    load_words_to_lds(src, a, b, pay, vec);
+    if (lane == 0) pay[b - a] = 0;
+    __builtin_amdgcn_wave_barrier();
+    if (UNI)
+        decode_tile<RUNS, false>(tu, geo, hdr, pay, (uint32_t)(S - 32 * a), w0, nw, out, vec && (w0 & 3) == 0);
+    else
+        decode_tile<RUNS, false>(ta, geo, hdr, pay, (uint32_t)(S - 32 * a), w0, nw, out, vec && (w0 & 3) == 0);
+}
+
+// ---------------------------------------------------------------------------
+// Launch.
+// ---------------------------------------------------------------------------
+static uint32_t runs_bucket(uint32_t runs) {
+    if (runs <= 4) return runs;
+    if (runs <= 8) return 8;
+    return 16;
+}
+
+// LDS bytes k_decode_small needs per workgroup, or 0 when it cannot run
+// (tables or planes too large for LDS).
+static size_t small_lds_bytes(const Geo& geo, int runs, bool uni, uint32_t* buf_words) {
+    *buf_words = ((uint32_t)geo.n_words + 8 + 3) & ~3u;
+    const uint64_t tab = uni ? 0 : (uint64_t)tab_rows(runs) * geo.Mw * 4;
+    const uint64_t planes = (uint64_t)(geo.Pc / geo.G) * kPlanes * 4;
+    if (tab > kMaxLdsTableBytes || planes > kMaxLdsPlaneBytes) return 0;
+    const uint64_t head = ((tab + planes) + 15) & ~15ull;
+    const uint64_t total = head + (uint64_t)kWavesPerBlock * *buf_words * 4;
+    return total <= kMaxLdsPerBlock ? (size_t)total : 0;
+}
+
+template <int RUNS, bool UNI>
+static hipError_t launch_small(const Tables& t, const Geo& geo, const void* slots, uint64_t n_slots,
+                               const uint32_t* bitmask, const int64_t* ids, uint64_t n_out, void* dst,
+                               uint32_t* err, uint32_t cu_count, size_t shm, uint32_t buf_words, hipStream_t s) {
+    uint32_t per_cu = (uint32_t)(kLdsPerCu / shm);
+    if (per_cu > 8) per_cu = 8;
+    if (per_cu < 1) per_cu = 1;
+    const uint64_t want = (n_out + kWavesPerBlock - 1) / kWavesPerBlock;
+    const uint64_t cap = (uint64_t)cu_count * per_cu;
+    const dim3 grid((uint32_t)(want < cap ? want : cap));
+    const dim3 block(kWave * kWavesPerBlock);
+    const uint8_t* sl = static_cast<const uint8_t*>(slots);
+    uint8_t* d = static_cast<uint8_t*>(dst);
+    const uint32_t stage = (uint32_t)((geo.n_words + 4 * kWave - 1) / (4 * kWave));
+#define IBP_SMALL(S)                                                                                      \
+    if (geo.Mw % 4 == 0)                                                                                  \
+        hipLaunchKernelGGL((k_decode_small<RUNS, UNI, true, S>), grid, block, shm, s, t, geo, sl, n_slots,  \
+                           bitmask, ids, n_out, d, err, buf_words);                                       \
+    else                                                                                                  \
+        hipLaunchKernelGGL((k_decode_small<RUNS, UNI, false, S>), grid, block, shm, s, t, geo, sl, n_slots, \
+                           bitmask, ids, n_out, d, err, buf_words)
+    if (stage <= 1)
+        IBP_SMALL(1);
+    else if (stage <= 2)
+        IBP_SMALL(2);
+    else if (stage <= 4)
+        IBP_SMALL(4);
+    else
+        IBP_SMALL(8);
+#undef IBP_SMALL
+    return hipGetLastError();
+}
+
+template <int RUNS, bool UNI, bool MULTI>
+static hipError_t launch_tiles(const Tables& t, const Geo& geo, const void* slots, uint64_t n_slots,
+                               const uint32_t* bitmask, const int64_t* ids, uint64_t n_out, void* dst,
+                               uint32_t* err, const LookBack& lb, hipStream_t s) {
+    const uint32_t lds_words = MULTI ? 64 + geo.tile_words + 8 : (uint32_t)geo.n_words + 8;
+    const uint64_t tiles = n_out * geo.tiles_per_tensor;
+    const dim3 grid((uint32_t)((tiles + kWavesPerBlock - 1) / kWavesPerBlock));
+    const dim3 block(kWave * kWavesPerBlock);
+    const size_t shm = (size_t)lds_words * 4 * kWavesPerBlock;
+    hipLaunchKernelGGL((k_decode_tiles<RUNS, UNI, MULTI>), grid, block, shm, s, t, geo,
+                       static_cast<const uint8_t*>(slots), n_slots, bitmask, ids, n_out,
+                       static_cast<uint8_t*>(dst), err, lb, lds_words);
+    return hipGetLastError();
+}
+
+template <int RUNS, bool UNI>
+static hipError_t launch_decode_r(const Tables& t, const Geo& geo, const void* slots, uint64_t n_slots,
+                                  const uint32_t* bitmask, const int64_t* ids, uint64_t n_out, void* dst,
+                                  uint32_t* err, const LookBack* lb, uint32_t cu_count, hipStream_t s) {
+    if (geo.tiles_per_tensor > 1)
+        return launch_tiles<RUNS, UNI, true>(t, geo, slots, n_slots, bitmask, ids, n_out, dst, err, *lb, s);
+    uint32_t buf_words = 0;
+    const size_t shm = small_lds_bytes(geo, RUNS, UNI, &buf_words);
+    if (geo.aligned16 && shm)
+        return launch_small<RUNS, UNI>(t, geo, slots, n_slots, bitmask, ids, n_out, dst, err, cu_count, shm,
+                                       buf_words, s);
+    return launch_tiles<RUNS, UNI, false>(t, geo, slots, n_slots, bitmask, ids, n_out, dst, err, LookBack{}, s);
+}
+
+hipError_t launch_decode(const Tables& t, const Geo& geo, uint32_t runs, bool uniform_meta, const void* slots,
+                         uint64_t n_slots, const uint32_t* bitmask, const int64_t* ids, uint64_t n_out,
+                         void* dst, uint32_t* err, const LookBack* lb, uint32_t cu_count, hipStream_t s) {
+    if (n_out == 0) return hipSuccess;
+#define IBP_R(R)                                                                                      \
+    return uniform_meta                                                                                \
+               ? launch_decode_r<R, true>(t, geo, slots, n_slots, bitmask, ids, n_out, dst, err, lb,    \
+                                          cu_count, s)                                                 \
+               : launch_decode_r<R, false>(t, geo, slots, n_slots, bitmask, ids, n_out, dst, err, lb,   \
+                                           cu_count, s)
+    switch (runs_bucket(runs)) {
+        case 0: IBP_R(0);
+        case 1: IBP_R(1);
+        case 2: IBP_R(2);
+        case 3: IBP_R(3);
+        case 4: IBP_R(4);
+        case 8: IBP_R(8);
+        default: IBP_R(16);
+    }
+#undef IBP_R
+}
+
+}  // namespace ibp

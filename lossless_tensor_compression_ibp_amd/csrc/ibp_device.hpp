@@ -8,6 +8,8 @@
 
 namespace ibp {
 
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
 __device__ __forceinline__ uint32_t lane_id() { return threadIdx.x & (kWave - 1); }
 
 __device__ __forceinline__ uint32_t uniform(uint32_t v) {
@@ -113,6 +115,178 @@ __device__ __forceinline__ uint32_t removed_bits(const Tables& t, const Geo& g, 
     uint32_t s = 0;
     for (uint32_t q = 0; q < g.np; ++q) s += (uint32_t)__builtin_popcount(hword & pl[q]) << q;
     return s;
+}
+
+// ---------------------------------------------------------------------------
+// Table accessors.  The per-position tables (structure of arrays, stride Mw)
+// are read either from arrays (staged in LDS or left in global memory) or,
+// when every position holds the same Mask/Bitval word, from wave-uniform
+// registers.
+// ---------------------------------------------------------------------------
+struct TabArrays {
+    const uint32_t* b;
+    const uint32_t* kd;
+    const uint32_t* dx;
+    const uint32_t* r;
+    uint32_t Mw;
+    __device__ __forceinline__ uint32_t kdw(uint32_t pos) const { return kd[pos]; }
+    __device__ __forceinline__ uint32_t bw(uint32_t pos) const { return b[pos]; }
+    __device__ __forceinline__ uint32_t rw(int j, uint32_t pos) const { return r[(uint32_t)j * Mw + pos]; }
+    __device__ __forceinline__ uint32_t dw(int j, uint32_t pos, uint32_t kdv) const {
+        if (j < 3) return kdv >> (8 * (j + 1));
+        return dx[(uint32_t)((j - 3) >> 2) * Mw + pos] >> (8 * ((j - 3) & 3));
+    }
+    // four consecutive positions starting at a multiple of 4 (Mw % 4 == 0)
+    __device__ __forceinline__ u32x4 kdw4(uint32_t pos) const { return *reinterpret_cast<const u32x4*>(kd + pos); }
+    __device__ __forceinline__ u32x4 bw4(uint32_t pos) const { return *reinterpret_cast<const u32x4*>(b + pos); }
+    __device__ __forceinline__ u32x4 rw4(int j, uint32_t pos) const {
+        return *reinterpret_cast<const u32x4*>(r + (uint32_t)j * Mw + pos);
+    }
+    __device__ __forceinline__ u32x4 dxw4(int q, uint32_t pos) const {
+        return *reinterpret_cast<const u32x4*>(dx + (uint32_t)q * Mw + pos);
+    }
+};
+
+template <int RUNS>
+struct TabUniform {
+    uint32_t kdv, bv;
+    uint32_t r[RUNS > 0 ? RUNS : 1];
+    uint32_t d[RUNS > 0 ? RUNS : 1];
+    __device__ __forceinline__ uint32_t kdw(uint32_t) const { return kdv; }
+    __device__ __forceinline__ uint32_t bw(uint32_t) const { return bv; }
+    __device__ __forceinline__ uint32_t rw(int j, uint32_t) const { return r[j]; }
+    __device__ __forceinline__ uint32_t dw(int j, uint32_t, uint32_t) const { return d[j]; }
+};
+
+template <class Tab>
+struct IsUniformTab { static constexpr bool value = false; };
+template <int R>
+struct IsUniformTab<TabUniform<R>> { static constexpr bool value = true; };
+
+// Position-0 entries of the global tables, moved to scalar registers.
+template <int RUNS>
+__device__ __forceinline__ TabUniform<RUNS> load_uniform(const Tables& t, uint32_t Mw) {
+    TabUniform<RUNS> u;
+    u.kdv = uniform(t.kd[0]);
+    u.bv = uniform(t.b[0]);
+#pragma unroll
+    for (int j = 0; j < RUNS; ++j) {
+        u.r[j] = uniform(t.r[(uint32_t)j * Mw]);
+        u.d[j] = j < 3 ? (u.kdv >> (8 * (j + 1))) & 31u
+                       : (uniform(t.dx[(uint32_t)((j - 3) >> 2) * Mw]) >> (8 * ((j - 3) & 3))) & 31u;
+    }
+    return u;
+}
+
+template <int RUNS, class Tab>
+__device__ __forceinline__ uint32_t deposit_t(const Tab& tab, uint32_t pos, uint32_t kdv, uint32_t f) {
+    uint32_t x = tab.bw(pos);
+#pragma unroll
+    for (int j = 0; j < RUNS; ++j) x |= (f << (tab.dw(j, pos, kdv) & 31u)) & tab.rw(j, pos);
+    return x;
+}
+
+template <int RUNS, class Tab>
+__device__ __forceinline__ uint32_t extract_t(const Tab& tab, uint32_t pos, uint32_t kdv, uint32_t x) {
+    uint32_t f = 0;
+#pragma unroll
+    for (int j = 0; j < RUNS; ++j) f |= (x & tab.rw(j, pos)) >> (tab.dw(j, pos, kdv) & 31u);
+    return f;
+}
+
+// Words of LDS the per-position arrays of RUNS runs take (b, kd, dx rows, r rows).
+__host__ __device__ constexpr uint32_t dx_rows(int runs) { return runs > 3 ? (uint32_t)(runs - 3 + 3) / 4 : 0u; }
+__host__ __device__ constexpr uint32_t tab_rows(int runs) { return 2u + dx_rows(runs) + (uint32_t)runs; }
+
+// ---------------------------------------------------------------------------
+// Memory movement helpers (one wave).
+// ---------------------------------------------------------------------------
+
+// Copy global words [a, b) of `src` into lds[0 .. b-a).  With `vec`, a and b
+// are multiples of 4 and `src` is 16-byte aligned: dwordx4 loads, four in
+// flight per lane before the LDS writes.
+__device__ __forceinline__ void load_words_to_lds(const uint32_t* __restrict__ src, uint64_t a,
+                                                  uint64_t b, uint32_t* lds, bool vec) {
+    const uint32_t lane = lane_id();
+    if (vec) {
+        const uint4* s4 = reinterpret_cast<const uint4*>(src + a);
+        uint4* l4 = reinterpret_cast<uint4*>(lds);
+        const uint32_t n4 = (uint32_t)((b - a) >> 2);
+        uint32_t i = lane;
+        for (; i + 3 * kWave < n4; i += 4 * kWave) {
+            uint4 v0 = s4[i], v1 = s4[i + kWave], v2 = s4[i + 2 * kWave], v3 = s4[i + 3 * kWave];
+            l4[i] = v0;
+            l4[i + kWave] = v1;
+            l4[i + 2 * kWave] = v2;
+            l4[i + 3 * kWave] = v3;
+        }
+        for (; i < n4; i += kWave) l4[i] = s4[i];
+    } else {
+        const uint32_t n = (uint32_t)(b - a);
+        for (uint32_t i = lane; i < n; i += kWave) lds[i] = src[a + i];
+    }
+}
+
+// Copy words [w0, w0 + nw) of a raw tensor.
+__device__ __forceinline__ void copy_words(const uint32_t* __restrict__ src, uint32_t* __restrict__ dst,
+                                           uint64_t w0, uint32_t nw, bool vec) {
+    const uint32_t lane = lane_id();
+    if (vec && (w0 & 3) == 0 && (nw & 3) == 0) {
+        const uint4* s4 = reinterpret_cast<const uint4*>(src + w0);
+        uint4* d4 = reinterpret_cast<uint4*>(dst + w0);
+        const uint32_t n4 = nw >> 2;
+        uint32_t i = lane;
+        for (; i + 3 * kWave < n4; i += 4 * kWave) {
+            uint4 v0 = s4[i], v1 = s4[i + kWave], v2 = s4[i + 2 * kWave], v3 = s4[i + 3 * kWave];
+            d4[i] = v0;
+            d4[i + kWave] = v1;
+            d4[i + 2 * kWave] = v2;
+            d4[i + 3 * kWave] = v3;
+        }
+        for (; i < n4; i += kWave) d4[i] = s4[i];
+    } else {
+        for (uint32_t i = lane; i < nw; i += kWave) dst[w0 + i] = src[w0 + i];
+    }
+}
+
+__device__ __forceinline__ void latch_error(uint32_t* err, uint32_t code) {
+    if (lane_id() == 0) atomicCAS(err, 0u, code);
+}
+
+// Removed bits of header word `hword` (global header word index j): the sum
+// over its set participation bits of that chunk's k, from the bit planes of
+// entry ((32 j) mod Pc) / G.
+__device__ __forceinline__ uint32_t removed_bits_pl(const uint32_t* planes, const Geo& g, uint64_t j,
+                                                    uint32_t hword) {
+    const uint32_t e = (uint32_t)(((32ull * j) % g.Pc) / g.G);
+    const uint32_t* pl = planes + e * (uint32_t)kPlanes;
+    uint32_t s = 0;
+    for (uint32_t q = 0; q < g.np; ++q) s += (uint32_t)__builtin_popcount(hword & pl[q]) << q;
+    return s;
+}
+
+// Sum over the tile's header words [hw0, hw0 + hw_t) of the removed bits;
+// flags non-zero header padding (bits past the tensor's last chunk).
+__device__ __forceinline__ uint32_t header_removed_bits(const uint32_t* planes, const Geo& geo,
+                                                        const uint32_t* hdr, uint64_t hw0, uint32_t hw_t,
+                                                        bool* bad_pad) {
+    const uint32_t lane = lane_id();
+    uint32_t rem = 0;
+    bool bad = false;
+    for (uint32_t j = lane; j < hw_t; j += kWave) {
+        uint32_t h = hdr[j];
+        const uint64_t gj = hw0 + j;
+        if (gj == geo.hdr_words - 1) {
+            const uint32_t valid = (uint32_t)(geo.n_chunks - 32ull * gj);
+            if (valid < 32) {
+                if (h >> valid) bad = true;
+                h &= (1u << valid) - 1u;
+            }
+        }
+        rem += removed_bits_pl(planes, geo, gj, h);
+    }
+    *bad_pad = ballot(bad) != 0;
+    return wave_sum(rem);
 }
 
 // ---------------------------------------------------------------------------

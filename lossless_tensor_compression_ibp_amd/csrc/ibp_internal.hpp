@@ -12,6 +12,10 @@ constexpr int kWavesPerBlock = 4;   // independent waves per workgroup
 constexpr int kMaxRuns = 16;        // a 32-bit word has at most 16 runs of ones
 constexpr int kPlanes = 11;         // bit planes of a per-chunk k (k <= 1024)
 constexpr uint32_t kMaxTileWords = 2048;  // largest tile one wave owns
+constexpr uint64_t kMaxLdsTableBytes = 48 * 1024;  // per-position tables staged in LDS
+constexpr uint64_t kMaxLdsPlaneBytes = 16 * 1024;  // header bit planes staged in LDS
+constexpr uint64_t kMaxLdsPerBlock = 64 * 1024;    // dynamic LDS of one workgroup
+constexpr uint64_t kLdsPerCu = 160 * 1024;         // gfx950 LDS per compute unit
 
 // Derived per-position tables in device memory (structure of arrays; every
 // array has Mw entries unless stated).  Position i of the metadata period is
@@ -76,9 +80,8 @@ hipError_t launch_tables(const uint32_t* mask, const uint32_t* bitval, uint32_t 
 hipError_t launch_encode(const Tables& t, const Geo& geo, uint32_t runs, const void* src,
                          uint64_t n_tensors, void* slots, uint32_t* bitmask, uint64_t* stored,
                          const LookBack* lb, hipStream_t s);
-hipError_t launch_decode(const Tables& t, const Geo& geo, uint32_t runs, const void* slots,
-                         uint64_t n_slots, const uint32_t* bitmask, const int64_t* ids,
-                         uint64_t n_out, void* dst, uint32_t* err, const LookBack* lb,
-                         hipStream_t s);
+hipError_t launch_decode(const Tables& t, const Geo& geo, uint32_t runs, bool uniform_meta, const void* slots,
+                         uint64_t n_slots, const uint32_t* bitmask, const int64_t* ids, uint64_t n_out,
+                         void* dst, uint32_t* err, const LookBack* lb, uint32_t cu_count, hipStream_t s);
 
 }  // namespace ibp

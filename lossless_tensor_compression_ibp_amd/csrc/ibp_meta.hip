@@ -1,0 +1,178 @@
+// ibp_meta.hip -- step 1 of Invariant Bit Packing on gfx950: preprocessing.
+//
+// Method: FR summary ("Résumé Technique : Réduire le goulot d'étranglement de
+// la mémoire GPU par la compression sans perte pour le ML") and KO summary
+// ("Reducing the GPU Memory Bottleneck with Lossless Compression for ML --
+// Extended"), section "Algorithme central" / "핵심 알고리즘", step 1: a batch
+// of tensors is scanned for bit positions that hold the same value in at
+// least a fraction T of them; the result is a fixed-size Mask and Bitval,
+// kept in GPU memory and reused for the whole dataset.  Also the derived
+// tables the encode and decode kernels read.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "ibp_device.hpp"
+#include "ibp_internal.hpp"
+
+namespace ibp {
+
+// Per-position histogram.  The sample is a sequence of observations of Mw
+// words; thread g of G (G a multiple of Mw) visits words g, g+G, g+2G, ...,
+// which all sit at position g mod Mw, so reads are coalesced.  Bits are
+// counted eight at a time in byte lanes (x >> k) & 0x01010101 and flushed
+// into 32 counters every 255 observations.
+__global__ __launch_bounds__(256) void k_meta_hist(const uint32_t* __restrict__ sample,
+                                                   uint64_t n_words, uint32_t Mw, uint64_t G,
+                                                   uint32_t* __restrict__ counts) {
+    const uint64_t g = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    uint32_t cnt[32];
+#pragma unroll
+    for (int b = 0; b < 32; ++b) cnt[b] = 0;
+    if (g < G) {
+        uint64_t i = g;
+        while (i < n_words) {
+            uint32_t acc[8];
+#pragma unroll
+            for (int k = 0; k < 8; ++k) acc[k] = 0;
+            for (int r = 0; r < 255 && i < n_words; ++r, i += G) {
+                uint32_t x = sample[i];
+#pragma unroll
+                for (int k = 0; k < 8; ++k) acc[k] += (x >> k) & 0x01010101u;
+            }
+#pragma unroll
+            for (int k = 0; k < 8; ++k)
+#pragma unroll
+                for (int q = 0; q < 4; ++q) cnt[8 * q + k] += (acc[k] >> (8 * q)) & 0xFFu;
+        }
+    }
+    const uint32_t w = (uint32_t)(g % Mw);
+    // Lanes of one wave that share a position are folded together first when
+    // the period divides the wave; the rest go straight to global atomics.
+    if (Mw < (uint32_t)kWave && (kWave % Mw) == 0) {
+#pragma unroll
+        for (int b = 0; b < 32; ++b)
+            for (uint32_t o = Mw; o < (uint32_t)kWave; o <<= 1) cnt[b] += __shfl_xor(cnt[b], (int)o);
+        if (lane_id() >= Mw || g >= G) return;
+    } else if (g >= G) {
+        return;
+    }
+#pragma unroll
+    for (int b = 0; b < 32; ++b)
+        if (cnt[b]) atomicAdd(&counts[32u * w + b], cnt[b]);
+}
+
+// Mask bit j = (max(ones, n - ones) >= K), Bitval bit j = Mask && ones > n - ones.
+__global__ void k_meta_finalize(const uint32_t* __restrict__ counts, uint32_t Mw, uint64_t n_obs,
+                                uint64_t K, uint32_t* __restrict__ mask, uint32_t* __restrict__ bitval) {
+    const uint32_t w = blockIdx.x * blockDim.x + threadIdx.x;
+    if (w >= Mw) return;
+    uint32_t m = 0, v = 0;
+    for (int b = 0; b < 32; ++b) {
+        uint64_t c1 = counts[32u * w + b];
+        uint64_t c0 = n_obs - c1;
+        uint64_t agree = c1 > c0 ? c1 : c0;
+        if (agree >= K) {
+            m |= 1u << b;
+            if (c1 > c0) v |= 1u << b;
+        }
+    }
+    mask[w] = m;
+    bitval[w] = v;
+}
+
+// Derived tables: per position the k, the run shifts and run masks of the
+// kept bits; per header-word entry the bit planes of the per-chunk k.
+__global__ void k_tables(const uint32_t* __restrict__ mask, const uint32_t* __restrict__ bitval,
+                         uint32_t Mw, uint32_t Pc, uint32_t g, uint32_t G, uint32_t* __restrict__ kd,
+                         uint32_t* __restrict__ dx, uint32_t* __restrict__ r,
+                         uint32_t* __restrict__ planes, Summary* summary) {
+    const uint32_t i = blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < Mw) {
+        const uint32_t m = mask[i];
+        const uint32_t k = (uint32_t)__builtin_popcount(m);
+        uint32_t keep = ~m;
+        uint32_t src = 0, j = 0;
+        uint32_t kdv = k;
+        uint32_t dxv[4] = {0, 0, 0, 0};
+        while (keep) {
+            const uint32_t s = (uint32_t)__builtin_ctz(keep);
+            const uint32_t shifted = keep >> s;  // the run starts at bit 0
+            const uint32_t len = shifted == 0xFFFFFFFFu ? 32u : (uint32_t)__builtin_ctz(~shifted);
+            const uint32_t rm = len == 32 ? 0xFFFFFFFFu : (((1u << len) - 1u) << s);
+            const uint32_t d = s - src;
+            r[j * Mw + i] = rm;
+            if (j < 3)
+                kdv |= d << (8 * (j + 1));
+            else
+                dxv[(j - 3) >> 2] |= d << (8 * ((j - 3) & 3));
+            src += len;
+            keep &= ~rm;
+            ++j;
+        }
+        for (uint32_t jj = j; jj < (uint32_t)kMaxRuns; ++jj) r[jj * Mw + i] = 0;
+        kd[i] = kdv;
+        for (int q = 0; q < 4; ++q) dx[q * Mw + i] = dxv[q];
+        atomicMax(&summary->max_runs, j);
+        atomicAdd(&summary->invariant_bits, (unsigned long long)k);
+        if (m != mask[0] || bitval[i] != bitval[0]) atomicAnd(&summary->uniform, 0u);
+    }
+    const uint32_t Ne = Pc / G;
+    if (i < Ne) {
+        uint32_t pl[kPlanes];
+        for (int q = 0; q < kPlanes; ++q) pl[q] = 0;
+        uint32_t kmax = 0;
+        for (uint32_t c = 0; c < 32; ++c) {
+            const uint32_t cp = (i * G + c) % Pc;
+            uint32_t kc = 0;
+            for (uint32_t t = 0; t < g; ++t) kc += (uint32_t)__builtin_popcount(mask[cp * g + t]);
+            kmax = kc > kmax ? kc : kmax;
+            for (int q = 0; q < kPlanes; ++q) pl[q] |= ((kc >> q) & 1u) << c;
+        }
+        for (int q = 0; q < kPlanes; ++q) planes[(uint64_t)i * kPlanes + q] = pl[q];
+        atomicMax(&summary->max_chunk_k, kmax);
+    }
+}
+
+__global__ void k_fill_u32(uint32_t* __restrict__ p, uint64_t n, uint32_t v) {
+    for (uint64_t i = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
+         i += (uint64_t)gridDim.x * blockDim.x)
+        p[i] = v;
+}
+
+hipError_t launch_fill_u32(uint32_t* p, uint64_t n, uint32_t v, hipStream_t s) {
+    if (n == 0) return hipSuccess;
+    uint64_t blocks = (n + 255) / 256;
+    if (blocks > 4096) blocks = 4096;
+    hipLaunchKernelGGL(k_fill_u32, dim3((uint32_t)blocks), dim3(256), 0, s, p, n, v);
+    return hipGetLastError();
+}
+
+hipError_t launch_meta_hist(const uint32_t* sample, uint64_t n_words, uint32_t Mw, uint32_t* counts,
+                            hipStream_t s) {
+    const uint64_t n_obs = n_words / Mw;
+    uint64_t reps = (256ull * 1024 + Mw - 1) / Mw;
+    if (reps > n_obs) reps = n_obs;
+    if (reps == 0) reps = 1;
+    const uint64_t G = reps * Mw;
+    const uint64_t blocks = (G + 255) / 256;
+    hipLaunchKernelGGL(k_meta_hist, dim3((uint32_t)blocks), dim3(256), 0, s, sample, n_words, Mw, G, counts);
+    return hipGetLastError();
+}
+
+hipError_t launch_meta_finalize(const uint32_t* counts, uint32_t Mw, uint64_t n_obs, uint64_t K,
+                                uint32_t* mask, uint32_t* bitval, hipStream_t s) {
+    hipLaunchKernelGGL(k_meta_finalize, dim3((Mw + 255) / 256), dim3(256), 0, s, counts, Mw, n_obs, K,
+                       mask, bitval);
+    return hipGetLastError();
+}
+
+hipError_t launch_tables(const uint32_t* mask, const uint32_t* bitval, uint32_t Mw, uint32_t Pc,
+                         uint32_t g, uint32_t G, uint32_t* kd, uint32_t* dx, uint32_t* r,
+                         uint32_t* planes, Summary* summary, hipStream_t s) {
+    const uint32_t n = Mw > Pc / G ? Mw : Pc / G;
+    hipLaunchKernelGGL(k_tables, dim3((n + 255) / 256), dim3(256), 0, s, mask, bitval, Mw, Pc, g, G, kd,
+                       dx, r, planes, summary);
+    return hipGetLastError();
+}
+
+}  // namespace ibp
