@@ -20,7 +20,7 @@ namespace {
 
 constexpr uint32_t kLongTileWords = 1024;  // tile of a tensor longer than kMaxTileWords
 constexpr uint32_t kMaxPeriodBits = 1u << 20;
-constexpr uint64_t kLineWords = 16;  // 64-byte memory transaction
+constexpr uint64_t kLineWords = 64;  // 256-byte first-read granule
 
 struct Scratch {
     unsigned long long* status = nullptr;
@@ -37,6 +37,7 @@ struct Scratch {
 struct ibp_meta_s {
     int device = 0;
     uint32_t cu_count = 0;
+    uint64_t first_read_bytes = 0;  // 0: default policy
     ibp_params params{};
     uint32_t Mw = 0, Pc = 0, g = 0, log2g = 0, G = 0, Ne = 0;
     std::vector<uint32_t> mask_h, bitval_h;
@@ -243,13 +244,18 @@ Geo make_geo(const ibp_meta_s* h, bool aligned16) {
         g.tiles_per_tensor = (g.n_words + kLongTileWords - 1) / kLongTileWords;
     }
     // First read of a single-tile record: every record is at least min_words
-    // long, so the read is cut at the last 64-byte line boundary inside that
-    // prefix (the second read then starts on a line and no line travels
-    // twice).  When no record can be shorter than 15/16 of the slot, the whole
-    // slot is read at once instead of paying a second round trip.
+    // long, so the read is cut at the last 256-byte boundary inside that
+    // prefix, and is never shorter than 256 bytes (the second read then starts
+    // on a 256-byte boundary; zero-copy reads of pinned host memory measured
+    // fastest with this split).  When no record can be shorter than 15/16 of
+    // the slot, the whole slot is read at once instead of paying a second
+    // round trip.
     const uint64_t min_words = (min_record_bits(h) + 31) / 32;
     uint64_t spec;
-    if ((g.n_words - min_words) * 16 <= g.n_words) {
+    if (h->first_read_bytes) {
+        spec = (h->first_read_bytes + 3) / 4;
+        if (spec < g.hdr_words) spec = g.hdr_words;
+    } else if ((g.n_words - min_words) * 16 <= g.n_words) {
         spec = g.n_words;
     } else {
         spec = (min_words / kLineWords) * kLineWords;
@@ -410,6 +416,12 @@ ibp_status ibp_meta_get_info(ibp_meta_t h, ibp_meta_info* info) {
     info->min_record_bytes = 4 * ((min_record_bits(h) + 31) / 32);
     info->max_runs = h->sum.max_runs;
     info->uniform = h->sum.uniform;
+    return IBP_OK;
+}
+
+ibp_status ibp_meta_set_first_read(ibp_meta_t h, uint64_t bytes) {
+    if (!h) return IBP_ERR_INVALID_ARG;
+    h->first_read_bytes = bytes;
     return IBP_OK;
 }
 

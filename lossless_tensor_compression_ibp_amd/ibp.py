@@ -27,7 +27,7 @@ IBP_ERR_RANGE = -6
 # every function the header declares (checked by the tests)
 ABI_FUNCTIONS = (
     "ibp_build_metadata", "ibp_meta_create", "ibp_meta_get", "ibp_meta_get_info",
-    "ibp_meta_destroy", "ibp_compress", "ibp_decompress", "ibp_gather_decompress",
+    "ibp_meta_set_first_read", "ibp_meta_destroy", "ibp_compress", "ibp_decompress", "ibp_gather_decompress",
     "ibp_check", "ibp_status_string",
 )
 
@@ -65,6 +65,7 @@ def lib():
         L.ibp_meta_create.argtypes = [P(ibp_params), p, p, P(p), p]
         L.ibp_meta_get.argtypes = [p, P(ibp_params), p, p]
         L.ibp_meta_get_info.argtypes = [p, P(ibp_meta_info)]
+        L.ibp_meta_set_first_read.argtypes = [p, u64]
         L.ibp_meta_destroy.argtypes = [p]
         L.ibp_compress.argtypes = [p, p, u64, p, p, p, p]
         L.ibp_decompress.argtypes = [p, p, p, u64, p, p]
@@ -166,6 +167,10 @@ def ibp_meta_get_info(meta: Meta) -> dict:
     _check(lib().ibp_meta_get_info(meta, ctypes.byref(info)), "ibp_meta_get_info")
     return dict(invariant_bits=info.invariant_bits, min_record_bytes=info.min_record_bytes,
                 max_runs=info.max_runs, uniform=info.uniform)
+
+
+def ibp_meta_set_first_read(meta: Meta, nbytes: int):
+    _check(lib().ibp_meta_set_first_read(meta, int(nbytes)), "ibp_meta_set_first_read")
 
 
 def ibp_meta_destroy(meta: Meta):
