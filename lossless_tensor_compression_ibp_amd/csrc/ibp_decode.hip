@@ -254,10 +254,9 @@ __global__ __launch_bounds__(256) void k_decode_small(Tables t, Geo geo, const u
             }
             uint32_t have = geo.spec_words;
             if (words > have) {
-                const uint32_t upto = min((words + 3u) & ~3u, nwords);
-                load_words_to_lds(reinterpret_cast<const uint32_t*>(slots + (uint64_t)tn * geo.L), have, upto,
-                                  buf + have, true);
-                have = upto;
+                load_exact_to_lds(reinterpret_cast<const uint32_t*>(slots + (uint64_t)tn * geo.L), have, words,
+                                  buf + have);
+                have = words;
             }
             if (lane == 0) buf[have] = 0;
             __builtin_amdgcn_wave_barrier();

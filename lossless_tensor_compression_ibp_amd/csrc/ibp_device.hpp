@@ -227,6 +227,32 @@ __device__ __forceinline__ void load_words_to_lds(const uint32_t* __restrict__ s
     }
 }
 
+// Copy global words [a, b) of `src` into lds[0 .. b-a) with non-temporal
+// loads and no over-read: dwordx4 for whole 16-byte groups (a is a multiple
+// of 4, src 16-byte aligned), single dwords for the tail.  Used for the part
+// of a record read after its header, where bytes past the record would only
+// cost link or HBM bandwidth.
+__device__ __forceinline__ void load_exact_to_lds(const uint32_t* __restrict__ src, uint64_t a, uint64_t b,
+                                                  uint32_t* lds) {
+    const uint32_t lane = lane_id();
+    const u32x4* s4 = reinterpret_cast<const u32x4*>(src + a);
+    u32x4* l4 = reinterpret_cast<u32x4*>(lds);
+    const uint32_t n = (uint32_t)(b - a);
+    const uint32_t n4 = n >> 2;
+    uint32_t i = lane;
+    for (; i + 3 * kWave < n4; i += 4 * kWave) {
+        const u32x4 v0 = __builtin_nontemporal_load(s4 + i), v1 = __builtin_nontemporal_load(s4 + i + kWave);
+        const u32x4 v2 = __builtin_nontemporal_load(s4 + i + 2 * kWave);
+        const u32x4 v3 = __builtin_nontemporal_load(s4 + i + 3 * kWave);
+        l4[i] = v0;
+        l4[i + kWave] = v1;
+        l4[i + 2 * kWave] = v2;
+        l4[i + 3 * kWave] = v3;
+    }
+    for (; i < n4; i += kWave) l4[i] = __builtin_nontemporal_load(s4 + i);
+    if (lane < (n & 3u)) lds[4 * n4 + lane] = __builtin_nontemporal_load(src + a + 4 * n4 + lane);
+}
+
 // Copy words [w0, w0 + nw) of a raw tensor.
 __device__ __forceinline__ void copy_words(const uint32_t* __restrict__ src, uint32_t* __restrict__ dst,
                                            uint64_t w0, uint32_t nw, bool vec) {
