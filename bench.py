@@ -281,6 +281,7 @@ def run_kv_bf16(args) -> dict:
     n, L = raw_np.shape
     dev = torch.device("cuda")
     src = torch.from_numpy(raw_np).to(dev)
+    del kv, raw_np
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     meta = ibp.ibp_build_metadata(src, w.n_sample, L, w.chunk_bits, w.period_bits, w.threshold)
@@ -288,7 +289,7 @@ def run_kv_bf16(args) -> dict:
     slots = torch.empty_like(src)
     bitmask = torch.zeros((n + 31) // 32, dtype=torch.int32, device=dev)
     stored = torch.zeros(n, dtype=torch.int64, device=dev)
-    enc_wall, enc_durs = timed(lambda i: ibp.ibp_compress(meta, src, n, slots, bitmask, stored), 5, 1)
+    _, enc_durs = timed(lambda i: ibp.ibp_compress(meta, src, n, slots, bitmask, stored), 5, 1)
     stored_np = stored.cpu().numpy()
     savings = 1.0 - stored_np.sum() / (n * L)
     out = torch.empty_like(src)
@@ -297,36 +298,234 @@ def run_kv_bf16(args) -> dict:
     if not torch.equal(out, src):
         raise SystemExit("decoded pages differ")
     hbm_bytes = float(stored_np.sum() + n * L + 4 * ((n + 31) // 32))
-    achieved = hbm_bytes / float(durs.mean()) / GB
-    copy_ceiling = copy_kernel_ceiling()
+    roof = hbm_roofline(hbm_bytes, durs)
+    roof["traffic"] = measured_traffic("kv_bf16") if layers == 32 else None
+    return base_result(
+        args, n * L * args.steps / wall / GB, wall,
+        {"workload": f"kv_bf16: {layers} layers x 32 heads x 4096 tokens x 128 bf16, 4 KiB pages in HBM slots, "
+                     f"W=32, M=32768, T=0.95, decode of all {n} pages per step", "pages": n, "tensor_bytes": L},
+        savings, "ibp::k_decode_small<3, false, true, 4>", durs, roof,
+        encode_GBps=round(n * L / float(np.mean(enc_durs)) / GB, 3), metadata_ms=round(t_meta * 1e3, 2),
+        meta=ibp.ibp_meta_get_info(meta))
+
+
+METRIC = "IBP decode GB/s (uncompressed out, 1 MI355X) + % of roofline + space savings %"
+
+
+def base_result(args, value, wall, config, savings, kernel, durs, roofline, **extra) -> dict:
     res = {
-        "metric": "IBP decode GB/s (uncompressed out, 1 MI355X) + % of roofline + space savings %",
-        "value": round(n * L * args.steps / wall / GB, 3), "unit": "GB/s", "n_gpus": 1,
+        "metric": METRIC, "value": round(value, 3), "unit": "GB/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(wall / args.steps * 1e3, 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "u32", "data": "synthetic",
-        "config": {"workload": f"kv_bf16: {layers} layers x 32 heads x 4096 tokens x 128 bf16, 4 KiB pages "
-                               f"in HBM slots, W=32, M=32768, T=0.95, decode of all {n} pages per step",
-                   "pages": n, "tensor_bytes": L},
-        "space_savings_pct": round(100 * savings, 3),
-        "kernel": "ibp::k_decode_small<3, false, true, 4>", "kernel_avg_us": round(float(durs.mean()) * 1e6, 2),
-        "roofline": {"bound": "hbm", "achieved": round(achieved, 3), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": measured_traffic("kv_bf16"),
-                     "copy_kernel_ceiling_measured": round(copy_ceiling, 3),
-                     "algorithmic_bytes_per_launch": int(hbm_bytes)},
-        "encode_GBps": round(n * L / float(enc_durs.mean()) / GB, 3),
-        "metadata_ms": round(t_meta * 1e3, 2), "meta": ibp.ibp_meta_get_info(meta),
+        "config": config, "space_savings_pct": round(100 * savings, 3), "kernel": kernel,
+        "kernel_avg_us": round(float(np.mean(durs)) * 1e6, 2), "roofline": roofline,
     }
+    res.update(extra)
     return res
 
 
-WORKLOADS = {"sparse_gnn": run_sparse_gnn, "kv_bf16": run_kv_bf16}
+def hbm_roofline(bytes_per_launch: float, durs) -> dict:
+    achieved = bytes_per_launch / float(np.mean(durs)) / GB
+    return {"bound": "hbm", "achieved": round(achieved, 3), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": None,
+            "copy_kernel_ceiling_measured": round(copy_kernel_ceiling(), 3),
+            "algorithmic_bytes_per_launch": int(bytes_per_launch)}
+
+
+def link_roofline(link_bytes_per_launch: float, durs, savings: float) -> dict:
+    achieved = link_bytes_per_launch / float(np.mean(durs)) / GB
+    h2d = h2d_ceiling()
+    return {"bound": "pcie", "achieved": round(achieved, 3), "peak": PCIE5_X16_GBPS, "unit": "GB/s",
+            "frac": round(achieved / PCIE5_X16_GBPS, 4), "traffic": None,
+            "link_ceiling_measured": round(h2d, 3), "frac_of_measured_ceiling": round(achieved / h2d, 4),
+            "algorithmic_bytes_per_launch": int(link_bytes_per_launch),
+            "decoded_roofline_GBps": round(h2d / (1.0 - savings), 3)}
+
+
+# ---------------------------------------------------------------------------
+# Dense GNN: 8 MiB of rows in HBM, contiguous decode of the whole table
+# ---------------------------------------------------------------------------
+def run_dense_gnn(args) -> dict:
+    w = WL.DENSE_GNN
+    x = WL.dense_gnn()
+    raw_np = np.ascontiguousarray(x).view(np.uint8).reshape(x.shape[0], -1)
+    n, L = raw_np.shape
+    dev = torch.device("cuda")
+    src = torch.from_numpy(raw_np).to(dev)
+    meta = ibp.ibp_build_metadata(src, w.n_sample, L, w.chunk_bits, w.period_bits, w.threshold)
+    slots = torch.empty_like(src)
+    bitmask = torch.zeros((n + 31) // 32, dtype=torch.int32, device=dev)
+    stored = torch.zeros(n, dtype=torch.int64, device=dev)
+    _, enc_durs = timed(lambda i: ibp.ibp_compress(meta, src, n, slots, bitmask, stored), 20, 2)
+    stored_np = stored.cpu().numpy()
+    savings = 1.0 - stored_np.sum() / (n * L)
+    out = torch.empty_like(src)
+    wall, durs = timed(lambda i: ibp.ibp_decompress(meta, slots, bitmask, n, out), args.steps, args.warmup)
+    assert ibp.ibp_check(meta) == ibp.IBP_OK
+    if not torch.equal(out, src):
+        raise SystemExit("decoded rows differ")
+    hbm_bytes = float(stored_np.sum() + n * L + 4 * ((n + 31) // 32))
+    return base_result(
+        args, n * L * args.steps / wall / GB, wall,
+        {"workload": f"dense_gnn: {n} rows x 128 fp32 |N(0,0.5)| with 3% N(0,50) rows, W=32, M=4096, T=0.95, "
+                     f"slots in HBM, contiguous decode of all rows per step", "rows": n, "tensor_bytes": L},
+        savings, "ibp::k_decode_small", durs, hbm_roofline(hbm_bytes, durs),
+        encode_GBps=round(n * L / float(np.mean(enc_durs)) / GB, 3), meta=ibp.ibp_meta_get_info(meta))
+
+
+# ---------------------------------------------------------------------------
+# DLRM: 2 GiB embedding table in pinned host slots, 26 gathers of 65,536 ids
+# ---------------------------------------------------------------------------
+def run_dlrm(args) -> dict:
+    w = WL.DLRM
+    n = w.n_tensors if not args.small else 262144
+    L = w.tensor_bytes
+    batch, per_step = 65536, 26
+    log(f"[bench] dlrm: generating {n} x 128 fp32 rows")
+    host = pinned((n, L), torch.uint8)
+    WL.dlrm(n, out=host.numpy().view(np.float32).reshape(n, 128))
+    raw_np = host.numpy()
+    dev = torch.device("cuda")
+    meta = ibp.ibp_build_metadata(host, w.n_sample, L, w.chunk_bits, w.period_bits, w.threshold)
+    slots = pinned((n, L), torch.uint8)
+    bitmask = torch.zeros((n + 31) // 32, dtype=torch.int32, device=dev)
+    stored = torch.zeros(n, dtype=torch.int64, device=dev)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ibp.ibp_compress(meta, host, n, slots, bitmask, stored)
+    torch.cuda.synchronize()
+    t_enc = time.perf_counter() - t0
+    stored_np = stored.cpu().numpy()
+    savings = 1.0 - stored_np.sum() / (n * L)
+    n_batches = per_step * (args.warmup + args.steps)
+    ids_np = WL.batch_ids(n, batch, n_batches, replace=True)
+    ids = torch.from_numpy(ids_np).to(dev)
+    out = torch.empty((2, batch, L), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream()
+    evs = []
+
+    def step(i):
+        for j in range(per_step):
+            k = i * per_step + j
+            if i >= args.warmup:
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record(stream)
+            ibp.ibp_gather_decompress(meta, slots, n, bitmask, ids[k], out[k & 1])
+            if i >= args.warmup:
+                e1.record(stream)
+                evs.append((e0, e1))
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.warmup, args.warmup + args.steps):
+        step(i)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    assert ibp.ibp_check(meta) == ibp.IBP_OK
+    last = n_batches - 1
+    if not np.array_equal(out[last & 1].cpu().numpy(), raw_np[ids_np[last]]):
+        raise SystemExit("decoded rows differ")
+    durs = np.array([a.elapsed_time(b) / 1e3 for a, b in evs])
+    link = float(stored_np[ids_np[args.warmup * per_step:]].sum(axis=1).mean())
+    value = args.steps * per_step * batch * L / wall / GB
+    return base_result(
+        args, value, wall,
+        {"workload": f"dlrm: {n} rows x 128 fp32 U(-0.01,0.01), W=32, M=4096, T=0.9, slots in pinned host "
+                     f"memory, {per_step} zero-copy gathers of {batch} random ids (with replacement) per step",
+         "rows": n, "tensor_bytes": L, "batch_ids": batch, "gathers_per_step": per_step},
+        savings, "ibp::k_decode_small", durs, link_roofline(link, durs, savings),
+        encode_GBps=round(n * L / t_enc / GB, 3), meta=ibp.ibp_meta_get_info(meta))
+
+
+# ---------------------------------------------------------------------------
+# LLM BF16 weights: 32 layers streamed from pinned host slots, one layer of
+# prefetch: decode of layer i+1 (stream A) overlaps a consumer of layer i
+# (stream B, y = x @ W on the decoded layer)
+# ---------------------------------------------------------------------------
+def run_llm_bf16(args) -> dict:
+    w = WL.LLM_BF16
+    layers = 32 if not args.small else 4
+    rows, cols = 4096, 11008
+    L = rows * cols * 2
+    log(f"[bench] llm_bf16: generating {layers} layers of {rows} x {cols} bf16")
+    host = pinned((layers, L), torch.uint8)
+    hv = host.numpy()
+    for l in range(layers):
+        hv[l] = WL.llm_layer(l, rows, cols).reshape(-1).view(np.uint8)
+    dev = torch.device("cuda")
+    meta = ibp.ibp_build_metadata(host, 1, L, w.chunk_bits, w.period_bits, w.threshold)
+    slots = pinned((layers, L), torch.uint8)
+    bitmask = torch.zeros((layers + 31) // 32, dtype=torch.int32, device=dev)
+    stored = torch.zeros(layers, dtype=torch.int64, device=dev)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ibp.ibp_compress(meta, host, layers, slots, bitmask, stored)
+    torch.cuda.synchronize()
+    t_enc = time.perf_counter() - t0
+    stored_np = stored.cpu().numpy()
+    savings = 1.0 - stored_np.sum() / (layers * L)
+    bufs = [torch.empty(L, dtype=torch.uint8, device=dev) for _ in range(2)]
+    ids = torch.arange(layers, dtype=torch.int64, device=dev)
+    x = torch.randn((1, rows), dtype=torch.bfloat16, device=dev)
+    y = torch.empty((1, cols), dtype=torch.bfloat16, device=dev)
+    sa, sb = torch.cuda.Stream(), torch.cuda.Stream()
+    evs = []
+
+    def one_pass(record: bool):
+        ready = [torch.cuda.Event() for _ in range(layers)]
+        freed = [torch.cuda.Event() for _ in range(layers)]
+        for l in range(layers):
+            with torch.cuda.stream(sa):
+                if l >= 2:
+                    sa.wait_event(freed[l - 2])
+                if record:
+                    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                    e0.record(sa)
+                ibp.ibp_gather_decompress(meta, slots, layers, bitmask, ids[l:l + 1], bufs[l & 1], stream=sa)
+                if record:
+                    e1.record(sa)
+                    evs.append((e0, e1))
+                ready[l].record(sa)
+            with torch.cuda.stream(sb):
+                sb.wait_event(ready[l])
+                torch.matmul(x, bufs[l & 1].view(torch.bfloat16).view(rows, cols), out=y)
+                freed[l].record(sb)
+
+    for _ in range(args.warmup):
+        one_pass(False)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        one_pass(True)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    assert ibp.ibp_check(meta) == ibp.IBP_OK
+    if not np.array_equal(bufs[(layers - 1) & 1].cpu().numpy(), hv[layers - 1]):
+        raise SystemExit("decoded layer differs")
+    durs = np.array([a.elapsed_time(b) / 1e3 for a, b in evs])
+    link = float(stored_np.mean())
+    value = args.steps * layers * L / wall / GB
+    return base_result(
+        args, value, wall,
+        {"workload": f"llm_bf16: {layers} layers of {rows}x{cols} bf16 N(0,0.02) (0.1% columns x20), W=32, M=32, "
+                     f"T=0.95, slots in pinned host memory, each layer decoded zero-copy into HBM on one stream "
+                     f"while a consumer (y = x @ W) reads the previous layer on another", "layers": layers,
+         "tensor_bytes": L},
+        savings, "ibp::k_decode_tiles (look-back)", durs, link_roofline(link, durs, savings),
+        encode_GBps=round(layers * L / t_enc / GB, 3), meta=ibp.ibp_meta_get_info(meta))
+
+
+WORKLOADS = {"sparse_gnn": run_sparse_gnn, "kv_bf16": run_kv_bf16, "dense_gnn": run_dense_gnn,
+             "dlrm": run_dlrm, "llm_bf16": run_llm_bf16}
 
 
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--steps", type=int, default=None, help="timed steps (default per workload)")
+    ap.add_argument("--warmup", type=int, default=None)
     ap.add_argument("--workload", default="sparse_gnn", choices=sorted(WORKLOADS))
     ap.add_argument("--small", action="store_true", help="scaled-down table (quick check)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
@@ -340,6 +539,11 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
+    defaults = {"sparse_gnn": (200, 10), "kv_bf16": (100, 5), "dense_gnn": (200, 10), "dlrm": (4, 1),
+                "llm_bf16": (3, 1)}
+    d_steps, d_warm = defaults[args.workload]
+    args.steps = d_steps if args.steps is None else args.steps
+    args.warmup = d_warm if args.warmup is None else args.warmup
     ibp.lib()
     res = WORKLOADS[args.workload](args)
     print(json.dumps(res), flush=True)
