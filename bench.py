@@ -451,9 +451,7 @@ def run_llm_bf16(args) -> dict:
     L = rows * cols * 2
     log(f"[bench] llm_bf16: generating {layers} layers of {rows} x {cols} bf16")
     host = pinned((layers, L), torch.uint8)
-    hv = host.numpy()
-    for l in range(layers):
-        hv[l] = WL.llm_layer(l, rows, cols).reshape(-1).view(np.uint8)
+    hv = WL.llm_layers(host.numpy(), rows, cols)
     dev = torch.device("cuda")
     meta = ibp.ibp_build_metadata(host, 1, L, w.chunk_bits, w.period_bits, w.threshold)
     slots = pinned((layers, L), torch.uint8)

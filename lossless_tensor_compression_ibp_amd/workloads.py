@@ -52,11 +52,15 @@ ALL = {w.name: w for w in (DENSE_GNN, SPARSE_GNN, DLRM, LLM_BF16, KV_BF16)}
 
 
 def to_bf16_bits(x: np.ndarray) -> np.ndarray:
-    """fp32 -> bfloat16 bit patterns, round to nearest even (finite inputs)."""
+    """fp32 -> bfloat16 bit patterns, round to nearest even (finite inputs).
+    Works in place on a float32 array it may overwrite."""
     u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32)
-    lsb = (u >> np.uint32(16)) & np.uint32(1)
-    r = (u + np.uint32(0x7FFF) + lsb) >> np.uint32(16)
-    return r.astype(np.uint16)
+    lsb = np.right_shift(u, np.uint32(16))
+    np.bitwise_and(lsb, np.uint32(1), out=lsb)
+    np.add(u, lsb, out=u)
+    np.add(u, np.uint32(0x7FFF), out=u)
+    np.right_shift(u, np.uint32(16), out=u)
+    return u.astype(np.uint16)
 
 
 def dense_gnn(n_rows: int = DENSE_GNN.n_tensors, seed: int = DATA_SEED) -> np.ndarray:
@@ -106,11 +110,26 @@ def llm_layer(layer: int, rows: int = 4096, cols: int = 11008, seed: int = DATA_
     """One weight layer as bf16 bit patterns (uint16, rows x cols): N(0, 0.02),
     round(0.1 %) of the columns (channels) scaled by 20 before rounding."""
     rng = np.random.default_rng([seed, layer])
-    w = rng.standard_normal((rows, cols), dtype=np.float32) * np.float32(0.02)
+    w = rng.standard_normal((rows, cols), dtype=np.float32)
+    w *= np.float32(0.02)
     n_ch = max(1, int(round(0.001 * cols)))
     ch = rng.choice(cols, size=n_ch, replace=False)
     w[:, ch] *= np.float32(20.0)
     return to_bf16_bits(w)
+
+
+def llm_layers(out: np.ndarray, rows: int = 4096, cols: int = 11008, seed: int = DATA_SEED,
+               threads: int = 8) -> np.ndarray:
+    """All layers into out (layers x rows*cols*2 bytes); layers are drawn from
+    independent seeds, so drawing them on several threads gives the same bytes."""
+    from concurrent.futures import ThreadPoolExecutor
+
+    def one(l):
+        out[l] = llm_layer(l, rows, cols, seed).reshape(-1).view(np.uint8)
+
+    with ThreadPoolExecutor(max_workers=threads) as ex:
+        list(ex.map(one, range(out.shape[0])))
+    return out
 
 
 def kv_cache(n_layers: int = 32, n_heads: int = 32, n_tokens: int = 4096, head_dim: int = 128,

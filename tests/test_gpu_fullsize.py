@@ -1,0 +1,180 @@
+"""GPU parity at the workloads' full sizes, in the launch configurations the
+benchmark uses.  The oracle recomputes metadata from the same sample and
+encodes sampled tensors one by one; every decoded byte is checked against the
+source (a property that holds at any size)."""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+from lossless_tensor_compression_ibp_amd import ibp
+from lossless_tensor_compression_ibp_amd import workloads as WL
+from oracle import oracle
+from tests.gpu_util import say
+
+pytestmark = [pytest.mark.gpu, pytest.mark.timeout(600)]
+
+DEV = "cuda:0"
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _oracle_built():
+    oracle.build(force=False)
+
+
+def pinned(shape, dtype=torch.uint8):
+    return torch.empty(shape, dtype=dtype, pin_memory=True)
+
+
+def check_metadata(meta, sample_np, n_sample, w: WL.Workload, L: int):
+    _, m, b = ibp.ibp_meta_get(meta)
+    om, ob = oracle.build_metadata(sample_np, 8 * L, w.chunk_bits, w.period_bits, w.threshold, n_sample)
+    np.testing.assert_array_equal(m.view(np.uint8), om, err_msg="Mask differs")
+    np.testing.assert_array_equal(b.view(np.uint8), ob, err_msg="Bitval differs")
+    return om, ob
+
+
+def check_sampled_slots(rows, raw_rows_np, slots_np_rows, bm_words_np, stored_np, w, L, om, ob):
+    """Oracle encodes the sampled tensors; the GPU's bitmask bits, stored bytes
+    and record prefixes (or raw slots) must match."""
+    o_slots, o_bm, o_stored = oracle.compress(raw_rows_np, L, w.chunk_bits, w.period_bits, om, ob, len(rows))
+    o_bits = np.unpackbits(o_bm.view(np.uint8), bitorder="little")[: len(rows)]
+    g_bits = (bm_words_np[rows >> 5] >> (rows & 31)) & 1
+    np.testing.assert_array_equal(g_bits, o_bits, err_msg="bitmask bits differ")
+    np.testing.assert_array_equal(stored_np[rows].astype(np.uint64), o_stored, err_msg="stored bytes differ")
+    for i in range(len(rows)):
+        k = int(o_stored[i])
+        if not np.array_equal(slots_np_rows[i, :k], o_slots[i, :k]):
+            raise AssertionError(f"slot of tensor {rows[i]} differs from the oracle's")
+    return int(o_bits.sum())
+
+
+def test_dense_gnn_full():
+    w = WL.DENSE_GNN
+    raw = np.ascontiguousarray(WL.dense_gnn()).view(np.uint8).reshape(w.n_tensors, -1)
+    n, L = raw.shape
+    say(f"[full] dense_gnn n={n} L={L}")
+    src = torch.from_numpy(raw).to(DEV)
+    meta = ibp.ibp_build_metadata(src, w.n_sample, L, w.chunk_bits, w.period_bits, w.threshold)
+    om, ob = check_metadata(meta, raw[: w.n_sample], w.n_sample, w, L)
+    slots = torch.empty_like(src)
+    bm = torch.zeros((n + 31) // 32, dtype=torch.int32, device=DEV)
+    stored = torch.zeros(n, dtype=torch.int64, device=DEV)
+    ibp.ibp_compress(meta, src, n, slots, bm, stored)
+    rows = np.arange(n)
+    ncomp = check_sampled_slots(rows, raw, slots.cpu().numpy(), bm.cpu().numpy().view(np.uint32),
+                                stored.cpu().numpy(), w, L, om, ob)
+    out = torch.empty_like(src)
+    ibp.ibp_decompress(meta, slots, bm, n, out)
+    assert ibp.ibp_check(meta) == ibp.IBP_OK
+    assert torch.equal(out, src)
+    say(f"[full] dense_gnn ok: all {n} slots equal to the oracle's ({ncomp} compressed)")
+
+
+def test_sparse_gnn_full():
+    w = WL.SPARSE_GNN
+    n, L = w.n_tensors, w.tensor_bytes
+    say(f"[full] sparse_gnn n={n} L={L} (pinned host slots)")
+    host = pinned((n, L))
+    WL.sparse_gnn(n, out=host.numpy().view(np.float32).reshape(n, 256))
+    raw = host.numpy()
+    meta = ibp.ibp_build_metadata(host, w.n_sample, L, w.chunk_bits, w.period_bits, w.threshold)
+    om, ob = check_metadata(meta, raw[: w.n_sample], w.n_sample, w, L)
+    slots = pinned((n, L))
+    bm = torch.zeros((n + 31) // 32, dtype=torch.int32, device=DEV)
+    stored = torch.zeros(n, dtype=torch.int64, device=DEV)
+    ibp.ibp_compress(meta, host, n, slots, bm, stored)
+    torch.cuda.synchronize()
+    rows = np.unique(np.concatenate([np.arange(256), np.random.default_rng(5).integers(0, n, 2048), [n - 1]]))
+    check_sampled_slots(rows, raw[rows], slots.numpy()[rows], bm.cpu().numpy().view(np.uint32),
+                        stored.cpu().numpy(), w, L, om, ob)
+    ids_all = WL.batch_ids(n, 8192, 4, replace=False)
+    out = torch.empty((8192, L), dtype=torch.uint8, device=DEV)
+    for b in range(ids_all.shape[0]):
+        ids = torch.from_numpy(ids_all[b]).to(DEV)
+        ibp.ibp_gather_decompress(meta, slots, n, bm, ids, out)
+        assert ibp.ibp_check(meta) == ibp.IBP_OK
+        np.testing.assert_array_equal(out.cpu().numpy(), raw[ids_all[b]])
+    full = torch.empty((n, L), dtype=torch.uint8, device=DEV)
+    ibp.ibp_decompress(meta, slots, bm, n, full)
+    assert ibp.ibp_check(meta) == ibp.IBP_OK
+    assert torch.equal(full, host.to(DEV))
+    say("[full] sparse_gnn ok")
+
+
+def test_dlrm_full():
+    w = WL.DLRM
+    n, L = w.n_tensors, w.tensor_bytes
+    say(f"[full] dlrm n={n} L={L} (pinned host slots)")
+    host = pinned((n, L))
+    WL.dlrm(n, out=host.numpy().view(np.float32).reshape(n, 128))
+    raw = host.numpy()
+    meta = ibp.ibp_build_metadata(host, w.n_sample, L, w.chunk_bits, w.period_bits, w.threshold)
+    om, ob = check_metadata(meta, raw[: w.n_sample], w.n_sample, w, L)
+    slots = pinned((n, L))
+    bm = torch.zeros((n + 31) // 32, dtype=torch.int32, device=DEV)
+    stored = torch.zeros(n, dtype=torch.int64, device=DEV)
+    ibp.ibp_compress(meta, host, n, slots, bm, stored)
+    torch.cuda.synchronize()
+    rows = np.unique(np.concatenate([np.arange(128), np.random.default_rng(6).integers(0, n, 2048), [n - 1]]))
+    check_sampled_slots(rows, raw[rows], slots.numpy()[rows], bm.cpu().numpy().view(np.uint32),
+                        stored.cpu().numpy(), w, L, om, ob)
+    ids_all = WL.batch_ids(n, 65536, 3, replace=True)
+    out = torch.empty((65536, L), dtype=torch.uint8, device=DEV)
+    for b in range(ids_all.shape[0]):
+        ids = torch.from_numpy(ids_all[b]).to(DEV)
+        ibp.ibp_gather_decompress(meta, slots, n, bm, ids, out)
+        assert ibp.ibp_check(meta) == ibp.IBP_OK
+        np.testing.assert_array_equal(out.cpu().numpy(), raw[ids_all[b]])
+    say("[full] dlrm ok")
+
+
+def test_llm_bf16_full():
+    w = WL.LLM_BF16
+    layers, L = w.n_tensors, w.tensor_bytes
+    say(f"[full] llm_bf16 layers={layers} L={L} (pinned host slots, multi-tile look-back)")
+    host = pinned((layers, L))
+    hv = WL.llm_layers(host.numpy())
+    meta = ibp.ibp_build_metadata(host, 1, L, w.chunk_bits, w.period_bits, w.threshold)
+    om, ob = check_metadata(meta, hv[:1], 1, w, L)
+    slots = pinned((layers, L))
+    bm = torch.zeros(1, dtype=torch.int32, device=DEV)
+    stored = torch.zeros(layers, dtype=torch.int64, device=DEV)
+    ibp.ibp_compress(meta, host, layers, slots, bm, stored)
+    torch.cuda.synchronize()
+    sv = slots.numpy()
+    rows = np.array([0, layers - 1])
+    check_sampled_slots(rows, hv[rows], sv[rows], bm.cpu().numpy().view(np.uint32), stored.cpu().numpy(),
+                        w, L, om, ob)
+    buf = torch.empty((1, L), dtype=torch.uint8, device=DEV)
+    for l in range(layers):
+        ids = torch.tensor([l], dtype=torch.int64, device=DEV)
+        ibp.ibp_gather_decompress(meta, slots, layers, bm, ids, buf)
+        assert ibp.ibp_check(meta) == ibp.IBP_OK
+        assert torch.equal(buf[0], host[l].to(DEV)), f"layer {l} differs"
+    say("[full] llm_bf16 ok")
+
+
+def test_kv_bf16_full():
+    w = WL.KV_BF16
+    kv = WL.kv_cache()
+    raw = kv.reshape(-1, 2048).view(np.uint8).reshape(-1, 4096)
+    n, L = raw.shape
+    say(f"[full] kv_bf16 pages={n} L={L} (HBM slots)")
+    src = torch.from_numpy(raw).to(DEV)
+    meta = ibp.ibp_build_metadata(src, w.n_sample, L, w.chunk_bits, w.period_bits, w.threshold)
+    om, ob = check_metadata(meta, raw[: w.n_sample], w.n_sample, w, L)
+    slots = torch.empty_like(src)
+    bm = torch.zeros((n + 31) // 32, dtype=torch.int32, device=DEV)
+    stored = torch.zeros(n, dtype=torch.int64, device=DEV)
+    ibp.ibp_compress(meta, src, n, slots, bm, stored)
+    rows = np.unique(np.concatenate([np.arange(64), np.random.default_rng(7).integers(0, n, 1024), [n - 1]]))
+    idx = torch.from_numpy(rows).to(DEV)
+    check_sampled_slots(rows, raw[rows], slots.index_select(0, idx).cpu().numpy(),
+                        bm.cpu().numpy().view(np.uint32), stored.cpu().numpy(), w, L, om, ob)
+    out = torch.empty_like(src)
+    ibp.ibp_decompress(meta, slots, bm, n, out)
+    assert ibp.ibp_check(meta) == ibp.IBP_OK
+    assert torch.equal(out, src)
+    say("[full] kv_bf16 ok")
