@@ -451,8 +451,8 @@ ibp_status ibp_compress(ibp_meta_t h, const void* src, uint64_t n_tensors, void*
         ibp_status st = lookback_for(h, stream, tiles, launched_waves(tiles), n_tensors, &lb);
         if (st != IBP_OK) return st;
     }
-    return from_hip(launch_encode(h->tabs, geo, h->sum.max_runs, src, n_tensors, dst_slots, bitmask,
-                                  stored_bytes, &lb, stream));
+    return from_hip(launch_encode(h->tabs, geo, h->sum.max_runs, h->sum.uniform != 0, src, n_tensors, dst_slots,
+                                  bitmask, stored_bytes, &lb, h->cu_count, stream));
 }
 
 static ibp_status decode_common(ibp_meta_t h, const void* slots, uint64_t n_slots, const uint32_t* bitmask,

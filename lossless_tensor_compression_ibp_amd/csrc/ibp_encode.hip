@@ -209,6 +209,208 @@ __global__ __launch_bounds__(256) void k_encode(Tables t, Geo geo, const uint8_t
     if (last && lane == 0) lb.totals[ti] = E;
 }
 
+// ---------------------------------------------------------------------------
+// Tensors of at most kMaxTileWords words with 16-byte aligned source and
+// slots: persistent workgroups, tables staged once in LDS, four words per lane
+// per step, and the next tensor's words in flight in registers while the
+// current one is packed.  The record is assembled in LDS (header words, then
+// the kept bits) and written with 16-byte stores; an incompressible tensor is
+// written from the registers that already hold it.
+// ---------------------------------------------------------------------------
+template <int RUNS, bool UNI, bool MW4, int STAGE>
+__global__ __launch_bounds__(256) void k_encode_small(Tables t, Geo geo, const uint8_t* __restrict__ src,
+                                                      uint64_t n_tensors, uint8_t* __restrict__ slots,
+                                                      uint32_t* __restrict__ bitmask, uint64_t* __restrict__ stored,
+                                                      uint32_t buf_words) {
+    extern __shared__ uint32_t smem[];
+    const uint32_t lane = lane_id();
+    const uint32_t wib = uniform(threadIdx.x / kWave);
+    const uint32_t Mw = geo.Mw;
+    // LDS: [m row + per-position tables (not for uniform metadata)][wave buffers]
+    const uint32_t rows = UNI ? 0u : 1u + tab_rows(RUNS);
+    for (uint32_t i = threadIdx.x; i < rows * Mw; i += blockDim.x) {
+        const uint32_t row = i / Mw, pos = i - row * Mw;
+        uint32_t v;
+        if (row == 0)
+            v = t.m[pos];
+        else if (row == 1)
+            v = t.b[pos];
+        else if (row == 2)
+            v = t.kd[pos];
+        else if (row < 3 + dx_rows(RUNS))
+            v = t.dx[(row - 3) * Mw + pos];
+        else
+            v = t.r[(row - 3 - dx_rows(RUNS)) * Mw + pos];
+        smem[i] = v;
+    }
+    __syncthreads();
+    uint32_t* buf = smem + ((rows * Mw + 3u) & ~3u) + wib * buf_words;
+    const uint32_t* mrow = smem;
+    const TabArrays ta{smem + Mw, smem + 2 * Mw, smem + 3 * Mw, smem + (3 + dx_rows(RUNS)) * Mw, Mw};
+    TabUniform<RUNS> tu;
+    uint32_t mu = 0;
+    if (UNI) {
+        tu = load_uniform<RUNS>(t, Mw);
+        mu = uniform(t.m[0]);
+    }
+
+    const uint32_t nw = (uint32_t)geo.n_words;
+    const uint32_t n4 = nw >> 2;
+    const uint32_t hw = (uint32_t)geo.hdr_words;
+    const uint32_t lg = geo.log2g;
+    const uint32_t g = 1u << lg;
+    const uint32_t step_inc = (uint32_t)(4 * kWave) % Mw;
+    const uint64_t stride = (uint64_t)gridDim.x * kWavesPerBlock;
+    uint64_t ti = (uint64_t)blockIdx.x * kWavesPerBlock + wib;
+    if (ti >= n_tensors) return;
+
+    u32x4 cur[STAGE], nxt[STAGE];
+    auto load_tensor = [&](uint64_t tn, u32x4 (&dst)[STAGE]) __attribute__((always_inline)) {
+        const u32x4* s4 = reinterpret_cast<const u32x4*>(src + tn * geo.L);
+#pragma unroll
+        for (int r = 0; r < STAGE; ++r) {
+            const uint32_t i = lane + (uint32_t)r * kWave;
+            if (i < n4) dst[r] = __builtin_nontemporal_load(s4 + i);
+        }
+    };
+    load_tensor(ti, cur);
+    for (; ti < n_tensors; ti += stride) {
+        const uint64_t tnext = ti + stride;
+        if (tnext < n_tensors) load_tensor(tnext, nxt);
+        // zero the record buffer: header words, then the kept bits
+        {
+            u32x4* b4 = reinterpret_cast<u32x4*>(buf);
+            for (uint32_t i = lane; i < (buf_words >> 2); i += kWave) b4[i] = u32x4{0u, 0u, 0u, 0u};
+        }
+        __builtin_amdgcn_wave_barrier();
+        uint32_t* pay = buf + hw;
+        uint32_t carry = 0;
+        uint32_t pos0 = UNI ? 0u : (4u * lane) % Mw;
+#pragma unroll
+        for (int s = 0; s < STAGE; ++s) {
+            const uint32_t lw0 = (uint32_t)s * (4 * kWave) + 4 * lane;
+            if ((uint32_t)s * (4 * kWave) >= nw) break;  // wave-uniform
+            const bool live = lw0 < nw;  // nw % 4 == 0: a live lane owns four words
+            const u32x4 xv = cur[s];
+            uint32_t x[4], m[4], bv[4], kd[4], pos[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) x[j] = xv[j];
+            if constexpr (UNI) {
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    pos[j] = 0;
+                    m[j] = mu;
+                    bv[j] = tu.bw(0);
+                    kd[j] = tu.kdw(0);
+                }
+            } else if constexpr (MW4) {
+                const u32x4 m4 = *reinterpret_cast<const u32x4*>(mrow + pos0);
+                const u32x4 b4 = ta.bw4(pos0), k4 = ta.kdw4(pos0);
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    pos[j] = pos0 + j;
+                    m[j] = m4[j];
+                    bv[j] = b4[j];
+                    kd[j] = k4[j];
+                }
+            } else {
+                pos[0] = pos0;
+#pragma unroll
+                for (int j = 1; j < 4; ++j) pos[j] = (pos[j - 1] + 1 == Mw) ? 0u : pos[j - 1] + 1;
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    m[j] = mrow[pos[j]];
+                    bv[j] = ta.bw(pos[j]);
+                    kd[j] = ta.kdw(pos[j]);
+                }
+            }
+            bool mis[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) mis[j] = live && ((x[j] ^ bv[j]) & m[j]) != 0;
+            // participation: a chunk matches when none of its words mismatches
+            bool p[4];
+            uint32_t hbits;  // this lane's header bits, already at their bit position
+            const uint32_t c0 = lw0 >> lg;
+            if (g == 1) {
+#pragma unroll
+                for (int j = 0; j < 4; ++j) p[j] = !mis[j];
+                hbits = (uint32_t)p[0] | ((uint32_t)p[1] << 1) | ((uint32_t)p[2] << 2) | ((uint32_t)p[3] << 3);
+            } else if (g == 2) {
+                const bool pa = !(mis[0] || mis[1]), pb = !(mis[2] || mis[3]);
+                p[0] = p[1] = pa;
+                p[2] = p[3] = pb;
+                hbits = (uint32_t)pa | ((uint32_t)pb << 1);
+            } else {
+                const uint32_t q = g >> 2;  // lanes per chunk
+                const uint64_t bal = ballot(mis[0] || mis[1] || mis[2] || mis[3]);
+                const uint32_t gs = lane & ~(q - 1u);
+                const uint64_t qmask = (q >= 64) ? ~0ull : ((1ull << q) - 1ull);
+                const bool pc = ((bal >> gs) & qmask) == 0;
+#pragma unroll
+                for (int j = 0; j < 4; ++j) p[j] = pc;
+                hbits = (lane & (q - 1u)) == 0 ? (uint32_t)pc : 0u;
+            }
+            if (live && hbits) atomicOr(&buf[c0 >> 5], hbits << (c0 & 31u));
+            uint32_t f[4], size[4];
+            uint32_t tot = 0;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                uint32_t e;
+                if constexpr (UNI)
+                    e = extract_t<RUNS>(tu, 0, kd[j], x[j]);
+                else
+                    e = extract_t<RUNS>(ta, pos[j], kd[j], x[j]);
+                f[j] = p[j] ? e : x[j];
+                size[j] = live ? (p[j] ? 32u - (kd[j] & 63u) : 32u) : 0u;
+                tot += size[j];
+            }
+            const uint32_t incl = wave_incl_scan(tot);
+            uint32_t off = carry + incl - tot;
+            carry += lane_value(incl, kWave - 1);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                if (size[j]) {
+                    const uint32_t q = off >> 5, sh = off & 31u;
+                    atomicOr(&pay[q], f[j] << sh);
+                    if (sh + size[j] > 32) atomicOr(&pay[q + 1], f[j] >> (32 - sh));
+                }
+                off += size[j];
+            }
+            if constexpr (!UNI) {
+                pos0 += step_inc;
+                if (pos0 >= Mw) pos0 -= Mw;
+            }
+        }
+        __builtin_amdgcn_wave_barrier();
+        const uint64_t R = 32ull * hw + carry;
+        const uint32_t words = (uint32_t)((R + 31) / 32);
+        const bool comp = 4ull * words < geo.L;
+        u32x4* slot4 = reinterpret_cast<u32x4*>(slots + ti * geo.L);
+        if (comp) {
+            const uint32_t w4 = (words + 3) >> 2;  // <= n4: the slot is a multiple of 16 bytes
+            const u32x4* b4 = reinterpret_cast<const u32x4*>(buf);
+            for (uint32_t i = lane; i < w4; i += kWave) __builtin_nontemporal_store(b4[i], slot4 + i);
+        } else {
+#pragma unroll
+            for (int r = 0; r < STAGE; ++r) {
+                const uint32_t i = lane + (uint32_t)r * kWave;
+                if (i < n4) __builtin_nontemporal_store(cur[r], slot4 + i);
+            }
+        }
+        if (lane == 0) {
+            const uint32_t bit = 1u << (ti & 31);
+            if (comp)
+                atomicOr(&bitmask[ti >> 5], bit);
+            else
+                atomicAnd(&bitmask[ti >> 5], ~bit);
+            if (stored) stored[ti] = comp ? 4ull * words : geo.L;
+        }
+        __builtin_amdgcn_wave_barrier();
+#pragma unroll
+        for (int r = 0; r < STAGE; ++r) cur[r] = nxt[r];
+    }
+}
+
 // After the tiles of long tensors: bitmask bit, stored bytes, and the raw
 // copy of a tensor whose record is not shorter than its slot.
 __global__ __launch_bounds__(256) void k_encode_finalize(Geo geo, const uint8_t* __restrict__ src,
@@ -264,16 +466,68 @@ static hipError_t launch_encode_t(const Tables& t, const Geo& geo, uint32_t runs
     return hipGetLastError();
 }
 
-hipError_t launch_encode(const Tables& t, const Geo& geo, uint32_t runs, const void* src,
-                         uint64_t n_tensors, void* slots, uint32_t* bitmask, uint64_t* stored,
-                         const LookBack* lb, hipStream_t s) {
-    if (n_tensors == 0) return hipSuccess;
+// LDS bytes k_encode_small needs per workgroup (0: it cannot run).
+static size_t small_encode_lds(const Geo& geo, int runs, bool uni, uint32_t* buf_words) {
+    // header words + kept bits + 2 spare words, rounded to 16 bytes
+    *buf_words = ((uint32_t)geo.hdr_words + (uint32_t)geo.n_words + 2 + 3) & ~3u;
+    const uint64_t tab = uni ? 0 : (uint64_t)(1 + tab_rows(runs)) * geo.Mw * 4;
+    if (tab > kMaxLdsTableBytes) return 0;
+    const uint64_t total = ((tab + 15) & ~15ull) + (uint64_t)kWavesPerBlock * *buf_words * 4;
+    return total <= kMaxLdsPerBlock ? (size_t)total : 0;
+}
+
+template <int RUNS, bool UNI>
+static hipError_t launch_encode_small(const Tables& t, const Geo& geo, const void* src, uint64_t n_tensors,
+                                      void* slots, uint32_t* bitmask, uint64_t* stored, uint32_t cu_count,
+                                      size_t shm, uint32_t buf_words, hipStream_t s) {
+    uint32_t per_cu = (uint32_t)(kLdsPerCu / shm);
+    if (per_cu > 8) per_cu = 8;
+    if (per_cu < 1) per_cu = 1;
+    const uint64_t want = (n_tensors + kWavesPerBlock - 1) / kWavesPerBlock;
+    const uint64_t cap = (uint64_t)cu_count * per_cu;
+    const dim3 grid((uint32_t)(want < cap ? want : cap));
+    const dim3 block(kWave * kWavesPerBlock);
+    const uint8_t* sr = static_cast<const uint8_t*>(src);
+    uint8_t* sl = static_cast<uint8_t*>(slots);
+    const uint32_t stage = (uint32_t)((geo.n_words + 4 * kWave - 1) / (4 * kWave));
+#define IBP_ENC_SMALL(S)                                                                                 \
+    if (geo.Mw % 4 == 0)                                                                                 \
+        hipLaunchKernelGGL((k_encode_small<RUNS, UNI, true, S>), grid, block, shm, s, t, geo, sr, n_tensors, \
+                           sl, bitmask, stored, buf_words);                                              \
+    else                                                                                                 \
+        hipLaunchKernelGGL((k_encode_small<RUNS, UNI, false, S>), grid, block, shm, s, t, geo, sr,         \
+                           n_tensors, sl, bitmask, stored, buf_words)
+    if (stage <= 1)
+        IBP_ENC_SMALL(1);
+    else if (stage <= 2)
+        IBP_ENC_SMALL(2);
+    else if (stage <= 4)
+        IBP_ENC_SMALL(4);
+    else
+        IBP_ENC_SMALL(8);
+#undef IBP_ENC_SMALL
+    return hipGetLastError();
+}
+
+template <int RUNS>
+static hipError_t launch_encode_r(const Tables& t, const Geo& geo, bool uniform_meta, const void* src,
+                                  uint64_t n_tensors, void* slots, uint32_t* bitmask, uint64_t* stored,
+                                  const LookBack* lb, uint32_t cu_count, hipStream_t s) {
     const uint32_t lds_words = 64 + geo.tile_words + 8;
-    if (geo.tiles_per_tensor == 1)
-        return launch_encode_t<false>(t, geo, runs, src, n_tensors, slots, bitmask, stored, LookBack{},
-                                      lds_words, s);
-    hipError_t e = launch_encode_t<true>(t, geo, runs, src, n_tensors, slots, bitmask, stored, *lb,
-                                         lds_words, s);
+    if (geo.tiles_per_tensor == 1) {
+        uint32_t buf_words = 0;
+        const size_t shm = small_encode_lds(geo, RUNS, uniform_meta, &buf_words);
+        if (geo.aligned16 && shm) {
+            if (uniform_meta)
+                return launch_encode_small<RUNS, true>(t, geo, src, n_tensors, slots, bitmask, stored, cu_count,
+                                                       shm, buf_words, s);
+            return launch_encode_small<RUNS, false>(t, geo, src, n_tensors, slots, bitmask, stored, cu_count, shm,
+                                                    buf_words, s);
+        }
+        return launch_encode_t<false>(t, geo, RUNS, src, n_tensors, slots, bitmask, stored, LookBack{}, lds_words,
+                                      s);
+    }
+    hipError_t e = launch_encode_t<true>(t, geo, RUNS, src, n_tensors, slots, bitmask, stored, *lb, lds_words, s);
     if (e != hipSuccess) return e;
     uint64_t per = (geo.n_words + 256ull * 64 - 1) / (256ull * 64);  // ~64 words per thread
     if (per > 1024) per = 1024;
@@ -282,6 +536,21 @@ hipError_t launch_encode(const Tables& t, const Geo& geo, uint32_t runs, const v
                        static_cast<const uint8_t*>(src), static_cast<uint8_t*>(slots), bitmask, stored,
                        lb->totals, bpt);
     return hipGetLastError();
+}
+
+hipError_t launch_encode(const Tables& t, const Geo& geo, uint32_t runs, bool uniform_meta, const void* src,
+                         uint64_t n_tensors, void* slots, uint32_t* bitmask, uint64_t* stored, const LookBack* lb,
+                         uint32_t cu_count, hipStream_t s) {
+    if (n_tensors == 0) return hipSuccess;
+    switch (runs_bucket(runs)) {
+        case 0: return launch_encode_r<0>(t, geo, uniform_meta, src, n_tensors, slots, bitmask, stored, lb, cu_count, s);
+        case 1: return launch_encode_r<1>(t, geo, uniform_meta, src, n_tensors, slots, bitmask, stored, lb, cu_count, s);
+        case 2: return launch_encode_r<2>(t, geo, uniform_meta, src, n_tensors, slots, bitmask, stored, lb, cu_count, s);
+        case 3: return launch_encode_r<3>(t, geo, uniform_meta, src, n_tensors, slots, bitmask, stored, lb, cu_count, s);
+        case 4: return launch_encode_r<4>(t, geo, uniform_meta, src, n_tensors, slots, bitmask, stored, lb, cu_count, s);
+        case 8: return launch_encode_r<8>(t, geo, uniform_meta, src, n_tensors, slots, bitmask, stored, lb, cu_count, s);
+        default: return launch_encode_r<16>(t, geo, uniform_meta, src, n_tensors, slots, bitmask, stored, lb, cu_count, s);
+    }
 }
 
 }  // namespace ibp

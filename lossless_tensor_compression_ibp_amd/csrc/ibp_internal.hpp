@@ -77,9 +77,9 @@ hipError_t launch_meta_finalize(const uint32_t* counts, uint32_t Mw, uint64_t n_
 hipError_t launch_tables(const uint32_t* mask, const uint32_t* bitval, uint32_t Mw, uint32_t Pc,
                          uint32_t g, uint32_t G, uint32_t* kd, uint32_t* dx, uint32_t* r,
                          uint32_t* planes, Summary* summary, hipStream_t s);
-hipError_t launch_encode(const Tables& t, const Geo& geo, uint32_t runs, const void* src,
-                         uint64_t n_tensors, void* slots, uint32_t* bitmask, uint64_t* stored,
-                         const LookBack* lb, hipStream_t s);
+hipError_t launch_encode(const Tables& t, const Geo& geo, uint32_t runs, bool uniform_meta, const void* src,
+                         uint64_t n_tensors, void* slots, uint32_t* bitmask, uint64_t* stored, const LookBack* lb,
+                         uint32_t cu_count, hipStream_t s);
 hipError_t launch_decode(const Tables& t, const Geo& geo, uint32_t runs, bool uniform_meta, const void* slots,
                          uint64_t n_slots, const uint32_t* bitmask, const int64_t* ids, uint64_t n_out,
                          void* dst, uint32_t* err, const LookBack* lb, uint32_t cu_count, hipStream_t s);
