@@ -181,26 +181,24 @@ __global__ __launch_bounds__(256) void k_decode_small(Tables t, Geo geo, const u
     const uint32_t n4_raw = nwords >> 2;
     const uint32_t n4_spec = geo.spec_words >> 2;
     const uint32_t hw = (uint32_t)geo.hdr_words;
-    const uint64_t stride = (uint64_t)gridDim.x * kWavesPerBlock;
-    const uint64_t first = (uint64_t)blockIdx.x * kWavesPerBlock + wib;
+    const uint32_t wpb = blockDim.x / kWave;
+    const uint64_t stride = (uint64_t)gridDim.x * wpb;
+    const uint64_t first = (uint64_t)blockIdx.x * wpb + wib;
     if (first >= n_out) return;
     const uint64_t my_tiles = (n_out - first + stride - 1) / stride;
 
     u32x4 st[STAGE];
     for (uint64_t base = 0; base < my_tiles; base += kWave) {
         const uint32_t cnt = (uint32_t)min((uint64_t)kWave, my_tiles - base);
-        // lane k: id and bitmask bit of tile base + k
+        // lane k: id of tile base + k; the first read of tile 0 (the same
+        // prefix for raw and compressed slots) goes out before the bitmask
+        // bits are fetched, so the two loads overlap
         int64_t my_tensor = -1;
-        uint32_t my_comp = 0;
         if (lane < cnt) {
             const uint64_t oi = first + (base + lane) * stride;
             const int64_t id = ids ? ids[oi] : (int64_t)oi;
-            if (id >= 0 && (uint64_t)id < n_slots) {
-                my_tensor = id;
-                my_comp = (bitmask[(uint64_t)id >> 5] >> ((uint64_t)id & 31)) & 1u;
-            }
+            if (id >= 0 && (uint64_t)id < n_slots) my_tensor = id;
         }
-        if (ballot(lane < cnt && my_tensor < 0)) latch_error(err, kErrRange);
         const uint32_t t_lo = (uint32_t)my_tensor, t_hi = (uint32_t)((uint64_t)my_tensor >> 32);
 
         auto tensor_of = [&](uint32_t k) __attribute__((always_inline)) -> int64_t {
@@ -210,34 +208,40 @@ __global__ __launch_bounds__(256) void k_decode_small(Tables t, Geo geo, const u
             const int64_t tn = tensor_of(k);
             if (tn < 0) return;
             const u32x4* s4 = reinterpret_cast<const u32x4*>(slots + (uint64_t)tn * geo.L);
-            const uint32_t n4 = lane_value(my_comp, k) ? n4_spec : n4_raw;
 #pragma unroll
             for (int r = 0; r < STAGE; ++r) {
                 const uint32_t i = lane + (uint32_t)r * kWave;
-                if (i < n4) st[r] = __builtin_nontemporal_load(s4 + i);
+                if (i < n4_spec) st[r] = __builtin_nontemporal_load(s4 + i);
             }
         };
 
         issue(0);
+        uint32_t my_comp = 0;
+        if (lane < cnt && my_tensor >= 0)
+            my_comp = (bitmask[(uint64_t)my_tensor >> 5] >> ((uint64_t)my_tensor & 31)) & 1u;
+        if (ballot(lane < cnt && my_tensor < 0)) latch_error(err, kErrRange);
         for (uint32_t k = 0; k < cnt; ++k) {
             const int64_t tn = tensor_of(k);
             const uint32_t comp = lane_value(my_comp, k);
             const uint64_t oi = first + (base + k) * stride;
             uint32_t* out = reinterpret_cast<uint32_t*>(dst + oi * geo.L);
-            const uint32_t n4 = comp ? n4_spec : n4_raw;
             if (tn >= 0) {
                 if (comp) {
 #pragma unroll
                     for (int r = 0; r < STAGE; ++r) {
                         const uint32_t i = lane + (uint32_t)r * kWave;
-                        if (i < n4) reinterpret_cast<u32x4*>(buf)[i] = st[r];
+                        if (i < n4_spec) reinterpret_cast<u32x4*>(buf)[i] = st[r];
                     }
                 } else {
+                    // raw slot: the prefix from registers, the rest copied
 #pragma unroll
                     for (int r = 0; r < STAGE; ++r) {
                         const uint32_t i = lane + (uint32_t)r * kWave;
-                        if (i < n4) __builtin_nontemporal_store(st[r], reinterpret_cast<u32x4*>(out) + i);
+                        if (i < n4_spec) __builtin_nontemporal_store(st[r], reinterpret_cast<u32x4*>(out) + i);
                     }
+                    if (n4_spec < n4_raw)
+                        copy_words(reinterpret_cast<const uint32_t*>(slots + (uint64_t)tn * geo.L), out,
+                                   4ull * n4_spec, 4u * (n4_raw - n4_spec), true);
                 }
             }
             if (k + 1 < cnt) issue(k + 1);
@@ -388,49 +392,51 @@ static uint32_t runs_bucket(uint32_t runs) {
     return 16;
 }
 
-// LDS bytes k_decode_small needs per workgroup, or 0 when it cannot run
-// (tables or planes too large for LDS).
-static size_t small_lds_bytes(const Geo& geo, int runs, bool uni, uint32_t* buf_words) {
+// LDS k_decode_small shares per workgroup (tables, planes) and needs per
+// wave (record buffer); false when the tables do not fit.
+static bool small_lds(const Geo& geo, int runs, bool uni, uint32_t* buf_words, size_t* head, size_t* wave) {
     *buf_words = ((uint32_t)geo.n_words + 8 + 3) & ~3u;
     const uint64_t tab = uni ? 0 : (uint64_t)tab_rows(runs) * geo.Mw * 4;
     const uint64_t planes = (uint64_t)(geo.Pc / geo.G) * kPlanes * 4;
-    if (tab > kMaxLdsTableBytes || planes > kMaxLdsPlaneBytes) return 0;
-    const uint64_t head = ((tab + planes) + 15) & ~15ull;
-    const uint64_t total = head + (uint64_t)kWavesPerBlock * *buf_words * 4;
-    return total <= kMaxLdsPerBlock ? (size_t)total : 0;
+    if (tab > kMaxLdsTableBytes || planes > kMaxLdsPlaneBytes) return false;
+    *head = (size_t)(((tab + planes) + 15) & ~15ull);
+    *wave = (size_t)*buf_words * 4;
+    return true;
+}
+
+template <int RUNS, bool UNI, bool MW4, int S>
+static hipError_t launch_small_s(const Tables& t, const Geo& geo, const void* slots, uint64_t n_slots,
+                                 const uint32_t* bitmask, const int64_t* ids, uint64_t n_out, void* dst,
+                                 uint32_t* err, uint32_t cu_count, size_t head, size_t wave, uint32_t buf_words,
+                                 hipStream_t s, bool* launched) {
+    const void* fn = reinterpret_cast<const void*>(&k_decode_small<RUNS, UNI, MW4, S>);
+    PersistentPlan plan;
+    *launched = false;
+    if (!plan_persistent(fn, head, wave, cu_count, n_out, &plan)) return hipSuccess;
+    hipLaunchKernelGGL((k_decode_small<RUNS, UNI, MW4, S>), dim3(plan.blocks), dim3(kWave * plan.wpb), plan.shm, s,
+                       t, geo, static_cast<const uint8_t*>(slots), n_slots, bitmask, ids, n_out,
+                       static_cast<uint8_t*>(dst), err, buf_words);
+    *launched = true;
+    return hipGetLastError();
 }
 
 template <int RUNS, bool UNI>
 static hipError_t launch_small(const Tables& t, const Geo& geo, const void* slots, uint64_t n_slots,
                                const uint32_t* bitmask, const int64_t* ids, uint64_t n_out, void* dst,
-                               uint32_t* err, uint32_t cu_count, size_t shm, uint32_t buf_words, hipStream_t s) {
-    uint32_t per_cu = (uint32_t)(kLdsPerCu / shm);
-    if (per_cu > 8) per_cu = 8;
-    if (per_cu < 1) per_cu = 1;
-    const uint64_t want = (n_out + kWavesPerBlock - 1) / kWavesPerBlock;
-    const uint64_t cap = (uint64_t)cu_count * per_cu;
-    const dim3 grid((uint32_t)(want < cap ? want : cap));
-    const dim3 block(kWave * kWavesPerBlock);
-    const uint8_t* sl = static_cast<const uint8_t*>(slots);
-    uint8_t* d = static_cast<uint8_t*>(dst);
+                               uint32_t* err, uint32_t cu_count, size_t head, size_t wave, uint32_t buf_words,
+                               hipStream_t s, bool* launched) {
     const uint32_t stage = (uint32_t)((geo.n_words + 4 * kWave - 1) / (4 * kWave));
-#define IBP_SMALL(S)                                                                                      \
-    if (geo.Mw % 4 == 0)                                                                                  \
-        hipLaunchKernelGGL((k_decode_small<RUNS, UNI, true, S>), grid, block, shm, s, t, geo, sl, n_slots,  \
-                           bitmask, ids, n_out, d, err, buf_words);                                       \
-    else                                                                                                  \
-        hipLaunchKernelGGL((k_decode_small<RUNS, UNI, false, S>), grid, block, shm, s, t, geo, sl, n_slots, \
-                           bitmask, ids, n_out, d, err, buf_words)
-    if (stage <= 1)
-        IBP_SMALL(1);
-    else if (stage <= 2)
-        IBP_SMALL(2);
-    else if (stage <= 4)
-        IBP_SMALL(4);
-    else
-        IBP_SMALL(8);
+    const bool mw4 = geo.Mw % 4 == 0;
+#define IBP_SMALL(S)                                                                                          \
+    return mw4 ? launch_small_s<RUNS, UNI, true, S>(t, geo, slots, n_slots, bitmask, ids, n_out, dst, err,     \
+                                                    cu_count, head, wave, buf_words, s, launched)               \
+               : launch_small_s<RUNS, UNI, false, S>(t, geo, slots, n_slots, bitmask, ids, n_out, dst, err,    \
+                                                     cu_count, head, wave, buf_words, s, launched)
+    if (stage <= 1) IBP_SMALL(1);
+    if (stage <= 2) IBP_SMALL(2);
+    if (stage <= 4) IBP_SMALL(4);
+    IBP_SMALL(8);
 #undef IBP_SMALL
-    return hipGetLastError();
 }
 
 template <int RUNS, bool UNI, bool MULTI>
@@ -455,10 +461,13 @@ static hipError_t launch_decode_r(const Tables& t, const Geo& geo, const void* s
     if (geo.tiles_per_tensor > 1)
         return launch_tiles<RUNS, UNI, true>(t, geo, slots, n_slots, bitmask, ids, n_out, dst, err, *lb, s);
     uint32_t buf_words = 0;
-    const size_t shm = small_lds_bytes(geo, RUNS, UNI, &buf_words);
-    if (geo.aligned16 && shm)
-        return launch_small<RUNS, UNI>(t, geo, slots, n_slots, bitmask, ids, n_out, dst, err, cu_count, shm,
-                                       buf_words, s);
+    size_t head = 0, wave = 0;
+    if (geo.aligned16 && small_lds(geo, RUNS, UNI, &buf_words, &head, &wave)) {
+        bool launched = false;
+        const hipError_t e = launch_small<RUNS, UNI>(t, geo, slots, n_slots, bitmask, ids, n_out, dst, err, cu_count,
+                                                     head, wave, buf_words, s, &launched);
+        if (e != hipSuccess || launched) return e;
+    }
     return launch_tiles<RUNS, UNI, false>(t, geo, slots, n_slots, bitmask, ids, n_out, dst, err, LookBack{}, s);
 }
 

@@ -260,8 +260,9 @@ __global__ __launch_bounds__(256) void k_encode_small(Tables t, Geo geo, const u
     const uint32_t lg = geo.log2g;
     const uint32_t g = 1u << lg;
     const uint32_t step_inc = (uint32_t)(4 * kWave) % Mw;
-    const uint64_t stride = (uint64_t)gridDim.x * kWavesPerBlock;
-    uint64_t ti = (uint64_t)blockIdx.x * kWavesPerBlock + wib;
+    const uint32_t wpb = blockDim.x / kWave;
+    const uint64_t stride = (uint64_t)gridDim.x * wpb;
+    uint64_t ti = (uint64_t)blockIdx.x * wpb + wib;
     if (ti >= n_tensors) return;
 
     u32x4 cur[STAGE], nxt[STAGE];
@@ -466,47 +467,51 @@ static hipError_t launch_encode_t(const Tables& t, const Geo& geo, uint32_t runs
     return hipGetLastError();
 }
 
-// LDS bytes k_encode_small needs per workgroup (0: it cannot run).
-static size_t small_encode_lds(const Geo& geo, int runs, bool uni, uint32_t* buf_words) {
+// LDS k_encode_small shares per workgroup (tables) and needs per wave (record
+// buffer); false when the tables do not fit.
+static bool small_encode_lds(const Geo& geo, int runs, bool uni, uint32_t* buf_words, size_t* head,
+                             size_t* wave) {
     // header words + kept bits + 2 spare words, rounded to 16 bytes
     *buf_words = ((uint32_t)geo.hdr_words + (uint32_t)geo.n_words + 2 + 3) & ~3u;
     const uint64_t tab = uni ? 0 : (uint64_t)(1 + tab_rows(runs)) * geo.Mw * 4;
-    if (tab > kMaxLdsTableBytes) return 0;
-    const uint64_t total = ((tab + 15) & ~15ull) + (uint64_t)kWavesPerBlock * *buf_words * 4;
-    return total <= kMaxLdsPerBlock ? (size_t)total : 0;
+    if (tab > kMaxLdsTableBytes) return false;
+    *head = (size_t)((tab + 15) & ~15ull);
+    *wave = (size_t)*buf_words * 4;
+    return true;
+}
+
+template <int RUNS, bool UNI, bool MW4, int S>
+static hipError_t launch_encode_small_s(const Tables& t, const Geo& geo, const void* src, uint64_t n_tensors,
+                                        void* slots, uint32_t* bitmask, uint64_t* stored, uint32_t cu_count,
+                                        size_t head, size_t wave, uint32_t buf_words, hipStream_t s,
+                                        bool* launched) {
+    const void* fn = reinterpret_cast<const void*>(&k_encode_small<RUNS, UNI, MW4, S>);
+    PersistentPlan plan;
+    *launched = false;
+    if (!plan_persistent(fn, head, wave, cu_count, n_tensors, &plan)) return hipSuccess;
+    hipLaunchKernelGGL((k_encode_small<RUNS, UNI, MW4, S>), dim3(plan.blocks), dim3(kWave * plan.wpb), plan.shm, s,
+                       t, geo, static_cast<const uint8_t*>(src), n_tensors, static_cast<uint8_t*>(slots), bitmask,
+                       stored, buf_words);
+    *launched = true;
+    return hipGetLastError();
 }
 
 template <int RUNS, bool UNI>
 static hipError_t launch_encode_small(const Tables& t, const Geo& geo, const void* src, uint64_t n_tensors,
                                       void* slots, uint32_t* bitmask, uint64_t* stored, uint32_t cu_count,
-                                      size_t shm, uint32_t buf_words, hipStream_t s) {
-    uint32_t per_cu = (uint32_t)(kLdsPerCu / shm);
-    if (per_cu > 8) per_cu = 8;
-    if (per_cu < 1) per_cu = 1;
-    const uint64_t want = (n_tensors + kWavesPerBlock - 1) / kWavesPerBlock;
-    const uint64_t cap = (uint64_t)cu_count * per_cu;
-    const dim3 grid((uint32_t)(want < cap ? want : cap));
-    const dim3 block(kWave * kWavesPerBlock);
-    const uint8_t* sr = static_cast<const uint8_t*>(src);
-    uint8_t* sl = static_cast<uint8_t*>(slots);
+                                      size_t head, size_t wave, uint32_t buf_words, hipStream_t s, bool* launched) {
     const uint32_t stage = (uint32_t)((geo.n_words + 4 * kWave - 1) / (4 * kWave));
-#define IBP_ENC_SMALL(S)                                                                                 \
-    if (geo.Mw % 4 == 0)                                                                                 \
-        hipLaunchKernelGGL((k_encode_small<RUNS, UNI, true, S>), grid, block, shm, s, t, geo, sr, n_tensors, \
-                           sl, bitmask, stored, buf_words);                                              \
-    else                                                                                                 \
-        hipLaunchKernelGGL((k_encode_small<RUNS, UNI, false, S>), grid, block, shm, s, t, geo, sr,         \
-                           n_tensors, sl, bitmask, stored, buf_words)
-    if (stage <= 1)
-        IBP_ENC_SMALL(1);
-    else if (stage <= 2)
-        IBP_ENC_SMALL(2);
-    else if (stage <= 4)
-        IBP_ENC_SMALL(4);
-    else
-        IBP_ENC_SMALL(8);
+    const bool mw4 = geo.Mw % 4 == 0;
+#define IBP_ENC_SMALL(S)                                                                                        \
+    return mw4 ? launch_encode_small_s<RUNS, UNI, true, S>(t, geo, src, n_tensors, slots, bitmask, stored,      \
+                                                           cu_count, head, wave, buf_words, s, launched)         \
+               : launch_encode_small_s<RUNS, UNI, false, S>(t, geo, src, n_tensors, slots, bitmask, stored,     \
+                                                            cu_count, head, wave, buf_words, s, launched)
+    if (stage <= 1) IBP_ENC_SMALL(1);
+    if (stage <= 2) IBP_ENC_SMALL(2);
+    if (stage <= 4) IBP_ENC_SMALL(4);
+    IBP_ENC_SMALL(8);
 #undef IBP_ENC_SMALL
-    return hipGetLastError();
 }
 
 template <int RUNS>
@@ -516,13 +521,15 @@ static hipError_t launch_encode_r(const Tables& t, const Geo& geo, bool uniform_
     const uint32_t lds_words = 64 + geo.tile_words + 8;
     if (geo.tiles_per_tensor == 1) {
         uint32_t buf_words = 0;
-        const size_t shm = small_encode_lds(geo, RUNS, uniform_meta, &buf_words);
-        if (geo.aligned16 && shm) {
-            if (uniform_meta)
-                return launch_encode_small<RUNS, true>(t, geo, src, n_tensors, slots, bitmask, stored, cu_count,
-                                                       shm, buf_words, s);
-            return launch_encode_small<RUNS, false>(t, geo, src, n_tensors, slots, bitmask, stored, cu_count, shm,
-                                                    buf_words, s);
+        size_t head = 0, wave = 0;
+        if (geo.aligned16 && small_encode_lds(geo, RUNS, uniform_meta, &buf_words, &head, &wave)) {
+            bool launched = false;
+            const hipError_t e =
+                uniform_meta ? launch_encode_small<RUNS, true>(t, geo, src, n_tensors, slots, bitmask, stored,
+                                                               cu_count, head, wave, buf_words, s, &launched)
+                             : launch_encode_small<RUNS, false>(t, geo, src, n_tensors, slots, bitmask, stored,
+                                                                cu_count, head, wave, buf_words, s, &launched);
+            if (e != hipSuccess || launched) return e;
         }
         return launch_encode_t<false>(t, geo, RUNS, src, n_tensors, slots, bitmask, stored, LookBack{}, lds_words,
                                       s);

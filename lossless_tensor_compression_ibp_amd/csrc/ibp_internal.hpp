@@ -68,7 +68,23 @@ struct Summary {
     unsigned long long removed_per_period;  // sum of k over the period
 };
 
-// Kernel launchers (ibp_kernels.hip).  All return hipError_t of the launch.
+// Launch shape of a persistent kernel: waves per workgroup, workgroups, and
+// dynamic LDS per workgroup.
+struct PersistentPlan {
+    uint32_t wpb = 0;
+    uint32_t blocks = 0;
+    size_t shm = 0;
+};
+
+// Chooses the waves per workgroup (currently 4) that keeps the most waves resident
+// per compute unit, given LDS shared by a workgroup (head_bytes), LDS per wave
+// (wave_bytes), the kernel's VGPR count and the LDS limits of the device.
+// blocks = min(workgroups that fill the device, items / wpb).  Returns false
+// when no shape fits.
+bool plan_persistent(const void* kernel, size_t head_bytes, size_t wave_bytes, uint32_t cu_count,
+                     uint64_t n_items, PersistentPlan* plan);
+
+// Kernel launchers.  All return hipError_t of the launch.
 hipError_t launch_fill_u32(uint32_t* p, uint64_t n, uint32_t v, hipStream_t s);
 hipError_t launch_meta_hist(const uint32_t* sample, uint64_t n_words, uint32_t Mw, uint32_t* counts,
                             hipStream_t s);

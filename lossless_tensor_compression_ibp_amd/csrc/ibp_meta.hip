@@ -175,4 +175,51 @@ hipError_t launch_tables(const uint32_t* mask, const uint32_t* bitval, uint32_t 
     return hipGetLastError();
 }
 
+bool plan_persistent(const void* kernel, size_t head_bytes, size_t wave_bytes, uint32_t cu_count,
+                     uint64_t n_items, PersistentPlan* plan) {
+    hipFuncAttributes attr;
+    uint32_t vgprs = 64;
+    if (hipFuncGetAttributes(&attr, kernel) == hipSuccess && attr.numRegs > 0) vgprs = (uint32_t)attr.numRegs;
+    (void)hipGetLastError();
+    int dev = 0, max_block_lds = 65536;
+    if (hipGetDevice(&dev) == hipSuccess)
+        (void)hipDeviceGetAttribute(&max_block_lds, hipDeviceAttributeMaxSharedMemoryPerBlock, dev);
+    (void)hipGetLastError();
+    const uint64_t block_cap = max_block_lds > 0 ? (uint64_t)max_block_lds : 65536;
+    // 512 VGPRs per SIMD lane, at most 8 waves per SIMD, 4 SIMDs per CU
+    uint32_t per_simd = 512 / ((vgprs + 7) & ~7u);
+    if (per_simd > 8) per_simd = 8;
+    if (per_simd < 1) per_simd = 1;
+    const uint32_t cu_waves = 4 * per_simd;
+    PersistentPlan best;
+    uint32_t best_waves = 0;
+    // Larger workgroups (8-16 waves sharing one table copy) were measured
+    // slower than four-wave groups on gfx950, so only four is tried.
+    for (uint32_t wpb : {4u}) {
+        const uint64_t shm = ((head_bytes + 15) & ~(size_t)15) + (uint64_t)wpb * wave_bytes;
+        if (shm > block_cap || shm > kLdsPerCu) continue;
+        uint64_t wgs = shm ? kLdsPerCu / shm : 64;
+        if (wgs * wpb > cu_waves) wgs = cu_waves / wpb;
+        if (wgs == 0) continue;
+        const uint32_t waves = (uint32_t)(wgs * wpb);
+        if (waves > best_waves) {
+            best_waves = waves;
+            best.wpb = wpb;
+            best.shm = (size_t)shm;
+            best.blocks = (uint32_t)(wgs * cu_count);
+        }
+    }
+    if (!best_waves) return false;
+    const uint64_t want = (n_items + best.wpb - 1) / best.wpb;
+    if (want < best.blocks) best.blocks = (uint32_t)want;
+    if (best.shm > 65536) {
+        if (hipFuncSetAttribute(kernel, hipFuncAttributeMaxDynamicSharedMemorySize, (int)best.shm) != hipSuccess) {
+            (void)hipGetLastError();
+            return false;
+        }
+    }
+    *plan = best;
+    return true;
+}
+
 }  // namespace ibp
