@@ -52,11 +52,19 @@ def kernel_source_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def measured_traffic(workload: str):
-    """HBM bytes per launch of the workload's decode kernel from the committed
+TRAFFIC_NOTE_LINK = ("bytes per launch from rocprofv3 FETCH_SIZE (host reads over the link plus the few HBM "
+                     "reads of ids and bitmask) and WRITE_SIZE (decoded rows into HBM), each scaled by what the "
+                     "counter reads for a copy of known size with the same access pattern; zero-copy reads move "
+                     "whole 128-byte lines")
+
+
+def measured_traffic(workload: str | None):
+    """Bytes per launch of the workload's decode kernel from the committed
     rocprofv3 counter runs (FETCH_SIZE and WRITE_SIZE, each scaled by what it
-    reads for a plain elementwise kernel of known size), or None when the
-    kernels changed since the counters were taken."""
+    reads for a copy kernel of known size), or None when the kernels changed
+    since the counters were taken."""
+    if workload is None:
+        return None
     path = os.path.join(ROOT, "profiles", "traffic.json")
     try:
         with open(path) as f:
@@ -127,6 +135,24 @@ def timed(fn, steps: int, warmup: int):
     wall = time.perf_counter() - t0
     durs = np.array([s.elapsed_time(e) / 1e3 for s, e in evs])
     return wall, durs
+
+
+def queued_durations(fn, steps: int, first: int = 0):
+    """Average launch duration of `steps` calls queued behind a bounded spin
+    kernel so that the GPU runs them back to back (one event pair over the
+    whole region, divided by the launches): for launches shorter than the
+    host's submission time, events around each launch would also measure the
+    idle gap before it."""
+    stream = torch.cuda.current_stream()
+    torch.cuda.synchronize()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda._sleep(50_000_000)
+    start.record(stream)
+    for i in range(steps):
+        fn(first + i)
+    end.record(stream)
+    torch.cuda.synchronize()
+    return np.full(steps, start.elapsed_time(end) / 1e3 / steps)
 
 
 def cpu_oracle_gather(raw_rows: np.ndarray, w: WL.Workload, batch: int, budget_s: float,
@@ -248,9 +274,8 @@ def run_sparse_gnn(args) -> dict:
             "peak": PCIE5_X16_GBPS,
             "unit": "GB/s",
             "frac": round(achieved / PCIE5_X16_GBPS, 4),
-            "traffic": measured_traffic("sparse_gnn"),
-            "traffic_note": "FETCH_SIZE*2 + WRITE_SIZE per launch; FETCH_SIZE includes the zero-copy host reads, "
-                            "which move whole 128-byte lines",
+            "traffic": None if args.small else measured_traffic("sparse_gnn"),
+            "traffic_note": TRAFFIC_NOTE_LINK,
             "link_ceiling_measured": round(h2d, 3),
             "frac_of_measured_ceiling": round(achieved / h2d, 4),
             "algorithmic_bytes_per_launch": int(link_bytes.mean()),
@@ -298,8 +323,7 @@ def run_kv_bf16(args) -> dict:
     if not torch.equal(out, src):
         raise SystemExit("decoded pages differ")
     hbm_bytes = float(stored_np.sum() + n * L + 4 * ((n + 31) // 32))
-    roof = hbm_roofline(hbm_bytes, durs)
-    roof["traffic"] = measured_traffic("kv_bf16") if layers == 32 else None
+    roof = hbm_roofline(hbm_bytes, durs, None if args.small else "kv_bf16")
     return base_result(
         args, n * L * args.steps / wall / GB, wall,
         {"workload": f"kv_bf16: {layers} layers x 32 heads x 4096 tokens x 128 bf16, 4 KiB pages in HBM slots, "
@@ -324,19 +348,20 @@ def base_result(args, value, wall, config, savings, kernel, durs, roofline, **ex
     return res
 
 
-def hbm_roofline(bytes_per_launch: float, durs) -> dict:
+def hbm_roofline(bytes_per_launch: float, durs, workload: str) -> dict:
     achieved = bytes_per_launch / float(np.mean(durs)) / GB
     return {"bound": "hbm", "achieved": round(achieved, 3), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-            "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": None,
+            "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": measured_traffic(workload),
             "copy_kernel_ceiling_measured": round(copy_kernel_ceiling(), 3),
             "algorithmic_bytes_per_launch": int(bytes_per_launch)}
 
 
-def link_roofline(link_bytes_per_launch: float, durs, savings: float) -> dict:
+def link_roofline(link_bytes_per_launch: float, durs, savings: float, workload: str) -> dict:
     achieved = link_bytes_per_launch / float(np.mean(durs)) / GB
     h2d = h2d_ceiling()
     return {"bound": "pcie", "achieved": round(achieved, 3), "peak": PCIE5_X16_GBPS, "unit": "GB/s",
-            "frac": round(achieved / PCIE5_X16_GBPS, 4), "traffic": None,
+            "frac": round(achieved / PCIE5_X16_GBPS, 4), "traffic": measured_traffic(workload),
+            "traffic_note": TRAFFIC_NOTE_LINK,
             "link_ceiling_measured": round(h2d, 3), "frac_of_measured_ceiling": round(achieved / h2d, 4),
             "algorithmic_bytes_per_launch": int(link_bytes_per_launch),
             "decoded_roofline_GBps": round(h2d / (1.0 - savings), 3)}
@@ -360,7 +385,9 @@ def run_dense_gnn(args) -> dict:
     stored_np = stored.cpu().numpy()
     savings = 1.0 - stored_np.sum() / (n * L)
     out = torch.empty_like(src)
-    wall, durs = timed(lambda i: ibp.ibp_decompress(meta, slots, bitmask, n, out), args.steps, args.warmup)
+    wall, _ = timed(lambda i: ibp.ibp_decompress(meta, slots, bitmask, n, out), args.steps, args.warmup)
+    # launches shorter than their host submission: time them queued back to back
+    durs = queued_durations(lambda i: ibp.ibp_decompress(meta, slots, bitmask, n, out), args.steps)
     assert ibp.ibp_check(meta) == ibp.IBP_OK
     if not torch.equal(out, src):
         raise SystemExit("decoded rows differ")
@@ -369,7 +396,7 @@ def run_dense_gnn(args) -> dict:
         args, n * L * args.steps / wall / GB, wall,
         {"workload": f"dense_gnn: {n} rows x 128 fp32 |N(0,0.5)| with 3% N(0,50) rows, W=32, M=4096, T=0.95, "
                      f"slots in HBM, contiguous decode of all rows per step", "rows": n, "tensor_bytes": L},
-        savings, "ibp::k_decode_small", durs, hbm_roofline(hbm_bytes, durs),
+        savings, "ibp::k_decode_small", durs, hbm_roofline(hbm_bytes, durs, "dense_gnn"),
         encode_GBps=round(n * L / float(np.mean(enc_durs)) / GB, 3), meta=ibp.ibp_meta_get_info(meta))
 
 
@@ -435,7 +462,7 @@ def run_dlrm(args) -> dict:
         {"workload": f"dlrm: {n} rows x 128 fp32 U(-0.01,0.01), W=32, M=4096, T=0.9, slots in pinned host "
                      f"memory, {per_step} zero-copy gathers of {batch} random ids (with replacement) per step",
          "rows": n, "tensor_bytes": L, "batch_ids": batch, "gathers_per_step": per_step},
-        savings, "ibp::k_decode_small", durs, link_roofline(link, durs, savings),
+        savings, "ibp::k_decode_small", durs, link_roofline(link, durs, savings, None if args.small else "dlrm"),
         encode_GBps=round(n * L / t_enc / GB, 3), meta=ibp.ibp_meta_get_info(meta))
 
 
@@ -511,7 +538,8 @@ def run_llm_bf16(args) -> dict:
                      f"T=0.95, slots in pinned host memory, each layer decoded zero-copy into HBM on one stream "
                      f"while a consumer (y = x @ W) reads the previous layer on another", "layers": layers,
          "tensor_bytes": L},
-        savings, "ibp::k_decode_tiles (look-back)", durs, link_roofline(link, durs, savings),
+        savings, "ibp::k_decode_tiles (look-back)", durs,
+        link_roofline(link, durs, savings, None if args.small else "llm_bf16"),
         encode_GBps=round(layers * L / t_enc / GB, 3), meta=ibp.ibp_meta_get_info(meta))
 
 

@@ -18,9 +18,13 @@ using namespace ibp;
 
 namespace {
 
-constexpr uint32_t kLongTileWords = 1024;  // tile of a tensor longer than kMaxTileWords
+// Tile of a tensor longer than kMaxTileWords.  Decode measured fastest with
+// the largest tile (fewer look-back hops per tensor), encode with half of it.
+constexpr uint32_t kLongTileWordsDecode = 2048;
+constexpr uint32_t kLongTileWordsEncode = 1024;
 constexpr uint32_t kMaxPeriodBits = 1u << 20;
-constexpr uint64_t kLineWords = 64;  // 256-byte first-read granule
+constexpr uint64_t kLineWords = 64;     // 256-byte first-read granule
+constexpr uint64_t kMemLineWords = 32;  // 128-byte line that memory reads move
 
 struct Scratch {
     unsigned long long* status = nullptr;
@@ -222,7 +226,7 @@ uint64_t min_record_bits(const ibp_meta_s* h) {
     return H + 8 * L - periods * h->sum.invariant_bits;
 }
 
-Geo make_geo(const ibp_meta_s* h, bool aligned16) {
+Geo make_geo(const ibp_meta_s* h, bool aligned16, uint32_t long_tile_words) {
     Geo g{};
     const uint64_t L = h->params.tensor_bytes;
     g.L = L;
@@ -240,22 +244,24 @@ Geo make_geo(const ibp_meta_s* h, bool aligned16) {
         g.tile_words = (uint32_t)g.n_words;
         g.tiles_per_tensor = 1;
     } else {
-        g.tile_words = kLongTileWords;
-        g.tiles_per_tensor = (g.n_words + kLongTileWords - 1) / kLongTileWords;
+        g.tile_words = long_tile_words;
+        g.tiles_per_tensor = (g.n_words + long_tile_words - 1) / long_tile_words;
     }
     // First read of a single-tile record: every record is at least min_words
     // long, so the read is cut at the last 256-byte boundary inside that
     // prefix, and is never shorter than 256 bytes (the second read then starts
     // on a 256-byte boundary; zero-copy reads of pinned host memory measured
-    // fastest with this split).  When no record can be shorter than 15/16 of
-    // the slot, the whole slot is read at once instead of paying a second
-    // round trip.
+    // fastest with this split).  Memory moves whole 128-byte lines, so when
+    // the shortest record already covers all but 1/16 of the slot's lines,
+    // the whole slot is read at once instead of paying a second round trip.
     const uint64_t min_words = (min_record_bits(h) + 31) / 32;
+    const uint64_t slot_lines = (g.n_words + kMemLineWords - 1) / kMemLineWords;
+    const uint64_t min_lines = (min_words + kMemLineWords - 1) / kMemLineWords;
     uint64_t spec;
     if (h->first_read_bytes) {
         spec = (h->first_read_bytes + 3) / 4;
         if (spec < g.hdr_words) spec = g.hdr_words;
-    } else if ((g.n_words - min_words) * 16 <= g.n_words) {
+    } else if (min_lines >= slot_lines || (slot_lines - min_lines) * 16 <= slot_lines) {
         spec = g.n_words;
     } else {
         spec = (min_words / kLineWords) * kLineWords;
@@ -444,7 +450,7 @@ ibp_status ibp_compress(ibp_meta_t h, const void* src, uint64_t n_tensors, void*
     if (!device_only(bitmask, h->device)) return IBP_ERR_INVALID_ARG;
     if (stored_bytes && !device_only(stored_bytes, h->device)) return IBP_ERR_INVALID_ARG;
     if (overlaps(src, n_tensors * L, dst_slots, n_tensors * L)) return IBP_ERR_INVALID_ARG;
-    const Geo geo = make_geo(h, aligned16(L, {src, dst_slots}));
+    const Geo geo = make_geo(h, aligned16(L, {src, dst_slots}), kLongTileWordsEncode);
     LookBack lb{};
     if (geo.tiles_per_tensor > 1) {
         const uint64_t tiles = n_tensors * geo.tiles_per_tensor;
@@ -467,7 +473,7 @@ static ibp_status decode_common(ibp_meta_t h, const void* slots, uint64_t n_slot
     if (!device_only(bitmask, h->device) || !device_only(dst, h->device)) return IBP_ERR_INVALID_ARG;
     if (ids && !device_only(ids, h->device)) return IBP_ERR_INVALID_ARG;
     if (overlaps(slots, n_slots * L, dst, n_out * L)) return IBP_ERR_INVALID_ARG;
-    const Geo geo = make_geo(h, aligned16(L, {slots, dst}));
+    const Geo geo = make_geo(h, aligned16(L, {slots, dst}), kLongTileWordsDecode);
     LookBack lb{};
     if (geo.tiles_per_tensor > 1) {
         const uint64_t tiles = n_out * geo.tiles_per_tensor;

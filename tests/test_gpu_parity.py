@@ -123,6 +123,40 @@ def test_mask_with_many_runs():
     assert ibp.ibp_meta_get_info(r.meta)["max_runs"] >= 9
 
 
+@pytest.mark.parametrize("wl", ["sparse_gnn", "dense_gnn", "kv_bf16"])
+def test_first_read_sizes(wl):
+    """Decode under every first-read split (the header-only read, reads cut
+    mid-record, unaligned sizes that round up, the whole slot, beyond the
+    slot): the decoded bytes never depend on it."""
+    w = WL.ALL[wl]
+    if wl == "sparse_gnn":
+        raw = as_rows(WL.sparse_gnn(900))
+    elif wl == "dense_gnn":
+        raw = as_rows(WL.dense_gnn(900))
+    else:
+        raw = WL.kv_cache(n_layers=1, n_heads=2, n_tokens=16 * 100).reshape(-1, 2048).view(np.uint8).reshape(-1, 4096)
+    n, L = raw.shape
+    dev = device()
+    pinned_slots = wl != "kv_bf16"
+    src = to_gpu(raw)
+    meta = ibp.ibp_build_metadata(src, min(n, w.n_sample), L, w.chunk_bits, w.period_bits, w.threshold)
+    slots = torch.empty((n, L), dtype=torch.uint8, pin_memory=True) if pinned_slots else torch.empty_like(src)
+    bm = torch.zeros((n + 31) // 32, dtype=torch.int32, device=dev)
+    ibp.ibp_compress(meta, src, n, slots, bm)
+    assert int(bm.count_nonzero()) > 0
+    ids = torch.from_numpy(np.random.default_rng(11).integers(0, n, 2 * n)).to(dev)
+    for fr in [0, 1, 4, 16, 100, 256, 384, L - 4, L, 10 * L]:
+        ibp.ibp_meta_set_first_read(meta, fr)
+        out = torch.full((n, L), 0xA5, dtype=torch.uint8, device=dev)
+        ibp.ibp_decompress(meta, slots, bm, n, out)
+        g = torch.empty((ids.numel(), L), dtype=torch.uint8, device=dev)
+        ibp.ibp_gather_decompress(meta, slots, n, bm, ids, g)
+        assert ibp.ibp_check(meta) == ibp.IBP_OK
+        assert torch.equal(out, src), f"{wl}: decode differs with first read {fr}"
+        assert torch.equal(g, src[ids]), f"{wl}: gather differs with first read {fr}"
+    say(f"[parity] {wl} first-read sizes ok")
+
+
 def test_meta_create_roundtrip_and_empty_calls():
     rng = np.random.default_rng(8)
     L, n = 512, 100
