@@ -212,13 +212,13 @@ __global__ __launch_bounds__(256) void k_encode(Tables t, Geo geo, const uint8_t
 // ---------------------------------------------------------------------------
 // Tensors of at most kMaxTileWords words with 16-byte aligned source and
 // slots: persistent workgroups, tables staged once in LDS, four words per lane
-// per step, and the next tensor's words in flight in registers while the
-// current one is packed.  The record is assembled in LDS (header words, then
-// the kept bits) and written with 16-byte stores; an incompressible tensor is
-// written from the registers that already hold it.
+// per step, and each step's words of the wave's next tensor in flight in the
+// registers the current step has just consumed.  The record is assembled in
+// LDS (header words, then the kept bits) and written with 16-byte stores; an
+// incompressible tensor is copied from its source again.
 // ---------------------------------------------------------------------------
 template <int RUNS, bool UNI, bool MW4, int STAGE>
-__global__ __launch_bounds__(256) void k_encode_small(Tables t, Geo geo, const uint8_t* __restrict__ src,
+__global__ __launch_bounds__(1024) void k_encode_small(Tables t, Geo geo, const uint8_t* __restrict__ src,
                                                       uint64_t n_tensors, uint8_t* __restrict__ slots,
                                                       uint32_t* __restrict__ bitmask, uint64_t* __restrict__ stored,
                                                       uint32_t buf_words) {
@@ -265,19 +265,21 @@ __global__ __launch_bounds__(256) void k_encode_small(Tables t, Geo geo, const u
     uint64_t ti = (uint64_t)blockIdx.x * wpb + wib;
     if (ti >= n_tensors) return;
 
-    u32x4 cur[STAGE], nxt[STAGE];
-    auto load_tensor = [&](uint64_t tn, u32x4 (&dst)[STAGE]) __attribute__((always_inline)) {
-        const u32x4* s4 = reinterpret_cast<const u32x4*>(src + tn * geo.L);
+    // cur[s]: the lane's four words of step s.  Once step s has taken them,
+    // the same registers receive step s of the wave's next tensor, so the
+    // prefetch costs no registers beyond one step's words.
+    u32x4 cur[STAGE];
+    {
+        const u32x4* s4 = reinterpret_cast<const u32x4*>(src + ti * geo.L);
 #pragma unroll
         for (int r = 0; r < STAGE; ++r) {
             const uint32_t i = lane + (uint32_t)r * kWave;
-            if (i < n4) dst[r] = __builtin_nontemporal_load(s4 + i);
+            if (i < n4) cur[r] = __builtin_nontemporal_load(s4 + i);
         }
-    };
-    load_tensor(ti, cur);
+    }
     for (; ti < n_tensors; ti += stride) {
         const uint64_t tnext = ti + stride;
-        if (tnext < n_tensors) load_tensor(tnext, nxt);
+        const u32x4* nx4 = reinterpret_cast<const u32x4*>(src + (tnext < n_tensors ? tnext : ti) * geo.L);
         // zero the record buffer: header words, then the kept bits
         {
             u32x4* b4 = reinterpret_cast<u32x4*>(buf);
@@ -293,6 +295,7 @@ __global__ __launch_bounds__(256) void k_encode_small(Tables t, Geo geo, const u
             if ((uint32_t)s * (4 * kWave) >= nw) break;  // wave-uniform
             const bool live = lw0 < nw;  // nw % 4 == 0: a live lane owns four words
             const u32x4 xv = cur[s];
+            if (tnext < n_tensors && live) cur[s] = __builtin_nontemporal_load(nx4 + lane + (uint32_t)s * kWave);
             uint32_t x[4], m[4], bv[4], kd[4], pos[4];
 #pragma unroll
             for (int j = 0; j < 4; ++j) x[j] = xv[j];
@@ -352,15 +355,30 @@ __global__ __launch_bounds__(256) void k_encode_small(Tables t, Geo geo, const u
                 hbits = (lane & (q - 1u)) == 0 ? (uint32_t)pc : 0u;
             }
             if (live && hbits) atomicOr(&buf[c0 >> 5], hbits << (c0 & 31u));
+            // run masks of the lane's four positions: one 16-byte read per run
+            uint32_t rr[RUNS > 0 ? RUNS : 1][4];
+            if constexpr (MW4 && !UNI) {
+#pragma unroll
+                for (int r = 0; r < RUNS; ++r) {
+                    const u32x4 v = ta.rw4(r, pos0);
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) rr[r][j] = v[j];
+                }
+            }
             uint32_t f[4], size[4];
             uint32_t tot = 0;
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 uint32_t e;
-                if constexpr (UNI)
+                if constexpr (UNI) {
                     e = extract_t<RUNS>(tu, 0, kd[j], x[j]);
-                else
+                } else if constexpr (MW4) {
+                    e = 0;
+#pragma unroll
+                    for (int r = 0; r < RUNS; ++r) e |= (x[j] & rr[r][j]) >> (ta.dw(r, pos[j], kd[j]) & 31u);
+                } else {
                     e = extract_t<RUNS>(ta, pos[j], kd[j], x[j]);
+                }
                 f[j] = p[j] ? e : x[j];
                 size[j] = live ? (p[j] ? 32u - (kd[j] & 63u) : 32u) : 0u;
                 tot += size[j];
@@ -392,11 +410,9 @@ __global__ __launch_bounds__(256) void k_encode_small(Tables t, Geo geo, const u
             const u32x4* b4 = reinterpret_cast<const u32x4*>(buf);
             for (uint32_t i = lane; i < w4; i += kWave) __builtin_nontemporal_store(b4[i], slot4 + i);
         } else {
-#pragma unroll
-            for (int r = 0; r < STAGE; ++r) {
-                const uint32_t i = lane + (uint32_t)r * kWave;
-                if (i < n4) __builtin_nontemporal_store(cur[r], slot4 + i);
-            }
+            // the registers already hold the next tensor: copy this one again
+            copy_words(reinterpret_cast<const uint32_t*>(src + ti * geo.L), reinterpret_cast<uint32_t*>(slot4), 0,
+                       nw, true);
         }
         if (lane == 0) {
             const uint32_t bit = 1u << (ti & 31);
@@ -407,8 +423,6 @@ __global__ __launch_bounds__(256) void k_encode_small(Tables t, Geo geo, const u
             if (stored) stored[ti] = comp ? 4ull * words : geo.L;
         }
         __builtin_amdgcn_wave_barrier();
-#pragma unroll
-        for (int r = 0; r < STAGE; ++r) cur[r] = nxt[r];
     }
 }
 

@@ -76,9 +76,10 @@ struct PersistentPlan {
     size_t shm = 0;
 };
 
-// Chooses the waves per workgroup (currently 4) that keeps the most waves resident
-// per compute unit, given LDS shared by a workgroup (head_bytes), LDS per wave
-// (wave_bytes), the kernel's VGPR count and the LDS limits of the device.
+// Chooses the waves per workgroup (4, 8, 12 or 16, within the kernel's launch
+// bounds) that keeps the most waves resident per compute unit, given LDS
+// shared by a workgroup (head_bytes), LDS per wave (wave_bytes), the kernel's
+// VGPR count and the LDS limits of the device.
 // blocks = min(workgroups that fill the device, items / wpb).  Returns false
 // when no shape fits.
 bool plan_persistent(const void* kernel, size_t head_bytes, size_t wave_bytes, uint32_t cu_count,

@@ -175,11 +175,16 @@ hipError_t launch_tables(const uint32_t* mask, const uint32_t* bitval, uint32_t 
     return hipGetLastError();
 }
 
+static const uint32_t kPlanWpb[] = {4u, 8u, 12u, 16u};
+
 bool plan_persistent(const void* kernel, size_t head_bytes, size_t wave_bytes, uint32_t cu_count,
                      uint64_t n_items, PersistentPlan* plan) {
     hipFuncAttributes attr;
-    uint32_t vgprs = 64;
-    if (hipFuncGetAttributes(&attr, kernel) == hipSuccess && attr.numRegs > 0) vgprs = (uint32_t)attr.numRegs;
+    uint32_t vgprs = 64, max_threads = 256;
+    if (hipFuncGetAttributes(&attr, kernel) == hipSuccess) {
+        if (attr.numRegs > 0) vgprs = (uint32_t)attr.numRegs;
+        if (attr.maxThreadsPerBlock > 0) max_threads = (uint32_t)attr.maxThreadsPerBlock;
+    }
     (void)hipGetLastError();
     int dev = 0, max_block_lds = 65536;
     if (hipGetDevice(&dev) == hipSuccess)
@@ -193,9 +198,11 @@ bool plan_persistent(const void* kernel, size_t head_bytes, size_t wave_bytes, u
     const uint32_t cu_waves = 4 * per_simd;
     PersistentPlan best;
     uint32_t best_waves = 0;
-    // Larger workgroups (8-16 waves sharing one table copy) were measured
-    // slower than four-wave groups on gfx950, so only four is tried.
-    for (uint32_t wpb : {4u}) {
+    // Waves per workgroup: the candidates the kernel's launch bounds allow,
+    // keeping the one with the most resident waves (ties: the smaller
+    // workgroup).  Larger groups share one LDS copy of the tables.
+    for (uint32_t wpb : kPlanWpb) {
+        if (wpb * kWave > max_threads) continue;
         const uint64_t shm = ((head_bytes + 15) & ~(size_t)15) + (uint64_t)wpb * wave_bytes;
         if (shm > block_cap || shm > kLdsPerCu) continue;
         uint64_t wgs = shm ? kLdsPerCu / shm : 64;
