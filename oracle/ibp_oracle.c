@@ -305,3 +305,104 @@ int ibp_ref_gather_decompress(uint64_t L, uint32_t W, uint32_t M,
     }
     return IBP_REF_OK;
 }
+
+/* ---------------------------------------------------------------------------
+ * Packed cache: the slot items of ibp_ref_compress stored back to back.
+ * ------------------------------------------------------------------------- */
+
+/* Bytes item t takes: its record when that is shorter than L, else L. */
+static int item_bytes(uint64_t L, uint32_t W, uint32_t M, const uint8_t* mask, const uint8_t* bitval,
+                      const uint8_t* x, uint8_t* rec, uint64_t cap, uint64_t* bytes, int* compressed) {
+    uint64_t R;
+    int st = ibp_ref_encode_record(8 * L, W, M, mask, bitval, x, rec, cap, &R);
+    if (st != IBP_REF_OK) return st;
+    uint64_t words = (R + 31) / 32;
+    *compressed = 4 * words < L;
+    *bytes = *compressed ? 4 * words : L;
+    return IBP_REF_OK;
+}
+
+static uint64_t round16(uint64_t b) { return (b + 15) / 16 * 16; }
+
+int ibp_ref_packed_offsets(uint64_t L, uint32_t W, uint32_t M,
+                           const uint8_t* mask, const uint8_t* bitval,
+                           const uint8_t* src, uint64_t n_tensors, uint64_t* offsets) {
+    if (!geometry_ok(8 * L, W, M)) return IBP_REF_ERR_INVALID;
+    if (!offsets || (n_tensors && !src)) return IBP_REF_ERR_INVALID;
+    uint64_t cap = ibp_ref_max_record_bits(8 * L, W);
+    uint8_t* rec = (uint8_t*)malloc((size_t)(cap / 8));
+    if (!rec) return IBP_REF_ERR_INVALID;
+    offsets[0] = 0;
+    for (uint64_t t = 0; t < n_tensors; ++t) {
+        uint64_t bytes;
+        int comp;
+        int st = item_bytes(L, W, M, mask, bitval, src + t * L, rec, cap, &bytes, &comp);
+        if (st != IBP_REF_OK) {
+            free(rec);
+            return st;
+        }
+        offsets[t + 1] = offsets[t] + round16(bytes);
+    }
+    free(rec);
+    return IBP_REF_OK;
+}
+
+int ibp_ref_compress_packed(uint64_t L, uint32_t W, uint32_t M,
+                            const uint8_t* mask, const uint8_t* bitval,
+                            const uint8_t* src, uint64_t n_tensors,
+                            uint8_t* buf, uint64_t capacity, uint64_t* offsets,
+                            uint32_t* bitmask) {
+    int st = ibp_ref_packed_offsets(L, W, M, mask, bitval, src, n_tensors, offsets);
+    if (st != IBP_REF_OK) return st;
+    if (offsets[n_tensors] > capacity) return IBP_REF_ERR_RANGE;
+    if (!bitmask || (capacity && !buf)) return IBP_REF_ERR_INVALID;
+    uint64_t cap = ibp_ref_max_record_bits(8 * L, W);
+    uint8_t* rec = (uint8_t*)malloc((size_t)(cap / 8));
+    if (!rec) return IBP_REF_ERR_INVALID;
+    memset(bitmask, 0, (size_t)(4 * ((n_tensors + 31) / 32)));
+    for (uint64_t t = 0; t < n_tensors; ++t) {
+        const uint8_t* x = src + t * L;
+        uint8_t* item = buf + offsets[t];
+        uint64_t bytes;
+        int comp;
+        st = item_bytes(L, W, M, mask, bitval, x, rec, cap, &bytes, &comp);
+        if (st != IBP_REF_OK) {
+            free(rec);
+            return st;
+        }
+        memset(item, 0, (size_t)(offsets[t + 1] - offsets[t]));
+        memcpy(item, comp ? rec : x, (size_t)bytes);
+        set_mask_bit(bitmask, t, comp);
+    }
+    free(rec);
+    return IBP_REF_OK;
+}
+
+int ibp_ref_gather_decompress_packed(uint64_t L, uint32_t W, uint32_t M,
+                                     const uint8_t* mask, const uint8_t* bitval,
+                                     const uint8_t* buf, const uint64_t* offsets,
+                                     uint64_t n_items, const uint32_t* bitmask,
+                                     const int64_t* ids, uint64_t n_ids, uint8_t* dst) {
+    if (!geometry_ok(8 * L, W, M)) return IBP_REF_ERR_INVALID;
+    if (!offsets || !bitmask || (n_ids && (!buf || !ids || !dst))) return IBP_REF_ERR_INVALID;
+    for (uint64_t i = 0; i < n_ids; ++i) {
+        int64_t id = ids[i];
+        if (id < 0 || (uint64_t)id >= n_items) return IBP_REF_ERR_RANGE;
+        uint64_t a = offsets[id], b = offsets[id + 1];
+        if (b < a) return IBP_REF_ERR_CORRUPT;
+        const uint8_t* item = buf + a;
+        uint8_t* out = dst + i * L;
+        if (!mask_bit(bitmask, (uint64_t)id)) {
+            if (b - a < L) return IBP_REF_ERR_CORRUPT;
+            memcpy(out, item, (size_t)L);
+            continue;
+        }
+        uint64_t R;
+        int st = ibp_ref_record_bits(8 * L, W, M, mask, item, 8 * (b - a), &R);
+        if (st != IBP_REF_OK) return st;
+        if (4 * ((R + 31) / 32) >= L) return IBP_REF_ERR_CORRUPT;
+        st = ibp_ref_decode_record(8 * L, W, M, mask, bitval, item, 8 * (b - a), out);
+        if (st != IBP_REF_OK) return st;
+    }
+    return IBP_REF_OK;
+}

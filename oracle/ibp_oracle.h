@@ -120,6 +120,36 @@ int ibp_ref_gather_decompress(uint64_t L, uint32_t W, uint32_t M,
                               const uint32_t* bitmask, const int64_t* ids,
                               uint64_t n_ids, uint8_t* dst);
 
+/* Packed cache (FR/KO summary, "Intégration au système": in the GPU
+ * software cache of GNN frameworks, compressing the cached tensors raises
+ * how many of them fit).  Item t is what slot t of ibp_ref_compress holds --
+ * the record (4*ceil(R/32) bytes) when that is shorter than L, else the raw
+ * tensor (L bytes) -- and the items are stored back to back: item t starts at
+ * byte offsets[t], offsets[0] = 0 and offsets[t+1] = offsets[t] + the item's
+ * bytes rounded up to a multiple of 16.  offsets has n_tensors + 1 entries.
+ * Bytes between an item's end and the next offset are written as zero. */
+int ibp_ref_packed_offsets(uint64_t L, uint32_t W, uint32_t M,
+                           const uint8_t* mask, const uint8_t* bitval,
+                           const uint8_t* src, uint64_t n_tensors, uint64_t* offsets);
+
+/* Writes offsets, the items into buf and the bitmask (as ibp_ref_compress).
+ * -6 when offsets[n_tensors] > capacity bytes; buf is then left untouched. */
+int ibp_ref_compress_packed(uint64_t L, uint32_t W, uint32_t M,
+                            const uint8_t* mask, const uint8_t* bitval,
+                            const uint8_t* src, uint64_t n_tensors,
+                            uint8_t* buf, uint64_t capacity, uint64_t* offsets,
+                            uint32_t* bitmask);
+
+/* dst row i = tensor ids[i] from a packed buffer of n_items items.  Item t
+ * spans bytes [offsets[t], offsets[t+1]); a compressed item whose header
+ * implies a record longer than that, or not shorter than L, is corrupt (-5),
+ * and so is a raw item shorter than L.  ids outside [0, n_items): -6. */
+int ibp_ref_gather_decompress_packed(uint64_t L, uint32_t W, uint32_t M,
+                                     const uint8_t* mask, const uint8_t* bitval,
+                                     const uint8_t* buf, const uint64_t* offsets,
+                                     uint64_t n_items, const uint32_t* bitmask,
+                                     const int64_t* ids, uint64_t n_ids, uint8_t* dst);
+
 #ifdef __cplusplus
 }
 #endif

@@ -57,9 +57,13 @@ def lib():
         L.ibp_ref_compress.argtypes = [u64, u32, u32, p, p, p, u64, p, p, p]
         L.ibp_ref_decompress.argtypes = [u64, u32, u32, p, p, p, p, u64, p]
         L.ibp_ref_gather_decompress.argtypes = [u64, u32, u32, p, p, p, u64, p, p, u64, p]
+        L.ibp_ref_packed_offsets.argtypes = [u64, u32, u32, p, p, p, u64, p]
+        L.ibp_ref_compress_packed.argtypes = [u64, u32, u32, p, p, p, u64, p, u64, p, p]
+        L.ibp_ref_gather_decompress_packed.argtypes = [u64, u32, u32, p, p, p, p, u64, p, p, u64, p]
         for name in ("ibp_ref_build_metadata", "ibp_ref_encode_record", "ibp_ref_record_bits",
                      "ibp_ref_decode_record", "ibp_ref_encode_records", "ibp_ref_decode_records",
-                     "ibp_ref_compress", "ibp_ref_decompress", "ibp_ref_gather_decompress"):
+                     "ibp_ref_compress", "ibp_ref_decompress", "ibp_ref_gather_decompress",
+                     "ibp_ref_packed_offsets", "ibp_ref_compress_packed", "ibp_ref_gather_decompress_packed"):
             getattr(L, name).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -190,4 +194,44 @@ def gather_decompress(slots, n_slots: int, bitmask, ids, L: int, W: int, M: int,
     _check(lib().ibp_ref_gather_decompress(L, W, M, _ptr(_u8(mask)), _ptr(_u8(bitval)), _ptr(s),
                                            n_slots, _ptr(bm), _ptr(ids), ids.size, _ptr(dst)),
            "gather_decompress")
+    return dst
+
+
+def packed_offsets(src, L: int, W: int, M: int, mask, bitval, n_tensors: int):
+    """Offsets (uint64, n + 1) of the items stored back to back."""
+    s = _u8(src)
+    assert s.size >= n_tensors * L
+    off = np.zeros(n_tensors + 1, np.uint64)
+    _check(lib().ibp_ref_packed_offsets(L, W, M, _ptr(_u8(mask)), _ptr(_u8(bitval)), _ptr(s), n_tensors,
+                                        _ptr(off)), "packed_offsets")
+    return off
+
+
+def compress_packed(src, L: int, W: int, M: int, mask, bitval, n_tensors: int, capacity: int | None = None):
+    """Returns (buf uint8 (capacity,), offsets uint64 (n + 1,), bitmask uint32)."""
+    s = _u8(src)
+    assert s.size >= n_tensors * L
+    if capacity is None:
+        capacity = n_tensors * ((L + 15) // 16 * 16)
+    buf = np.zeros(max(capacity, 1), np.uint8)
+    off = np.zeros(n_tensors + 1, np.uint64)
+    bitmask = np.zeros((n_tensors + 31) // 32, np.uint32)
+    _check(lib().ibp_ref_compress_packed(L, W, M, _ptr(_u8(mask)), _ptr(_u8(bitval)), _ptr(s), n_tensors,
+                                         _ptr(buf), capacity, _ptr(off), _ptr(bitmask if bitmask.size else
+                                                                                np.zeros(1, np.uint32))),
+           "compress_packed")
+    return buf[:capacity], off, bitmask
+
+
+def gather_decompress_packed(buf, offsets, n_items: int, bitmask, ids, L: int, W: int, M: int, mask, bitval):
+    b = _u8(buf) if np.asarray(buf).size else np.zeros(1, np.uint8)
+    off = np.ascontiguousarray(offsets, dtype=np.uint64)
+    bm = np.ascontiguousarray(bitmask, dtype=np.uint32)
+    if bm.size == 0:
+        bm = np.zeros(1, np.uint32)
+    ids = np.ascontiguousarray(ids, dtype=np.int64)
+    dst = np.zeros((ids.size, L), np.uint8)
+    _check(lib().ibp_ref_gather_decompress_packed(L, W, M, _ptr(_u8(mask)), _ptr(_u8(bitval)), _ptr(b),
+                                                  _ptr(off), n_items, _ptr(bm), _ptr(ids), ids.size,
+                                                  _ptr(dst)), "gather_decompress_packed")
     return dst

@@ -13,6 +13,7 @@ The oracle is checked against things other than itself:
 from __future__ import annotations
 
 import ctypes
+import os
 import subprocess
 
 import numpy as np
@@ -367,3 +368,110 @@ def test_workload_savings_bands():
     assert 0.28 < s2 < 0.46, s2
     s3 = _savings(WL.dlrm(4096), WL.DLRM, 1024)
     assert 0.05 < s3 < 0.13, s3
+
+
+# --------------------------------------------------------------------------
+# Packed cache (FR/KO summary, "Intégration au système": a software cache of
+# compressed tensors holds more of them).  Items stored back to back on
+# 16-byte boundaries.
+# --------------------------------------------------------------------------
+def _packed_golden():
+    path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden", "packed_vectors.txt")
+    d = {}
+    with open(path) as f:
+        for raw in f:
+            line = raw.split("#", 1)[0].strip()
+            if line:
+                k, v = (t.strip() for t in line.split(":", 1))
+                d[k] = v
+    L, W, M = int(d["L"]), int(d["W"]), int(d["M"])
+    mism = {}
+    for tok in d["mismatch"].split():
+        t, rng = tok.split(":")
+        a, b = map(int, rng.split("-")) if "-" in rng else (int(rng), int(rng))
+        mism[int(t)] = set(range(a, b + 1))
+    n = len(d["bitmask_bits"].split())
+    words = np.zeros((n, L // 4), np.uint32)
+    for t in range(n):
+        for i in range(L // 4):
+            hi = 0x4000 if i in mism.get(t, ()) else 0x3F80
+            words[t, i] = (hi << 16) | (0x1000 + i)
+    return dict(L=L, W=W, M=M, mask=np.array([int(d["mask"], 16)], np.uint32),
+                bitval=np.array([int(d["bitval"], 16)], np.uint32), x=words,
+                offsets=np.array([int(v) for v in d["offsets"].split()], np.uint64),
+                bits=np.array([int(v) for v in d["bitmask_bits"].split()]),
+                record0=np.array([int(v, 16) for v in d["record0"].split()], np.uint32))
+
+
+def test_packed_hand_vector():
+    g = _packed_golden()
+    L, W, M, n = g["L"], g["W"], g["M"], g["x"].shape[0]
+    off = O.packed_offsets(g["x"], L, W, M, g["mask"], g["bitval"], n)
+    np.testing.assert_array_equal(off, g["offsets"])
+    buf, off2, bm = O.compress_packed(g["x"], L, W, M, g["mask"], g["bitval"], n, capacity=int(off[-1]))
+    np.testing.assert_array_equal(off2, g["offsets"])
+    bits = (bm[0] >> np.arange(n)) & 1
+    np.testing.assert_array_equal(bits, g["bits"])
+    rec0 = buf[: 4 * g["record0"].size].view(np.uint32)
+    np.testing.assert_array_equal(rec0, g["record0"])
+    assert not buf[36:48].any(), "padding after an item is zero"
+    # the raw item is the tensor itself
+    np.testing.assert_array_equal(buf[112:176].view(np.uint32), g["x"][2])
+    out = O.gather_decompress_packed(buf, off, n, bm, [3, 2, 1, 0, 0], L, W, M, g["mask"], g["bitval"])
+    np.testing.assert_array_equal(out.view(np.uint32), g["x"][[3, 2, 1, 0, 0]])
+
+
+@pytest.mark.parametrize("wl", ["sparse_gnn", "dense_gnn", "dlrm"])
+def test_packed_items_are_the_slot_items(wl):
+    """Cross-mode invariant: item t of the packed buffer is byte for byte the
+    stored prefix of slot t, the offsets advance by that prefix rounded up to
+    16 bytes, and gathers round-trip."""
+    w = WL.ALL[wl]
+    gen = {"sparse_gnn": WL.sparse_gnn, "dense_gnn": WL.dense_gnn, "dlrm": WL.dlrm}[wl]
+    raw = np.ascontiguousarray(gen(700)).view(np.uint8).reshape(700, -1)
+    n, L = raw.shape
+    m, b = O.build_metadata(raw, 8 * L, w.chunk_bits, w.period_bits, w.threshold, 512)
+    slots, bm_s, stored = O.compress(raw, L, w.chunk_bits, w.period_bits, m, b, n)
+    buf, off, bm = O.compress_packed(raw, L, w.chunk_bits, w.period_bits, m, b, n)
+    np.testing.assert_array_equal(bm, bm_s)
+    assert off[0] == 0
+    np.testing.assert_array_equal(np.diff(off.astype(np.int64)), (stored.astype(np.int64) + 15) // 16 * 16)
+    for t in range(n):
+        k = int(stored[t])
+        assert np.array_equal(buf[int(off[t]): int(off[t]) + k], slots[t, :k]), t
+    assert off[-1] < n * L  # the cache holds more
+    ids = np.random.default_rng(3).integers(0, n, 900)
+    out = O.gather_decompress_packed(buf, off, n, bm, ids, L, w.chunk_bits, w.period_bits, m, b)
+    np.testing.assert_array_equal(out, raw[ids])
+
+
+def test_packed_edge_cases():
+    g = _packed_golden()
+    L, W, M, n = g["L"], g["W"], g["M"], g["x"].shape[0]
+    mk, bv = g["mask"], g["bitval"]
+    # empty input
+    off = O.packed_offsets(np.zeros(0, np.uint8), L, W, M, mk, bv, 0)
+    np.testing.assert_array_equal(off, [0])
+    # capacity: exactly enough works, one byte less is a range error
+    need = int(g["offsets"][-1])
+    O.compress_packed(g["x"], L, W, M, mk, bv, n, capacity=need)
+    with pytest.raises(O.OracleError) as e:
+        O.compress_packed(g["x"], L, W, M, mk, bv, n, capacity=need - 1)
+    assert e.value.code == O.ERR_RANGE
+    buf, off, bm = O.compress_packed(g["x"], L, W, M, mk, bv, n, capacity=need)
+    # an id past the items
+    with pytest.raises(O.OracleError) as e:
+        O.gather_decompress_packed(buf, off, n, bm, [n], L, W, M, mk, bv)
+    assert e.value.code == O.ERR_RANGE
+    # an item cut shorter than its record (offsets of tensor 1 end early)
+    bad = off.copy()
+    bad[2] = bad[1] + 48  # the 52-byte record of tensor 1 no longer fits
+    with pytest.raises(O.OracleError) as e:
+        O.gather_decompress_packed(buf, bad, n, bm, [1], L, W, M, mk, bv)
+    assert e.value.code == O.ERR_CORRUPT
+    # a raw item shorter than the tensor
+    bad = off.copy()
+    bad[3] = bad[2] + 48
+    with pytest.raises(O.OracleError) as e:
+        O.gather_decompress_packed(buf, bad, n, bm, [2], L, W, M, mk, bv)
+    assert e.value.code == O.ERR_CORRUPT
