@@ -543,8 +543,79 @@ def run_llm_bf16(args) -> dict:
         encode_GBps=round(layers * L / t_enc / GB, 3), meta=ibp.ibp_meta_get_info(meta))
 
 
+# ---------------------------------------------------------------------------
+# Sparse GNN feature cache in HBM, packed layout (items back to back)
+# ---------------------------------------------------------------------------
+def run_sparse_gnn_cache(args) -> dict:
+    w = WL.SPARSE_GNN
+    n, L = w.n_tensors if not args.small else 65536, w.tensor_bytes
+    batch = 8192
+    dev = torch.device("cuda")
+    log(f"[bench] sparse_gnn_cache: generating {n} x 256 fp32 rows")
+    host = pinned((n, L), torch.uint8)
+    WL.sparse_gnn(n, out=host.numpy().view(np.float32).reshape(n, 256))
+    raw_np = host.numpy()
+    meta = ibp.ibp_build_metadata(host, w.n_sample, L, w.chunk_bits, w.period_bits, w.threshold)
+
+    log("[bench] cache fill: item offsets, then the packed items into HBM (zero copy from pinned memory)")
+    offsets = torch.empty(n + 1, dtype=torch.int64, device=dev)
+    bitmask = torch.zeros((n + 31) // 32, dtype=torch.int32, device=dev)
+    ibp.ibp_packed_offsets(meta, host, n, offsets)
+    total = int(offsets[-1].item())
+    buf = torch.empty(total, dtype=torch.uint8, device=dev)
+    ibp.ibp_compress_packed(meta, host, n, offsets, buf, bitmask)
+    torch.cuda.synchronize()
+    fill_s = []
+    for _ in range(3):
+        t0 = time.perf_counter()
+        ibp.ibp_packed_offsets(meta, host, n, offsets)
+        ibp.ibp_compress_packed(meta, host, n, offsets, buf, bitmask)
+        torch.cuda.synchronize()
+        fill_s.append(time.perf_counter() - t0)
+    assert ibp.ibp_check(meta) == ibp.IBP_OK
+    off_np = offsets.cpu().numpy()
+    item_bytes = np.diff(off_np)
+
+    ids_all = WL.batch_ids(n, batch, args.warmup + args.steps, replace=False)
+    ids_dev = torch.from_numpy(ids_all).to(dev)
+    out = torch.empty((2, batch, L), dtype=torch.uint8, device=dev)
+
+    def step(i):
+        ibp.ibp_gather_decompress_packed(meta, buf, offsets, n, bitmask, ids_dev[i], out[i & 1])
+
+    log(f"[bench] timing {args.steps} gathers of {batch} rows from the packed HBM cache")
+    wall, _ = timed(step, args.steps, args.warmup)
+    durs = queued_durations(step, args.steps, args.warmup)
+    assert ibp.ibp_check(meta) == ibp.IBP_OK
+    last = args.warmup + args.steps - 1
+    step(last)
+    if not np.array_equal(out[last & 1].cpu().numpy(), raw_np[ids_all[last]]):
+        raise SystemExit("decoded rows differ from the source rows")
+    timed_ids = ids_all[args.warmup:]
+    # algorithmic bytes per launch: items read + rows written + ids, offsets and bitmask words
+    hbm_bytes = float(item_bytes[timed_ids].sum(axis=1).mean() + batch * (L + 8 + 16 + 4))
+
+    # the same gathers from an uncompressed HBM copy of the table
+    table = host.to(dev)
+    raw_wall, _ = timed(lambda i: torch.index_select(table, 0, ids_dev[i], out=out[i & 1]), args.steps,
+                        args.warmup)
+    del table
+    return base_result(
+        args, batch * L * args.steps / wall / GB, wall,
+        {"workload": f"sparse_gnn_cache: {n} rows x 256 fp32 (97% zeros), W=1024, M=8192, T=0.95, all rows "
+                     f"compressed into one packed HBM buffer (items back to back, 16-byte aligned), gather of "
+                     f"{batch} distinct random row ids per step into HBM", "rows": n, "tensor_bytes": L,
+         "batch_ids": batch},
+        1.0 - total / (n * L), "ibp::k_decode_small (packed items)", durs,
+        hbm_roofline(hbm_bytes, durs, None if args.small else "sparse_gnn_cache"),
+        cache_bytes=total, capacity_gain=round(n * L / total, 4),
+        fill_GBps=round(n * L / float(np.median(fill_s)) / GB, 3),
+        uncompressed_hbm_gather_GBps=round(batch * L * args.steps / raw_wall / GB, 3),
+        meta=ibp.ibp_meta_get_info(meta))
+
+
 WORKLOADS = {"sparse_gnn": run_sparse_gnn, "kv_bf16": run_kv_bf16, "dense_gnn": run_dense_gnn,
-             "dlrm": run_dlrm, "llm_bf16": run_llm_bf16}
+             "dlrm": run_dlrm, "llm_bf16": run_llm_bf16, "sparse_gnn_cache": run_sparse_gnn_cache}
 
 
 def main():
@@ -566,6 +637,7 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
     defaults = {"sparse_gnn": (200, 10), "kv_bf16": (100, 5), "dense_gnn": (200, 10), "dlrm": (4, 1),
+                "sparse_gnn_cache": (200, 10),
                 "llm_bf16": (3, 1)}
     d_steps, d_warm = defaults[args.workload]
     args.steps = d_steps if args.steps is None else args.steps

@@ -141,6 +141,53 @@ ibp_status ibp_gather_decompress(ibp_meta_t meta, const void* slots, uint64_t n_
                                  const uint32_t* bitmask, const int64_t* ids, uint64_t n_ids,
                                  void* dst, hipStream_t stream);
 
+/* ---------------------------------------------------------------------------
+ * Packed cache (FR/KO summary, "Intégration au système": in the GPU software
+ * cache of GNN frameworks, compressing the cached tensors raises how many of
+ * them fit).  Instead of fixed L-byte slots, the items -- what slot t would
+ * hold: the record when 4*ceil(R/32) < L, else the raw tensor -- are stored
+ * back to back.  Item t spans bytes [offsets[t], offsets[t+1]) of the buffer;
+ * offsets[0] = 0 and offsets[t+1] = offsets[t] + the item's bytes rounded up
+ * to a multiple of 16 (the bytes after an item up to the next offset are
+ * zero).  offsets: device memory, n + 1 uint64 entries, 8-byte aligned.  The
+ * bitmask is the same as for slots.
+ *
+ * These calls need L to be a multiple of 16 and at most 8 KiB, 16-byte
+ * aligned data pointers, and per-position tables that fit the kernels' LDS
+ * (every workload shape of the benchmark does); otherwise they return
+ * IBP_ERR_UNSUPPORTED.
+ * ------------------------------------------------------------------------- */
+
+/* offsets <- the item offsets of the n_tensors tensors at src (device or
+ * pinned); offsets[n_tensors] is the buffer size ibp_compress_packed needs.
+ * Reads src once (the record lengths only).  Asynchronous. */
+ibp_status ibp_packed_offsets(ibp_meta_t meta, const void* src, uint64_t n_tensors, uint64_t* offsets,
+                              hipStream_t stream);
+
+/* Writes item t of src at dst + offsets[t] (dst: device or pinned, capacity
+ * bytes, must not overlap src) and bitmask bits 0..n_tensors-1.  offsets
+ * must come from ibp_packed_offsets for the same src and handle: an item
+ * whose offsets disagree with its length is not written and latches
+ * IBP_ERR_CORRUPT, one that would end past capacity latches IBP_ERR_RANGE. */
+ibp_status ibp_compress_packed(ibp_meta_t meta, const void* src, uint64_t n_tensors, const uint64_t* offsets,
+                               void* dst, uint64_t capacity, uint32_t* bitmask, hipStream_t stream);
+
+/* Tensor t of dst (device, n_items * L bytes) <- item t of the packed
+ * buffer buf (device or pinned, buf_bytes bytes).  Each item is read whole
+ * in one pass, its length being known from the offsets.  An item whose
+ * offsets are not 16-byte multiples, pass buf_bytes, exceed L rounded up to
+ * 16, or do not hold its record (or, raw, the whole tensor) latches
+ * IBP_ERR_CORRUPT; no byte outside [offsets[t], offsets[t+1]) is read. */
+ibp_status ibp_decompress_packed(ibp_meta_t meta, const void* buf, uint64_t buf_bytes, const uint64_t* offsets,
+                                 const uint32_t* bitmask, uint64_t n_items, void* dst, hipStream_t stream);
+
+/* Gather on decode from a packed buffer: row i of dst <- item ids[i]
+ * (device int64, repeats allowed; an id outside [0, n_items) latches
+ * IBP_ERR_RANGE). */
+ibp_status ibp_gather_decompress_packed(ibp_meta_t meta, const void* buf, uint64_t buf_bytes,
+                                        const uint64_t* offsets, uint64_t n_items, const uint32_t* bitmask,
+                                        const int64_t* ids, uint64_t n_ids, void* dst, hipStream_t stream);
+
 /* Waits for `stream`, returns the first error latched by a kernel of this
  * handle since the last ibp_check (IBP_OK if none) and clears it. */
 ibp_status ibp_check(ibp_meta_t meta, hipStream_t stream);

@@ -495,6 +495,91 @@ ibp_status ibp_gather_decompress(ibp_meta_t h, const void* slots, uint64_t n_slo
     return decode_common(h, slots, n_slots, bitmask, ids, n_ids, dst, stream);
 }
 
+// ---------------------------------------------------------------------------
+// Packed cache.
+// ---------------------------------------------------------------------------
+ibp_status ibp_packed_offsets(ibp_meta_t h, const void* src, uint64_t n_tensors, uint64_t* offsets,
+                              hipStream_t stream) {
+    if (!h || !offsets) return IBP_ERR_INVALID_ARG;
+    DeviceGuard guard(h->device);
+    if (!guard.ok) return IBP_ERR_DEVICE;
+    const uint64_t L = h->params.tensor_bytes;
+    if (n_tensors > (~0ull) / L - 1) return IBP_ERR_INVALID_ARG;
+    if (!device_only(offsets, h->device) || reinterpret_cast<uintptr_t>(offsets) % 8) return IBP_ERR_INVALID_ARG;
+    if (n_tensors && !device_or_pinned(src, h->device)) return IBP_ERR_INVALID_ARG;
+    const Geo geo = make_geo(h, aligned16(L, {src}), kLongTileWordsEncode);
+    const bool uni = h->sum.uniform != 0;
+    if (!packed_supported(geo, h->sum.max_runs, uni) || !packed_decode_supported(geo, h->sum.max_runs, uni))
+        return IBP_ERR_UNSUPPORTED;
+    if (n_tensors) {
+        IBP_TRY(launch_item_sizes(h->tabs, geo, h->sum.max_runs, uni, src, n_tensors, offsets + 1, h->cu_count,
+                                  stream));
+    }
+    LookBack lb{};
+    const uint64_t blocks = (n_tensors + kScanBlock - 1) / kScanBlock;
+    if (n_tensors) {
+        ibp_status st = lookback_for(h, stream, blocks, scan_waves(n_tensors), 0, &lb);
+        if (st != IBP_OK) return st;
+    }
+    return from_hip(launch_scan_sizes(offsets, n_tensors, lb, stream));
+}
+
+ibp_status ibp_compress_packed(ibp_meta_t h, const void* src, uint64_t n_tensors, const uint64_t* offsets,
+                               void* dst, uint64_t capacity, uint32_t* bitmask, hipStream_t stream) {
+    if (!h || !offsets) return IBP_ERR_INVALID_ARG;
+    if (n_tensors == 0) return IBP_OK;
+    DeviceGuard guard(h->device);
+    if (!guard.ok) return IBP_ERR_DEVICE;
+    const uint64_t L = h->params.tensor_bytes;
+    if (n_tensors > (~0ull) / L - 1) return IBP_ERR_INVALID_ARG;
+    if (!device_or_pinned(src, h->device) || !device_or_pinned(dst, h->device)) return IBP_ERR_INVALID_ARG;
+    if (!device_only(offsets, h->device) || !device_only(bitmask, h->device)) return IBP_ERR_INVALID_ARG;
+    if (reinterpret_cast<uintptr_t>(offsets) % 8) return IBP_ERR_INVALID_ARG;
+    if (overlaps(src, n_tensors * L, dst, capacity)) return IBP_ERR_INVALID_ARG;
+    const Geo geo = make_geo(h, aligned16(L, {src, dst}), kLongTileWordsEncode);
+    const bool uni = h->sum.uniform != 0;
+    if (!packed_supported(geo, h->sum.max_runs, uni)) return IBP_ERR_UNSUPPORTED;
+    return from_hip(launch_encode_packed(h->tabs, geo, h->sum.max_runs, uni, src, n_tensors, dst,
+                                         Items{offsets, capacity}, bitmask, h->d_err, h->cu_count, stream));
+}
+
+static ibp_status decode_packed_common(ibp_meta_t h, const void* buf, uint64_t buf_bytes, const uint64_t* offsets,
+                                       uint64_t n_items, const uint32_t* bitmask, const int64_t* ids,
+                                       uint64_t n_out, void* dst, hipStream_t stream) {
+    if (!h || !offsets) return IBP_ERR_INVALID_ARG;
+    if (n_out == 0) return IBP_OK;
+    DeviceGuard guard(h->device);
+    if (!guard.ok) return IBP_ERR_DEVICE;
+    const uint64_t L = h->params.tensor_bytes;
+    if (n_out > (~0ull) / L) return IBP_ERR_INVALID_ARG;
+    if (!device_or_pinned(buf, h->device)) return IBP_ERR_INVALID_ARG;
+    if (!device_only(offsets, h->device) || !device_only(bitmask, h->device) || !device_only(dst, h->device))
+        return IBP_ERR_INVALID_ARG;
+    if (ids && !device_only(ids, h->device)) return IBP_ERR_INVALID_ARG;
+    if (reinterpret_cast<uintptr_t>(offsets) % 8) return IBP_ERR_INVALID_ARG;
+    if (overlaps(buf, buf_bytes, dst, n_out * L)) return IBP_ERR_INVALID_ARG;
+    Geo geo = make_geo(h, aligned16(L, {buf, dst}), kLongTileWordsDecode);
+    const bool uni = h->sum.uniform != 0;
+    if (!packed_decode_supported(geo, h->sum.max_runs, uni)) return IBP_ERR_UNSUPPORTED;
+    // an item's length is known from the offsets: read it whole at once
+    geo.spec_words = (uint32_t)geo.n_words;
+    const Items items{offsets, buf_bytes};
+    return from_hip(launch_decode(h->tabs, geo, h->sum.max_runs, uni, buf, n_items, bitmask, ids, n_out, dst,
+                                  h->d_err, nullptr, h->cu_count, stream, &items));
+}
+
+ibp_status ibp_decompress_packed(ibp_meta_t h, const void* buf, uint64_t buf_bytes, const uint64_t* offsets,
+                                 const uint32_t* bitmask, uint64_t n_items, void* dst, hipStream_t stream) {
+    return decode_packed_common(h, buf, buf_bytes, offsets, n_items, bitmask, nullptr, n_items, dst, stream);
+}
+
+ibp_status ibp_gather_decompress_packed(ibp_meta_t h, const void* buf, uint64_t buf_bytes, const uint64_t* offsets,
+                                        uint64_t n_items, const uint32_t* bitmask, const int64_t* ids,
+                                        uint64_t n_ids, void* dst, hipStream_t stream) {
+    if (n_ids && !ids) return IBP_ERR_INVALID_ARG;
+    return decode_packed_common(h, buf, buf_bytes, offsets, n_items, bitmask, ids, n_ids, dst, stream);
+}
+
 ibp_status ibp_check(ibp_meta_t h, hipStream_t stream) {
     if (!h) return IBP_ERR_INVALID_ARG;
     DeviceGuard guard(h->device);

@@ -155,13 +155,17 @@ __device__ __forceinline__ void stage_tables(const Tables& t, uint32_t Mw, uint3
 // next 64 tiles are fetched first (one lane per tile); then the first read of
 // tile k+1 (the whole slot of a raw tensor, the first spec_words of a record)
 // is in flight in registers while tile k is decoded.
+//
+// Packed cache layout (items.offsets set): each lane also fetches its tile's
+// item span; every read stays inside that span, and an item whose span does
+// not fit its record (or the buffer) latches a corrupt-record error.
 // ---------------------------------------------------------------------------
 template <int RUNS, bool UNI, bool MW4, int STAGE>
 __global__ __launch_bounds__(256) void k_decode_small(Tables t, Geo geo, const uint8_t* __restrict__ slots,
                                                       uint64_t n_slots, const uint32_t* __restrict__ bitmask,
                                                       const int64_t* __restrict__ ids, uint64_t n_out,
                                                       uint8_t* __restrict__ dst, uint32_t* err,
-                                                      uint32_t buf_words) {
+                                                      uint32_t buf_words, Items items) {
     extern __shared__ uint32_t smem[];
     const uint32_t lane = lane_id();
     const uint32_t wib = uniform(threadIdx.x / kWave);
@@ -193,25 +197,54 @@ __global__ __launch_bounds__(256) void k_decode_small(Tables t, Geo geo, const u
         // lane k: id of tile base + k; the first read of tile 0 (the same
         // prefix for raw and compressed slots) goes out before the bitmask
         // bits are fetched, so the two loads overlap
+        const bool packed = items.offsets != nullptr;
         int64_t my_tensor = -1;
+        bool bad_id = false, bad_item = false;
+        uint64_t my_off = 0;
+        uint32_t my_len = 0;
         if (lane < cnt) {
             const uint64_t oi = first + (base + lane) * stride;
             const int64_t id = ids ? ids[oi] : (int64_t)oi;
-            if (id >= 0 && (uint64_t)id < n_slots) my_tensor = id;
+            if (id >= 0 && (uint64_t)id < n_slots) {
+                my_tensor = id;
+                if (packed) {
+                    const uint64_t a = items.offsets[id], b = items.offsets[id + 1];
+                    bad_item = b < a || b > items.bytes || ((a | b) & 15) || b - a > ((geo.L + 15) & ~15ull);
+                    if (bad_item) {
+                        my_tensor = -1;
+                    } else {
+                        my_off = a;
+                        my_len = (uint32_t)(b - a);
+                    }
+                }
+            } else {
+                bad_id = true;
+            }
         }
         const uint32_t t_lo = (uint32_t)my_tensor, t_hi = (uint32_t)((uint64_t)my_tensor >> 32);
+        const uint32_t o_lo = (uint32_t)my_off, o_hi = (uint32_t)(my_off >> 32);
 
         auto tensor_of = [&](uint32_t k) __attribute__((always_inline)) -> int64_t {
             return (int64_t)(((uint64_t)lane_value(t_hi, k) << 32) | lane_value(t_lo, k));
         };
+        // byte offset of tile k's slot or item, and 16-byte vectors its first read takes
+        auto where_of = [&](uint32_t k, int64_t tn, uint32_t* n4_first) __attribute__((always_inline)) -> uint64_t {
+            if (!packed) {
+                *n4_first = n4_spec;
+                return (uint64_t)tn * geo.L;
+            }
+            *n4_first = min(n4_spec, lane_value(my_len, k) >> 4);
+            return ((uint64_t)lane_value(o_hi, k) << 32) | lane_value(o_lo, k);
+        };
         auto issue = [&](uint32_t k) __attribute__((always_inline)) {
             const int64_t tn = tensor_of(k);
             if (tn < 0) return;
-            const u32x4* s4 = reinterpret_cast<const u32x4*>(slots + (uint64_t)tn * geo.L);
+            uint32_t n4_first;
+            const u32x4* s4 = reinterpret_cast<const u32x4*>(slots + where_of(k, tn, &n4_first));
 #pragma unroll
             for (int r = 0; r < STAGE; ++r) {
                 const uint32_t i = lane + (uint32_t)r * kWave;
-                if (i < n4_spec) st[r] = __builtin_nontemporal_load(s4 + i);
+                if (i < n4_first) st[r] = __builtin_nontemporal_load(s4 + i);
             }
         };
 
@@ -219,29 +252,36 @@ __global__ __launch_bounds__(256) void k_decode_small(Tables t, Geo geo, const u
         uint32_t my_comp = 0;
         if (lane < cnt && my_tensor >= 0)
             my_comp = (bitmask[(uint64_t)my_tensor >> 5] >> ((uint64_t)my_tensor & 31)) & 1u;
-        if (ballot(lane < cnt && my_tensor < 0)) latch_error(err, kErrRange);
+        if (ballot(bad_id)) latch_error(err, kErrRange);
+        if (ballot(bad_item)) latch_error(err, kErrCorrupt);
         for (uint32_t k = 0; k < cnt; ++k) {
             const int64_t tn = tensor_of(k);
             const uint32_t comp = lane_value(my_comp, k);
             const uint64_t oi = first + (base + k) * stride;
             uint32_t* out = reinterpret_cast<uint32_t*>(dst + oi * geo.L);
+            uint32_t n4_first = 0, len = 0;
+            const uint8_t* item = nullptr;
             if (tn >= 0) {
+                item = slots + where_of(k, tn, &n4_first);
+                len = packed ? lane_value(my_len, k) : (uint32_t)geo.L;
                 if (comp) {
 #pragma unroll
                     for (int r = 0; r < STAGE; ++r) {
                         const uint32_t i = lane + (uint32_t)r * kWave;
-                        if (i < n4_spec) reinterpret_cast<u32x4*>(buf)[i] = st[r];
+                        if (i < n4_first) reinterpret_cast<u32x4*>(buf)[i] = st[r];
                     }
+                } else if (len < geo.L) {
+                    latch_error(err, kErrCorrupt);  // a raw item shorter than the tensor
                 } else {
                     // raw slot: the prefix from registers, the rest copied
 #pragma unroll
                     for (int r = 0; r < STAGE; ++r) {
                         const uint32_t i = lane + (uint32_t)r * kWave;
-                        if (i < n4_spec) __builtin_nontemporal_store(st[r], reinterpret_cast<u32x4*>(out) + i);
+                        if (i < n4_first) __builtin_nontemporal_store(st[r], reinterpret_cast<u32x4*>(out) + i);
                     }
-                    if (n4_spec < n4_raw)
-                        copy_words(reinterpret_cast<const uint32_t*>(slots + (uint64_t)tn * geo.L), out,
-                                   4ull * n4_spec, 4u * (n4_raw - n4_spec), true);
+                    if (n4_first < n4_raw)
+                        copy_words(reinterpret_cast<const uint32_t*>(item), out, 4ull * n4_first,
+                                   4u * (n4_raw - n4_first), true);
                 }
             }
             if (k + 1 < cnt) issue(k + 1);
@@ -252,14 +292,13 @@ __global__ __launch_bounds__(256) void k_decode_small(Tables t, Geo geo, const u
             const uint32_t rem = header_removed_bits(planes, geo, buf, 0, hw, &bad_pad);
             const uint64_t R = 32ull * hw + 32ull * nwords - rem;
             const uint32_t words = (uint32_t)((R + 31) / 32);
-            if (bad_pad || 4ull * words >= geo.L) {
+            if (bad_pad || 4ull * words >= geo.L || 4ull * words > len) {
                 latch_error(err, kErrCorrupt);
                 continue;
             }
-            uint32_t have = geo.spec_words;
+            uint32_t have = 4 * n4_first;
             if (words > have) {
-                load_exact_to_lds(reinterpret_cast<const uint32_t*>(slots + (uint64_t)tn * geo.L), have, words,
-                                  buf + have);
+                load_exact_to_lds(reinterpret_cast<const uint32_t*>(item), have, words, buf + have);
                 have = words;
             }
             if (lane == 0) buf[have] = 0;
@@ -408,14 +447,14 @@ template <int RUNS, bool UNI, bool MW4, int S>
 static hipError_t launch_small_s(const Tables& t, const Geo& geo, const void* slots, uint64_t n_slots,
                                  const uint32_t* bitmask, const int64_t* ids, uint64_t n_out, void* dst,
                                  uint32_t* err, uint32_t cu_count, size_t head, size_t wave, uint32_t buf_words,
-                                 hipStream_t s, bool* launched) {
+                                 const Items& items, hipStream_t s, bool* launched) {
     const void* fn = reinterpret_cast<const void*>(&k_decode_small<RUNS, UNI, MW4, S>);
     PersistentPlan plan;
     *launched = false;
     if (!plan_persistent(fn, head, wave, cu_count, n_out, &plan)) return hipSuccess;
     hipLaunchKernelGGL((k_decode_small<RUNS, UNI, MW4, S>), dim3(plan.blocks), dim3(kWave * plan.wpb), plan.shm, s,
                        t, geo, static_cast<const uint8_t*>(slots), n_slots, bitmask, ids, n_out,
-                       static_cast<uint8_t*>(dst), err, buf_words);
+                       static_cast<uint8_t*>(dst), err, buf_words, items);
     *launched = true;
     return hipGetLastError();
 }
@@ -424,14 +463,14 @@ template <int RUNS, bool UNI>
 static hipError_t launch_small(const Tables& t, const Geo& geo, const void* slots, uint64_t n_slots,
                                const uint32_t* bitmask, const int64_t* ids, uint64_t n_out, void* dst,
                                uint32_t* err, uint32_t cu_count, size_t head, size_t wave, uint32_t buf_words,
-                               hipStream_t s, bool* launched) {
+                               const Items& items, hipStream_t s, bool* launched) {
     const uint32_t stage = (uint32_t)((geo.n_words + 4 * kWave - 1) / (4 * kWave));
     const bool mw4 = geo.Mw % 4 == 0;
 #define IBP_SMALL(S)                                                                                          \
     return mw4 ? launch_small_s<RUNS, UNI, true, S>(t, geo, slots, n_slots, bitmask, ids, n_out, dst, err,     \
-                                                    cu_count, head, wave, buf_words, s, launched)               \
+                                                    cu_count, head, wave, buf_words, items, s, launched)        \
                : launch_small_s<RUNS, UNI, false, S>(t, geo, slots, n_slots, bitmask, ids, n_out, dst, err,    \
-                                                     cu_count, head, wave, buf_words, s, launched)
+                                                     cu_count, head, wave, buf_words, items, s, launched)
     if (stage <= 1) IBP_SMALL(1);
     if (stage <= 2) IBP_SMALL(2);
     if (stage <= 4) IBP_SMALL(4);
@@ -457,30 +496,43 @@ static hipError_t launch_tiles(const Tables& t, const Geo& geo, const void* slot
 template <int RUNS, bool UNI>
 static hipError_t launch_decode_r(const Tables& t, const Geo& geo, const void* slots, uint64_t n_slots,
                                   const uint32_t* bitmask, const int64_t* ids, uint64_t n_out, void* dst,
-                                  uint32_t* err, const LookBack* lb, uint32_t cu_count, hipStream_t s) {
-    if (geo.tiles_per_tensor > 1)
+                                  uint32_t* err, const LookBack* lb, uint32_t cu_count, hipStream_t s,
+                                  const Items& items) {
+    if (geo.tiles_per_tensor > 1) {
+        if (items.offsets) return hipErrorInvalidValue;
         return launch_tiles<RUNS, UNI, true>(t, geo, slots, n_slots, bitmask, ids, n_out, dst, err, *lb, s);
+    }
     uint32_t buf_words = 0;
     size_t head = 0, wave = 0;
     if (geo.aligned16 && small_lds(geo, RUNS, UNI, &buf_words, &head, &wave)) {
         bool launched = false;
         const hipError_t e = launch_small<RUNS, UNI>(t, geo, slots, n_slots, bitmask, ids, n_out, dst, err, cu_count,
-                                                     head, wave, buf_words, s, &launched);
+                                                     head, wave, buf_words, items, s, &launched);
         if (e != hipSuccess || launched) return e;
     }
+    if (items.offsets) return hipErrorInvalidValue;  // the packed layout runs on k_decode_small only
     return launch_tiles<RUNS, UNI, false>(t, geo, slots, n_slots, bitmask, ids, n_out, dst, err, LookBack{}, s);
+}
+
+bool packed_decode_supported(const Geo& geo, uint32_t runs, bool uniform_meta) {
+    uint32_t buf_words = 0;
+    size_t head = 0, wave = 0;
+    return geo.tiles_per_tensor == 1 && geo.aligned16 &&
+           small_lds(geo, (int)runs_bucket(runs), uniform_meta, &buf_words, &head, &wave);
 }
 
 hipError_t launch_decode(const Tables& t, const Geo& geo, uint32_t runs, bool uniform_meta, const void* slots,
                          uint64_t n_slots, const uint32_t* bitmask, const int64_t* ids, uint64_t n_out,
-                         void* dst, uint32_t* err, const LookBack* lb, uint32_t cu_count, hipStream_t s) {
+                         void* dst, uint32_t* err, const LookBack* lb, uint32_t cu_count, hipStream_t s,
+                         const Items* items) {
     if (n_out == 0) return hipSuccess;
+    const Items it = items ? *items : Items{nullptr, 0};
 #define IBP_R(R)                                                                                      \
     return uniform_meta                                                                                \
                ? launch_decode_r<R, true>(t, geo, slots, n_slots, bitmask, ids, n_out, dst, err, lb,    \
-                                          cu_count, s)                                                 \
+                                          cu_count, s, it)                                             \
                : launch_decode_r<R, false>(t, geo, slots, n_slots, bitmask, ids, n_out, dst, err, lb,   \
-                                           cu_count, s)
+                                           cu_count, s, it)
     switch (runs_bucket(runs)) {
         case 0: IBP_R(0);
         case 1: IBP_R(1);

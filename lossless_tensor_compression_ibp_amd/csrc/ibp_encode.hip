@@ -216,12 +216,18 @@ __global__ __launch_bounds__(256) void k_encode(Tables t, Geo geo, const uint8_t
 // registers the current step has just consumed.  The record is assembled in
 // LDS (header words, then the kept bits) and written with 16-byte stores; an
 // incompressible tensor is copied from its source again.
+//
+// Item placement: fixed slots (items.offsets == nullptr) or the packed cache
+// layout, where the item goes to its offset once its length has been checked
+// against the offsets.  SIZES: only the item lengths, rounded up to 16 bytes,
+// are computed and written to sizes[] (no record buffer, no slot writes).
 // ---------------------------------------------------------------------------
-template <int RUNS, bool UNI, bool MW4, int STAGE>
+template <int RUNS, bool UNI, bool MW4, int STAGE, bool SIZES>
 __global__ __launch_bounds__(1024) void k_encode_small(Tables t, Geo geo, const uint8_t* __restrict__ src,
                                                       uint64_t n_tensors, uint8_t* __restrict__ slots,
                                                       uint32_t* __restrict__ bitmask, uint64_t* __restrict__ stored,
-                                                      uint32_t buf_words) {
+                                                      uint32_t buf_words, Items items, uint64_t* __restrict__ sizes,
+                                                      uint32_t* err) {
     extern __shared__ uint32_t smem[];
     const uint32_t lane = lane_id();
     const uint32_t wib = uniform(threadIdx.x / kWave);
@@ -280,8 +286,14 @@ __global__ __launch_bounds__(1024) void k_encode_small(Tables t, Geo geo, const 
     for (; ti < n_tensors; ti += stride) {
         const uint64_t tnext = ti + stride;
         const u32x4* nx4 = reinterpret_cast<const u32x4*>(src + (tnext < n_tensors ? tnext : ti) * geo.L);
+        // packed placement: this tensor's item span, needed once the record is built
+        uint64_t item_a = 0, item_b = 0;
+        if (!SIZES && items.offsets) {
+            item_a = items.offsets[ti];
+            item_b = items.offsets[ti + 1];
+        }
         // zero the record buffer: header words, then the kept bits
-        {
+        if constexpr (!SIZES) {
             u32x4* b4 = reinterpret_cast<u32x4*>(buf);
             for (uint32_t i = lane; i < (buf_words >> 2); i += kWave) b4[i] = u32x4{0u, 0u, 0u, 0u};
         }
@@ -354,7 +366,7 @@ __global__ __launch_bounds__(1024) void k_encode_small(Tables t, Geo geo, const 
                 for (int j = 0; j < 4; ++j) p[j] = pc;
                 hbits = (lane & (q - 1u)) == 0 ? (uint32_t)pc : 0u;
             }
-            if (live && hbits) atomicOr(&buf[c0 >> 5], hbits << (c0 & 31u));
+            if (!SIZES && live && hbits) atomicOr(&buf[c0 >> 5], hbits << (c0 & 31u));
             // run masks of the lane's four positions: one 16-byte read per run
             uint32_t rr[RUNS > 0 ? RUNS : 1][4];
             if constexpr (MW4 && !UNI) {
@@ -383,17 +395,21 @@ __global__ __launch_bounds__(1024) void k_encode_small(Tables t, Geo geo, const 
                 size[j] = live ? (p[j] ? 32u - (kd[j] & 63u) : 32u) : 0u;
                 tot += size[j];
             }
-            const uint32_t incl = wave_incl_scan(tot);
-            uint32_t off = carry + incl - tot;
-            carry += lane_value(incl, kWave - 1);
+            if constexpr (SIZES) {
+                carry += wave_sum(tot);
+            } else {
+                const uint32_t incl = wave_incl_scan(tot);
+                uint32_t off = carry + incl - tot;
+                carry += lane_value(incl, kWave - 1);
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                if (size[j]) {
-                    const uint32_t q = off >> 5, sh = off & 31u;
-                    atomicOr(&pay[q], f[j] << sh);
-                    if (sh + size[j] > 32) atomicOr(&pay[q + 1], f[j] >> (32 - sh));
+                for (int j = 0; j < 4; ++j) {
+                    if (size[j]) {
+                        const uint32_t q = off >> 5, sh = off & 31u;
+                        atomicOr(&pay[q], f[j] << sh);
+                        if (sh + size[j] > 32) atomicOr(&pay[q + 1], f[j] >> (32 - sh));
+                    }
+                    off += size[j];
                 }
-                off += size[j];
             }
             if constexpr (!UNI) {
                 pos0 += step_inc;
@@ -404,7 +420,19 @@ __global__ __launch_bounds__(1024) void k_encode_small(Tables t, Geo geo, const 
         const uint64_t R = 32ull * hw + carry;
         const uint32_t words = (uint32_t)((R + 31) / 32);
         const bool comp = 4ull * words < geo.L;
-        u32x4* slot4 = reinterpret_cast<u32x4*>(slots + ti * geo.L);
+        const uint64_t item16 = ((comp ? 4ull * words : geo.L) + 15) & ~15ull;
+        if constexpr (SIZES) {
+            if (lane == 0) sizes[ti] = item16;
+            continue;
+        }
+        u32x4* slot4 = reinterpret_cast<u32x4*>(slots + (items.offsets ? item_a : ti * geo.L));
+        if (items.offsets && (item_b < item_a || item_b - item_a != item16 || item_b > items.bytes ||
+                              (item_a & 15))) {
+            // offsets that do not describe this tensor's item: write nothing
+            latch_error(err, item_b > items.bytes ? kErrRange : kErrCorrupt);
+            __builtin_amdgcn_wave_barrier();
+            continue;
+        }
         if (comp) {
             const uint32_t w4 = (words + 3) >> 2;  // <= n4: the slot is a multiple of 16 bytes
             const u32x4* b4 = reinterpret_cast<const u32x4*>(buf);
@@ -494,33 +522,44 @@ static bool small_encode_lds(const Geo& geo, int runs, bool uni, uint32_t* buf_w
     return true;
 }
 
-template <int RUNS, bool UNI, bool MW4, int S>
+// Extra arguments of the packed-cache modes (defaults: fixed slots).
+struct SmallArgs {
+    Items items{nullptr, 0};
+    uint64_t* sizes = nullptr;
+    uint32_t* err = nullptr;
+};
+
+template <int RUNS, bool UNI, bool MW4, int S, bool SIZES>
 static hipError_t launch_encode_small_s(const Tables& t, const Geo& geo, const void* src, uint64_t n_tensors,
                                         void* slots, uint32_t* bitmask, uint64_t* stored, uint32_t cu_count,
-                                        size_t head, size_t wave, uint32_t buf_words, hipStream_t s,
-                                        bool* launched) {
-    const void* fn = reinterpret_cast<const void*>(&k_encode_small<RUNS, UNI, MW4, S>);
+                                        size_t head, size_t wave, uint32_t buf_words, const SmallArgs& xa,
+                                        hipStream_t s, bool* launched) {
+    const void* fn = reinterpret_cast<const void*>(&k_encode_small<RUNS, UNI, MW4, S, SIZES>);
     PersistentPlan plan;
     *launched = false;
-    if (!plan_persistent(fn, head, wave, cu_count, n_tensors, &plan)) return hipSuccess;
-    hipLaunchKernelGGL((k_encode_small<RUNS, UNI, MW4, S>), dim3(plan.blocks), dim3(kWave * plan.wpb), plan.shm, s,
-                       t, geo, static_cast<const uint8_t*>(src), n_tensors, static_cast<uint8_t*>(slots), bitmask,
-                       stored, buf_words);
+    if (!plan_persistent(fn, head, SIZES ? 0 : wave, cu_count, n_tensors, &plan)) return hipSuccess;
+    hipLaunchKernelGGL((k_encode_small<RUNS, UNI, MW4, S, SIZES>), dim3(plan.blocks), dim3(kWave * plan.wpb),
+                       plan.shm, s, t, geo, static_cast<const uint8_t*>(src), n_tensors,
+                       static_cast<uint8_t*>(slots), bitmask, stored, SIZES ? 0u : buf_words, xa.items, xa.sizes,
+                       xa.err);
     *launched = true;
     return hipGetLastError();
 }
 
-template <int RUNS, bool UNI>
+template <int RUNS, bool UNI, bool SIZES>
 static hipError_t launch_encode_small(const Tables& t, const Geo& geo, const void* src, uint64_t n_tensors,
                                       void* slots, uint32_t* bitmask, uint64_t* stored, uint32_t cu_count,
-                                      size_t head, size_t wave, uint32_t buf_words, hipStream_t s, bool* launched) {
+                                      size_t head, size_t wave, uint32_t buf_words, const SmallArgs& xa,
+                                      hipStream_t s, bool* launched) {
     const uint32_t stage = (uint32_t)((geo.n_words + 4 * kWave - 1) / (4 * kWave));
     const bool mw4 = geo.Mw % 4 == 0;
 #define IBP_ENC_SMALL(S)                                                                                        \
-    return mw4 ? launch_encode_small_s<RUNS, UNI, true, S>(t, geo, src, n_tensors, slots, bitmask, stored,      \
-                                                           cu_count, head, wave, buf_words, s, launched)         \
-               : launch_encode_small_s<RUNS, UNI, false, S>(t, geo, src, n_tensors, slots, bitmask, stored,     \
-                                                            cu_count, head, wave, buf_words, s, launched)
+    return mw4 ? launch_encode_small_s<RUNS, UNI, true, S, SIZES>(t, geo, src, n_tensors, slots, bitmask,       \
+                                                                  stored, cu_count, head, wave, buf_words, xa,  \
+                                                                  s, launched)                                  \
+               : launch_encode_small_s<RUNS, UNI, false, S, SIZES>(t, geo, src, n_tensors, slots, bitmask,      \
+                                                                   stored, cu_count, head, wave, buf_words, xa, \
+                                                                   s, launched)
     if (stage <= 1) IBP_ENC_SMALL(1);
     if (stage <= 2) IBP_ENC_SMALL(2);
     if (stage <= 4) IBP_ENC_SMALL(4);
@@ -538,11 +577,14 @@ static hipError_t launch_encode_r(const Tables& t, const Geo& geo, bool uniform_
         size_t head = 0, wave = 0;
         if (geo.aligned16 && small_encode_lds(geo, RUNS, uniform_meta, &buf_words, &head, &wave)) {
             bool launched = false;
+            const SmallArgs xa;
             const hipError_t e =
-                uniform_meta ? launch_encode_small<RUNS, true>(t, geo, src, n_tensors, slots, bitmask, stored,
-                                                               cu_count, head, wave, buf_words, s, &launched)
-                             : launch_encode_small<RUNS, false>(t, geo, src, n_tensors, slots, bitmask, stored,
-                                                                cu_count, head, wave, buf_words, s, &launched);
+                uniform_meta ? launch_encode_small<RUNS, true, false>(t, geo, src, n_tensors, slots, bitmask, stored,
+                                                                      cu_count, head, wave, buf_words, xa, s,
+                                                                      &launched)
+                             : launch_encode_small<RUNS, false, false>(t, geo, src, n_tensors, slots, bitmask,
+                                                                       stored, cu_count, head, wave, buf_words, xa,
+                                                                       s, &launched);
             if (e != hipSuccess || launched) return e;
         }
         return launch_encode_t<false>(t, geo, RUNS, src, n_tensors, slots, bitmask, stored, LookBack{}, lds_words,
@@ -557,6 +599,119 @@ static hipError_t launch_encode_r(const Tables& t, const Geo& geo, bool uniform_
                        static_cast<const uint8_t*>(src), static_cast<uint8_t*>(slots), bitmask, stored,
                        lb->totals, bpt);
     return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Item offsets of the packed cache: offsets[1..n] hold the item sizes and are
+// turned into their inclusive prefix sums in place (offsets[0] <- 0).  One
+// wave per block of kScanBlock sizes (eight consecutive per lane); blocks
+// take dynamic tickets and chain their totals by decoupled look-back.  Items
+// are at most 8 KiB, so a block's total fits in 32 bits.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void k_scan_sizes(uint64_t* __restrict__ offsets, uint64_t n, LookBack lb) {
+    const uint32_t lane = lane_id();
+    uint32_t tk = 0;
+    if (lane == 0) tk = atomicAdd(lb.ticket, 1u);
+    const uint64_t blk = (uint32_t)(uniform(tk) - lb.ticket_base);
+    const uint64_t n_blocks = (n + kScanBlock - 1) / kScanBlock;
+    if (blk >= n_blocks) return;
+    uint64_t* sz = offsets + 1;
+    const uint64_t i0 = blk * kScanBlock + (uint64_t)lane * kScanPerLane;
+    uint32_t v[kScanPerLane];
+    uint32_t run = 0;
+#pragma unroll
+    for (uint32_t j = 0; j < kScanPerLane; ++j) {
+        run += (i0 + j < n) ? (uint32_t)sz[i0 + j] : 0u;
+        v[j] = run;
+    }
+    const uint32_t incl = wave_incl_scan(run);
+    const uint32_t agg = lane_value(incl, kWave - 1);
+    const uint64_t base = lookback_exclusive(lb.status, 0, blk, agg, 0, lb.epoch);
+    const uint64_t pre = base + (incl - run);
+#pragma unroll
+    for (uint32_t j = 0; j < kScanPerLane; ++j)
+        if (i0 + j < n) sz[i0 + j] = pre + v[j];
+    if (blk == 0 && lane == 0) offsets[0] = 0;
+}
+
+uint64_t scan_waves(uint64_t n) {
+    const uint64_t n_blocks = (n + kScanBlock - 1) / kScanBlock;
+    return ((n_blocks + kWavesPerBlock - 1) / kWavesPerBlock) * kWavesPerBlock;
+}
+
+hipError_t launch_scan_sizes(uint64_t* offsets, uint64_t n, const LookBack& lb, hipStream_t s) {
+    if (n == 0) return launch_fill_u32(reinterpret_cast<uint32_t*>(offsets), 2, 0, s);
+    const uint64_t waves = scan_waves(n);
+    hipLaunchKernelGGL(k_scan_sizes, dim3((uint32_t)(waves / kWavesPerBlock)), dim3(kWave * kWavesPerBlock), 0, s,
+                       offsets, n, lb);
+    return hipGetLastError();
+}
+
+// Packed-cache entry points: the persistent small-tensor kernel in its
+// sizes-only or packed-placement mode.
+template <int RUNS>
+static hipError_t launch_packed_r(const Tables& t, const Geo& geo, bool uniform_meta, bool sizes_only,
+                                  const void* src, uint64_t n_tensors, void* dst, uint32_t* bitmask,
+                                  const SmallArgs& xa, uint32_t cu_count, hipStream_t s) {
+    uint32_t buf_words = 0;
+    size_t head = 0, wave = 0;
+    if (geo.tiles_per_tensor != 1 || !geo.aligned16 || !small_encode_lds(geo, RUNS, uniform_meta, &buf_words, &head, &wave))
+        return hipErrorInvalidValue;
+    bool launched = false;
+    hipError_t e;
+    if (sizes_only)
+        e = uniform_meta ? launch_encode_small<RUNS, true, true>(t, geo, src, n_tensors, nullptr, nullptr, nullptr,
+                                                                 cu_count, head, wave, buf_words, xa, s, &launched)
+                         : launch_encode_small<RUNS, false, true>(t, geo, src, n_tensors, nullptr, nullptr, nullptr,
+                                                                  cu_count, head, wave, buf_words, xa, s, &launched);
+    else
+        e = uniform_meta ? launch_encode_small<RUNS, true, false>(t, geo, src, n_tensors, dst, bitmask, nullptr,
+                                                                  cu_count, head, wave, buf_words, xa, s, &launched)
+                         : launch_encode_small<RUNS, false, false>(t, geo, src, n_tensors, dst, bitmask, nullptr,
+                                                                   cu_count, head, wave, buf_words, xa, s,
+                                                                   &launched);
+    if (e != hipSuccess) return e;
+    return launched ? hipSuccess : hipErrorInvalidValue;
+}
+
+static hipError_t launch_packed(const Tables& t, const Geo& geo, uint32_t runs, bool uniform_meta, bool sizes_only,
+                                const void* src, uint64_t n_tensors, void* dst, uint32_t* bitmask,
+                                const SmallArgs& xa, uint32_t cu_count, hipStream_t s) {
+    if (n_tensors == 0) return hipSuccess;
+#define IBP_PK(R) return launch_packed_r<R>(t, geo, uniform_meta, sizes_only, src, n_tensors, dst, bitmask, xa, cu_count, s)
+    switch (runs_bucket(runs)) {
+        case 0: IBP_PK(0);
+        case 1: IBP_PK(1);
+        case 2: IBP_PK(2);
+        case 3: IBP_PK(3);
+        case 4: IBP_PK(4);
+        case 8: IBP_PK(8);
+        default: IBP_PK(16);
+    }
+#undef IBP_PK
+}
+
+bool packed_supported(const Geo& geo, uint32_t runs, bool uniform_meta) {
+    uint32_t buf_words = 0;
+    size_t head = 0, wave = 0;
+    return geo.tiles_per_tensor == 1 && geo.aligned16 &&
+           small_encode_lds(geo, (int)runs_bucket(runs), uniform_meta, &buf_words, &head, &wave);
+}
+
+hipError_t launch_item_sizes(const Tables& t, const Geo& geo, uint32_t runs, bool uniform_meta, const void* src,
+                             uint64_t n_tensors, uint64_t* sizes, uint32_t cu_count, hipStream_t s) {
+    SmallArgs xa;
+    xa.sizes = sizes;
+    return launch_packed(t, geo, runs, uniform_meta, true, src, n_tensors, nullptr, nullptr, xa, cu_count, s);
+}
+
+hipError_t launch_encode_packed(const Tables& t, const Geo& geo, uint32_t runs, bool uniform_meta,
+                                const void* src, uint64_t n_tensors, void* dst, const Items& items,
+                                uint32_t* bitmask, uint32_t* err, uint32_t cu_count, hipStream_t s) {
+    SmallArgs xa;
+    xa.items = items;
+    xa.err = err;
+    return launch_packed(t, geo, runs, uniform_meta, false, src, n_tensors, dst, bitmask, xa, cu_count, s);
 }
 
 hipError_t launch_encode(const Tables& t, const Geo& geo, uint32_t runs, bool uniform_meta, const void* src,

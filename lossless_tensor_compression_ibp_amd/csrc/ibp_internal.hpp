@@ -58,6 +58,15 @@ struct LookBack {
 
 enum DeviceError : uint32_t { kErrNone = 0, kErrCorrupt = 5, kErrRange = 6 };
 
+// Where tensor t's stored item lives.  offsets == nullptr: fixed slots, slot
+// t at byte t * L.  Otherwise the packed cache layout: item t spans bytes
+// [offsets[t], offsets[t+1]) of a buffer of `bytes` bytes, each item starting
+// on a 16-byte boundary and its length a multiple of 16.
+struct Items {
+    const uint64_t* offsets;
+    uint64_t bytes;
+};
+
 // Summary written by the table builder, read back by the host.
 struct Summary {
     uint32_t max_runs;
@@ -99,6 +108,28 @@ hipError_t launch_encode(const Tables& t, const Geo& geo, uint32_t runs, bool un
                          uint32_t cu_count, hipStream_t s);
 hipError_t launch_decode(const Tables& t, const Geo& geo, uint32_t runs, bool uniform_meta, const void* slots,
                          uint64_t n_slots, const uint32_t* bitmask, const int64_t* ids, uint64_t n_out,
-                         void* dst, uint32_t* err, const LookBack* lb, uint32_t cu_count, hipStream_t s);
+                         void* dst, uint32_t* err, const LookBack* lb, uint32_t cu_count, hipStream_t s,
+                         const Items* items = nullptr);
+
+// Packed cache.  These run only on the persistent small-tensor kernels
+// (16-byte aligned tensors of at most kMaxTileWords words whose tables fit in
+// LDS); packed_supported() says whether a geometry qualifies.
+bool packed_supported(const Geo& geo, uint32_t runs, bool uniform_meta);         // encode side
+bool packed_decode_supported(const Geo& geo, uint32_t runs, bool uniform_meta);  // decode side
+// sizes[t] <- bytes of tensor t's item rounded up to 16 (record or raw).
+hipError_t launch_item_sizes(const Tables& t, const Geo& geo, uint32_t runs, bool uniform_meta, const void* src,
+                             uint64_t n_tensors, uint64_t* sizes, uint32_t cu_count, hipStream_t s);
+// Items of src written at their offsets (packed), bitmask as for slots;
+// items whose offsets disagree with their length or pass the buffer's end
+// are skipped and latch an error.
+hipError_t launch_encode_packed(const Tables& t, const Geo& geo, uint32_t runs, bool uniform_meta,
+                                const void* src, uint64_t n_tensors, void* dst, const Items& items,
+                                uint32_t* bitmask, uint32_t* err, uint32_t cu_count, hipStream_t s);
+// offsets[1..n] hold sizes on entry and their inclusive prefix sums on exit;
+// offsets[0] <- 0.  One look-back entry per block of kScanBlock sizes.
+constexpr uint32_t kScanPerLane = 8;
+constexpr uint32_t kScanBlock = kScanPerLane * kWave;
+hipError_t launch_scan_sizes(uint64_t* offsets, uint64_t n, const LookBack& lb, hipStream_t s);
+uint64_t scan_waves(uint64_t n);
 
 }  // namespace ibp

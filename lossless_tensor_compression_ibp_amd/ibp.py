@@ -29,6 +29,7 @@ ABI_FUNCTIONS = (
     "ibp_build_metadata", "ibp_meta_create", "ibp_meta_get", "ibp_meta_get_info",
     "ibp_meta_set_first_read", "ibp_meta_destroy", "ibp_compress", "ibp_decompress", "ibp_gather_decompress",
     "ibp_check", "ibp_status_string",
+    "ibp_packed_offsets", "ibp_compress_packed", "ibp_decompress_packed", "ibp_gather_decompress_packed",
 )
 
 
@@ -71,6 +72,10 @@ def lib():
         L.ibp_decompress.argtypes = [p, p, p, u64, p, p]
         L.ibp_gather_decompress.argtypes = [p, p, u64, p, p, u64, p, p]
         L.ibp_check.argtypes = [p, p]
+        L.ibp_packed_offsets.argtypes = [p, p, u64, p, p]
+        L.ibp_compress_packed.argtypes = [p, p, u64, p, p, u64, p, p]
+        L.ibp_decompress_packed.argtypes = [p, p, u64, p, p, u64, p, p]
+        L.ibp_gather_decompress_packed.argtypes = [p, p, u64, p, u64, p, p, u64, p, p]
         L.ibp_status_string.argtypes = [st]
         L.ibp_status_string.restype = ctypes.c_char_p
         for f in ABI_FUNCTIONS:
@@ -201,3 +206,42 @@ def ibp_gather_decompress(meta: Meta, slots: torch.Tensor, n_slots: int, bitmask
 def ibp_check(meta: Meta, stream=None) -> int:
     """Synchronises the stream; returns the latched device status (0 = ok)."""
     return int(lib().ibp_check(meta, _stream(stream)))
+
+
+# ---------------------------------------------------------------------------
+# Packed cache: items back to back at 16-byte aligned offsets.
+# ---------------------------------------------------------------------------
+def ibp_packed_offsets(meta: Meta, src: torch.Tensor, n_tensors: int, offsets: torch.Tensor, stream=None):
+    """offsets: device int64 tensor of n_tensors + 1 entries (written)."""
+    if offsets.dtype != torch.int64 or offsets.numel() < n_tensors + 1:
+        raise ValueError("offsets must be int64 with n_tensors + 1 entries")
+    _check(lib().ibp_packed_offsets(meta, _ptr(src) if n_tensors else None, int(n_tensors), _ptr(offsets),
+                                    _stream(stream)), "ibp_packed_offsets")
+
+
+def ibp_compress_packed(meta: Meta, src: torch.Tensor, n_tensors: int, offsets: torch.Tensor, dst: torch.Tensor,
+                        bitmask: torch.Tensor, capacity: int | None = None, stream=None):
+    if capacity is None:
+        capacity = dst.numel() * dst.element_size()
+    _check(lib().ibp_compress_packed(meta, _ptr(src), int(n_tensors), _ptr(offsets), _ptr(dst), int(capacity),
+                                     _ptr(bitmask), _stream(stream)), "ibp_compress_packed")
+
+
+def ibp_decompress_packed(meta: Meta, buf: torch.Tensor, offsets: torch.Tensor, bitmask: torch.Tensor,
+                          n_items: int, dst: torch.Tensor, buf_bytes: int | None = None, stream=None):
+    if buf_bytes is None:
+        buf_bytes = buf.numel() * buf.element_size()
+    _check(lib().ibp_decompress_packed(meta, _ptr(buf), int(buf_bytes), _ptr(offsets), _ptr(bitmask),
+                                       int(n_items), _ptr(dst), _stream(stream)), "ibp_decompress_packed")
+
+
+def ibp_gather_decompress_packed(meta: Meta, buf: torch.Tensor, offsets: torch.Tensor, n_items: int,
+                                 bitmask: torch.Tensor, ids: torch.Tensor, dst: torch.Tensor,
+                                 buf_bytes: int | None = None, stream=None):
+    if ids.dtype != torch.int64:
+        raise ValueError("ids must be int64")
+    if buf_bytes is None:
+        buf_bytes = buf.numel() * buf.element_size()
+    _check(lib().ibp_gather_decompress_packed(meta, _ptr(buf), int(buf_bytes), _ptr(offsets), int(n_items),
+                                              _ptr(bitmask), _ptr(ids), int(ids.numel()), _ptr(dst),
+                                              _stream(stream)), "ibp_gather_decompress_packed")

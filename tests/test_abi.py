@@ -45,3 +45,9 @@ def test_status_strings_and_host_side_argument_checks():
     assert L.ibp_build_metadata(ctypes.byref(prm), None, 1, ctypes.byref(out), None) == ibp.IBP_ERR_UNSUPPORTED
     assert L.ibp_meta_destroy(None) == ibp.IBP_ERR_INVALID_ARG
     assert L.ibp_check(None, None) == ibp.IBP_ERR_INVALID_ARG
+    # packed-cache calls: a null handle or null offsets is rejected on the host
+    assert L.ibp_packed_offsets(None, None, 0, None, None) == ibp.IBP_ERR_INVALID_ARG
+    assert L.ibp_compress_packed(None, None, 1, None, None, 0, None, None) == ibp.IBP_ERR_INVALID_ARG
+    assert L.ibp_decompress_packed(None, None, 0, None, None, 1, None, None) == ibp.IBP_ERR_INVALID_ARG
+    assert L.ibp_gather_decompress_packed(None, None, 0, None, 1, None, None, 1, None, None) == \
+        ibp.IBP_ERR_INVALID_ARG
