@@ -118,21 +118,29 @@ def copy_kernel_ceiling(nbytes: int = 1 << 30, reps: int = 5) -> float:
     return 2 * nbytes / float(np.median(times[1:])) / GB
 
 
-def timed(fn, steps: int, warmup: int):
+def timed(fn, steps: int, warmup: int, per_launch: bool = True):
     """Runs fn(i) warmup times, then times exactly `steps` calls.  Returns
-    (wall seconds, per-launch event durations in seconds)."""
+    (wall seconds, per-launch event durations in seconds).  per_launch=False
+    records no events inside the timed loop (for launches so short that the
+    event calls themselves would slow the host loop); durations are then None
+    and come from queued_durations()."""
     stream = torch.cuda.current_stream()
     for i in range(warmup):
         fn(i)
     torch.cuda.synchronize()
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(steps if per_launch else 0)]
     t0 = time.perf_counter()
     for i in range(steps):
-        evs[i][0].record(stream)
+        if per_launch:
+            evs[i][0].record(stream)
         fn(warmup + i)
-        evs[i][1].record(stream)
+        if per_launch:
+            evs[i][1].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    if not per_launch:
+        return wall, None
     durs = np.array([s.elapsed_time(e) / 1e3 for s, e in evs])
     return wall, durs
 
@@ -385,7 +393,8 @@ def run_dense_gnn(args) -> dict:
     stored_np = stored.cpu().numpy()
     savings = 1.0 - stored_np.sum() / (n * L)
     out = torch.empty_like(src)
-    wall, _ = timed(lambda i: ibp.ibp_decompress(meta, slots, bitmask, n, out), args.steps, args.warmup)
+    wall, _ = timed(lambda i: ibp.ibp_decompress(meta, slots, bitmask, n, out), args.steps, args.warmup,
+                    per_launch=False)
     # launches shorter than their host submission: time them queued back to back
     durs = queued_durations(lambda i: ibp.ibp_decompress(meta, slots, bitmask, n, out), args.steps)
     assert ibp.ibp_check(meta) == ibp.IBP_OK
@@ -584,7 +593,7 @@ def run_sparse_gnn_cache(args) -> dict:
         ibp.ibp_gather_decompress_packed(meta, buf, offsets, n, bitmask, ids_dev[i], out[i & 1])
 
     log(f"[bench] timing {args.steps} gathers of {batch} rows from the packed HBM cache")
-    wall, _ = timed(step, args.steps, args.warmup)
+    wall, _ = timed(step, args.steps, args.warmup, per_launch=False)
     durs = queued_durations(step, args.steps, args.warmup)
     assert ibp.ibp_check(meta) == ibp.IBP_OK
     last = args.warmup + args.steps - 1
@@ -598,7 +607,7 @@ def run_sparse_gnn_cache(args) -> dict:
     # the same gathers from an uncompressed HBM copy of the table
     table = host.to(dev)
     raw_wall, _ = timed(lambda i: torch.index_select(table, 0, ids_dev[i], out=out[i & 1]), args.steps,
-                        args.warmup)
+                        args.warmup, per_launch=False)
     del table
     return base_result(
         args, batch * L * args.steps / wall / GB, wall,

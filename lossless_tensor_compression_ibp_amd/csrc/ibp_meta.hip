@@ -9,6 +9,9 @@
 // kept in GPU memory and reused for the whole dataset.  Also the derived
 // tables the encode and decode kernels read.
 #include <hip/hip_runtime.h>
+
+#include <mutex>
+#include <unordered_map>
 #include <stdint.h>
 
 #include "ibp_device.hpp"
@@ -177,8 +180,30 @@ hipError_t launch_tables(const uint32_t* mask, const uint32_t* bitval, uint32_t 
 
 static const uint32_t kPlanWpb[] = {4u, 8u, 12u, 16u};
 
-bool plan_persistent(const void* kernel, size_t head_bytes, size_t wave_bytes, uint32_t cu_count,
-                     uint64_t n_items, PersistentPlan* plan) {
+// The launch shape depends only on the kernel, its LDS needs and the device,
+// so it is worked out once per combination and kept (small launches would
+// otherwise pay for the attribute queries on every call).
+struct PlanKey {
+    const void* kernel;
+    size_t head, wave;
+    uint32_t cu_count;
+    int device;
+    bool operator==(const PlanKey& o) const {
+        return kernel == o.kernel && head == o.head && wave == o.wave && cu_count == o.cu_count &&
+               device == o.device;
+    }
+};
+struct PlanKeyHash {
+    size_t operator()(const PlanKey& k) const {
+        size_t h = std::hash<const void*>()(k.kernel);
+        h = h * 1000003u ^ std::hash<size_t>()(k.head);
+        h = h * 1000003u ^ std::hash<size_t>()(k.wave);
+        return h * 1000003u ^ (size_t)k.cu_count ^ ((size_t)k.device << 20);
+    }
+};
+
+static bool plan_uncached(const void* kernel, size_t head_bytes, size_t wave_bytes, uint32_t cu_count,
+                          PersistentPlan* plan) {
     hipFuncAttributes attr;
     uint32_t vgprs = 64, max_threads = 256;
     if (hipFuncGetAttributes(&attr, kernel) == hipSuccess) {
@@ -217,8 +242,6 @@ bool plan_persistent(const void* kernel, size_t head_bytes, size_t wave_bytes, u
         }
     }
     if (!best_waves) return false;
-    const uint64_t want = (n_items + best.wpb - 1) / best.wpb;
-    if (want < best.blocks) best.blocks = (uint32_t)want;
     if (best.shm > 65536) {
         if (hipFuncSetAttribute(kernel, hipFuncAttributeMaxDynamicSharedMemorySize, (int)best.shm) != hipSuccess) {
             (void)hipGetLastError();
@@ -226,6 +249,32 @@ bool plan_persistent(const void* kernel, size_t head_bytes, size_t wave_bytes, u
         }
     }
     *plan = best;
+    return true;
+}
+
+bool plan_persistent(const void* kernel, size_t head_bytes, size_t wave_bytes, uint32_t cu_count,
+                     uint64_t n_items, PersistentPlan* plan) {
+    static std::mutex mu;
+    static std::unordered_map<PlanKey, std::pair<bool, PersistentPlan>, PlanKeyHash> cache;
+    int dev = 0;
+    (void)hipGetDevice(&dev);
+    const PlanKey key{kernel, head_bytes, wave_bytes, cu_count, dev};
+    std::pair<bool, PersistentPlan> entry;
+    {
+        std::lock_guard<std::mutex> lock(mu);
+        auto it = cache.find(key);
+        if (it != cache.end()) {
+            entry = it->second;
+        } else {
+            entry.first = plan_uncached(kernel, head_bytes, wave_bytes, cu_count, &entry.second);
+            cache.emplace(key, entry);
+        }
+    }
+    if (!entry.first) return false;
+    PersistentPlan p = entry.second;
+    const uint64_t want = (n_items + p.wpb - 1) / p.wpb;
+    if (want < p.blocks) p.blocks = (uint32_t)want;
+    *plan = p;
     return true;
 }
 
