@@ -406,3 +406,88 @@ int ibp_ref_gather_decompress_packed(uint64_t L, uint32_t W, uint32_t M,
     }
     return IBP_REF_OK;
 }
+
+/* ---------------------------------------------------------------------------
+ * Headers in GPU memory: the slot keeps the payload, the header words go to a
+ * separate array.
+ * ------------------------------------------------------------------------- */
+
+int ibp_ref_compress_split(uint64_t L, uint32_t W, uint32_t M,
+                           const uint8_t* mask, const uint8_t* bitval,
+                           const uint8_t* src, uint64_t n_tensors,
+                           uint8_t* slots, uint32_t* headers, uint32_t* bitmask, uint64_t* stored) {
+    uint64_t tbits = 8 * L;
+    if (!geometry_ok(tbits, W, M)) return IBP_REF_ERR_INVALID;
+    if (n_tensors && (!src || !slots || !headers || !bitmask)) return IBP_REF_ERR_INVALID;
+    uint64_t hw = ((tbits / W) + 31) / 32; /* header words */
+    uint64_t cap = ibp_ref_max_record_bits(tbits, W);
+    uint8_t* rec = (uint8_t*)malloc((size_t)(cap / 8));
+    if (!rec) return IBP_REF_ERR_INVALID;
+    memset(bitmask, 0, (size_t)(4 * ((n_tensors + 31) / 32)));
+    for (uint64_t t = 0; t < n_tensors; ++t) {
+        const uint8_t* x = src + t * L;
+        uint8_t* slot = slots + t * L;
+        uint32_t* hdr = headers + t * hw;
+        uint64_t R;
+        int st = ibp_ref_encode_record(tbits, W, M, mask, bitval, x, rec, cap, &R);
+        if (st != IBP_REF_OK) {
+            free(rec);
+            return st;
+        }
+        uint64_t words = (R + 31) / 32;
+        if (4 * words < L) {
+            memcpy(hdr, rec, (size_t)(4 * hw));
+            memset(slot, 0, (size_t)L);
+            memcpy(slot, rec + 4 * hw, (size_t)(4 * (words - hw)));
+            set_mask_bit(bitmask, t, 1);
+            if (stored) stored[t] = 4 * (words - hw);
+        } else {
+            memset(hdr, 0, (size_t)(4 * hw));
+            memcpy(slot, x, (size_t)L);
+            set_mask_bit(bitmask, t, 0);
+            if (stored) stored[t] = L;
+        }
+    }
+    free(rec);
+    return IBP_REF_OK;
+}
+
+int ibp_ref_gather_decompress_split(uint64_t L, uint32_t W, uint32_t M,
+                                    const uint8_t* mask, const uint8_t* bitval,
+                                    const uint8_t* slots, uint64_t n_slots, const uint32_t* headers,
+                                    const uint32_t* bitmask, const int64_t* ids, uint64_t n_ids,
+                                    uint8_t* dst) {
+    uint64_t tbits = 8 * L;
+    if (!geometry_ok(tbits, W, M)) return IBP_REF_ERR_INVALID;
+    if (n_ids && (!slots || !headers || !bitmask || !ids || !dst)) return IBP_REF_ERR_INVALID;
+    uint64_t hw = ((tbits / W) + 31) / 32;
+    /* the record rebuilt in front of the decoder: header words, then the
+     * whole slot (the header tells how much of it is payload) */
+    uint8_t* rec = (uint8_t*)malloc((size_t)(4 * hw + L));
+    if (!rec) return IBP_REF_ERR_INVALID;
+    for (uint64_t i = 0; i < n_ids; ++i) {
+        int64_t id = ids[i];
+        if (id < 0 || (uint64_t)id >= n_slots) {
+            free(rec);
+            return IBP_REF_ERR_RANGE;
+        }
+        const uint8_t* slot = slots + (uint64_t)id * L;
+        uint8_t* out = dst + i * L;
+        if (!mask_bit(bitmask, (uint64_t)id)) {
+            memcpy(out, slot, (size_t)L);
+            continue;
+        }
+        memcpy(rec, headers + (uint64_t)id * hw, (size_t)(4 * hw));
+        memcpy(rec + 4 * hw, slot, (size_t)L);
+        uint64_t R;
+        int st = ibp_ref_record_bits(tbits, W, M, mask, rec, 8 * (4 * hw + L), &R);
+        if (st == IBP_REF_OK && 4 * ((R + 31) / 32) >= L) st = IBP_REF_ERR_CORRUPT;
+        if (st == IBP_REF_OK) st = ibp_ref_decode_record(tbits, W, M, mask, bitval, rec, 8 * (4 * hw + L), out);
+        if (st != IBP_REF_OK) {
+            free(rec);
+            return st;
+        }
+    }
+    free(rec);
+    return IBP_REF_OK;
+}

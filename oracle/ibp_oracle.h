@@ -150,6 +150,28 @@ int ibp_ref_gather_decompress_packed(uint64_t L, uint32_t W, uint32_t M,
                                      uint64_t n_items, const uint32_t* bitmask,
                                      const int64_t* ids, uint64_t n_ids, uint8_t* dst);
 
+/* Headers in GPU memory ("Intégration au système" keeps the bitmask of
+ * compressed slots in GPU memory; this layout keeps each compressed tensor's
+ * header words there as well, so that what crosses the host link is payload
+ * only).  Same compressed/raw decision as ibp_ref_compress.  For a compressed
+ * tensor, slot t holds the record's payload words (record words hw .. end,
+ * hw = ceil(n/32)) followed by zeros, and headers[t*hw .. t*hw+hw) holds its
+ * header words; for a raw tensor the slot holds the tensor and its header
+ * words are zero.  stored (nullable): payload bytes, or L when raw. */
+int ibp_ref_compress_split(uint64_t L, uint32_t W, uint32_t M,
+                           const uint8_t* mask, const uint8_t* bitval,
+                           const uint8_t* src, uint64_t n_tensors,
+                           uint8_t* slots, uint32_t* headers, uint32_t* bitmask, uint64_t* stored);
+
+/* dst row i = tensor ids[i] from that layout (ids in [0, n_slots), else -6).
+ * A compressed tensor whose header padding bits are set, or whose header
+ * implies 4*ceil(R/32) >= L, is corrupt (-5). */
+int ibp_ref_gather_decompress_split(uint64_t L, uint32_t W, uint32_t M,
+                                    const uint8_t* mask, const uint8_t* bitval,
+                                    const uint8_t* slots, uint64_t n_slots, const uint32_t* headers,
+                                    const uint32_t* bitmask, const int64_t* ids, uint64_t n_ids,
+                                    uint8_t* dst);
+
 #ifdef __cplusplus
 }
 #endif

@@ -60,10 +60,13 @@ def lib():
         L.ibp_ref_packed_offsets.argtypes = [u64, u32, u32, p, p, p, u64, p]
         L.ibp_ref_compress_packed.argtypes = [u64, u32, u32, p, p, p, u64, p, u64, p, p]
         L.ibp_ref_gather_decompress_packed.argtypes = [u64, u32, u32, p, p, p, p, u64, p, p, u64, p]
+        L.ibp_ref_compress_split.argtypes = [u64, u32, u32, p, p, p, u64, p, p, p, p]
+        L.ibp_ref_gather_decompress_split.argtypes = [u64, u32, u32, p, p, p, u64, p, p, p, u64, p]
         for name in ("ibp_ref_build_metadata", "ibp_ref_encode_record", "ibp_ref_record_bits",
                      "ibp_ref_decode_record", "ibp_ref_encode_records", "ibp_ref_decode_records",
                      "ibp_ref_compress", "ibp_ref_decompress", "ibp_ref_gather_decompress",
-                     "ibp_ref_packed_offsets", "ibp_ref_compress_packed", "ibp_ref_gather_decompress_packed"):
+                     "ibp_ref_packed_offsets", "ibp_ref_compress_packed", "ibp_ref_gather_decompress_packed",
+                     "ibp_ref_compress_split", "ibp_ref_gather_decompress_split"):
             getattr(L, name).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -234,4 +237,35 @@ def gather_decompress_packed(buf, offsets, n_items: int, bitmask, ids, L: int, W
     _check(lib().ibp_ref_gather_decompress_packed(L, W, M, _ptr(_u8(mask)), _ptr(_u8(bitval)), _ptr(b),
                                                   _ptr(off), n_items, _ptr(bm), _ptr(ids), ids.size,
                                                   _ptr(dst)), "gather_decompress_packed")
+    return dst
+
+
+def header_words(L: int, W: int) -> int:
+    return (8 * L // W + 31) // 32
+
+
+def compress_split(src, L: int, W: int, M: int, mask, bitval, n_tensors: int):
+    """Returns (slots (n, L) uint8, headers (n, hw) uint32, bitmask, stored)."""
+    s = _u8(src)
+    assert s.size >= n_tensors * L
+    hw = header_words(L, W)
+    slots = np.zeros((n_tensors, L), np.uint8)
+    headers = np.zeros((max(n_tensors, 1), hw), np.uint32)
+    bitmask = np.zeros(max(1, (n_tensors + 31) // 32), np.uint32)
+    stored = np.zeros(max(n_tensors, 1), np.uint64)
+    _check(lib().ibp_ref_compress_split(L, W, M, _ptr(_u8(mask)), _ptr(_u8(bitval)), _ptr(s), n_tensors,
+                                        _ptr(slots), _ptr(headers), _ptr(bitmask), _ptr(stored)),
+           "compress_split")
+    return slots, headers[:n_tensors], bitmask[: (n_tensors + 31) // 32], stored[:n_tensors]
+
+
+def gather_decompress_split(slots, n_slots: int, headers, bitmask, ids, L: int, W: int, M: int, mask, bitval):
+    s = _u8(slots)
+    h = np.ascontiguousarray(headers, dtype=np.uint32)
+    bm = np.ascontiguousarray(bitmask, dtype=np.uint32)
+    ids = np.ascontiguousarray(ids, dtype=np.int64)
+    dst = np.zeros((ids.size, L), np.uint8)
+    _check(lib().ibp_ref_gather_decompress_split(L, W, M, _ptr(_u8(mask)), _ptr(_u8(bitval)), _ptr(s), n_slots,
+                                                 _ptr(h), _ptr(bm), _ptr(ids), ids.size, _ptr(dst)),
+           "gather_decompress_split")
     return dst

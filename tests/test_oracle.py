@@ -475,3 +475,74 @@ def test_packed_edge_cases():
     with pytest.raises(O.OracleError) as e:
         O.gather_decompress_packed(buf, bad, n, bm, [2], L, W, M, mk, bv)
     assert e.value.code == O.ERR_CORRUPT
+
+
+# --------------------------------------------------------------------------
+# Headers in GPU memory: the slot keeps the payload, the header words live in
+# a separate (GPU-resident) array.
+# --------------------------------------------------------------------------
+@pytest.mark.parametrize("case", [c for c in CASES if c.get("L") and "record" in c], ids=lambda c: c["case"])
+def test_split_hand_vectors(case):
+    """The hand-derived records, cut at the header: header words to the
+    array, the rest to the slot (or the raw tensor when the record is not
+    shorter than the slot)."""
+    W, M, L = case["W"], case["M"], case["L"]
+    mask, bitval, x, rec = case["mask"], case["bitval"], case["x"], case["record"]
+    hw = O.header_words(L, W)
+    slots, headers, bm, stored = O.compress_split(x, L, W, M, mask, bitval, 1)
+    if case["slot"] == "raw":
+        assert bm[0] == 0 and stored[0] == L
+        assert not headers.any()
+        np.testing.assert_array_equal(slots[0].view(np.uint32), x)
+    else:
+        assert bm[0] == 1 and stored[0] == 4 * (rec.size - hw)
+        np.testing.assert_array_equal(headers[0], rec[:hw])
+        np.testing.assert_array_equal(slots[0, : 4 * (rec.size - hw)].view(np.uint32), rec[hw:])
+        assert not slots[0, 4 * (rec.size - hw):].any()
+    back = O.gather_decompress_split(slots, 1, headers, bm, [0, 0], L, W, M, mask, bitval)
+    np.testing.assert_array_equal(back.view(np.uint32).reshape(2, -1), np.stack([x, x]))
+
+
+@pytest.mark.parametrize("wl", ["sparse_gnn", "dense_gnn", "dlrm"])
+def test_split_is_the_slot_record_cut_at_the_header(wl):
+    w = WL.ALL[wl]
+    gen = {"sparse_gnn": WL.sparse_gnn, "dense_gnn": WL.dense_gnn, "dlrm": WL.dlrm}[wl]
+    raw = np.ascontiguousarray(gen(600)).view(np.uint8).reshape(600, -1)
+    n, L = raw.shape
+    hw = O.header_words(L, w.chunk_bits)
+    m, b = O.build_metadata(raw, 8 * L, w.chunk_bits, w.period_bits, w.threshold, 512)
+    slots, bm, stored = O.compress(raw, L, w.chunk_bits, w.period_bits, m, b, n)
+    s2, hdr, bm2, st2 = O.compress_split(raw, L, w.chunk_bits, w.period_bits, m, b, n)
+    np.testing.assert_array_equal(bm2, bm)
+    comp = ((bm[np.arange(n) >> 5] >> (np.arange(n) & 31)) & 1).astype(bool)
+    np.testing.assert_array_equal(st2[comp], stored[comp] - 4 * hw)
+    np.testing.assert_array_equal(st2[~comp], stored[~comp])
+    for t in range(n):
+        k = int(stored[t])
+        if comp[t]:
+            np.testing.assert_array_equal(hdr[t], slots[t, : 4 * hw].view(np.uint32))
+            assert np.array_equal(s2[t, : k - 4 * hw], slots[t, 4 * hw: k]), t
+        else:
+            assert not hdr[t].any() and np.array_equal(s2[t], slots[t]), t
+    ids = np.random.default_rng(4).integers(0, n, 800)
+    out = O.gather_decompress_split(s2, n, hdr, bm2, ids, L, w.chunk_bits, w.period_bits, m, b)
+    np.testing.assert_array_equal(out, raw[ids])
+
+
+def test_split_errors():
+    w = WL.DENSE_GNN
+    raw = np.ascontiguousarray(WL.dense_gnn(64)).view(np.uint8).reshape(64, -1)
+    n, L = raw.shape
+    m, b = O.build_metadata(raw, 8 * L, w.chunk_bits, w.period_bits, w.threshold, 64)
+    s2, hdr, bm, _ = O.compress_split(raw, L, w.chunk_bits, w.period_bits, m, b, n)
+    with pytest.raises(O.OracleError) as e:
+        O.gather_decompress_split(s2, n, hdr, bm, [n], L, w.chunk_bits, w.period_bits, m, b)
+    assert e.value.code == O.ERR_RANGE
+    t = int(np.nonzero((bm[np.arange(n) >> 5] >> (np.arange(n) & 31)) & 1)[0][0])
+    bad = hdr.copy()
+    bad[t, -1] |= np.uint32(1 << 31) if (8 * L // w.chunk_bits) % 32 else 0
+    if (8 * L // w.chunk_bits) % 32 == 0:
+        bad[t, :] = 0  # every chunk verbatim: the record would not be shorter than the slot
+    with pytest.raises(O.OracleError) as e:
+        O.gather_decompress_split(s2, n, bad, bm, [t], L, w.chunk_bits, w.period_bits, m, b)
+    assert e.value.code == O.ERR_CORRUPT
