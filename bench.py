@@ -118,31 +118,25 @@ def copy_kernel_ceiling(nbytes: int = 1 << 30, reps: int = 5) -> float:
     return 2 * nbytes / float(np.median(times[1:])) / GB
 
 
-def timed(fn, steps: int, warmup: int, per_launch: bool = True):
-    """Runs fn(i) warmup times, then times exactly `steps` calls.  Returns
-    (wall seconds, per-launch event durations in seconds).  per_launch=False
-    records no events inside the timed loop (for launches so short that the
-    event calls themselves would slow the host loop); durations are then None
-    and come from queued_durations()."""
+def timed(fn, steps: int, warmup: int):
+    """Runs fn(i) warmup times, then times exactly `steps` calls between two
+    synchronisations.  Returns (wall seconds, launch durations in seconds):
+    one HIP event pair on the launching stream brackets the whole timed
+    region, and each launch is credited the region's GPU time / steps (events
+    around every launch would put their own gaps between the kernels)."""
     stream = torch.cuda.current_stream()
     for i in range(warmup):
         fn(i)
     torch.cuda.synchronize()
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(steps if per_launch else 0)]
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     t0 = time.perf_counter()
+    start.record(stream)
     for i in range(steps):
-        if per_launch:
-            evs[i][0].record(stream)
         fn(warmup + i)
-        if per_launch:
-            evs[i][1].record(stream)
+    end.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    if not per_launch:
-        return wall, None
-    durs = np.array([s.elapsed_time(e) / 1e3 for s, e in evs])
-    return wall, durs
+    return wall, np.full(steps, start.elapsed_time(end) / 1e3 / steps)
 
 
 def queued_durations(fn, steps: int, first: int = 0):
@@ -165,8 +159,9 @@ def queued_durations(fn, steps: int, first: int = 0):
 
 def cpu_oracle_gather(raw_rows: np.ndarray, w: WL.Workload, batch: int, budget_s: float,
                       sample_rows: int) -> dict:
-    """The oracle, single-threaded, decoding random batches of rows from its
-    own slots until the time budget is spent (encode excluded)."""
+    """The oracle, single-threaded, decoding random batches of rows (headers
+    in a separate array, as the GPU line does) from its own slots until the
+    time budget is spent (encode excluded)."""
     from oracle import oracle
 
     oracle.build(force=False)
@@ -174,13 +169,14 @@ def cpu_oracle_gather(raw_rows: np.ndarray, w: WL.Workload, batch: int, budget_s
     L = sub.shape[1]
     mask, bitval = oracle.build_metadata(sub[: w.n_sample], 8 * L, w.chunk_bits, w.period_bits,
                                          w.threshold, min(w.n_sample, sub.shape[0]))
-    slots, bm, stored = oracle.compress(sub, L, w.chunk_bits, w.period_bits, mask, bitval, sub.shape[0])
+    slots, headers, bm, _ = oracle.compress_split(sub, L, w.chunk_bits, w.period_bits, mask, bitval, sub.shape[0])
     rng = np.random.default_rng(WL.ID_SEED)
     rows = 0
     t0 = time.perf_counter()
     while time.perf_counter() - t0 < budget_s:
         ids = rng.choice(sub.shape[0], batch, replace=False)
-        oracle.gather_decompress(slots, sub.shape[0], bm, ids, L, w.chunk_bits, w.period_bits, mask, bitval)
+        oracle.gather_decompress_split(slots, sub.shape[0], headers, bm, ids, L, w.chunk_bits, w.period_bits,
+                                       mask, bitval)
         rows += batch
     dt = time.perf_counter() - t0
     return {"value": round(rows * L / dt / GB, 6), "unit": "GB/s", "cores": 1, "kind": "oracle",
@@ -192,6 +188,11 @@ def cpu_oracle_gather(raw_rows: np.ndarray, w: WL.Workload, batch: int, budget_s
 # Sparse GNN: zero-copy gather from pinned host slots (default workload)
 # ---------------------------------------------------------------------------
 def run_sparse_gnn(args) -> dict:
+    """Zero-copy gathers of 8,192 random rows from pinned host slots.  The
+    timed layout keeps each compressed row's header word in HBM beside the
+    bitmask, so the host link carries payload only (a row of j non-zero
+    chunks costs j lines of 128 bytes instead of j + 1); the plain slot layout
+    (header in the slot) and the uncompressed rows are timed in the same run."""
     w = WL.SPARSE_GNN
     n, L = w.n_tensors if not args.small else 65536, w.tensor_bytes
     batch = 8192
@@ -207,40 +208,57 @@ def run_sparse_gnn(args) -> dict:
     meta = ibp.ibp_build_metadata(host, w.n_sample, L, w.chunk_bits, w.period_bits, w.threshold)
     t_meta = time.perf_counter() - t0
     info = ibp.ibp_meta_get_info(meta)
+    hw = ibp.header_words(meta)
 
-    log("[bench] compress all rows into pinned host slots (zero copy both ways)")
+    log("[bench] compress all rows into pinned host slots, headers in HBM (zero copy both ways)")
     slots = pinned((n, L), torch.uint8)
+    headers = torch.zeros((n, hw), dtype=torch.int32, device=dev)
     bitmask = torch.zeros((n + 31) // 32, dtype=torch.int32, device=dev)
     stored = torch.zeros(n, dtype=torch.int64, device=dev)
-    ibp.ibp_compress(meta, host, n, slots, bitmask, stored)
-    torch.cuda.synchronize()
     enc_s = []
-    for _ in range(3):
+    for _ in range(4):
         t0 = time.perf_counter()
-        ibp.ibp_compress(meta, host, n, slots, bitmask, stored)
+        ibp.ibp_compress_split(meta, host, n, slots, headers, bitmask, stored)
         torch.cuda.synchronize()
         enc_s.append(time.perf_counter() - t0)
-    stored_np = stored.cpu().numpy()
-    savings = 1.0 - stored_np.sum() / (n * L)
+    payload_np = stored.cpu().numpy()
+    comp_np = (bitmask.cpu().numpy().view(np.uint32)[np.arange(n) >> 5] >> (np.arange(n) & 31)) & 1
+    # compressed bytes: payload in the slots plus the header words kept in HBM
+    savings = 1.0 - (payload_np.sum() + 4 * hw * comp_np.sum()) / (n * L)
+
+    log("[bench] the plain slot layout (header in the slot) for comparison")
+    slots_plain = pinned((n, L), torch.uint8)
+    bitmask_plain = torch.zeros_like(bitmask)
+    stored_plain = torch.zeros(n, dtype=torch.int64, device=dev)
+    ibp.ibp_compress(meta, host, n, slots_plain, bitmask_plain, stored_plain)
+    torch.cuda.synchronize()
+    stored_plain_np = stored_plain.cpu().numpy()
 
     ids_all = WL.batch_ids(n, batch, args.warmup + args.steps, replace=False)
     ids_dev = torch.from_numpy(ids_all).to(dev)
     out = torch.empty((2, batch, L), dtype=torch.uint8, device=dev)
+    last = args.warmup + args.steps - 1
 
     def step(i):
-        ibp.ibp_gather_decompress(meta, slots, n, bitmask, ids_dev[i], out[i & 1])
+        ibp.ibp_gather_decompress_split(meta, slots, n, headers, bitmask, ids_dev[i], out[i & 1])
 
     log(f"[bench] timing {args.steps} gather steps of {batch} rows (warmup {args.warmup})")
     wall, durs = timed(step, args.steps, args.warmup)
     assert ibp.ibp_check(meta) == ibp.IBP_OK
-    last = args.warmup + args.steps - 1
-    ok = np.array_equal(out[last & 1].cpu().numpy(), raw_np[ids_all[last]])
-    if not ok:
+    if not np.array_equal(out[last & 1].cpu().numpy(), raw_np[ids_all[last]]):
         raise SystemExit("decoded rows differ from the source rows")
     timed_ids = ids_all[args.warmup:]
-    link_bytes = stored_np[timed_ids].sum(axis=1)        # bytes read over the link per launch
+    link_bytes = payload_np[timed_ids].sum(axis=1)        # bytes read over the link per launch
     out_bytes = batch * L
     value = args.steps * out_bytes / wall / GB
+
+    def plain_step(i):
+        ibp.ibp_gather_decompress(meta, slots_plain, n, bitmask_plain, ids_dev[i], out[i & 1])
+
+    plain_wall, plain_durs = timed(plain_step, args.steps, args.warmup)
+    assert ibp.ibp_check(meta) == ibp.IBP_OK
+    if not np.array_equal(out[last & 1].cpu().numpy(), raw_np[ids_all[last]]):
+        raise SystemExit("decoded rows (slot layout) differ from the source rows")
 
     # raw zero-copy gather of the same rows (every bitmask bit 0): the
     # uncompressed transfer the codec competes with
@@ -255,6 +273,7 @@ def run_sparse_gnn(args) -> dict:
         raw_wall, _ = timed(raw_step, args.steps, args.warmup)
     h2d = h2d_ceiling()
     achieved = float(link_bytes.mean() / durs.mean() / GB)
+    comp_fraction = 1.0 - savings
     res = {
         "metric": "IBP decode GB/s (uncompressed out, 1 MI355X) + % of roofline + space savings %",
         "value": round(value, 3),
@@ -269,12 +288,14 @@ def run_sparse_gnn(args) -> dict:
         "dtype": "u32",
         "data": "synthetic",
         "config": {"workload": f"sparse_gnn: {n} rows x 256 fp32 (97% zeros), W=1024, M=8192, T=0.95, "
-                               f"1 KiB slots in pinned host memory, zero-copy gather of {batch} "
-                               f"distinct random row ids per step into HBM",
+                               f"1 KiB slots in pinned host memory (payload only; each compressed row's header "
+                               f"word in HBM beside the bitmask), zero-copy gather of {batch} distinct random "
+                               f"row ids per step into HBM",
                    "rows": n, "tensor_bytes": L, "batch_ids": batch, "chunk_bits": w.chunk_bits,
-                   "period_bits": w.period_bits, "threshold": w.threshold},
+                   "period_bits": w.period_bits, "threshold": w.threshold, "layout": "headers in HBM",
+                   "hbm_header_bytes": int(4 * hw * n), "hbm_bitmask_bytes": int(4 * ((n + 31) // 32))},
         "space_savings_pct": round(100 * savings, 3),
-        "kernel": "ibp::k_decode_small<0, true, true, 1>",
+        "kernel": "ibp::k_decode_small<0, true, true, 1, true>",
         "kernel_avg_us": round(float(durs.mean()) * 1e6, 2),
         "roofline": {
             "bound": "pcie",
@@ -288,10 +309,16 @@ def run_sparse_gnn(args) -> dict:
             "frac_of_measured_ceiling": round(achieved / h2d, 4),
             "algorithmic_bytes_per_launch": int(link_bytes.mean()),
         },
-        "decoded_roofline_GBps": round(h2d / (1.0 - savings), 3),
+        # decoded throughput against link bandwidth / compressed fraction
+        "decoded_roofline_GBps": round(h2d / comp_fraction, 3),
+        "decoded_frac_of_roofline": round(value / (h2d / comp_fraction), 4),
+        "decoded_frac_of_published_link_roofline": round(value / (PCIE5_X16_GBPS / comp_fraction), 4),
+        "slot_layout": {"decoded_GBps": round(args.steps * out_bytes / plain_wall / GB, 3),
+                        "kernel_avg_us": round(float(plain_durs.mean()) * 1e6, 2),
+                        "link_bytes_per_launch": int(stored_plain_np[timed_ids].sum(axis=1).mean())},
         "raw_zero_copy_gather_GBps": round(args.steps * out_bytes / raw_wall / GB, 3),
         "speedup_vs_raw_zero_copy": round(raw_wall / wall, 3),
-        "encode_GBps": round(n * L / float(np.median(enc_s)) / GB, 3),
+        "encode_GBps": round(n * L / float(np.median(enc_s[1:])) / GB, 3),
         "metadata_ms": round(t_meta * 1e3, 2),
         "meta": info,
     }
@@ -393,8 +420,7 @@ def run_dense_gnn(args) -> dict:
     stored_np = stored.cpu().numpy()
     savings = 1.0 - stored_np.sum() / (n * L)
     out = torch.empty_like(src)
-    wall, _ = timed(lambda i: ibp.ibp_decompress(meta, slots, bitmask, n, out), args.steps, args.warmup,
-                    per_launch=False)
+    wall, _ = timed(lambda i: ibp.ibp_decompress(meta, slots, bitmask, n, out), args.steps, args.warmup)
     # launches shorter than their host submission: time them queued back to back
     durs = queued_durations(lambda i: ibp.ibp_decompress(meta, slots, bitmask, n, out), args.steps)
     assert ibp.ibp_check(meta) == ibp.IBP_OK
@@ -437,33 +463,17 @@ def run_dlrm(args) -> dict:
     ids_np = WL.batch_ids(n, batch, n_batches, replace=True)
     ids = torch.from_numpy(ids_np).to(dev)
     out = torch.empty((2, batch, L), dtype=torch.uint8, device=dev)
-    stream = torch.cuda.current_stream()
-    evs = []
-
     def step(i):
         for j in range(per_step):
             k = i * per_step + j
-            if i >= args.warmup:
-                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-                e0.record(stream)
             ibp.ibp_gather_decompress(meta, slots, n, bitmask, ids[k], out[k & 1])
-            if i >= args.warmup:
-                e1.record(stream)
-                evs.append((e0, e1))
 
-    for i in range(args.warmup):
-        step(i)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(args.warmup, args.warmup + args.steps):
-        step(i)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
+    wall, step_durs = timed(step, args.steps, args.warmup)
     assert ibp.ibp_check(meta) == ibp.IBP_OK
     last = n_batches - 1
     if not np.array_equal(out[last & 1].cpu().numpy(), raw_np[ids_np[last]]):
         raise SystemExit("decoded rows differ")
-    durs = np.array([a.elapsed_time(b) / 1e3 for a, b in evs])
+    durs = np.full(args.steps * per_step, float(step_durs.mean()) / per_step)  # per gather launch
     link = float(stored_np[ids_np[args.warmup * per_step:]].sum(axis=1).mean())
     value = args.steps * per_step * batch * L / wall / GB
     return base_result(
@@ -593,7 +603,7 @@ def run_sparse_gnn_cache(args) -> dict:
         ibp.ibp_gather_decompress_packed(meta, buf, offsets, n, bitmask, ids_dev[i], out[i & 1])
 
     log(f"[bench] timing {args.steps} gathers of {batch} rows from the packed HBM cache")
-    wall, _ = timed(step, args.steps, args.warmup, per_launch=False)
+    wall, _ = timed(step, args.steps, args.warmup)
     durs = queued_durations(step, args.steps, args.warmup)
     assert ibp.ibp_check(meta) == ibp.IBP_OK
     last = args.warmup + args.steps - 1
@@ -607,7 +617,7 @@ def run_sparse_gnn_cache(args) -> dict:
     # the same gathers from an uncompressed HBM copy of the table
     table = host.to(dev)
     raw_wall, _ = timed(lambda i: torch.index_select(table, 0, ids_dev[i], out=out[i & 1]), args.steps,
-                        args.warmup, per_launch=False)
+                        args.warmup)
     del table
     return base_result(
         args, batch * L * args.steps / wall / GB, wall,

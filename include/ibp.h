@@ -188,6 +188,39 @@ ibp_status ibp_gather_decompress_packed(ibp_meta_t meta, const void* buf, uint64
                                         const uint64_t* offsets, uint64_t n_items, const uint32_t* bitmask,
                                         const int64_t* ids, uint64_t n_ids, void* dst, hipStream_t stream);
 
+/* ---------------------------------------------------------------------------
+ * Headers in GPU memory ("Intégration au système" keeps the bitmask of
+ * compressed slots in GPU memory; this layout keeps each compressed tensor's
+ * header words there too).  Zero-copy reads of pinned host memory move whole
+ * 128-byte lines, so a record of 4 + 128*j bytes costs j + 1 lines while its
+ * payload alone costs j; with the header in GPU memory the decoder also knows
+ * the payload length before it reads the slot, and reads it in one pass.
+ *
+ * Same compressed/raw decision as ibp_compress.  headers: device memory,
+ * n * hw uint32 (hw = ceil(n_chunks/32), at most 4, i.e. at most 128 chunks
+ * per tensor), 4-byte aligned; entry t*hw .. t*hw+hw-1 holds tensor t's
+ * header words, zero for a raw tensor.  Slot t holds the record's payload
+ * words (the record minus its header) when compressed, else the tensor; slot
+ * bytes after the payload are unspecified.  stored_bytes (device or NULL):
+ * payload bytes, or L when raw.  Needs L a multiple of 16 and at most 8 KiB,
+ * 16-byte aligned data pointers and tables that fit the kernels' LDS;
+ * otherwise IBP_ERR_UNSUPPORTED.
+ * ------------------------------------------------------------------------- */
+ibp_status ibp_compress_split(ibp_meta_t meta, const void* src, uint64_t n_tensors, void* dst_slots,
+                              uint32_t* headers, uint32_t* bitmask, uint64_t* stored_bytes, hipStream_t stream);
+
+/* Tensor t of dst (device) <- slot t (device or pinned) with its header
+ * words from headers.  A compressed tensor whose header padding bits are set
+ * or whose header implies 4*ceil(R/32) >= L latches IBP_ERR_CORRUPT. */
+ibp_status ibp_decompress_split(ibp_meta_t meta, const void* slots, const uint32_t* headers,
+                                const uint32_t* bitmask, uint64_t n_tensors, void* dst, hipStream_t stream);
+
+/* Gather on decode in that layout: row i of dst <- tensor ids[i] (device
+ * int64; an id outside [0, n_slots) latches IBP_ERR_RANGE). */
+ibp_status ibp_gather_decompress_split(ibp_meta_t meta, const void* slots, uint64_t n_slots,
+                                       const uint32_t* headers, const uint32_t* bitmask, const int64_t* ids,
+                                       uint64_t n_ids, void* dst, hipStream_t stream);
+
 /* Waits for `stream`, returns the first error latched by a kernel of this
  * handle since the last ibp_check (IBP_OK if none) and clears it. */
 ibp_status ibp_check(ibp_meta_t meta, hipStream_t stream);

@@ -580,6 +580,63 @@ ibp_status ibp_gather_decompress_packed(ibp_meta_t h, const void* buf, uint64_t 
     return decode_packed_common(h, buf, buf_bytes, offsets, n_items, bitmask, ids, n_ids, dst, stream);
 }
 
+// ---------------------------------------------------------------------------
+// Headers in GPU memory.
+// ---------------------------------------------------------------------------
+ibp_status ibp_compress_split(ibp_meta_t h, const void* src, uint64_t n_tensors, void* dst_slots, uint32_t* headers,
+                              uint32_t* bitmask, uint64_t* stored_bytes, hipStream_t stream) {
+    if (!h) return IBP_ERR_INVALID_ARG;
+    if (n_tensors == 0) return IBP_OK;
+    DeviceGuard guard(h->device);
+    if (!guard.ok) return IBP_ERR_DEVICE;
+    const uint64_t L = h->params.tensor_bytes;
+    if (n_tensors > (~0ull) / L) return IBP_ERR_INVALID_ARG;
+    if (!device_or_pinned(src, h->device) || !device_or_pinned(dst_slots, h->device)) return IBP_ERR_INVALID_ARG;
+    if (!device_only(bitmask, h->device) || !device_only(headers, h->device)) return IBP_ERR_INVALID_ARG;
+    if (stored_bytes && !device_only(stored_bytes, h->device)) return IBP_ERR_INVALID_ARG;
+    if (reinterpret_cast<uintptr_t>(headers) % 4) return IBP_ERR_INVALID_ARG;
+    if (overlaps(src, n_tensors * L, dst_slots, n_tensors * L)) return IBP_ERR_INVALID_ARG;
+    const Geo geo = make_geo(h, aligned16(L, {src, dst_slots}), kLongTileWordsEncode);
+    if (!split_supported(geo, h->sum.max_runs, h->sum.uniform != 0)) return IBP_ERR_UNSUPPORTED;
+    return from_hip(launch_encode_split(h->tabs, geo, h->sum.max_runs, h->sum.uniform != 0, src, n_tensors,
+                                        dst_slots, headers, bitmask, stored_bytes, h->cu_count, stream));
+}
+
+static ibp_status decode_split_common(ibp_meta_t h, const void* slots, uint64_t n_slots, const uint32_t* headers,
+                                      const uint32_t* bitmask, const int64_t* ids, uint64_t n_out, void* dst,
+                                      hipStream_t stream) {
+    if (!h) return IBP_ERR_INVALID_ARG;
+    if (n_out == 0) return IBP_OK;
+    DeviceGuard guard(h->device);
+    if (!guard.ok) return IBP_ERR_DEVICE;
+    const uint64_t L = h->params.tensor_bytes;
+    if (n_out > (~0ull) / L || n_slots > (~0ull) / L) return IBP_ERR_INVALID_ARG;
+    if (!device_or_pinned(slots, h->device)) return IBP_ERR_INVALID_ARG;
+    if (!device_only(bitmask, h->device) || !device_only(dst, h->device) || !device_only(headers, h->device))
+        return IBP_ERR_INVALID_ARG;
+    if (ids && !device_only(ids, h->device)) return IBP_ERR_INVALID_ARG;
+    if (reinterpret_cast<uintptr_t>(headers) % 4) return IBP_ERR_INVALID_ARG;
+    if (overlaps(slots, n_slots * L, dst, n_out * L)) return IBP_ERR_INVALID_ARG;
+    const Geo geo = make_geo(h, aligned16(L, {slots, dst}), kLongTileWordsDecode);
+    const bool uni = h->sum.uniform != 0;
+    if (geo.hdr_words > kMaxSplitHeaderWords || !packed_decode_supported(geo, h->sum.max_runs, uni))
+        return IBP_ERR_UNSUPPORTED;
+    return from_hip(launch_decode(h->tabs, geo, h->sum.max_runs, uni, slots, n_slots, bitmask, ids, n_out, dst,
+                                  h->d_err, nullptr, h->cu_count, stream, nullptr, headers));
+}
+
+ibp_status ibp_decompress_split(ibp_meta_t h, const void* slots, const uint32_t* headers, const uint32_t* bitmask,
+                                uint64_t n_tensors, void* dst, hipStream_t stream) {
+    return decode_split_common(h, slots, n_tensors, headers, bitmask, nullptr, n_tensors, dst, stream);
+}
+
+ibp_status ibp_gather_decompress_split(ibp_meta_t h, const void* slots, uint64_t n_slots, const uint32_t* headers,
+                                       const uint32_t* bitmask, const int64_t* ids, uint64_t n_ids, void* dst,
+                                       hipStream_t stream) {
+    if (n_ids && !ids) return IBP_ERR_INVALID_ARG;
+    return decode_split_common(h, slots, n_slots, headers, bitmask, ids, n_ids, dst, stream);
+}
+
 ibp_status ibp_check(ibp_meta_t h, hipStream_t stream) {
     if (!h) return IBP_ERR_INVALID_ARG;
     DeviceGuard guard(h->device);

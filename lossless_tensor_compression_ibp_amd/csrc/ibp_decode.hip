@@ -159,13 +159,20 @@ __device__ __forceinline__ void stage_tables(const Tables& t, uint32_t Mw, uint3
 // Packed cache layout (items.offsets set): each lane also fetches its tile's
 // item span; every read stays inside that span, and an item whose span does
 // not fit its record (or the buffer) latches a corrupt-record error.
+//
+// SPLIT (headers in GPU memory, at most 4 header words): each lane fetches
+// its tile's header words with the bitmask bit and works out the payload
+// length from them, so the slot read takes exactly the payload (rounded up
+// to 16 bytes) in one pass; the header is put back in LDS beside the payload
+// for the rebuild.
 // ---------------------------------------------------------------------------
-template <int RUNS, bool UNI, bool MW4, int STAGE>
+template <int RUNS, bool UNI, bool MW4, int STAGE, bool SPLIT>
 __global__ __launch_bounds__(256) void k_decode_small(Tables t, Geo geo, const uint8_t* __restrict__ slots,
                                                       uint64_t n_slots, const uint32_t* __restrict__ bitmask,
                                                       const int64_t* __restrict__ ids, uint64_t n_out,
                                                       uint8_t* __restrict__ dst, uint32_t* err,
-                                                      uint32_t buf_words, Items items) {
+                                                      uint32_t buf_words, Items items,
+                                                      const uint32_t* __restrict__ headers) {
     extern __shared__ uint32_t smem[];
     const uint32_t lane = lane_id();
     const uint32_t wib = uniform(threadIdx.x / kWave);
@@ -227,8 +234,60 @@ __global__ __launch_bounds__(256) void k_decode_small(Tables t, Geo geo, const u
         auto tensor_of = [&](uint32_t k) __attribute__((always_inline)) -> int64_t {
             return (int64_t)(((uint64_t)lane_value(t_hi, k) << 32) | lane_value(t_lo, k));
         };
+        // SPLIT: the bitmask bit and header words of each lane's tile, and
+        // from them the payload words its slot read takes
+        uint32_t my_comp = 0, my_pw = 0;
+        uint32_t h0 = 0, h1 = 0, h2 = 0, h3 = 0;
+        bool bad_rec = false;
+        if constexpr (SPLIT) {
+            if (lane < cnt && my_tensor >= 0) {
+                my_comp = (bitmask[(uint64_t)my_tensor >> 5] >> ((uint64_t)my_tensor & 31)) & 1u;
+                if (my_comp) {
+                    const uint32_t* hp = headers + (uint64_t)my_tensor * hw;
+                    uint32_t hv[4] = {0u, 0u, 0u, 0u};
+                    uint32_t rem = 0;
+#pragma unroll
+                    for (uint32_t j = 0; j < 4; ++j) {
+                        if (j < hw) {
+                            uint32_t h = hp[j];
+                            hv[j] = h;
+                            if (j == hw - 1) {
+                                const uint32_t valid = (uint32_t)(geo.n_chunks - 32ull * j);
+                                if (valid < 32) {
+                                    if (h >> valid) bad_rec = true;
+                                    h &= (1u << valid) - 1u;
+                                }
+                            }
+                            rem += removed_bits_pl(planes, geo, j, h);
+                        }
+                    }
+                    const uint64_t R = 32ull * hw + 32ull * nwords - rem;
+                    const uint32_t words = (uint32_t)((R + 31) / 32);
+                    if (4ull * words >= geo.L) bad_rec = true;
+                    if (bad_rec) {
+                        my_tensor = -1;
+                    } else {
+                        my_pw = words - hw;
+                        h0 = hv[0];
+                        h1 = hv[1];
+                        h2 = hv[2];
+                        h3 = hv[3];
+                    }
+                }
+            }
+        }
+        const uint32_t t_lo2 = (uint32_t)my_tensor, t_hi2 = (uint32_t)((uint64_t)my_tensor >> 32);
+        auto tensor_of2 = [&](uint32_t k) __attribute__((always_inline)) -> int64_t {
+            if constexpr (!SPLIT) return tensor_of(k);
+            return (int64_t)(((uint64_t)lane_value(t_hi2, k) << 32) | lane_value(t_lo2, k));
+        };
+
         // byte offset of tile k's slot or item, and 16-byte vectors its first read takes
         auto where_of = [&](uint32_t k, int64_t tn, uint32_t* n4_first) __attribute__((always_inline)) -> uint64_t {
+            if constexpr (SPLIT) {
+                *n4_first = lane_value(my_comp, k) ? (lane_value(my_pw, k) + 3) >> 2 : n4_raw;
+                return (uint64_t)tn * geo.L;
+            }
             if (!packed) {
                 *n4_first = n4_spec;
                 return (uint64_t)tn * geo.L;
@@ -237,7 +296,7 @@ __global__ __launch_bounds__(256) void k_decode_small(Tables t, Geo geo, const u
             return ((uint64_t)lane_value(o_hi, k) << 32) | lane_value(o_lo, k);
         };
         auto issue = [&](uint32_t k) __attribute__((always_inline)) {
-            const int64_t tn = tensor_of(k);
+            const int64_t tn = tensor_of2(k);
             if (tn < 0) return;
             uint32_t n4_first;
             const u32x4* s4 = reinterpret_cast<const u32x4*>(slots + where_of(k, tn, &n4_first));
@@ -249,13 +308,14 @@ __global__ __launch_bounds__(256) void k_decode_small(Tables t, Geo geo, const u
         };
 
         issue(0);
-        uint32_t my_comp = 0;
-        if (lane < cnt && my_tensor >= 0)
-            my_comp = (bitmask[(uint64_t)my_tensor >> 5] >> ((uint64_t)my_tensor & 31)) & 1u;
+        if constexpr (!SPLIT) {
+            if (lane < cnt && my_tensor >= 0)
+                my_comp = (bitmask[(uint64_t)my_tensor >> 5] >> ((uint64_t)my_tensor & 31)) & 1u;
+        }
         if (ballot(bad_id)) latch_error(err, kErrRange);
-        if (ballot(bad_item)) latch_error(err, kErrCorrupt);
+        if (ballot(bad_item || bad_rec)) latch_error(err, kErrCorrupt);
         for (uint32_t k = 0; k < cnt; ++k) {
-            const int64_t tn = tensor_of(k);
+            const int64_t tn = tensor_of2(k);
             const uint32_t comp = lane_value(my_comp, k);
             const uint64_t oi = first + (base + k) * stride;
             uint32_t* out = reinterpret_cast<uint32_t*>(dst + oi * geo.L);
@@ -287,6 +347,21 @@ __global__ __launch_bounds__(256) void k_decode_small(Tables t, Geo geo, const u
             if (k + 1 < cnt) issue(k + 1);
             if (tn < 0 || !comp) continue;
 
+            if constexpr (SPLIT) {
+                // header words back in LDS after the payload area, then rebuild
+                uint32_t* hdr = buf + nwords + 4;
+                const uint32_t H0 = lane_value(h0, k), H1 = lane_value(h1, k), H2 = lane_value(h2, k),
+                               H3 = lane_value(h3, k);
+                if (lane < hw) hdr[lane] = lane == 0 ? H0 : lane == 1 ? H1 : lane == 2 ? H2 : H3;
+                if (lane == 0) buf[4 * n4_first] = 0;
+                __builtin_amdgcn_wave_barrier();
+                if (UNI)
+                    decode_tile<RUNS, MW4>(tu, geo, hdr, buf, 0, 0, nwords, out, true);
+                else
+                    decode_tile<RUNS, MW4>(ta, geo, hdr, buf, 0, 0, nwords, out, true);
+                __builtin_amdgcn_wave_barrier();
+                continue;
+            }
             __builtin_amdgcn_wave_barrier();
             bool bad_pad;
             const uint32_t rem = header_removed_bits(planes, geo, buf, 0, hw, &bad_pad);
@@ -443,18 +518,18 @@ static bool small_lds(const Geo& geo, int runs, bool uni, uint32_t* buf_words, s
     return true;
 }
 
-template <int RUNS, bool UNI, bool MW4, int S>
+template <int RUNS, bool UNI, bool MW4, int S, bool SPLIT>
 static hipError_t launch_small_s(const Tables& t, const Geo& geo, const void* slots, uint64_t n_slots,
                                  const uint32_t* bitmask, const int64_t* ids, uint64_t n_out, void* dst,
                                  uint32_t* err, uint32_t cu_count, size_t head, size_t wave, uint32_t buf_words,
-                                 const Items& items, hipStream_t s, bool* launched) {
-    const void* fn = reinterpret_cast<const void*>(&k_decode_small<RUNS, UNI, MW4, S>);
+                                 const Items& items, const uint32_t* headers, hipStream_t s, bool* launched) {
+    const void* fn = reinterpret_cast<const void*>(&k_decode_small<RUNS, UNI, MW4, S, SPLIT>);
     PersistentPlan plan;
     *launched = false;
     if (!plan_persistent(fn, head, wave, cu_count, n_out, &plan)) return hipSuccess;
-    hipLaunchKernelGGL((k_decode_small<RUNS, UNI, MW4, S>), dim3(plan.blocks), dim3(kWave * plan.wpb), plan.shm, s,
-                       t, geo, static_cast<const uint8_t*>(slots), n_slots, bitmask, ids, n_out,
-                       static_cast<uint8_t*>(dst), err, buf_words, items);
+    hipLaunchKernelGGL((k_decode_small<RUNS, UNI, MW4, S, SPLIT>), dim3(plan.blocks), dim3(kWave * plan.wpb),
+                       plan.shm, s, t, geo, static_cast<const uint8_t*>(slots), n_slots, bitmask, ids, n_out,
+                       static_cast<uint8_t*>(dst), err, buf_words, items, headers);
     *launched = true;
     return hipGetLastError();
 }
@@ -463,19 +538,29 @@ template <int RUNS, bool UNI>
 static hipError_t launch_small(const Tables& t, const Geo& geo, const void* slots, uint64_t n_slots,
                                const uint32_t* bitmask, const int64_t* ids, uint64_t n_out, void* dst,
                                uint32_t* err, uint32_t cu_count, size_t head, size_t wave, uint32_t buf_words,
-                               const Items& items, hipStream_t s, bool* launched) {
+                               const Items& items, const uint32_t* headers, hipStream_t s, bool* launched) {
     const uint32_t stage = (uint32_t)((geo.n_words + 4 * kWave - 1) / (4 * kWave));
     const bool mw4 = geo.Mw % 4 == 0;
-#define IBP_SMALL(S)                                                                                          \
-    return mw4 ? launch_small_s<RUNS, UNI, true, S>(t, geo, slots, n_slots, bitmask, ids, n_out, dst, err,     \
-                                                    cu_count, head, wave, buf_words, items, s, launched)        \
-               : launch_small_s<RUNS, UNI, false, S>(t, geo, slots, n_slots, bitmask, ids, n_out, dst, err,    \
-                                                     cu_count, head, wave, buf_words, items, s, launched)
+#define IBP_SMALL_X(S, SPLIT)                                                                                  \
+    return mw4 ? launch_small_s<RUNS, UNI, true, S, SPLIT>(t, geo, slots, n_slots, bitmask, ids, n_out, dst,   \
+                                                           err, cu_count, head, wave, buf_words, items, headers, \
+                                                           s, launched)                                          \
+               : launch_small_s<RUNS, UNI, false, S, SPLIT>(t, geo, slots, n_slots, bitmask, ids, n_out, dst,  \
+                                                            err, cu_count, head, wave, buf_words, items,         \
+                                                            headers, s, launched)
+#define IBP_SMALL(S)               \
+    do {                           \
+        if (headers) {             \
+            IBP_SMALL_X(S, true);  \
+        }                          \
+        IBP_SMALL_X(S, false);     \
+    } while (0)
     if (stage <= 1) IBP_SMALL(1);
     if (stage <= 2) IBP_SMALL(2);
     if (stage <= 4) IBP_SMALL(4);
     IBP_SMALL(8);
 #undef IBP_SMALL
+#undef IBP_SMALL_X
 }
 
 template <int RUNS, bool UNI, bool MULTI>
@@ -497,9 +582,9 @@ template <int RUNS, bool UNI>
 static hipError_t launch_decode_r(const Tables& t, const Geo& geo, const void* slots, uint64_t n_slots,
                                   const uint32_t* bitmask, const int64_t* ids, uint64_t n_out, void* dst,
                                   uint32_t* err, const LookBack* lb, uint32_t cu_count, hipStream_t s,
-                                  const Items& items) {
+                                  const Items& items, const uint32_t* headers) {
     if (geo.tiles_per_tensor > 1) {
-        if (items.offsets) return hipErrorInvalidValue;
+        if (items.offsets || headers) return hipErrorInvalidValue;
         return launch_tiles<RUNS, UNI, true>(t, geo, slots, n_slots, bitmask, ids, n_out, dst, err, *lb, s);
     }
     uint32_t buf_words = 0;
@@ -507,10 +592,11 @@ static hipError_t launch_decode_r(const Tables& t, const Geo& geo, const void* s
     if (geo.aligned16 && small_lds(geo, RUNS, UNI, &buf_words, &head, &wave)) {
         bool launched = false;
         const hipError_t e = launch_small<RUNS, UNI>(t, geo, slots, n_slots, bitmask, ids, n_out, dst, err, cu_count,
-                                                     head, wave, buf_words, items, s, &launched);
+                                                     head, wave, buf_words, items, headers, s, &launched);
         if (e != hipSuccess || launched) return e;
     }
-    if (items.offsets) return hipErrorInvalidValue;  // the packed layout runs on k_decode_small only
+    // the packed and header-in-GPU-memory layouts run on k_decode_small only
+    if (items.offsets || headers) return hipErrorInvalidValue;
     return launch_tiles<RUNS, UNI, false>(t, geo, slots, n_slots, bitmask, ids, n_out, dst, err, LookBack{}, s);
 }
 
@@ -524,15 +610,15 @@ bool packed_decode_supported(const Geo& geo, uint32_t runs, bool uniform_meta) {
 hipError_t launch_decode(const Tables& t, const Geo& geo, uint32_t runs, bool uniform_meta, const void* slots,
                          uint64_t n_slots, const uint32_t* bitmask, const int64_t* ids, uint64_t n_out,
                          void* dst, uint32_t* err, const LookBack* lb, uint32_t cu_count, hipStream_t s,
-                         const Items* items) {
+                         const Items* items, const uint32_t* headers) {
     if (n_out == 0) return hipSuccess;
     const Items it = items ? *items : Items{nullptr, 0};
 #define IBP_R(R)                                                                                      \
     return uniform_meta                                                                                \
                ? launch_decode_r<R, true>(t, geo, slots, n_slots, bitmask, ids, n_out, dst, err, lb,    \
-                                          cu_count, s, it)                                             \
+                                          cu_count, s, it, headers)                                    \
                : launch_decode_r<R, false>(t, geo, slots, n_slots, bitmask, ids, n_out, dst, err, lb,   \
-                                           cu_count, s, it)
+                                           cu_count, s, it, headers)
     switch (runs_bucket(runs)) {
         case 0: IBP_R(0);
         case 1: IBP_R(1);

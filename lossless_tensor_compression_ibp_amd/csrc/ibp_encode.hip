@@ -221,13 +221,17 @@ __global__ __launch_bounds__(256) void k_encode(Tables t, Geo geo, const uint8_t
 // layout, where the item goes to its offset once its length has been checked
 // against the offsets.  SIZES: only the item lengths, rounded up to 16 bytes,
 // are computed and written to sizes[] (no record buffer, no slot writes).
+// headers != nullptr (at most 4 header words): the header words go to
+// headers[t * hw ...] in GPU memory and the slot receives the payload only,
+// which the record buffer then keeps 16-byte aligned after a 4-word header
+// area.
 // ---------------------------------------------------------------------------
 template <int RUNS, bool UNI, bool MW4, int STAGE, bool SIZES>
 __global__ __launch_bounds__(1024) void k_encode_small(Tables t, Geo geo, const uint8_t* __restrict__ src,
                                                       uint64_t n_tensors, uint8_t* __restrict__ slots,
                                                       uint32_t* __restrict__ bitmask, uint64_t* __restrict__ stored,
                                                       uint32_t buf_words, Items items, uint64_t* __restrict__ sizes,
-                                                      uint32_t* err) {
+                                                      uint32_t* err, uint32_t* __restrict__ headers) {
     extern __shared__ uint32_t smem[];
     const uint32_t lane = lane_id();
     const uint32_t wib = uniform(threadIdx.x / kWave);
@@ -298,7 +302,7 @@ __global__ __launch_bounds__(1024) void k_encode_small(Tables t, Geo geo, const 
             for (uint32_t i = lane; i < (buf_words >> 2); i += kWave) b4[i] = u32x4{0u, 0u, 0u, 0u};
         }
         __builtin_amdgcn_wave_barrier();
-        uint32_t* pay = buf + hw;
+        uint32_t* pay = buf + (headers ? 4u : hw);
         uint32_t carry = 0;
         uint32_t pos0 = UNI ? 0u : (4u * lane) % Mw;
 #pragma unroll
@@ -433,9 +437,13 @@ __global__ __launch_bounds__(1024) void k_encode_small(Tables t, Geo geo, const 
             __builtin_amdgcn_wave_barrier();
             continue;
         }
+        // header words to GPU memory (zero for a raw tensor) when they live there
+        if (headers && lane < hw) headers[ti * hw + lane] = comp ? buf[lane] : 0u;
         if (comp) {
-            const uint32_t w4 = (words + 3) >> 2;  // <= n4: the slot is a multiple of 16 bytes
-            const u32x4* b4 = reinterpret_cast<const u32x4*>(buf);
+            // the record, or with headers in GPU memory its payload alone;
+            // either fits the slot, a multiple of 16 bytes
+            const uint32_t w4 = ((headers ? words - hw : words) + 3) >> 2;
+            const u32x4* b4 = reinterpret_cast<const u32x4*>(headers ? pay : buf);
             for (uint32_t i = lane; i < w4; i += kWave) __builtin_nontemporal_store(b4[i], slot4 + i);
         } else {
             // the registers already hold the next tensor: copy this one again
@@ -448,7 +456,7 @@ __global__ __launch_bounds__(1024) void k_encode_small(Tables t, Geo geo, const 
                 atomicOr(&bitmask[ti >> 5], bit);
             else
                 atomicAnd(&bitmask[ti >> 5], ~bit);
-            if (stored) stored[ti] = comp ? 4ull * words : geo.L;
+            if (stored) stored[ti] = comp ? 4ull * (headers ? words - hw : words) : geo.L;
         }
         __builtin_amdgcn_wave_barrier();
     }
@@ -513,8 +521,11 @@ static hipError_t launch_encode_t(const Tables& t, const Geo& geo, uint32_t runs
 // buffer); false when the tables do not fit.
 static bool small_encode_lds(const Geo& geo, int runs, bool uni, uint32_t* buf_words, size_t* head,
                              size_t* wave) {
-    // header words + kept bits + 2 spare words, rounded to 16 bytes
-    *buf_words = ((uint32_t)geo.hdr_words + (uint32_t)geo.n_words + 2 + 3) & ~3u;
+    // header words (at least a 4-word area, so that a payload written
+    // without its header stays 16-byte aligned) + kept bits + 2 spare words,
+    // rounded to 16 bytes
+    const uint32_t hdr_area = geo.hdr_words < 4 ? 4u : (uint32_t)geo.hdr_words;
+    *buf_words = (hdr_area + (uint32_t)geo.n_words + 2 + 3) & ~3u;
     const uint64_t tab = uni ? 0 : (uint64_t)(1 + tab_rows(runs)) * geo.Mw * 4;
     if (tab > kMaxLdsTableBytes) return false;
     *head = (size_t)((tab + 15) & ~15ull);
@@ -527,6 +538,7 @@ struct SmallArgs {
     Items items{nullptr, 0};
     uint64_t* sizes = nullptr;
     uint32_t* err = nullptr;
+    uint32_t* headers = nullptr;
 };
 
 template <int RUNS, bool UNI, bool MW4, int S, bool SIZES>
@@ -541,7 +553,7 @@ static hipError_t launch_encode_small_s(const Tables& t, const Geo& geo, const v
     hipLaunchKernelGGL((k_encode_small<RUNS, UNI, MW4, S, SIZES>), dim3(plan.blocks), dim3(kWave * plan.wpb),
                        plan.shm, s, t, geo, static_cast<const uint8_t*>(src), n_tensors,
                        static_cast<uint8_t*>(slots), bitmask, stored, SIZES ? 0u : buf_words, xa.items, xa.sizes,
-                       xa.err);
+                       xa.err, xa.headers);
     *launched = true;
     return hipGetLastError();
 }
@@ -689,6 +701,46 @@ static hipError_t launch_packed(const Tables& t, const Geo& geo, uint32_t runs, 
         default: IBP_PK(16);
     }
 #undef IBP_PK
+}
+
+bool split_supported(const Geo& geo, uint32_t runs, bool uniform_meta) {
+    return geo.hdr_words <= kMaxSplitHeaderWords && packed_supported(geo, runs, uniform_meta);
+}
+
+template <int RUNS>
+static hipError_t launch_encode_split_r(const Tables& t, const Geo& geo, bool uniform_meta, const void* src,
+                                        uint64_t n_tensors, void* slots, uint32_t* headers, uint32_t* bitmask,
+                                        uint64_t* stored, uint32_t cu_count, hipStream_t s) {
+    uint32_t buf_words = 0;
+    size_t head = 0, wave = 0;
+    if (!small_encode_lds(geo, RUNS, uniform_meta, &buf_words, &head, &wave)) return hipErrorInvalidValue;
+    SmallArgs xa;
+    xa.headers = headers;
+    bool launched = false;
+    const hipError_t e =
+        uniform_meta ? launch_encode_small<RUNS, true, false>(t, geo, src, n_tensors, slots, bitmask, stored, cu_count,
+                                                              head, wave, buf_words, xa, s, &launched)
+                     : launch_encode_small<RUNS, false, false>(t, geo, src, n_tensors, slots, bitmask, stored,
+                                                               cu_count, head, wave, buf_words, xa, s, &launched);
+    if (e != hipSuccess) return e;
+    return launched ? hipSuccess : hipErrorInvalidValue;
+}
+
+hipError_t launch_encode_split(const Tables& t, const Geo& geo, uint32_t runs, bool uniform_meta, const void* src,
+                               uint64_t n_tensors, void* slots, uint32_t* headers, uint32_t* bitmask,
+                               uint64_t* stored, uint32_t cu_count, hipStream_t s) {
+    if (n_tensors == 0) return hipSuccess;
+#define IBP_SP(R) return launch_encode_split_r<R>(t, geo, uniform_meta, src, n_tensors, slots, headers, bitmask, stored, cu_count, s)
+    switch (runs_bucket(runs)) {
+        case 0: IBP_SP(0);
+        case 1: IBP_SP(1);
+        case 2: IBP_SP(2);
+        case 3: IBP_SP(3);
+        case 4: IBP_SP(4);
+        case 8: IBP_SP(8);
+        default: IBP_SP(16);
+    }
+#undef IBP_SP
 }
 
 bool packed_supported(const Geo& geo, uint32_t runs, bool uniform_meta) {

@@ -109,7 +109,7 @@ hipError_t launch_encode(const Tables& t, const Geo& geo, uint32_t runs, bool un
 hipError_t launch_decode(const Tables& t, const Geo& geo, uint32_t runs, bool uniform_meta, const void* slots,
                          uint64_t n_slots, const uint32_t* bitmask, const int64_t* ids, uint64_t n_out,
                          void* dst, uint32_t* err, const LookBack* lb, uint32_t cu_count, hipStream_t s,
-                         const Items* items = nullptr);
+                         const Items* items = nullptr, const uint32_t* headers = nullptr);
 
 // Packed cache.  These run only on the persistent small-tensor kernels
 // (16-byte aligned tensors of at most kMaxTileWords words whose tables fit in
@@ -125,6 +125,15 @@ hipError_t launch_item_sizes(const Tables& t, const Geo& geo, uint32_t runs, boo
 hipError_t launch_encode_packed(const Tables& t, const Geo& geo, uint32_t runs, bool uniform_meta,
                                 const void* src, uint64_t n_tensors, void* dst, const Items& items,
                                 uint32_t* bitmask, uint32_t* err, uint32_t cu_count, hipStream_t s);
+// Headers in GPU memory: header words of each compressed tensor in an array
+// beside the bitmask, the payload alone in the slot.  At most
+// kMaxSplitHeaderWords header words (128 chunks) per tensor, persistent
+// small-tensor kernels only.
+constexpr uint64_t kMaxSplitHeaderWords = 4;
+bool split_supported(const Geo& geo, uint32_t runs, bool uniform_meta);
+hipError_t launch_encode_split(const Tables& t, const Geo& geo, uint32_t runs, bool uniform_meta, const void* src,
+                               uint64_t n_tensors, void* slots, uint32_t* headers, uint32_t* bitmask,
+                               uint64_t* stored, uint32_t cu_count, hipStream_t s);
 // offsets[1..n] hold sizes on entry and their inclusive prefix sums on exit;
 // offsets[0] <- 0.  One look-back entry per block of kScanBlock sizes.
 constexpr uint32_t kScanPerLane = 8;

@@ -30,6 +30,7 @@ ABI_FUNCTIONS = (
     "ibp_meta_set_first_read", "ibp_meta_destroy", "ibp_compress", "ibp_decompress", "ibp_gather_decompress",
     "ibp_check", "ibp_status_string",
     "ibp_packed_offsets", "ibp_compress_packed", "ibp_decompress_packed", "ibp_gather_decompress_packed",
+    "ibp_compress_split", "ibp_decompress_split", "ibp_gather_decompress_split",
 )
 
 
@@ -76,6 +77,9 @@ def lib():
         L.ibp_compress_packed.argtypes = [p, p, u64, p, p, u64, p, p]
         L.ibp_decompress_packed.argtypes = [p, p, u64, p, p, u64, p, p]
         L.ibp_gather_decompress_packed.argtypes = [p, p, u64, p, u64, p, p, u64, p, p]
+        L.ibp_compress_split.argtypes = [p, p, u64, p, p, p, p, p]
+        L.ibp_decompress_split.argtypes = [p, p, p, p, u64, p, p]
+        L.ibp_gather_decompress_split.argtypes = [p, p, u64, p, p, p, u64, p, p]
         L.ibp_status_string.argtypes = [st]
         L.ibp_status_string.restype = ctypes.c_char_p
         for f in ABI_FUNCTIONS:
@@ -252,3 +256,33 @@ def ibp_gather_decompress_packed(meta: Meta, buf: torch.Tensor, offsets: torch.T
     _check(lib().ibp_gather_decompress_packed(meta, _ptr(buf), int(buf_bytes), _ptr(offsets), int(n_items),
                                               _ptr(bitmask), _ptr(ids), int(ids.numel()), _ptr(dst),
                                               _stream(stream)), "ibp_gather_decompress_packed")
+
+
+# ---------------------------------------------------------------------------
+# Headers in GPU memory: header words beside the bitmask, payload in the slot.
+# ---------------------------------------------------------------------------
+def header_words(meta: Meta) -> int:
+    prm, _, _ = ibp_meta_get(meta)
+    return (8 * prm["tensor_bytes"] // prm["chunk_bits"] + 31) // 32
+
+
+def ibp_compress_split(meta: Meta, src: torch.Tensor, n_tensors: int, dst_slots: torch.Tensor,
+                       headers: torch.Tensor, bitmask: torch.Tensor, stored_bytes: torch.Tensor | None = None,
+                       stream=None):
+    _check(lib().ibp_compress_split(meta, _ptr(src), int(n_tensors), _ptr(dst_slots), _ptr(headers),
+                                    _ptr(bitmask), _ptr(stored_bytes), _stream(stream)), "ibp_compress_split")
+
+
+def ibp_decompress_split(meta: Meta, slots: torch.Tensor, headers: torch.Tensor, bitmask: torch.Tensor,
+                         n_tensors: int, dst: torch.Tensor, stream=None):
+    _check(lib().ibp_decompress_split(meta, _ptr(slots), _ptr(headers), _ptr(bitmask), int(n_tensors), _ptr(dst),
+                                      _stream(stream)), "ibp_decompress_split")
+
+
+def ibp_gather_decompress_split(meta: Meta, slots: torch.Tensor, n_slots: int, headers: torch.Tensor,
+                                bitmask: torch.Tensor, ids: torch.Tensor, dst: torch.Tensor, stream=None):
+    if ids.dtype != torch.int64:
+        raise ValueError("ids must be int64")
+    _check(lib().ibp_gather_decompress_split(meta, _ptr(slots), int(n_slots), _ptr(headers), _ptr(bitmask),
+                                             _ptr(ids), int(ids.numel()), _ptr(dst), _stream(stream)),
+           "ibp_gather_decompress_split")

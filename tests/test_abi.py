@@ -51,3 +51,7 @@ def test_status_strings_and_host_side_argument_checks():
     assert L.ibp_decompress_packed(None, None, 0, None, None, 1, None, None) == ibp.IBP_ERR_INVALID_ARG
     assert L.ibp_gather_decompress_packed(None, None, 0, None, 1, None, None, 1, None, None) == \
         ibp.IBP_ERR_INVALID_ARG
+    # header-in-GPU-memory calls
+    assert L.ibp_compress_split(None, None, 1, None, None, None, None, None) == ibp.IBP_ERR_INVALID_ARG
+    assert L.ibp_decompress_split(None, None, None, None, 1, None, None) == ibp.IBP_ERR_INVALID_ARG
+    assert L.ibp_gather_decompress_split(None, None, 1, None, None, None, 1, None, None) == ibp.IBP_ERR_INVALID_ARG
