@@ -633,8 +633,87 @@ def run_sparse_gnn_cache(args) -> dict:
         meta=ibp.ibp_meta_get_info(meta))
 
 
+# ---------------------------------------------------------------------------
+# Chunk width x threshold sweep (sparse rows) and an fp16 variant (dense rows)
+# ---------------------------------------------------------------------------
+def run_sweep(args) -> dict:
+    """Savings and gather rate across chunk widths W and thresholds T on a
+    262,144-row slice of the sparse_gnn table (pinned slots, plain layout,
+    8,192 distinct ids per gather), and the dense_gnn rows stored as fp16.
+    `value` is the point of the sparse_gnn line itself (W = 1,024, T = 0.95)."""
+    w = WL.SPARSE_GNN
+    n, L = (262144 if not args.small else 32768), w.tensor_bytes
+    batch = 8192
+    dev = torch.device("cuda")
+    log(f"[bench] sweep: generating {n} x 256 fp32 sparse rows")
+    host = pinned((n, L), torch.uint8)
+    WL.sparse_gnn(n, out=host.numpy().view(np.float32).reshape(n, 256))
+    raw_np = host.numpy()
+    slots = pinned((n, L), torch.uint8)
+    bitmask = torch.zeros((n + 31) // 32, dtype=torch.int32, device=dev)
+    stored = torch.zeros(n, dtype=torch.int64, device=dev)
+    ids_all = WL.batch_ids(n, batch, args.warmup + args.steps, replace=False)
+    ids_dev = torch.from_numpy(ids_all).to(dev)
+    out = torch.empty((2, batch, L), dtype=torch.uint8, device=dev)
+    points, value, wall_at, durs_at = [], None, None, None
+    for W in (32, 64, 128, 256, 512, 1024):
+        for T in (0.9, 0.95, 0.99):
+            meta = ibp.ibp_build_metadata(host, w.n_sample, L, W, w.period_bits, T)
+            ibp.ibp_compress(meta, host, n, slots, bitmask, stored)
+            st = stored.cpu().numpy()
+
+            def step(i, meta=meta):
+                ibp.ibp_gather_decompress(meta, slots, n, bitmask, ids_dev[i], out[i & 1])
+
+            wall, durs = timed(step, args.steps, args.warmup)
+            assert ibp.ibp_check(meta) == ibp.IBP_OK
+            last = args.warmup + args.steps - 1
+            if not np.array_equal(out[last & 1].cpu().numpy(), raw_np[ids_all[last]]):
+                raise SystemExit(f"decoded rows differ at W={W} T={T}")
+            gbps = args.steps * batch * L / wall / GB
+            points.append({"W": W, "T": T, "savings_pct": round(100 * (1 - st.sum() / (n * L)), 3),
+                           "decoded_GBps": round(gbps, 3), "kernel_avg_us": round(float(durs.mean()) * 1e6, 2),
+                           "link_bytes_per_launch": int(st[ids_all[args.warmup:]].sum(axis=1).mean()),
+                           "uniform_metadata": bool(ibp.ibp_meta_get_info(meta)["uniform"])})
+            log(f"[bench] sweep W={W} T={T}: {points[-1]['savings_pct']} % saved, {gbps:.1f} GB/s decoded")
+            if W == w.chunk_bits and T == w.threshold:
+                value, wall_at, durs_at = gbps, wall, durs
+                link_at = float(points[-1]["link_bytes_per_launch"])
+                savings_at = points[-1]["savings_pct"] / 100
+            meta.close()
+    # dense_gnn rows as fp16: 16,384 rows x 128 half, HBM slots, all rows per step
+    wd = WL.DENSE_GNN
+    x16 = WL.dense_gnn().astype(np.float16)
+    raw16 = np.ascontiguousarray(x16).view(np.uint8).reshape(x16.shape[0], -1)
+    src16 = torch.from_numpy(raw16).to(dev)
+    n16, L16 = raw16.shape
+    fp16 = []
+    for W in (32, 64):
+        meta = ibp.ibp_build_metadata(src16, wd.n_sample, L16, W, 8 * L16, wd.threshold)
+        s16 = torch.empty_like(src16)
+        b16 = torch.zeros((n16 + 31) // 32, dtype=torch.int32, device=dev)
+        st16 = torch.zeros(n16, dtype=torch.int64, device=dev)
+        ibp.ibp_compress(meta, src16, n16, s16, b16, st16)
+        o16 = torch.empty_like(src16)
+        wall, _ = timed(lambda i: ibp.ibp_decompress(meta, s16, b16, n16, o16), args.steps, args.warmup)
+        assert ibp.ibp_check(meta) == ibp.IBP_OK and torch.equal(o16, src16)
+        fp16.append({"W": W, "T": wd.threshold, "M": 8 * L16,
+                     "savings_pct": round(100 * (1 - st16.cpu().numpy().sum() / (n16 * L16)), 3),
+                     "decoded_GBps": round(args.steps * n16 * L16 / wall / GB, 3)})
+        meta.close()
+    return base_result(
+        args, value, wall_at,
+        {"workload": f"sweep: sparse_gnn rows ({n} x 256 fp32, 97% zeros), M=8192, chunk widths W=32..1024 x "
+                     f"thresholds T=0.9/0.95/0.99, pinned slots (plain layout), gathers of {batch} distinct ids; "
+                     f"value at W=1024, T=0.95; plus dense_gnn rows as fp16 (16384 x 128 half, HBM)",
+         "rows": n, "tensor_bytes": L, "batch_ids": batch},
+        savings_at, "ibp::k_decode_small", durs_at, link_roofline(link_at, durs_at, savings_at, None),
+        sweep=points, fp16_dense_gnn=fp16)
+
+
 WORKLOADS = {"sparse_gnn": run_sparse_gnn, "kv_bf16": run_kv_bf16, "dense_gnn": run_dense_gnn,
-             "dlrm": run_dlrm, "llm_bf16": run_llm_bf16, "sparse_gnn_cache": run_sparse_gnn_cache}
+             "dlrm": run_dlrm, "llm_bf16": run_llm_bf16, "sparse_gnn_cache": run_sparse_gnn_cache,
+             "sweep": run_sweep}
 
 
 def main():
@@ -656,7 +735,7 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
     defaults = {"sparse_gnn": (200, 10), "kv_bf16": (100, 5), "dense_gnn": (200, 10), "dlrm": (4, 1),
-                "sparse_gnn_cache": (200, 10),
+                "sparse_gnn_cache": (200, 10), "sweep": (30, 5),
                 "llm_bf16": (3, 1)}
     d_steps, d_warm = defaults[args.workload]
     args.steps = d_steps if args.steps is None else args.steps
