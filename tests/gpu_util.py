@@ -35,10 +35,26 @@ def to_gpu(a: np.ndarray, pinned: bool = False) -> torch.Tensor:
     return t.to(device())
 
 
-def empty_like_loc(shape, dtype, pinned: bool):
+def empty_like_loc(shape, dtype, pinned: bool, misalign: int = 0):
+    """Uninitialised uint8 tensor; with misalign > 0 its data pointer sits
+    `misalign` bytes past an allocation boundary (a view into a larger
+    buffer), which takes the kernels' unaligned paths."""
+    if misalign:
+        assert dtype == torch.uint8
+        nbytes = int(np.prod(shape))
+        flat = empty_like_loc((nbytes + misalign,), dtype, pinned)
+        return flat[misalign:].view(*shape)
     if pinned:
         return torch.empty(shape, dtype=dtype, pin_memory=True)
     return torch.empty(shape, dtype=dtype, device=device())
+
+
+def to_gpu_off(a: np.ndarray, misalign: int, pinned: bool = False) -> torch.Tensor:
+    if not misalign:
+        return to_gpu(a, pinned)
+    t = empty_like_loc(a.shape, torch.uint8, pinned, misalign)
+    t.copy_(torch.from_numpy(np.ascontiguousarray(a)))
+    return t
 
 
 def bitmask_bits(bm_words: np.ndarray, n: int) -> np.ndarray:
@@ -52,7 +68,7 @@ class Result:
 
 def compare_codec(raw: np.ndarray, W: int, M: int, T: float, n_sample: int, *, sample: np.ndarray | None = None,
                   src_pinned: bool = False, slots_pinned: bool = False, ids: np.ndarray | None = None,
-                  check_slots: bool = True, label: str = "") -> Result:
+                  check_slots: bool = True, label: str = "", misalign: int = 0) -> Result:
     """Metadata, compress, decompress (and gather when ids is given) on the
     GPU and in the oracle; asserts bit-exact agreement."""
     n, L = raw.shape
@@ -68,8 +84,8 @@ def compare_codec(raw: np.ndarray, W: int, M: int, T: float, n_sample: int, *, s
     np.testing.assert_array_equal(g_mask.view(np.uint8), o_mask, err_msg="Mask differs")
     np.testing.assert_array_equal(g_bitval.view(np.uint8), o_bitval, err_msg="Bitval differs")
     # compress
-    src = to_gpu(raw, pinned=src_pinned)
-    slots = empty_like_loc((n, L), torch.uint8, slots_pinned)
+    src = to_gpu_off(raw, misalign, pinned=src_pinned)
+    slots = empty_like_loc((n, L), torch.uint8, slots_pinned, misalign)
     bm = torch.zeros((n + 31) // 32, dtype=torch.int32, device=dev)
     stored = torch.zeros(n, dtype=torch.int64, device=dev)
     ibp.ibp_compress(meta, src, n, slots, bm, stored)
@@ -90,7 +106,7 @@ def compare_codec(raw: np.ndarray, W: int, M: int, T: float, n_sample: int, *, s
         raw_rows = np.flatnonzero(~comp)
         np.testing.assert_array_equal(g_slots[raw_rows], raw[raw_rows], err_msg="raw slots differ")
     # decompress
-    out = torch.empty((n, L), dtype=torch.uint8, device=dev)
+    out = empty_like_loc((n, L), torch.uint8, False, misalign)
     ibp.ibp_decompress(meta, slots, bm, n, out)
     assert ibp.ibp_check(meta) == ibp.IBP_OK
     np.testing.assert_array_equal(out.cpu().numpy(), raw, err_msg="decompress differs")
@@ -103,7 +119,7 @@ def compare_codec(raw: np.ndarray, W: int, M: int, T: float, n_sample: int, *, s
     np.testing.assert_array_equal(out2.cpu().numpy(), raw, err_msg="decode of oracle slots differs")
     if ids is not None:
         g_ids = torch.from_numpy(np.ascontiguousarray(ids, dtype=np.int64)).to(dev)
-        gout = torch.empty((ids.size, L), dtype=torch.uint8, device=dev)
+        gout = empty_like_loc((ids.size, L), torch.uint8, False, misalign)
         ibp.ibp_gather_decompress(meta, slots, n, bm, g_ids, gout)
         assert ibp.ibp_check(meta) == ibp.IBP_OK
         np.testing.assert_array_equal(gout.cpu().numpy(), raw[ids], err_msg="gather differs")

@@ -95,6 +95,53 @@ def test_shapes(W, M, L, n):
     compare_codec(raw, W, M, 0.9, min(n, 64), ids=ids, label=f"shape W={W} M={M} L={L}")
 
 
+@pytest.mark.parametrize("W,M,L,n", [
+    (32, 800, 100, 70),        # L not a multiple of 16: 25 words, period of 25 words
+    (64, 320, 40, 90),         # 10-word period, W = 64
+    (32, 32, 8212, 5),         # two tiles, 2,053 words
+])
+def test_unaligned_lengths(W, M, L, n):
+    """Tensors whose length is not a multiple of 16 bytes take the general
+    (non-vector) kernels."""
+    rng = np.random.default_rng(L)
+    raw = _structured(rng, n, L)
+    ids = rng.integers(0, n, size=2 * n)
+    compare_codec(np.ascontiguousarray(raw), W, M, 0.9, n, ids=ids, label=f"unaligned L={L}")
+
+
+@pytest.mark.parametrize("wl,misalign,pinned", [("dense_gnn", 4, False), ("sparse_gnn", 8, True),
+                                                ("kv_bf16", 4, False)])
+def test_misaligned_pointers(wl, misalign, pinned):
+    """Source, slots and output 4 or 8 bytes past a 16-byte boundary."""
+    w = WL.ALL[wl]
+    if wl == "dense_gnn":
+        raw = as_rows(WL.dense_gnn(700))
+    elif wl == "sparse_gnn":
+        raw = as_rows(WL.sparse_gnn(700))
+    else:
+        raw = WL.kv_cache(n_layers=1, n_heads=1, n_tokens=16 * 40).reshape(-1, 2048).view(np.uint8).reshape(-1, 4096)
+    ids = np.random.default_rng(5).integers(0, raw.shape[0], 300)
+    compare_codec(raw, w.chunk_bits, w.period_bits, w.threshold, min(raw.shape[0], 1024), ids=ids,
+                  src_pinned=pinned, slots_pinned=pinned, misalign=misalign, label=f"{wl} misaligned by {misalign}")
+
+
+def test_packed_and_split_need_aligned_data():
+    dev = device()
+    rng = np.random.default_rng(100)
+    raw = _structured(rng, 40, 100)
+    src = to_gpu(raw)
+    meta = ibp.ibp_build_metadata(src, 40, 100, 32, 800, 0.9)
+    off = torch.zeros(41, dtype=torch.int64, device=dev)
+    with pytest.raises(ibp.IBPError) as e:
+        ibp.ibp_packed_offsets(meta, src, 40, off)
+    assert e.value.status == ibp.IBP_ERR_UNSUPPORTED
+    with pytest.raises(ibp.IBPError) as e:
+        ibp.ibp_compress_split(meta, src, 40, torch.empty_like(src), torch.zeros((40, 1), dtype=torch.int32,
+                                                                                 device=dev),
+                               torch.zeros(2, dtype=torch.int32, device=dev))
+    assert e.value.status == ibp.IBP_ERR_UNSUPPORTED
+
+
 def test_incompressible_and_fully_compressible():
     rng = np.random.default_rng(4)
     L = 1024
