@@ -139,6 +139,19 @@ def timed(fn, steps: int, warmup: int):
     return wall, np.full(steps, start.elapsed_time(end) / 1e3 / steps)
 
 
+def encode_seconds(fn, reps: int = 3) -> float:
+    """Median wall time of `reps` synchronised calls after one untimed call."""
+    fn()
+    torch.cuda.synchronize()
+    ts = []
+    for _ in range(reps):
+        t0 = time.perf_counter()
+        fn()
+        torch.cuda.synchronize()
+        ts.append(time.perf_counter() - t0)
+    return float(np.median(ts))
+
+
 def queued_durations(fn, steps: int, first: int = 0):
     """Average launch duration of `steps` calls queued behind a bounded spin
     kernel so that the GPU runs them back to back (one event pair over the
@@ -452,11 +465,7 @@ def run_dlrm(args) -> dict:
     slots = pinned((n, L), torch.uint8)
     bitmask = torch.zeros((n + 31) // 32, dtype=torch.int32, device=dev)
     stored = torch.zeros(n, dtype=torch.int64, device=dev)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    ibp.ibp_compress(meta, host, n, slots, bitmask, stored)
-    torch.cuda.synchronize()
-    t_enc = time.perf_counter() - t0
+    t_enc = encode_seconds(lambda: ibp.ibp_compress(meta, host, n, slots, bitmask, stored))
     stored_np = stored.cpu().numpy()
     savings = 1.0 - stored_np.sum() / (n * L)
     n_batches = per_step * (args.warmup + args.steps)
@@ -503,11 +512,7 @@ def run_llm_bf16(args) -> dict:
     slots = pinned((layers, L), torch.uint8)
     bitmask = torch.zeros((layers + 31) // 32, dtype=torch.int32, device=dev)
     stored = torch.zeros(layers, dtype=torch.int64, device=dev)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    ibp.ibp_compress(meta, host, layers, slots, bitmask, stored)
-    torch.cuda.synchronize()
-    t_enc = time.perf_counter() - t0
+    t_enc = encode_seconds(lambda: ibp.ibp_compress(meta, host, layers, slots, bitmask, stored))
     stored_np = stored.cpu().numpy()
     savings = 1.0 - stored_np.sum() / (layers * L)
     bufs = [torch.empty(L, dtype=torch.uint8, device=dev) for _ in range(2)]

@@ -104,8 +104,9 @@ ibp_status ibp_meta_get_info(ibp_meta_t meta, ibp_meta_info* info);
  * the record header (a record's length is known only from its header, so a
  * second read fetches the rest).  0 restores the default: the largest
  * 256-byte-aligned prefix no record can be shorter than, but at least 256
- * bytes, or the whole slot when the shortest possible record spans all but
- * at most 1/16 of the slot's 128-byte lines.
+ * bytes -- or fewer whole 128-byte lines when the median record of the
+ * metadata sample fits in them -- or the whole slot when the shortest
+ * possible record spans all but at most 1/16 of the slot's 128-byte lines.
  * Rounded up to a multiple of 16 bytes and to at least the header; capped at
  * the slot.  Affects later decode calls on any stream. */
 ibp_status ibp_meta_set_first_read(ibp_meta_t meta, uint64_t bytes);

@@ -6,6 +6,7 @@
 #include <stdint.h>
 #include <string.h>
 
+#include <algorithm>
 #include <map>
 #include <mutex>
 #include <new>
@@ -42,6 +43,7 @@ struct ibp_meta_s {
     int device = 0;
     uint32_t cu_count = 0;
     uint64_t first_read_bytes = 0;  // 0: default policy
+    uint64_t typical_item_bytes = 0; // median stored bytes over the metadata sample (0: unknown)
     ibp_params params{};
     uint32_t Mw = 0, Pc = 0, g = 0, log2g = 0, G = 0, Ne = 0;
     std::vector<uint32_t> mask_h, bitval_h;
@@ -206,6 +208,12 @@ ibp_status finish_handle(ibp_meta_s* h, hipStream_t s) {
     return IBP_OK;
 }
 
+// Median stored bytes (record, or L when raw) over the metadata sample, from
+// the record-length kernel; sets typical_item_bytes, or leaves it 0 when the
+// geometry has no record-length kernel.  Synchronous (the handle is being
+// built).
+ibp_status sample_item_stats(ibp_meta_s* h, const void* sample, uint64_t n_sample, hipStream_t s);
+
 void free_handle(ibp_meta_s* h) {
     if (!h) return;
     (void)hipDeviceSynchronize();
@@ -266,6 +274,12 @@ Geo make_geo(const ibp_meta_s* h, bool aligned16, uint32_t long_tile_words) {
     } else {
         spec = (min_words / kLineWords) * kLineWords;
         if (spec < kLineWords) spec = kLineWords;
+        // records of the sample mostly shorter than that: one 128-byte line
+        // (rounded up to whole lines) covers the usual record in one read
+        if (h->typical_item_bytes) {
+            const uint64_t usual = (h->typical_item_bytes + 4 * kMemLineWords - 1) / (4 * kMemLineWords) * kMemLineWords;
+            if (usual < spec) spec = usual;
+        }
         if (spec < g.hdr_words) spec = g.hdr_words;
     }
     if (aligned16) spec = (spec + 3) & ~3ull;
@@ -279,6 +293,25 @@ bool aligned16(uint64_t L, std::initializer_list<const void*> ptrs) {
     for (const void* p : ptrs)
         if (reinterpret_cast<uintptr_t>(p) % 16 != 0) return false;
     return true;
+}
+
+ibp_status sample_item_stats(ibp_meta_s* h, const void* sample, uint64_t n_sample, hipStream_t s) {
+    const uint64_t L = h->params.tensor_bytes;
+    const Geo geo = make_geo(h, aligned16(L, {sample}), kLongTileWordsEncode);
+    if (!packed_supported(geo, h->sum.max_runs, h->sum.uniform != 0)) return IBP_OK;
+    uint64_t* d_sizes = nullptr;
+    IBP_TRY(hipMalloc(&d_sizes, n_sample * sizeof(uint64_t)));
+    std::vector<uint64_t> sizes(n_sample);
+    hipError_t e = launch_item_sizes(h->tabs, geo, h->sum.max_runs, h->sum.uniform != 0, sample, n_sample, d_sizes,
+                                     h->cu_count, s);
+    if (e == hipSuccess)
+        e = hipMemcpyAsync(sizes.data(), d_sizes, n_sample * sizeof(uint64_t), hipMemcpyDeviceToHost, s);
+    if (e == hipSuccess) e = hipStreamSynchronize(s);
+    (void)hipFree(d_sizes);
+    IBP_TRY(e);
+    std::nth_element(sizes.begin(), sizes.begin() + n_sample / 2, sizes.end());
+    h->typical_item_bytes = sizes[n_sample / 2];
+    return IBP_OK;
 }
 
 // Look-back state for one launch of `waves` waves over `tiles` tiles on
@@ -376,6 +409,7 @@ ibp_status ibp_build_metadata(const ibp_params* params, const void* sample, uint
     if (e == hipSuccess) e = launch_meta_finalize(counts, h->Mw, n_obs, K, h->d_mask, h->d_bitval, stream);
     st = from_hip(e);
     if (st == IBP_OK) st = finish_handle(h, stream);
+    if (st == IBP_OK) st = sample_item_stats(h, sample, n_sample, stream);
     if (counts) (void)hipFree(counts);
     if (st != IBP_OK) {
         free_handle(h);

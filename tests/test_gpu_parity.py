@@ -125,6 +125,17 @@ def test_misaligned_pointers(wl, misalign, pinned):
                   src_pinned=pinned, slots_pinned=pinned, misalign=misalign, label=f"{wl} misaligned by {misalign}")
 
 
+@pytest.mark.parametrize("W", [32, 64, 256])
+def test_sparse_rows_narrow_chunks(W):
+    """Sparse rows with narrow chunks: records mostly shorter than one
+    128-byte line, so the first read of a slot is a single line."""
+    raw = as_rows(WL.sparse_gnn(1500))
+    ids = np.random.default_rng(W).choice(raw.shape[0], 700, replace=False)
+    r = compare_codec(raw, W, 8192, 0.95, 1024, ids=ids, slots_pinned=True, src_pinned=True,
+                      label=f"sparse W={W}")
+    assert r.savings > 0.7
+
+
 def test_packed_and_split_need_aligned_data():
     dev = device()
     rng = np.random.default_rng(100)
