@@ -1,0 +1,78 @@
+"""Concurrency and capture: one handle used from two streams at once (the
+multi-tile look-back keeps its scratch per stream), and single-tile decode
+captured in a HIP graph and replayed."""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+from lossless_tensor_compression_ibp_amd import ibp
+from lossless_tensor_compression_ibp_amd import workloads as WL
+from tests.gpu_util import as_rows, device, say
+
+pytestmark = pytest.mark.gpu
+
+
+def test_one_handle_two_streams():
+    dev = device()
+    # multi-tile tensors: 3 x 64 KiB bf16 rows (look-back per stream)
+    layers = [WL.llm_layer(l, rows=32, cols=1024) for l in range(3)]
+    raw = np.stack([x.reshape(-1).view(np.uint8) for x in layers])
+    n, L = raw.shape
+    src = torch.from_numpy(raw).to(dev)
+    w = WL.LLM_BF16
+    meta = ibp.ibp_build_metadata(src, 1, L, w.chunk_bits, w.period_bits, w.threshold)
+    slots = torch.empty_like(src)
+    bm = torch.zeros(1, dtype=torch.int32, device=dev)
+    ibp.ibp_compress(meta, src, n, slots, bm)
+    torch.cuda.synchronize()
+    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+    outs1 = [torch.empty((n, L), dtype=torch.uint8, device=dev) for _ in range(6)]
+    outs2 = [torch.empty((n, L), dtype=torch.uint8, device=dev) for _ in range(6)]
+    ids = torch.tensor([2, 0, 1], dtype=torch.int64, device=dev)
+    for i in range(6):  # interleaved launches on both streams
+        with torch.cuda.stream(s1):
+            ibp.ibp_decompress(meta, slots, bm, n, outs1[i], stream=s1)
+        with torch.cuda.stream(s2):
+            ibp.ibp_gather_decompress(meta, slots, n, bm, ids, outs2[i], stream=s2)
+    torch.cuda.synchronize()
+    assert ibp.ibp_check(meta) == ibp.IBP_OK
+    for i in range(6):
+        assert torch.equal(outs1[i], src), f"stream 1 launch {i}"
+        assert torch.equal(outs2[i], src[ids]), f"stream 2 launch {i}"
+    say("[streams] two streams, multi-tile look-back: ok")
+
+
+def test_single_tile_decode_in_a_graph():
+    dev = device()
+    w = WL.SPARSE_GNN
+    raw = as_rows(WL.sparse_gnn(4096))
+    n, L = raw.shape
+    src = torch.from_numpy(raw).to(dev)
+    meta = ibp.ibp_build_metadata(src, 1024, L, w.chunk_bits, w.period_bits, w.threshold)
+    slots = torch.empty_like(src)
+    bm = torch.zeros((n + 31) // 32, dtype=torch.int32, device=dev)
+    ibp.ibp_compress(meta, src, n, slots, bm)
+    ids = torch.zeros(1024, dtype=torch.int64, device=dev)
+    out = torch.empty((1024, L), dtype=torch.uint8, device=dev)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):  # warm up (launch plans, code objects) outside the capture
+        ibp.ibp_gather_decompress(meta, slots, n, bm, ids, out, stream=s)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        ibp.ibp_gather_decompress(meta, slots, n, bm, ids, out, stream=s)
+    rng = np.random.default_rng(4)
+    for r in range(5):  # new ids each replay, with eager work and syncs between replays
+        new_ids = rng.choice(n, 1024, replace=False)
+        ids.copy_(torch.from_numpy(new_ids).to(dev))
+        out.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, src[torch.from_numpy(new_ids).to(dev)]), f"replay {r}"
+    assert ibp.ibp_check(meta) == ibp.IBP_OK
+    say("[graph] five replays of a captured gather: ok")
