@@ -215,6 +215,24 @@ def test_first_read_sizes(wl):
     say(f"[parity] {wl} first-read sizes ok")
 
 
+def test_tables_too_large_for_lds():
+    """A per-position Mask over 8 KiB tensors with up to 16 runs of kept bits
+    per word: 2,048 positions x 22 table rows do not fit in LDS, so encode
+    and decode read their tables from global memory."""
+    rng = np.random.default_rng(12)
+    L, n = 8192, 40
+    base = rng.integers(0, 2**32, size=L // 4, dtype=np.uint64).astype(np.uint32)
+    x = np.tile(base, (n, 1))
+    # alternate invariant and varying bits, with a different pattern per position
+    vary = np.where(np.arange(L // 4) % 3 == 0, np.uint32(0x55555555), np.uint32(0x0F0F0F0F))
+    x ^= rng.integers(0, 2**32, size=x.shape, dtype=np.uint64).astype(np.uint32) & vary
+    x[::9, ::7] ^= np.uint32(0xAAAAAAAA)
+    raw = x.view(np.uint8).reshape(n, L)
+    ids = rng.integers(0, n, size=3 * n)
+    r = compare_codec(raw, 32, 8 * L, 0.9, n, ids=ids, label="tables beyond LDS")
+    assert ibp.ibp_meta_get_info(r.meta)["max_runs"] > 8
+
+
 def test_meta_create_roundtrip_and_empty_calls():
     rng = np.random.default_rng(8)
     L, n = 512, 100
