@@ -395,6 +395,26 @@ __global__ __launch_bounds__(256) void k_decode_small(Tables t, Geo geo, const u
                 continue;
             }
             __builtin_amdgcn_wave_barrier();
+            if (4 * n4_first >= nwords) {
+                // The whole slot is in LDS already, so the record length is
+                // needed only to validate it: the rebuild returns the payload
+                // bits it consumed (its reads stay inside the slot even for a
+                // corrupt header), and only the last header word can hold
+                // padding bits.
+                const uint32_t valid = (uint32_t)(geo.n_chunks - 32ull * (hw - 1));
+                const bool bad_pad = valid < 32 && (buf[hw - 1] >> valid) != 0;
+                if (lane == 0) buf[4 * n4_first] = 0;
+                __builtin_amdgcn_wave_barrier();
+                uint32_t pbits;
+                if (UNI)
+                    pbits = decode_tile<RUNS, MW4, (STAGE >= 4)>(tu, geo, buf, buf + hw, 0, 0, nwords, out, true);
+                else
+                    pbits = decode_tile<RUNS, MW4, (STAGE >= 4)>(ta, geo, buf, buf + hw, 0, 0, nwords, out, true);
+                const uint64_t words = hw + (pbits + 31) / 32;
+                if (bad_pad || 4ull * words >= geo.L || 4ull * words > len) latch_error(err, kErrCorrupt);
+                __builtin_amdgcn_wave_barrier();
+                continue;
+            }
             bool bad_pad;
             const uint32_t rem = header_removed_bits(planes, geo, buf, 0, hw, &bad_pad);
             const uint64_t R = 32ull * hw + 32ull * nwords - rem;
