@@ -395,12 +395,13 @@ __global__ __launch_bounds__(256) void k_decode_small(Tables t, Geo geo, const u
                 continue;
             }
             __builtin_amdgcn_wave_barrier();
-            if (4 * n4_first >= nwords) {
-                // The whole slot is in LDS already, so the record length is
+            if (packed || 4 * n4_first >= nwords) {
+                // The whole slot (or the whole packed item, whose length the
+                // offsets give) is in LDS already, so the record length is
                 // needed only to validate it: the rebuild returns the payload
-                // bits it consumed (its reads stay inside the slot even for a
-                // corrupt header), and only the last header word can hold
-                // padding bits.
+                // bits it consumed (its reads stay inside the slot-sized
+                // buffer even for a corrupt header), and only the last header
+                // word can hold padding bits.
                 const uint32_t valid = (uint32_t)(geo.n_chunks - 32ull * (hw - 1));
                 const bool bad_pad = valid < 32 && (buf[hw - 1] >> valid) != 0;
                 if (lane == 0) buf[4 * n4_first] = 0;
