@@ -440,12 +440,20 @@ def run_dense_gnn(args) -> dict:
     if not torch.equal(out, src):
         raise SystemExit("decoded rows differ")
     hbm_bytes = float(stored_np.sum() + n * L + 4 * ((n + 31) // 32))
+    # the same rows held uncompressed: a plain device copy of them, timed the
+    # same two ways (the floor of any pass over this many bytes at this size)
+    raw_copy = torch.empty_like(src)
+    raw_wall, _ = timed(lambda i: raw_copy.copy_(src), args.steps, args.warmup)
+    raw_durs = queued_durations(lambda i: raw_copy.copy_(src), args.steps)
+    del raw_copy
     return base_result(
         args, n * L * args.steps / wall / GB, wall,
         {"workload": f"dense_gnn: {n} rows x 128 fp32 |N(0,0.5)| with 3% N(0,50) rows, W=32, M=4096, T=0.95, "
                      f"slots in HBM, contiguous decode of all rows per step", "rows": n, "tensor_bytes": L},
         savings, "ibp::k_decode_small", durs, hbm_roofline(hbm_bytes, durs, "dense_gnn"),
-        encode_GBps=round(n * L / float(np.mean(enc_durs)) / GB, 3), meta=ibp.ibp_meta_get_info(meta))
+        encode_GBps=round(n * L / float(np.mean(enc_durs)) / GB, 3),
+        uncompressed_hbm_copy_GBps=round(n * L * args.steps / raw_wall / GB, 3),
+        uncompressed_copy_kernel_us=round(float(np.mean(raw_durs)) * 1e6, 2), meta=ibp.ibp_meta_get_info(meta))
 
 
 # ---------------------------------------------------------------------------
@@ -623,6 +631,8 @@ def run_sparse_gnn_cache(args) -> dict:
     table = host.to(dev)
     raw_wall, _ = timed(lambda i: torch.index_select(table, 0, ids_dev[i], out=out[i & 1]), args.steps,
                         args.warmup)
+    raw_durs = queued_durations(lambda i: torch.index_select(table, 0, ids_dev[i], out=out[i & 1]), args.steps,
+                                args.warmup)
     del table
     return base_result(
         args, batch * L * args.steps / wall / GB, wall,
@@ -635,6 +645,7 @@ def run_sparse_gnn_cache(args) -> dict:
         cache_bytes=total, capacity_gain=round(n * L / total, 4),
         fill_GBps=round(n * L / float(np.median(fill_s)) / GB, 3),
         uncompressed_hbm_gather_GBps=round(batch * L * args.steps / raw_wall / GB, 3),
+        uncompressed_gather_kernel_us=round(float(np.mean(raw_durs)) * 1e6, 2),
         meta=ibp.ibp_meta_get_info(meta))
 
 

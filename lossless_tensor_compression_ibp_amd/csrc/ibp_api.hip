@@ -503,11 +503,13 @@ static ibp_status decode_common(ibp_meta_t h, const void* slots, uint64_t n_slot
     if (!guard.ok) return IBP_ERR_DEVICE;
     const uint64_t L = h->params.tensor_bytes;
     if (n_out > (~0ull) / L || n_slots > (~0ull) / L) return IBP_ERR_INVALID_ARG;
-    if (!device_or_pinned(slots, h->device)) return IBP_ERR_INVALID_ARG;
+    const Kind slots_kind = pointer_kind(slots, h->device);
+    if (slots_kind == Kind::Bad) return IBP_ERR_INVALID_ARG;
     if (!device_only(bitmask, h->device) || !device_only(dst, h->device)) return IBP_ERR_INVALID_ARG;
     if (ids && !device_only(ids, h->device)) return IBP_ERR_INVALID_ARG;
     if (overlaps(slots, n_slots * L, dst, n_out * L)) return IBP_ERR_INVALID_ARG;
-    const Geo geo = make_geo(h, aligned16(L, {slots, dst}), kLongTileWordsDecode);
+    Geo geo = make_geo(h, aligned16(L, {slots, dst}), kLongTileWordsDecode);
+    geo.src_in_hbm = slots_kind == Kind::Device;
     LookBack lb{};
     if (geo.tiles_per_tensor > 1) {
         const uint64_t tiles = n_out * geo.tiles_per_tensor;
@@ -586,13 +588,15 @@ static ibp_status decode_packed_common(ibp_meta_t h, const void* buf, uint64_t b
     if (!guard.ok) return IBP_ERR_DEVICE;
     const uint64_t L = h->params.tensor_bytes;
     if (n_out > (~0ull) / L) return IBP_ERR_INVALID_ARG;
-    if (!device_or_pinned(buf, h->device)) return IBP_ERR_INVALID_ARG;
+    const Kind buf_kind = pointer_kind(buf, h->device);
+    if (buf_kind == Kind::Bad) return IBP_ERR_INVALID_ARG;
     if (!device_only(offsets, h->device) || !device_only(bitmask, h->device) || !device_only(dst, h->device))
         return IBP_ERR_INVALID_ARG;
     if (ids && !device_only(ids, h->device)) return IBP_ERR_INVALID_ARG;
     if (reinterpret_cast<uintptr_t>(offsets) % 8) return IBP_ERR_INVALID_ARG;
     if (overlaps(buf, buf_bytes, dst, n_out * L)) return IBP_ERR_INVALID_ARG;
     Geo geo = make_geo(h, aligned16(L, {buf, dst}), kLongTileWordsDecode);
+    geo.src_in_hbm = buf_kind == Kind::Device;
     const bool uni = h->sum.uniform != 0;
     if (!packed_decode_supported(geo, h->sum.max_runs, uni)) return IBP_ERR_UNSUPPORTED;
     // an item's length is known from the offsets: read it whole at once
@@ -645,13 +649,15 @@ static ibp_status decode_split_common(ibp_meta_t h, const void* slots, uint64_t 
     if (!guard.ok) return IBP_ERR_DEVICE;
     const uint64_t L = h->params.tensor_bytes;
     if (n_out > (~0ull) / L || n_slots > (~0ull) / L) return IBP_ERR_INVALID_ARG;
-    if (!device_or_pinned(slots, h->device)) return IBP_ERR_INVALID_ARG;
+    const Kind slots_kind = pointer_kind(slots, h->device);
+    if (slots_kind == Kind::Bad) return IBP_ERR_INVALID_ARG;
     if (!device_only(bitmask, h->device) || !device_only(dst, h->device) || !device_only(headers, h->device))
         return IBP_ERR_INVALID_ARG;
     if (ids && !device_only(ids, h->device)) return IBP_ERR_INVALID_ARG;
     if (reinterpret_cast<uintptr_t>(headers) % 4) return IBP_ERR_INVALID_ARG;
     if (overlaps(slots, n_slots * L, dst, n_out * L)) return IBP_ERR_INVALID_ARG;
-    const Geo geo = make_geo(h, aligned16(L, {slots, dst}), kLongTileWordsDecode);
+    Geo geo = make_geo(h, aligned16(L, {slots, dst}), kLongTileWordsDecode);
+    geo.src_in_hbm = slots_kind == Kind::Device;
     const bool uni = h->sum.uniform != 0;
     if (geo.hdr_words > kMaxSplitHeaderWords || !packed_decode_supported(geo, h->sum.max_runs, uni))
         return IBP_ERR_UNSUPPORTED;

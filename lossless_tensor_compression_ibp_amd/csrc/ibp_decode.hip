@@ -162,22 +162,7 @@ __device__ __forceinline__ uint32_t decode_tile(const Tab& tab, const Geo& geo, 
 template <int RUNS>
 __device__ __forceinline__ void stage_tables(const Tables& t, uint32_t Mw, uint32_t n_planes_words,
                                              bool per_position, uint32_t* lds) {
-    const uint32_t rows = per_position ? tab_rows(RUNS) : 0u;
-    for (uint32_t i = threadIdx.x; i < rows * Mw; i += blockDim.x) {
-        const uint32_t row = i / Mw, pos = i - row * Mw;
-        uint32_t v;
-        if (row == 0)
-            v = t.b[pos];
-        else if (row == 1)
-            v = t.kd[pos];
-        else if (row < 2 + dx_rows(RUNS))
-            v = t.dx[(row - 2) * Mw + pos];
-        else
-            v = t.r[(row - 2 - dx_rows(RUNS)) * Mw + pos];
-        lds[i] = v;
-    }
-    uint32_t* pl = lds + rows * Mw;
-    for (uint32_t i = threadIdx.x; i < n_planes_words; i += blockDim.x) pl[i] = t.planes[i];
+    stage_table_image<dx_rows(RUNS)>(t, 1, per_position ? tab_rows(RUNS) : 0u, Mw, t.planes, n_planes_words, lds);
 }
 
 // ---------------------------------------------------------------------------
@@ -571,6 +556,15 @@ static bool small_lds(const Geo& geo, int runs, bool uni, uint32_t* buf_words, s
     return true;
 }
 
+// Resident waves per SIMD the small-tensor decode keeps at most when the
+// stored items are in device memory.  Short tiles give each wave only a few
+// tiles per launch, and every wave pays a fixed start (table staging, the
+// batch's ids and bitmask words, the first read): with 7 or 8 waves per SIMD,
+// 512-byte and 1 KiB rows in HBM decoded 10-25 % slower than with 4 to 6
+// (measured on MI355X).  Items read over the host link keep every wave the
+// registers allow, since there the reads in flight set the rate.
+constexpr uint32_t kSmallDecodeWavesPerSimdHbm = 5;
+
 template <int RUNS, bool UNI, bool MW4, int S, bool SPLIT>
 static hipError_t launch_small_s(const Tables& t, const Geo& geo, const void* slots, uint64_t n_slots,
                                  const uint32_t* bitmask, const int64_t* ids, uint64_t n_out, void* dst,
@@ -579,7 +573,8 @@ static hipError_t launch_small_s(const Tables& t, const Geo& geo, const void* sl
     const void* fn = reinterpret_cast<const void*>(&k_decode_small<RUNS, UNI, MW4, S, SPLIT>);
     PersistentPlan plan;
     *launched = false;
-    if (!plan_persistent(fn, head, wave, cu_count, n_out, &plan)) return hipSuccess;
+    if (!plan_persistent(fn, head, wave, cu_count, n_out, &plan, geo.src_in_hbm ? kSmallDecodeWavesPerSimdHbm : 8u))
+        return hipSuccess;
     hipLaunchKernelGGL((k_decode_small<RUNS, UNI, MW4, S, SPLIT>), dim3(plan.blocks), dim3(kWave * plan.wpb),
                        plan.shm, s, t, geo, static_cast<const uint8_t*>(slots), n_slots, bitmask, ids, n_out,
                        static_cast<uint8_t*>(dst), err, buf_words, items, headers);

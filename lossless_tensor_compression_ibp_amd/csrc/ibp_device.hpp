@@ -198,6 +198,79 @@ __device__ __forceinline__ uint32_t extract_t(const Tab& tab, uint32_t pos, uint
 __host__ __device__ constexpr uint32_t dx_rows(int runs) { return runs > 3 ? (uint32_t)(runs - 3 + 3) / 4 : 0u; }
 __host__ __device__ constexpr uint32_t tab_rows(int runs) { return 2u + dx_rows(runs) + (uint32_t)runs; }
 
+// Word `e` of rows [row0, row0 + nrows) of the table image m, b, kd, dx rows
+// (DXR of them), r rows, each Mw words, in device memory.  The dx and r rows
+// are each one array, so a word's source takes compares and selects, no
+// division (e differs across lanes).
+template <uint32_t DXR>
+__device__ __forceinline__ const uint32_t* table_image_word(const Tables& t, uint32_t row0, uint32_t Mw,
+                                                            uint32_t e) {
+    const uint32_t a = row0 * Mw + e;  // word of the whole image
+    const uint32_t* p = a < Mw ? t.m + a : t.b + (a - Mw);
+    p = a >= 2 * Mw ? t.kd + (a - 2 * Mw) : p;
+    if (DXR > 0) p = a >= 3 * Mw ? t.dx + (a - 3 * Mw) : p;
+    p = a >= (3 + DXR) * Mw ? t.r + (a - (3 + DXR) * Mw) : p;
+    return p;
+}
+
+// Whole workgroup: rows [row0, row0 + nrows) of the table image into lds,
+// then n_extra words of `extra` right after them.  A thread issues all loads
+// of a round (four 16-byte vectors when Mw is a multiple of 4, else eight
+// words) before its LDS writes, and the first two extra words per thread are
+// loaded ahead of the table rounds, so staging costs one memory latency per
+// round rather than one per element.
+template <uint32_t DXR>
+__device__ __forceinline__ void stage_table_image(const Tables& t, uint32_t row0, uint32_t nrows, uint32_t Mw,
+                                                  const uint32_t* __restrict__ extra, uint32_t n_extra,
+                                                  uint32_t* lds) {
+    const uint32_t tid = threadIdx.x, nt = blockDim.x;
+    const uint32_t tab = nrows * Mw;
+    uint32_t ev[2] = {0u, 0u};
+#pragma unroll
+    for (uint32_t u = 0; u < 2; ++u) {
+        const uint32_t e = u * nt + tid;
+        if (e < n_extra) ev[u] = extra[e];
+    }
+    if ((Mw & 3u) == 0) {
+        const uint32_t nv = tab >> 2;
+        for (uint32_t base = 0; base < nv; base += 4 * nt) {
+            u32x4 v[4];
+#pragma unroll
+            for (uint32_t u = 0; u < 4; ++u) {
+                // past the end: a load of the last vector again (no branch
+                // around the load, so all four stay in flight together)
+                const uint32_t e = min(base + u * nt + tid, nv - 1);
+                v[u] = *reinterpret_cast<const u32x4*>(table_image_word<DXR>(t, row0, Mw, 4 * e));
+            }
+#pragma unroll
+            for (uint32_t u = 0; u < 4; ++u) {
+                const uint32_t e = base + u * nt + tid;
+                if (e < nv) reinterpret_cast<u32x4*>(lds)[e] = v[u];
+            }
+        }
+    } else {
+        for (uint32_t base = 0; base < tab; base += 8 * nt) {
+            uint32_t v[8];
+#pragma unroll
+            for (uint32_t u = 0; u < 8; ++u) {
+                const uint32_t e = min(base + u * nt + tid, tab - 1);
+                v[u] = *table_image_word<DXR>(t, row0, Mw, e);
+            }
+#pragma unroll
+            for (uint32_t u = 0; u < 8; ++u) {
+                const uint32_t e = base + u * nt + tid;
+                if (e < tab) lds[e] = v[u];
+            }
+        }
+    }
+#pragma unroll
+    for (uint32_t u = 0; u < 2; ++u) {
+        const uint32_t e = u * nt + tid;
+        if (e < n_extra) lds[tab + e] = ev[u];
+    }
+    for (uint32_t e = 2 * nt + tid; e < n_extra; e += nt) lds[tab + e] = extra[e];
+}
+
 // ---------------------------------------------------------------------------
 // Memory movement helpers (one wave).
 // ---------------------------------------------------------------------------

@@ -238,21 +238,7 @@ __global__ __launch_bounds__(1024) void k_encode_small(Tables t, Geo geo, const 
     const uint32_t Mw = geo.Mw;
     // LDS: [m row + per-position tables (not for uniform metadata)][wave buffers]
     const uint32_t rows = UNI ? 0u : 1u + tab_rows(RUNS);
-    for (uint32_t i = threadIdx.x; i < rows * Mw; i += blockDim.x) {
-        const uint32_t row = i / Mw, pos = i - row * Mw;
-        uint32_t v;
-        if (row == 0)
-            v = t.m[pos];
-        else if (row == 1)
-            v = t.b[pos];
-        else if (row == 2)
-            v = t.kd[pos];
-        else if (row < 3 + dx_rows(RUNS))
-            v = t.dx[(row - 3) * Mw + pos];
-        else
-            v = t.r[(row - 3 - dx_rows(RUNS)) * Mw + pos];
-        smem[i] = v;
-    }
+    stage_table_image<dx_rows(RUNS)>(t, 0, rows, Mw, nullptr, 0, smem);
     __syncthreads();
     uint32_t* buf = smem + ((rows * Mw + 3u) & ~3u) + wib * buf_words;
     const uint32_t* mrow = smem;

@@ -44,6 +44,7 @@ struct Geo {
     uint64_t tiles_per_tensor;
     uint32_t spec_words;     // first-read words of a single-tile record (multiple of 4)
     uint32_t aligned16;      // slot base and L allow 16-byte vector access
+    uint32_t src_in_hbm;     // decode: stored items in device memory (not read over the host link)
 };
 
 // Decoupled look-back state for multi-tile tensors.  A status word packs
@@ -88,11 +89,12 @@ struct PersistentPlan {
 // Chooses the waves per workgroup (4, 8, 12 or 16, within the kernel's launch
 // bounds) that keeps the most waves resident per compute unit, given LDS
 // shared by a workgroup (head_bytes), LDS per wave (wave_bytes), the kernel's
-// VGPR count and the LDS limits of the device.
+// VGPR count, the LDS limits of the device and at most max_waves_per_simd
+// resident waves per SIMD.
 // blocks = min(workgroups that fill the device, items / wpb).  Returns false
 // when no shape fits.
 bool plan_persistent(const void* kernel, size_t head_bytes, size_t wave_bytes, uint32_t cu_count,
-                     uint64_t n_items, PersistentPlan* plan);
+                     uint64_t n_items, PersistentPlan* plan, uint32_t max_waves_per_simd = 8);
 
 // Kernel launchers.  All return hipError_t of the launch.
 hipError_t launch_fill_u32(uint32_t* p, uint64_t n, uint32_t v, hipStream_t s);

@@ -187,10 +187,11 @@ struct PlanKey {
     const void* kernel;
     size_t head, wave;
     uint32_t cu_count;
+    uint32_t max_per_simd;
     int device;
     bool operator==(const PlanKey& o) const {
         return kernel == o.kernel && head == o.head && wave == o.wave && cu_count == o.cu_count &&
-               device == o.device;
+               max_per_simd == o.max_per_simd && device == o.device;
     }
 };
 struct PlanKeyHash {
@@ -198,12 +199,12 @@ struct PlanKeyHash {
         size_t h = std::hash<const void*>()(k.kernel);
         h = h * 1000003u ^ std::hash<size_t>()(k.head);
         h = h * 1000003u ^ std::hash<size_t>()(k.wave);
-        return h * 1000003u ^ (size_t)k.cu_count ^ ((size_t)k.device << 20);
+        return h * 1000003u ^ (size_t)k.cu_count ^ ((size_t)k.max_per_simd << 12) ^ ((size_t)k.device << 20);
     }
 };
 
 static bool plan_uncached(const void* kernel, size_t head_bytes, size_t wave_bytes, uint32_t cu_count,
-                          PersistentPlan* plan) {
+                          uint32_t max_per_simd, PersistentPlan* plan) {
     hipFuncAttributes attr;
     uint32_t vgprs = 64, max_threads = 256;
     if (hipFuncGetAttributes(&attr, kernel) == hipSuccess) {
@@ -219,6 +220,7 @@ static bool plan_uncached(const void* kernel, size_t head_bytes, size_t wave_byt
     // 512 VGPRs per SIMD lane, at most 8 waves per SIMD, 4 SIMDs per CU
     uint32_t per_simd = 512 / ((vgprs + 7) & ~7u);
     if (per_simd > 8) per_simd = 8;
+    if (per_simd > max_per_simd) per_simd = max_per_simd;
     if (per_simd < 1) per_simd = 1;
     const uint32_t cu_waves = 4 * per_simd;
     PersistentPlan best;
@@ -253,12 +255,12 @@ static bool plan_uncached(const void* kernel, size_t head_bytes, size_t wave_byt
 }
 
 bool plan_persistent(const void* kernel, size_t head_bytes, size_t wave_bytes, uint32_t cu_count,
-                     uint64_t n_items, PersistentPlan* plan) {
+                     uint64_t n_items, PersistentPlan* plan, uint32_t max_waves_per_simd) {
     static std::mutex mu;
     static std::unordered_map<PlanKey, std::pair<bool, PersistentPlan>, PlanKeyHash> cache;
     int dev = 0;
     (void)hipGetDevice(&dev);
-    const PlanKey key{kernel, head_bytes, wave_bytes, cu_count, dev};
+    const PlanKey key{kernel, head_bytes, wave_bytes, cu_count, max_waves_per_simd, dev};
     std::pair<bool, PersistentPlan> entry;
     {
         std::lock_guard<std::mutex> lock(mu);
@@ -266,7 +268,7 @@ bool plan_persistent(const void* kernel, size_t head_bytes, size_t wave_bytes, u
         if (it != cache.end()) {
             entry = it->second;
         } else {
-            entry.first = plan_uncached(kernel, head_bytes, wave_bytes, cu_count, &entry.second);
+            entry.first = plan_uncached(kernel, head_bytes, wave_bytes, cu_count, max_waves_per_simd, &entry.second);
             cache.emplace(key, entry);
         }
     }
