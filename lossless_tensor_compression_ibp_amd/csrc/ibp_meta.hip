@@ -274,8 +274,15 @@ bool plan_persistent(const void* kernel, size_t head_bytes, size_t wave_bytes, u
     }
     if (!entry.first) return false;
     PersistentPlan p = entry.second;
+    // Beyond kMaxItemsPerWave items per resident wave the launch adds
+    // workgroups past the resident fill; the hardware dispatches them as
+    // earlier ones retire, and each re-stages the tables once.
     const uint64_t want = (n_items + p.wpb - 1) / p.wpb;
-    if (want < p.blocks) p.blocks = (uint32_t)want;
+    const uint64_t cap = (n_items + (uint64_t)p.wpb * kMaxItemsPerWave - 1) / ((uint64_t)p.wpb * kMaxItemsPerWave);
+    uint64_t blocks = cap > p.blocks ? cap : (uint64_t)p.blocks;
+    if (blocks > want) blocks = want;
+    if (blocks > 0x7fffffffull) blocks = 0x7fffffffull;
+    p.blocks = (uint32_t)blocks;
     *plan = p;
     return true;
 }
