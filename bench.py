@@ -376,7 +376,7 @@ def run_kv_bf16(args) -> dict:
         args, n * L * args.steps / wall / GB, wall,
         {"workload": f"kv_bf16: {layers} layers x 32 heads x 4096 tokens x 128 bf16, 4 KiB pages in HBM slots, "
                      f"W=32, M=32768, T=0.95, decode of all {n} pages per step", "pages": n, "tensor_bytes": L},
-        savings, "ibp::k_decode_small<3, false, true, 4>", durs, roof,
+        savings, "ibp::k_decode_small<3, false, true, 4, false>", durs, roof,
         encode_GBps=round(n * L / float(np.mean(enc_durs)) / GB, 3), metadata_ms=round(t_meta * 1e3, 2),
         meta=ibp.ibp_meta_get_info(meta))
 
@@ -450,7 +450,7 @@ def run_dense_gnn(args) -> dict:
         args, n * L * args.steps / wall / GB, wall,
         {"workload": f"dense_gnn: {n} rows x 128 fp32 |N(0,0.5)| with 3% N(0,50) rows, W=32, M=4096, T=0.95, "
                      f"slots in HBM, contiguous decode of all rows per step", "rows": n, "tensor_bytes": L},
-        savings, "ibp::k_decode_small", durs, hbm_roofline(hbm_bytes, durs, "dense_gnn"),
+        savings, "ibp::k_decode_small<1, false, true, 1, false>", durs, hbm_roofline(hbm_bytes, durs, "dense_gnn"),
         encode_GBps=round(n * L / float(np.mean(enc_durs)) / GB, 3),
         uncompressed_hbm_copy_GBps=round(n * L * args.steps / raw_wall / GB, 3),
         uncompressed_copy_kernel_us=round(float(np.mean(raw_durs)) * 1e6, 2), meta=ibp.ibp_meta_get_info(meta))
@@ -498,7 +498,8 @@ def run_dlrm(args) -> dict:
         {"workload": f"dlrm: {n} rows x 128 fp32 U(-0.01,0.01), W=32, M=4096, T=0.9, slots in pinned host "
                      f"memory, {per_step} zero-copy gathers of {batch} random ids (with replacement) per step",
          "rows": n, "tensor_bytes": L, "batch_ids": batch, "gathers_per_step": per_step},
-        savings, "ibp::k_decode_small", durs, link_roofline(link, durs, savings, None if args.small else "dlrm"),
+        savings, "ibp::k_decode_small<2, true, true, 1, false>", durs,
+        link_roofline(link, durs, savings, None if args.small else "dlrm"),
         encode_GBps=round(n * L / t_enc / GB, 3), meta=ibp.ibp_meta_get_info(meta))
 
 
@@ -570,7 +571,7 @@ def run_llm_bf16(args) -> dict:
                      f"T=0.95, slots in pinned host memory, each layer decoded zero-copy into HBM on one stream "
                      f"while a consumer (y = x @ W) reads the previous layer on another", "layers": layers,
          "tensor_bytes": L},
-        savings, "ibp::k_decode_tiles (look-back)", durs,
+        savings, "ibp::k_decode_tiles<3, true, true> (look-back)", durs,
         link_roofline(link, durs, savings, None if args.small else "llm_bf16"),
         encode_GBps=round(layers * L / t_enc / GB, 3), meta=ibp.ibp_meta_get_info(meta))
 
@@ -640,7 +641,7 @@ def run_sparse_gnn_cache(args) -> dict:
                      f"compressed into one packed HBM buffer (items back to back, 16-byte aligned), gather of "
                      f"{batch} distinct random row ids per step into HBM", "rows": n, "tensor_bytes": L,
          "batch_ids": batch},
-        1.0 - total / (n * L), "ibp::k_decode_small (packed items)", durs,
+        1.0 - total / (n * L), "ibp::k_decode_small<0, true, true, 1, false> (packed items)", durs,
         hbm_roofline(hbm_bytes, durs, None if args.small else "sparse_gnn_cache"),
         cache_bytes=total, capacity_gain=round(n * L / total, 4),
         fill_GBps=round(n * L / float(np.median(fill_s)) / GB, 3),
