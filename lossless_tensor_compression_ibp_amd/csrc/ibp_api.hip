@@ -1,6 +1,7 @@
 // ibp_api.hip -- host side of libibp: argument checks, the metadata handle,
 // per-stream look-back scratch, and kernel dispatch.  The C ABI is declared
-// in include/ibp.h; every step of the codec runs in ibp_kernels.hip.
+// in include/ibp.h; every step of the codec runs in the kernels of
+// ibp_meta.hip, ibp_encode.hip and ibp_decode.hip.
 #include <hip/hip_runtime.h>
 #include <math.h>
 #include <stdint.h>

@@ -12,7 +12,7 @@
 // and only the record prefix of a slot is read.
 //
 // Layout of the work: one wave64 decodes one tile (all of a tensor of at most
-// 2048 words, or a 1024-word tile of a longer one).  A lane rebuilds four
+// 2048 words, or a 2048-word tile of a longer one).  A lane rebuilds four
 // consecutive 32-bit words per step (256 words per wave step), so a step
 // costs one DPP scan and one dwordx4 store per lane.
 #include <hip/hip_runtime.h>
@@ -197,6 +197,15 @@ __global__ __launch_bounds__(256) void k_decode_small(Tables t, Geo geo, const u
     // LDS: [per-position tables (not for uniform metadata)][bit planes][wave buffers]
     const uint32_t tab_words = UNI ? 0u : tab_rows(RUNS) * Mw;
     const uint32_t planes_words = (geo.Pc / geo.G) * (uint32_t)kPlanes;
+    const uint32_t wpb = blockDim.x / kWave;
+    const uint64_t stride = (uint64_t)gridDim.x * wpb;
+    const uint64_t first = (uint64_t)blockIdx.x * wpb + wib;
+    const uint64_t my_tiles = first < n_out ? (n_out - first + stride - 1) / stride : 0;
+    // A gather fetches the ids of the wave's first 64 tiles before the tables
+    // are staged: the staging loads are issued after it, so waiting for them
+    // also covers it, and the two latencies overlap.
+    int64_t first_id = -1;
+    if (ids && lane < min((uint64_t)kWave, my_tiles)) first_id = ids[first + lane * stride];
     stage_tables<RUNS>(t, Mw, planes_words, !UNI, smem);
     __syncthreads();
     const uint32_t* planes = smem + tab_words;
@@ -209,11 +218,7 @@ __global__ __launch_bounds__(256) void k_decode_small(Tables t, Geo geo, const u
     const uint32_t n4_raw = nwords >> 2;
     const uint32_t n4_spec = geo.spec_words >> 2;
     const uint32_t hw = (uint32_t)geo.hdr_words;
-    const uint32_t wpb = blockDim.x / kWave;
-    const uint64_t stride = (uint64_t)gridDim.x * wpb;
-    const uint64_t first = (uint64_t)blockIdx.x * wpb + wib;
     if (first >= n_out) return;
-    const uint64_t my_tiles = (n_out - first + stride - 1) / stride;
 
     u32x4 st[STAGE];
     for (uint64_t base = 0; base < my_tiles; base += kWave) {
@@ -228,7 +233,7 @@ __global__ __launch_bounds__(256) void k_decode_small(Tables t, Geo geo, const u
         uint32_t my_len = 0;
         if (lane < cnt) {
             const uint64_t oi = first + (base + lane) * stride;
-            const int64_t id = ids ? ids[oi] : (int64_t)oi;
+            const int64_t id = ids ? (base == 0 ? first_id : ids[oi]) : (int64_t)oi;
             if (id >= 0 && (uint64_t)id < n_slots) {
                 my_tensor = id;
                 if (packed) {
