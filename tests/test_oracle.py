@@ -162,18 +162,20 @@ def _submasks(m: int):
         s = (s - 1) & m
 
 
-@pytest.mark.parametrize("W,periods", [(1, 1), (2, 1), (3, 1), (4, 1), (5, 1), (6, 1), (2, 2), (3, 2), (4, 2)])
-def test_exhaustive_tiny_chunks(W, periods, bmi2):
-    """Every (Mask, Bitval subset of Mask) pair and every two-chunk tensor:
-    round trip, header = match test, record length formula, verbatim rule,
-    and matched payload = PEXT of the chunk."""
+@pytest.mark.parametrize("W,periods,n_chunks", [(1, 1, 2), (2, 1, 2), (3, 1, 2), (4, 1, 2), (5, 1, 2), (6, 1, 2),
+                                                (2, 2, 2), (3, 2, 2), (4, 2, 2), (7, 1, 1), (8, 1, 1)])
+def test_exhaustive_tiny_chunks(W, periods, n_chunks, bmi2):
+    """Every (Mask, Bitval subset of Mask) pair and every tensor of n_chunks
+    chunks (two chunks up to W = 6, one chunk at W = 7 and 8: 6,561 pairs x
+    256 values): round trip, header = match test, record length formula,
+    verbatim rule, and matched payload = PEXT of the chunk."""
     M = W * periods
-    tb = 2 * W
+    tb = n_chunks * W
     full = (1 << W) - 1
     v = np.arange(1 << tb, dtype=np.uint64)
     nbytes = (tb + 7) // 8
     xs = np.stack([((v >> np.uint64(8 * i)) & np.uint64(0xFF)).astype(np.uint8) for i in range(nbytes)], axis=1)
-    xc = [((v >> np.uint64(c * W)) & np.uint64(full)).astype(np.uint32) for c in range(2)]
+    xc = [((v >> np.uint64(c * W)) & np.uint64(full)).astype(np.uint32) for c in range(n_chunks)]
     n_pairs = 0
     for mask_int in range(1 << M):
         for bv_int in _submasks(mask_int):
@@ -184,11 +186,12 @@ def test_exhaustive_tiny_chunks(W, periods, bmi2):
             rv = recs.view(np.uint64).reshape(-1)  # records fit in 64 bits here
             back = O.decode_records(recs, tb, W, M, mask, bitval)
             np.testing.assert_array_equal(back, xs)
-            assert np.all((rv >> np.uint64(2)) & np.uint64(0x3FFFFFFF) == 0)  # header padding
+            pad = np.uint64((1 << (32 - n_chunks)) - 1)
+            assert np.all((rv >> np.uint64(n_chunks)) & pad == 0)  # header padding
             payload = rv >> np.uint64(32)
             offset = np.zeros_like(v)
             expect_R = np.full(v.shape, 32, np.uint64)
-            for c in range(2):
+            for c in range(n_chunks):
                 mc = (mask_int >> ((c * W) % M)) & full
                 bc = (bv_int >> ((c * W) % M)) & full
                 k = bin(mc).count("1")
