@@ -310,3 +310,47 @@ def test_pageable_host_memory_is_rejected():
         ibp.ibp_compress(meta, src, n, slots, bm)
     assert e.value.status == ibp.IBP_ERR_INVALID_ARG
     say("[parity] pageable rejected ok")
+
+
+# --------------------------------------------------------------------------
+# Metadata at the threshold boundary ("Algorithme central", step 1)
+# --------------------------------------------------------------------------
+@pytest.mark.parametrize("T,n,L,M", [
+    (0.95, 1024, 64, 512),    # K = ceil(972.8) = 973
+    (0.9, 1024, 64, 512),     # K = 922
+    (0.75, 1024, 64, 512),    # T * n exact: K = 768
+    (0.56, 25, 64, 512),      # 0.56 * 25 = 14.000000000000002 in double: K = 15 (14 in exact arithmetic)
+    (0.5000001, 7, 64, 512),  # K = 4: a strict majority is invariant
+    (1.0, 1000, 64, 512),     # only unanimous positions
+    (0.95, 1024, 4, 32),      # one word per tensor
+])
+def test_metadata_threshold_boundaries(T, n, L, M):
+    """Per-position counts of ones placed at K - 1, K, K + 1, their
+    complements, 0 and n; Mask = (max(ones, zeros) >= K), Bitval = the
+    majority value where Mask is set, K = ceil(T * n) with the product in
+    IEEE double.  GPU against that rule and against the oracle."""
+    K = int(np.ceil(T * float(n)))
+    bits_per = 8 * L
+    assert M == bits_per  # one observation per sampled tensor
+    interesting = sorted({c for c in (0, 1, n - K - 1, n - K, n - K + 1, K - 1, K, K + 1, n - 1, n) if 0 <= c <= n})
+    rng = np.random.default_rng(n + L)
+    counts = np.array([interesting[j % len(interesting)] for j in range(bits_per)])
+    rng.shuffle(counts)
+    bits = np.zeros((n, bits_per), np.uint8)
+    for j, c in enumerate(counts):
+        bits[rng.permutation(n)[:c], j] = 1
+    sample = np.packbits(bits, axis=1, bitorder="little")
+    assert sample.shape == (n, L)
+    exp_mask = (np.maximum(counts, n - counts) >= K).astype(np.uint8)
+    exp_bitval = exp_mask & (counts > n - counts).astype(np.uint8)
+    exp_mask_b = np.packbits(exp_mask, bitorder="little")
+    exp_bitval_b = np.packbits(exp_bitval, bitorder="little")
+    say(f"[metadata] T={T} n={n} K={K} L={L} M={M} counts={interesting}")
+    meta = ibp.ibp_build_metadata(to_gpu(sample), n, L, 32, M, T)
+    _, g_mask, g_bitval = ibp.ibp_meta_get(meta)
+    np.testing.assert_array_equal(g_mask.view(np.uint8), exp_mask_b, err_msg="Mask differs from the rule")
+    np.testing.assert_array_equal(g_bitval.view(np.uint8), exp_bitval_b, err_msg="Bitval differs from the rule")
+    o_mask, o_bitval = oracle.build_metadata(sample, 8 * L, 32, M, T, n)
+    np.testing.assert_array_equal(o_mask, exp_mask_b)
+    np.testing.assert_array_equal(o_bitval, exp_bitval_b)
+    meta.close()
