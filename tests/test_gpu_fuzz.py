@@ -140,3 +140,90 @@ def test_random_format(seed):
     np.testing.assert_array_equal(gout.cpu().numpy(), raw[ids], err_msg="gather of oracle slots differs")
     say(f"[fuzz] seed={seed} ok: {int(comp.sum())} of {n} compressed, runs={ibp.ibp_meta_get_info(meta)['max_runs']}")
     meta.close()
+
+
+def _layout_applies(c, max_header_words=None) -> bool:
+    """The packed and header-in-GPU-memory layouts take 16-byte aligned
+    tensors of one tile (at most 2,048 words)."""
+    if c["L"] % 16 or c["L"] // 4 > 2048:
+        return False
+    return max_header_words is None or oracle.header_words(c["L"], c["W"]) <= max_header_words
+
+
+def _or_skip_unsupported(fn, *a, **k):
+    try:
+        fn(*a, **k)
+    except ibp.IBPError as e:
+        if e.status == ibp.IBP_ERR_UNSUPPORTED:
+            pytest.skip("metadata tables beyond the packed layout's LDS limit")
+        raise
+
+
+@pytest.mark.parametrize("seed", range(N_CASES))
+def test_random_format_packed(seed):
+    c = make_case(seed)
+    if not _layout_applies(c):
+        pytest.skip("the packed layout takes 16-byte aligned single-tile tensors")
+    W, M, L, n, raw = c["W"], c["M"], c["L"], c["n"], c["raw"]
+    say(f"[fuzz packed] seed={seed} W={W} M={M} L={L} n={n} mask={c['kind']} q={c['q']} pinned={c['pinned']}")
+    dev = device()
+    meta = ibp.ibp_meta_create(L, W, M, c["mask"], c["bitval"])
+    mb, bb = c["mask"].view(np.uint8), c["bitval"].view(np.uint8)
+    src = to_gpu(raw, pinned=c["pinned"])
+    off = torch.full((n + 1,), -1, dtype=torch.int64, device=dev)
+    _or_skip_unsupported(ibp.ibp_packed_offsets, meta, src, n, off)
+    o_buf, o_off, o_bm = oracle.compress_packed(raw, L, W, M, mb, bb, n)
+    np.testing.assert_array_equal(off.cpu().numpy().astype(np.uint64), o_off, err_msg="offsets differ")
+    total = int(o_off[-1])
+    cap = total + 64
+    buf = torch.full((cap,), 0xEE, dtype=torch.uint8, pin_memory=True) if c["pinned"] else \
+        torch.full((cap,), 0xEE, dtype=torch.uint8, device=dev)
+    bm = torch.zeros(max(1, (n + 31) // 32), dtype=torch.int32, device=dev)
+    ibp.ibp_compress_packed(meta, src, n, off, buf, bm, capacity=cap)
+    assert ibp.ibp_check(meta) == ibp.IBP_OK
+    b = buf.cpu().numpy()
+    np.testing.assert_array_equal(b[:total], o_buf[:total], err_msg="packed bytes differ")
+    assert (b[total:] == 0xEE).all(), "wrote past the last item"
+    np.testing.assert_array_equal(bm.cpu().numpy().view(np.uint32)[: o_bm.size], o_bm, err_msg="bitmask differs")
+    ids = c["ids"]
+    g = torch.empty((ids.size, L), dtype=torch.uint8, device=dev)
+    ibp.ibp_gather_decompress_packed(meta, buf, off, n, bm, torch.from_numpy(ids).to(dev), g, buf_bytes=cap)
+    assert ibp.ibp_check(meta) == ibp.IBP_OK
+    np.testing.assert_array_equal(g.cpu().numpy(), raw[ids], err_msg="packed gather differs")
+    meta.close()
+
+
+@pytest.mark.parametrize("seed", range(N_CASES))
+def test_random_format_split(seed):
+    c = make_case(seed)
+    if not _layout_applies(c, max_header_words=4):
+        pytest.skip("headers in GPU memory take 16-byte aligned single-tile tensors of at most 128 chunks")
+    W, M, L, n, raw = c["W"], c["M"], c["L"], c["n"], c["raw"]
+    hw = oracle.header_words(L, W)
+    say(f"[fuzz split] seed={seed} W={W} M={M} L={L} n={n} hw={hw} mask={c['kind']} q={c['q']} pinned={c['pinned']}")
+    dev = device()
+    meta = ibp.ibp_meta_create(L, W, M, c["mask"], c["bitval"])
+    mb, bb = c["mask"].view(np.uint8), c["bitval"].view(np.uint8)
+    src = to_gpu(raw)
+    slots = torch.full((n, L), 0xEE, dtype=torch.uint8, pin_memory=True) if c["pinned"] else \
+        torch.full((n, L), 0xEE, dtype=torch.uint8, device=dev)
+    headers = torch.full((n, hw), -1, dtype=torch.int32, device=dev)
+    bm = torch.zeros(max(1, (n + 31) // 32), dtype=torch.int32, device=dev)
+    stored = torch.zeros(n, dtype=torch.int64, device=dev)
+    _or_skip_unsupported(ibp.ibp_compress_split, meta, src, n, slots, headers, bm, stored)
+    torch.cuda.synchronize()
+    o_slots, o_hdr, o_bm, o_st = oracle.compress_split(raw, L, W, M, mb, bb, n)
+    np.testing.assert_array_equal(bm.cpu().numpy().view(np.uint32)[: o_bm.size], o_bm, err_msg="bitmask differs")
+    np.testing.assert_array_equal(headers.cpu().numpy().view(np.uint32), o_hdr, err_msg="header words differ")
+    st = stored.cpu().numpy().astype(np.uint64)
+    np.testing.assert_array_equal(st, o_st, err_msg="stored bytes differ")
+    sl = slots.cpu().numpy()
+    for t in range(n):
+        k = int(st[t])
+        np.testing.assert_array_equal(sl[t, :k], o_slots[t, :k], err_msg=f"slot {t} differs")
+    ids = c["ids"]
+    g = torch.empty((ids.size, L), dtype=torch.uint8, device=dev)
+    ibp.ibp_gather_decompress_split(meta, slots, n, headers, bm, torch.from_numpy(ids).to(dev), g)
+    assert ibp.ibp_check(meta) == ibp.IBP_OK
+    np.testing.assert_array_equal(g.cpu().numpy(), raw[ids], err_msg="split gather differs")
+    meta.close()
