@@ -44,20 +44,38 @@ def _mask_word(rng, kind: str) -> int:
     return m
 
 
-def make_case(seed: int):
-    """A random format and n tensors whose chunks match at a chosen rate."""
-    rng = np.random.default_rng(10_000 + seed)
+def _format(rng, layout):
+    """Chunk width, chunks per tensor and period (in chunks).  The packed
+    and header-in-GPU-memory layouts take 16-byte aligned tensors of one tile
+    (headers in GPU memory: at most 128 chunks) with tables in LDS."""
     W = int(rng.choice([32, 64, 128, 256, 512, 1024]))
     g = W // 32
-    shape = rng.choice(["small", "small", "small", "multi"])
-    if shape == "multi":
-        n_chunks = int(rng.integers(2049 // g + 1, 9000 // g + 2))
+    if layout is None:
+        shape = rng.choice(["small", "small", "small", "multi"])
+        if shape == "multi":
+            n_chunks = int(rng.integers(2049 // g + 1, 9000 // g + 2))
+        else:
+            n_chunks = int(rng.integers(1, max(2, 2048 // g) + 1))
+        max_m = 1 << 20
     else:
-        n_chunks = int(rng.integers(1, max(2, 2048 // g) + 1))
+        step = max(1, 4 // g)  # whole 16-byte vectors
+        top = min(2048 // g, 128 if layout == "split" else 2048 // g)
+        n_chunks = step * int(rng.integers(1, top // step + 1))
+        max_m = 8192
+    divisors = [d for d in range(1, n_chunks + 1) if n_chunks % d == 0 and d * W <= max_m]
+    if not divisors:
+        divisors = [1]
+    d = int(rng.choice(divisors[:12] + divisors[-3:]))
+    return W, n_chunks, d
+
+
+def make_case(seed: int, layout: str | None = None):
+    """A random format and n tensors whose chunks match at a chosen rate."""
+    rng = np.random.default_rng((10_000 if layout is None else 20_000 if layout == "packed" else 30_000) + seed)
+    W, n_chunks, d = _format(rng, layout)
+    g = W // 32
     n_words = n_chunks * g
     L = 4 * n_words
-    divisors = [d for d in range(1, n_chunks + 1) if n_chunks % d == 0 and d * W <= 1 << 20]
-    d = int(rng.choice(divisors[:12] + divisors[-3:]))
     M = d * W
     Mw = M // 32
     kind = str(rng.choice(["none", "all", "high", "dense", "few", "mixed", "uniform"]))
@@ -150,20 +168,10 @@ def _layout_applies(c, max_header_words=None) -> bool:
     return max_header_words is None or oracle.header_words(c["L"], c["W"]) <= max_header_words
 
 
-def _or_skip_unsupported(fn, *a, **k):
-    try:
-        fn(*a, **k)
-    except ibp.IBPError as e:
-        if e.status == ibp.IBP_ERR_UNSUPPORTED:
-            pytest.skip("metadata tables beyond the packed layout's LDS limit")
-        raise
-
-
 @pytest.mark.parametrize("seed", range(N_CASES))
 def test_random_format_packed(seed):
-    c = make_case(seed)
-    if not _layout_applies(c):
-        pytest.skip("the packed layout takes 16-byte aligned single-tile tensors")
+    c = make_case(seed, "packed")
+    assert _layout_applies(c)
     W, M, L, n, raw = c["W"], c["M"], c["L"], c["n"], c["raw"]
     say(f"[fuzz packed] seed={seed} W={W} M={M} L={L} n={n} mask={c['kind']} q={c['q']} pinned={c['pinned']}")
     dev = device()
@@ -171,7 +179,7 @@ def test_random_format_packed(seed):
     mb, bb = c["mask"].view(np.uint8), c["bitval"].view(np.uint8)
     src = to_gpu(raw, pinned=c["pinned"])
     off = torch.full((n + 1,), -1, dtype=torch.int64, device=dev)
-    _or_skip_unsupported(ibp.ibp_packed_offsets, meta, src, n, off)
+    ibp.ibp_packed_offsets(meta, src, n, off)
     o_buf, o_off, o_bm = oracle.compress_packed(raw, L, W, M, mb, bb, n)
     np.testing.assert_array_equal(off.cpu().numpy().astype(np.uint64), o_off, err_msg="offsets differ")
     total = int(o_off[-1])
@@ -195,9 +203,8 @@ def test_random_format_packed(seed):
 
 @pytest.mark.parametrize("seed", range(N_CASES))
 def test_random_format_split(seed):
-    c = make_case(seed)
-    if not _layout_applies(c, max_header_words=4):
-        pytest.skip("headers in GPU memory take 16-byte aligned single-tile tensors of at most 128 chunks")
+    c = make_case(seed, "split")
+    assert _layout_applies(c, max_header_words=4)
     W, M, L, n, raw = c["W"], c["M"], c["L"], c["n"], c["raw"]
     hw = oracle.header_words(L, W)
     say(f"[fuzz split] seed={seed} W={W} M={M} L={L} n={n} hw={hw} mask={c['kind']} q={c['q']} pinned={c['pinned']}")
@@ -210,7 +217,7 @@ def test_random_format_split(seed):
     headers = torch.full((n, hw), -1, dtype=torch.int32, device=dev)
     bm = torch.zeros(max(1, (n + 31) // 32), dtype=torch.int32, device=dev)
     stored = torch.zeros(n, dtype=torch.int64, device=dev)
-    _or_skip_unsupported(ibp.ibp_compress_split, meta, src, n, slots, headers, bm, stored)
+    ibp.ibp_compress_split(meta, src, n, slots, headers, bm, stored)
     torch.cuda.synchronize()
     o_slots, o_hdr, o_bm, o_st = oracle.compress_split(raw, L, W, M, mb, bb, n)
     np.testing.assert_array_equal(bm.cpu().numpy().view(np.uint32)[: o_bm.size], o_bm, err_msg="bitmask differs")
