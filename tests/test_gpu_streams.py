@@ -76,3 +76,58 @@ def test_single_tile_decode_in_a_graph():
         assert torch.equal(out, src[torch.from_numpy(new_ids).to(dev)]), f"replay {r}"
     assert ibp.ibp_check(meta) == ibp.IBP_OK
     say("[graph] five replays of a captured gather: ok")
+
+
+@pytest.mark.parametrize("layout", ["split", "packed"])
+def test_layout_gathers_in_a_graph(layout):
+    """The gathers of the header-in-GPU-memory layout (pinned slots, as the
+    sparse_gnn line) and of the packed HBM cache captured in a HIP graph and
+    replayed five times with new ids, eager work and synchronisations between
+    the replays; every replay checked against the source rows."""
+    dev = device()
+    w = WL.SPARSE_GNN
+    raw = as_rows(WL.sparse_gnn(4096))
+    n, L = raw.shape
+    src = torch.from_numpy(raw).to(dev)
+    meta = ibp.ibp_build_metadata(src, 1024, L, w.chunk_bits, w.period_bits, w.threshold)
+    bm = torch.zeros((n + 31) // 32, dtype=torch.int32, device=dev)
+    if layout == "split":
+        hw = ibp.header_words(meta)
+        slots = torch.empty((n, L), dtype=torch.uint8, pin_memory=True)
+        headers = torch.zeros((n, hw), dtype=torch.int32, device=dev)
+        ibp.ibp_compress_split(meta, src, n, slots, headers, bm)
+    else:
+        off = torch.zeros(n + 1, dtype=torch.int64, device=dev)
+        ibp.ibp_packed_offsets(meta, src, n, off)
+        buf = torch.empty(int(off[-1].item()), dtype=torch.uint8, device=dev)
+        ibp.ibp_compress_packed(meta, src, n, off, buf, bm)
+    torch.cuda.synchronize()
+    ids = torch.zeros(1024, dtype=torch.int64, device=dev)
+    out = torch.empty((1024, L), dtype=torch.uint8, device=dev)
+
+    def gather(s):
+        if layout == "split":
+            ibp.ibp_gather_decompress_split(meta, slots, n, headers, bm, ids, out, stream=s)
+        else:
+            ibp.ibp_gather_decompress_packed(meta, buf, off, n, bm, ids, out, stream=s)
+
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):  # warm up (launch plans, code objects) outside the capture
+        gather(s)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        gather(s)
+    rng = np.random.default_rng(5)
+    for r in range(5):
+        new_ids = rng.integers(0, n, 1024)
+        ids.copy_(torch.from_numpy(new_ids).to(dev))
+        out.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, src[torch.from_numpy(new_ids).to(dev)]), f"{layout} replay {r}"
+    assert ibp.ibp_check(meta) == ibp.IBP_OK
+    say(f"[graph] five replays of a captured {layout} gather: ok")
