@@ -131,3 +131,75 @@ def test_layout_gathers_in_a_graph(layout):
         assert torch.equal(out, src[torch.from_numpy(new_ids).to(dev)]), f"{layout} replay {r}"
     assert ibp.ibp_check(meta) == ibp.IBP_OK
     say(f"[graph] five replays of a captured {layout} gather: ok")
+
+
+def test_two_threads_two_handles():
+    """Two host threads call the library at the same time, each with its own
+    handle and stream: one gathers rows of the header-in-GPU-memory layout,
+    the other decodes multi-tile tensors (look-back scratch).  The launch-plan
+    cache and the handles' scratch are shared host state; every output is
+    checked."""
+    import threading
+
+    dev = device()
+    w = WL.SPARSE_GNN
+    raw_a = as_rows(WL.sparse_gnn(4096))
+    na, La = raw_a.shape
+    src_a = torch.from_numpy(raw_a).to(dev)
+    meta_a = ibp.ibp_build_metadata(src_a, 1024, La, w.chunk_bits, w.period_bits, w.threshold)
+    hw = ibp.header_words(meta_a)
+    slots_a = torch.empty((na, La), dtype=torch.uint8, pin_memory=True)
+    headers = torch.zeros((na, hw), dtype=torch.int32, device=dev)
+    bm_a = torch.zeros((na + 31) // 32, dtype=torch.int32, device=dev)
+    ibp.ibp_compress_split(meta_a, src_a, na, slots_a, headers, bm_a)
+
+    wl = WL.LLM_BF16
+    raw_b = np.stack([WL.llm_layer(l, rows=48).reshape(-1).view(np.uint8) for l in range(4)])
+    nb, Lb = raw_b.shape
+    src_b = torch.from_numpy(raw_b).to(dev)
+    meta_b = ibp.ibp_build_metadata(src_b, 1, Lb, wl.chunk_bits, wl.period_bits, wl.threshold)
+    slots_b = torch.empty_like(src_b)
+    bm_b = torch.zeros(1, dtype=torch.int32, device=dev)
+    ibp.ibp_compress(meta_b, src_b, nb, slots_b, bm_b)
+    torch.cuda.synchronize()
+
+    sa, sb = torch.cuda.Stream(), torch.cuda.Stream()
+    rng = np.random.default_rng(6)
+    id_sets = [rng.integers(0, na, 2048) for _ in range(20)]
+    outs_a = [torch.empty((2048, La), dtype=torch.uint8, device=dev) for _ in range(20)]
+    outs_b = [torch.empty((nb, Lb), dtype=torch.uint8, device=dev) for _ in range(20)]
+    ids_dev = [torch.from_numpy(x).to(dev) for x in id_sets]
+    errors = []
+    start = threading.Barrier(2)
+
+    def run_a():
+        try:
+            start.wait()
+            for i in range(20):
+                ibp.ibp_gather_decompress_split(meta_a, slots_a, na, headers, bm_a, ids_dev[i], outs_a[i], stream=sa)
+            sa.synchronize()
+        except Exception as e:  # reported by the main thread
+            errors.append(e)
+
+    def run_b():
+        try:
+            start.wait()
+            for i in range(20):
+                ibp.ibp_decompress(meta_b, slots_b, bm_b, nb, outs_b[i], stream=sb)
+            sb.synchronize()
+        except Exception as e:
+            errors.append(e)
+
+    ta, tb = threading.Thread(target=run_a), threading.Thread(target=run_b)
+    ta.start()
+    tb.start()
+    ta.join(timeout=60)
+    tb.join(timeout=60)
+    assert not ta.is_alive() and not tb.is_alive(), "a thread did not finish"
+    assert not errors, errors
+    torch.cuda.synchronize()
+    assert ibp.ibp_check(meta_a) == ibp.IBP_OK and ibp.ibp_check(meta_b) == ibp.IBP_OK
+    for i in range(20):
+        assert torch.equal(outs_a[i], src_a[ids_dev[i]]), f"thread A call {i}"
+        assert torch.equal(outs_b[i], src_b), f"thread B call {i}"
+    say("[threads] two threads, two handles, two streams: ok")
