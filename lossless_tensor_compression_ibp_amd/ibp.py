@@ -98,6 +98,25 @@ def _check(status: int, what: str):
         raise IBPError(status, what)
 
 
+def _need(t: torch.Tensor | None, nbytes: int, what: str):
+    """Buffers reach the library as plain pointers: check here that each one
+    holds what the call will read or write."""
+    if t is not None and t.nbytes < nbytes:
+        raise ValueError(f"{what} holds {t.nbytes} bytes, the call needs {nbytes}")
+
+
+def _bitmask_bytes(n: int) -> int:
+    return 4 * ((int(n) + 31) // 32)
+
+
+def _need_all(*checks):
+    """(tensor, bytes, name) triples; raises for the first buffer that is too
+    small.  Called only after a combined test failed, so the common path of a
+    hot call costs one comparison per buffer."""
+    for t, nbytes, what in checks:
+        _need(t, nbytes, what)
+
+
 def _ptr(t: torch.Tensor | None):
     if t is None:
         return None
@@ -120,10 +139,15 @@ def _stream(stream) -> ctypes.c_void_p:
 
 
 class Meta:
-    """Owns an ibp_meta_t handle."""
+    """Owns an ibp_meta_t handle; keeps the tensor length L and chunk width W
+    so that the calls below can check buffer sizes before the library sees
+    plain pointers."""
 
-    def __init__(self, handle: ctypes.c_void_p):
+    def __init__(self, handle: ctypes.c_void_p, tensor_bytes: int = 0, chunk_bits: int = 0):
         self.handle = handle
+        self.tensor_bytes = int(tensor_bytes)
+        self.chunk_bits = int(chunk_bits)
+        self.hdr_words = (8 * self.tensor_bytes // self.chunk_bits + 31) // 32 if self.chunk_bits else 0
 
     @property
     def _as_parameter_(self):
@@ -149,9 +173,10 @@ def ibp_build_metadata(sample: torch.Tensor, n_sample: int, tensor_bytes: int, c
                        period_bits: int, threshold: float, stream=None) -> Meta:
     prm = _params(tensor_bytes, chunk_bits, period_bits, threshold)
     out = ctypes.c_void_p()
+    _need(sample, int(n_sample) * int(tensor_bytes), "sample")
     _check(lib().ibp_build_metadata(ctypes.byref(prm), _ptr(sample), int(n_sample), ctypes.byref(out),
                                     _stream(stream)), "ibp_build_metadata")
-    return Meta(out)
+    return Meta(out, tensor_bytes, chunk_bits)
 
 
 def ibp_meta_create(tensor_bytes: int, chunk_bits: int, period_bits: int, mask, bitval, stream=None) -> Meta:
@@ -159,10 +184,12 @@ def ibp_meta_create(tensor_bytes: int, chunk_bits: int, period_bits: int, mask, 
     bitval = np.ascontiguousarray(bitval, dtype=np.uint32)
     prm = _params(tensor_bytes, chunk_bits, period_bits)
     out = ctypes.c_void_p()
+    if mask.size < period_bits // 32 or bitval.size < period_bits // 32:
+        raise ValueError("mask and bitval need period_bits / 32 words each")
     _check(lib().ibp_meta_create(ctypes.byref(prm), ctypes.c_void_p(mask.ctypes.data),
                                  ctypes.c_void_p(bitval.ctypes.data), ctypes.byref(out), _stream(stream)),
            "ibp_meta_create")
-    return Meta(out)
+    return Meta(out, tensor_bytes, chunk_bits)
 
 
 def ibp_meta_get(meta: Meta):
@@ -195,12 +222,21 @@ def ibp_meta_destroy(meta: Meta):
 
 def ibp_compress(meta: Meta, src: torch.Tensor, n_tensors: int, dst_slots: torch.Tensor,
                  bitmask: torch.Tensor, stored_bytes: torch.Tensor | None = None, stream=None):
+    L, n = meta.tensor_bytes, int(n_tensors)
+    _need(src, n * L, "src")
+    _need(dst_slots, n * L, "dst_slots")
+    _need(bitmask, _bitmask_bytes(n), "bitmask")
+    _need(stored_bytes, 8 * n, "stored_bytes")
     _check(lib().ibp_compress(meta, _ptr(src), int(n_tensors), _ptr(dst_slots), _ptr(bitmask),
                               _ptr(stored_bytes), _stream(stream)), "ibp_compress")
 
 
 def ibp_decompress(meta: Meta, slots: torch.Tensor, bitmask: torch.Tensor, n_tensors: int,
                    dst: torch.Tensor, stream=None):
+    L, n = meta.tensor_bytes, int(n_tensors)
+    _need(slots, n * L, "slots")
+    _need(bitmask, _bitmask_bytes(n), "bitmask")
+    _need(dst, n * L, "dst")
     _check(lib().ibp_decompress(meta, _ptr(slots), _ptr(bitmask), int(n_tensors), _ptr(dst),
                                 _stream(stream)), "ibp_decompress")
 
@@ -209,6 +245,9 @@ def ibp_gather_decompress(meta: Meta, slots: torch.Tensor, n_slots: int, bitmask
                           ids: torch.Tensor, dst: torch.Tensor, stream=None):
     if ids.dtype != torch.int64:
         raise ValueError("ids must be int64")
+    L, n, k = meta.tensor_bytes, int(n_slots), ids.numel()
+    if slots.nbytes < n * L or bitmask.nbytes < 4 * ((n + 31) // 32) or dst.nbytes < k * L:
+        _need_all((slots, n * L, "slots"), (bitmask, _bitmask_bytes(n), "bitmask"), (dst, k * L, "dst"))
     _check(lib().ibp_gather_decompress(meta, _ptr(slots), int(n_slots), _ptr(bitmask), _ptr(ids),
                                        int(ids.numel()), _ptr(dst), _stream(stream)),
            "ibp_gather_decompress")
@@ -226,6 +265,8 @@ def ibp_packed_offsets(meta: Meta, src: torch.Tensor, n_tensors: int, offsets: t
     """offsets: device int64 tensor of n_tensors + 1 entries (written)."""
     if offsets.dtype != torch.int64 or offsets.numel() < n_tensors + 1:
         raise ValueError("offsets must be int64 with n_tensors + 1 entries")
+    if n_tensors:
+        _need(src, int(n_tensors) * meta.tensor_bytes, "src")
     _check(lib().ibp_packed_offsets(meta, _ptr(src) if n_tensors else None, int(n_tensors), _ptr(offsets),
                                     _stream(stream)), "ibp_packed_offsets")
 
@@ -233,7 +274,13 @@ def ibp_packed_offsets(meta: Meta, src: torch.Tensor, n_tensors: int, offsets: t
 def ibp_compress_packed(meta: Meta, src: torch.Tensor, n_tensors: int, offsets: torch.Tensor, dst: torch.Tensor,
                         bitmask: torch.Tensor, capacity: int | None = None, stream=None):
     if capacity is None:
-        capacity = dst.numel() * dst.element_size()
+        capacity = dst.nbytes
+    elif capacity > dst.nbytes:
+        raise ValueError(f"capacity {capacity} exceeds dst ({dst.nbytes} bytes)")
+    n = int(n_tensors)
+    _need(src, n * meta.tensor_bytes, "src")
+    _need(offsets, 8 * (n + 1), "offsets")
+    _need(bitmask, _bitmask_bytes(n), "bitmask")
     _check(lib().ibp_compress_packed(meta, _ptr(src), int(n_tensors), _ptr(offsets), _ptr(dst), int(capacity),
                                      _ptr(bitmask), _stream(stream)), "ibp_compress_packed")
 
@@ -241,7 +288,13 @@ def ibp_compress_packed(meta: Meta, src: torch.Tensor, n_tensors: int, offsets: 
 def ibp_decompress_packed(meta: Meta, buf: torch.Tensor, offsets: torch.Tensor, bitmask: torch.Tensor,
                           n_items: int, dst: torch.Tensor, buf_bytes: int | None = None, stream=None):
     if buf_bytes is None:
-        buf_bytes = buf.numel() * buf.element_size()
+        buf_bytes = buf.nbytes
+    elif buf_bytes > buf.nbytes:
+        raise ValueError(f"buf_bytes {buf_bytes} exceeds buf ({buf.nbytes} bytes)")
+    n = int(n_items)
+    _need(offsets, 8 * (n + 1), "offsets")
+    _need(bitmask, _bitmask_bytes(n), "bitmask")
+    _need(dst, n * meta.tensor_bytes, "dst")
     _check(lib().ibp_decompress_packed(meta, _ptr(buf), int(buf_bytes), _ptr(offsets), _ptr(bitmask),
                                        int(n_items), _ptr(dst), _stream(stream)), "ibp_decompress_packed")
 
@@ -252,7 +305,12 @@ def ibp_gather_decompress_packed(meta: Meta, buf: torch.Tensor, offsets: torch.T
     if ids.dtype != torch.int64:
         raise ValueError("ids must be int64")
     if buf_bytes is None:
-        buf_bytes = buf.numel() * buf.element_size()
+        buf_bytes = buf.nbytes
+    elif buf_bytes > buf.nbytes:
+        raise ValueError(f"buf_bytes {buf_bytes} exceeds buf ({buf.nbytes} bytes)")
+    n, k = int(n_items), ids.numel() * meta.tensor_bytes
+    if offsets.nbytes < 8 * (n + 1) or bitmask.nbytes < 4 * ((n + 31) // 32) or dst.nbytes < k:
+        _need_all((offsets, 8 * (n + 1), "offsets"), (bitmask, _bitmask_bytes(n), "bitmask"), (dst, k, "dst"))
     _check(lib().ibp_gather_decompress_packed(meta, _ptr(buf), int(buf_bytes), _ptr(offsets), int(n_items),
                                               _ptr(bitmask), _ptr(ids), int(ids.numel()), _ptr(dst),
                                               _stream(stream)), "ibp_gather_decompress_packed")
@@ -261,6 +319,10 @@ def ibp_gather_decompress_packed(meta: Meta, buf: torch.Tensor, offsets: torch.T
 # ---------------------------------------------------------------------------
 # Headers in GPU memory: header words beside the bitmask, payload in the slot.
 # ---------------------------------------------------------------------------
+def _header_words(meta: Meta) -> int:
+    return meta.hdr_words
+
+
 def header_words(meta: Meta) -> int:
     prm, _, _ = ibp_meta_get(meta)
     return (8 * prm["tensor_bytes"] // prm["chunk_bits"] + 31) // 32
@@ -269,12 +331,23 @@ def header_words(meta: Meta) -> int:
 def ibp_compress_split(meta: Meta, src: torch.Tensor, n_tensors: int, dst_slots: torch.Tensor,
                        headers: torch.Tensor, bitmask: torch.Tensor, stored_bytes: torch.Tensor | None = None,
                        stream=None):
+    L, n = meta.tensor_bytes, int(n_tensors)
+    _need(src, n * L, "src")
+    _need(dst_slots, n * L, "dst_slots")
+    _need(headers, 4 * n * _header_words(meta), "headers")
+    _need(bitmask, _bitmask_bytes(n), "bitmask")
+    _need(stored_bytes, 8 * n, "stored_bytes")
     _check(lib().ibp_compress_split(meta, _ptr(src), int(n_tensors), _ptr(dst_slots), _ptr(headers),
                                     _ptr(bitmask), _ptr(stored_bytes), _stream(stream)), "ibp_compress_split")
 
 
 def ibp_decompress_split(meta: Meta, slots: torch.Tensor, headers: torch.Tensor, bitmask: torch.Tensor,
                          n_tensors: int, dst: torch.Tensor, stream=None):
+    L, n = meta.tensor_bytes, int(n_tensors)
+    _need(slots, n * L, "slots")
+    _need(headers, 4 * n * _header_words(meta), "headers")
+    _need(bitmask, _bitmask_bytes(n), "bitmask")
+    _need(dst, n * L, "dst")
     _check(lib().ibp_decompress_split(meta, _ptr(slots), _ptr(headers), _ptr(bitmask), int(n_tensors), _ptr(dst),
                                       _stream(stream)), "ibp_decompress_split")
 
@@ -283,6 +356,12 @@ def ibp_gather_decompress_split(meta: Meta, slots: torch.Tensor, n_slots: int, h
                                 bitmask: torch.Tensor, ids: torch.Tensor, dst: torch.Tensor, stream=None):
     if ids.dtype != torch.int64:
         raise ValueError("ids must be int64")
+    L, n, k = meta.tensor_bytes, int(n_slots), ids.numel()
+    hb = 4 * n * _header_words(meta)
+    if (slots.nbytes < n * L or headers.nbytes < hb or bitmask.nbytes < 4 * ((n + 31) // 32)
+            or dst.nbytes < k * L):
+        _need_all((slots, n * L, "slots"), (headers, hb, "headers"), (bitmask, _bitmask_bytes(n), "bitmask"),
+                  (dst, k * L, "dst"))
     _check(lib().ibp_gather_decompress_split(meta, _ptr(slots), int(n_slots), _ptr(headers), _ptr(bitmask),
                                              _ptr(ids), int(ids.numel()), _ptr(dst), _stream(stream)),
            "ibp_gather_decompress_split")
