@@ -69,7 +69,17 @@ def test_dense_gnn_full():
     ibp.ibp_decompress(meta, slots, bm, n, out)
     assert ibp.ibp_check(meta) == ibp.IBP_OK
     assert torch.equal(out, src)
-    say(f"[full] dense_gnn ok: all {n} slots equal to the oracle's ({ncomp} compressed)")
+    # the whole round trip on the oracle, and the GPU decoding the oracle's slots
+    o_slots, o_bm, _ = oracle.compress(raw, L, w.chunk_bits, w.period_bits, om, ob, n)
+    np.testing.assert_array_equal(oracle.decompress(o_slots, o_bm, L, w.chunk_bits, w.period_bits, om, ob, n), raw,
+                                  err_msg="oracle round trip")
+    out2 = torch.empty_like(src)
+    ibp.ibp_decompress(meta, torch.from_numpy(o_slots).to(DEV), torch.from_numpy(o_bm.view(np.int32).copy()).to(DEV),
+                       n, out2)
+    assert ibp.ibp_check(meta) == ibp.IBP_OK
+    assert torch.equal(out2, src), "GPU decode of the oracle's slots differs"
+    say(f"[full] dense_gnn ok: all {n} slots equal to the oracle's ({ncomp} compressed); oracle round trip and "
+        f"GPU decode of the oracle's slots exact")
 
 
 def test_sparse_gnn_full():
