@@ -192,13 +192,75 @@ def cpu_oracle_gather(raw_rows: np.ndarray, w: WL.Workload, batch: int, budget_s
                                        mask, bitval)
         rows += batch
     dt = time.perf_counter() - t0
-    return {"value": round(rows * L / dt / GB, 6), "unit": "GB/s", "cores": 1, "kind": "oracle",
+    return {"value": round(rows * L / dt / GB, 6), "unit": "GB/s", "cores": 1, "host_cores": os.cpu_count(),
+            "kind": "oracle",
             "sample": f"{rows} rows decoded by gather in batches of {batch} ids from the oracle's slots of "
                       f"the first {sample_rows} rows ({dt:.1f} s, single thread)"}
 
 
 # ---------------------------------------------------------------------------
 # Sparse GNN: zero-copy gather from pinned host slots (default workload)
+def cpu_oracle_roundtrip(rows: np.ndarray, w: WL.Workload, n_sample: int, budget_s: float, what: str) -> dict:
+    """The oracle, single-threaded: metadata from the first n_sample rows,
+    then compress and decompress of all the rows, repeated until the time
+    budget is spent.  value: GB/s of decoded tensor; encode_GBps beside it."""
+    from oracle import oracle
+
+    oracle.build(force=False)
+    rows = np.ascontiguousarray(rows)
+    n, L = rows.shape
+    mask, bitval = oracle.build_metadata(rows[:n_sample], 8 * L, w.chunk_bits, w.period_bits, w.threshold,
+                                         n_sample)
+    t_enc = t_dec = 0.0
+    reps = 0
+    t0 = time.perf_counter()
+    while reps == 0 or time.perf_counter() - t0 < budget_s:
+        a = time.perf_counter()
+        slots, bm, _ = oracle.compress(rows, L, w.chunk_bits, w.period_bits, mask, bitval, n)
+        b = time.perf_counter()
+        out = oracle.decompress(slots, bm, L, w.chunk_bits, w.period_bits, mask, bitval, n)
+        t_enc += b - a
+        t_dec += time.perf_counter() - b
+        reps += 1
+    if not np.array_equal(out, rows):
+        raise SystemExit("oracle round trip differs")
+    return {"value": round(reps * n * L / t_dec / GB, 6), "unit": "GB/s", "cores": 1, "host_cores": os.cpu_count(),
+            "kind": "oracle", "encode_GBps": round(reps * n * L / t_enc / GB, 6),
+            "sample": f"{what}: {reps} compress + decompress round trips ({t_enc + t_dec:.1f} s, single thread)"}
+
+
+def cpu_oracle_gather_slots(rows: np.ndarray, w: WL.Workload, batch: int, budget_s: float, what: str,
+                            packed: bool = False, replace: bool = True) -> dict:
+    """The oracle, single-threaded, decoding random id batches from its own
+    slots (or packed items) of the sampled rows until the time budget is
+    spent (encode excluded)."""
+    from oracle import oracle
+
+    oracle.build(force=False)
+    rows = np.ascontiguousarray(rows)
+    n, L = rows.shape
+    ns = min(w.n_sample, n)
+    mask, bitval = oracle.build_metadata(rows[:ns], 8 * L, w.chunk_bits, w.period_bits, w.threshold, ns)
+    if packed:
+        buf, off, bm = oracle.compress_packed(rows, L, w.chunk_bits, w.period_bits, mask, bitval, n)
+    else:
+        slots, bm, _ = oracle.compress(rows, L, w.chunk_bits, w.period_bits, mask, bitval, n)
+    rng = np.random.default_rng(WL.ID_SEED)
+    done = 0
+    t0 = time.perf_counter()
+    while done == 0 or time.perf_counter() - t0 < budget_s:
+        ids = rng.choice(n, batch, replace=replace)
+        if packed:
+            oracle.gather_decompress_packed(buf, off, n, bm, ids, L, w.chunk_bits, w.period_bits, mask, bitval)
+        else:
+            oracle.gather_decompress(slots, n, bm, ids, L, w.chunk_bits, w.period_bits, mask, bitval)
+        done += batch
+    dt = time.perf_counter() - t0
+    return {"value": round(done * L / dt / GB, 6), "unit": "GB/s", "cores": 1, "host_cores": os.cpu_count(),
+            "kind": "oracle", "sample": f"{done} rows decoded by gather in batches of {batch} ids from the oracle's "
+                                        f"{'packed items' if packed else 'slots'} of {what} ({dt:.1f} s, single thread)"}
+
+
 # ---------------------------------------------------------------------------
 def run_sparse_gnn(args) -> dict:
     """Zero-copy gathers of 8,192 random rows from pinned host slots.  The
@@ -372,13 +434,21 @@ def run_kv_bf16(args) -> dict:
         raise SystemExit("decoded pages differ")
     hbm_bytes = float(stored_np.sum() + n * L + 4 * ((n + 31) // 32))
     roof = hbm_roofline(hbm_bytes, durs, None if args.small else "kv_bf16")
-    return base_result(
+    cpu = None
+    if not args.no_cpu:
+        log("[bench] CPU oracle baseline")
+        cpu = cpu_oracle_roundtrip(src[:2048].cpu().numpy(), w, w.n_sample, args.cpu_budget,
+                                   "the first 2,048 pages (8 MiB; metadata from their first 1,024)")
+    res = base_result(
         args, n * L * args.steps / wall / GB, wall,
         {"workload": f"kv_bf16: {layers} layers x 32 heads x 4096 tokens x 128 bf16, 4 KiB pages in HBM slots, "
                      f"W=32, M=32768, T=0.95, decode of all {n} pages per step", "pages": n, "tensor_bytes": L},
         savings, "ibp::k_decode_small<3, false, true, 4, false>", durs, roof,
         encode_GBps=round(n * L / float(np.mean(enc_durs)) / GB, 3), metadata_ms=round(t_meta * 1e3, 2),
         meta=ibp.ibp_meta_get_info(meta))
+    if cpu:
+        res["cpu_baseline"] = cpu
+    return res
 
 
 METRIC = "IBP decode GB/s (uncompressed out, 1 MI355X) + % of roofline + space savings %"
@@ -446,7 +516,12 @@ def run_dense_gnn(args) -> dict:
     raw_wall, _ = timed(lambda i: raw_copy.copy_(src), args.steps, args.warmup)
     raw_durs = queued_durations(lambda i: raw_copy.copy_(src), args.steps)
     del raw_copy
-    return base_result(
+    cpu = None
+    if not args.no_cpu:
+        log("[bench] CPU oracle baseline")
+        cpu = cpu_oracle_roundtrip(src.cpu().numpy(), w, w.n_sample, args.cpu_budget,
+                                   f"all {n} rows (8 MiB; metadata from the first 1,024)")
+    res = base_result(
         args, n * L * args.steps / wall / GB, wall,
         {"workload": f"dense_gnn: {n} rows x 128 fp32 |N(0,0.5)| with 3% N(0,50) rows, W=32, M=4096, T=0.95, "
                      f"slots in HBM, contiguous decode of all rows per step", "rows": n, "tensor_bytes": L},
@@ -454,6 +529,9 @@ def run_dense_gnn(args) -> dict:
         encode_GBps=round(n * L / float(np.mean(enc_durs)) / GB, 3),
         uncompressed_hbm_copy_GBps=round(n * L * args.steps / raw_wall / GB, 3),
         uncompressed_copy_kernel_us=round(float(np.mean(raw_durs)) * 1e6, 2), meta=ibp.ibp_meta_get_info(meta))
+    if cpu:
+        res["cpu_baseline"] = cpu
+    return res
 
 
 # ---------------------------------------------------------------------------
@@ -493,7 +571,11 @@ def run_dlrm(args) -> dict:
     durs = np.full(args.steps * per_step, float(step_durs.mean()) / per_step)  # per gather launch
     link = float(stored_np[ids_np[args.warmup * per_step:]].sum(axis=1).mean())
     value = args.steps * per_step * batch * L / wall / GB
-    return base_result(
+    cpu = None
+    if not args.no_cpu:
+        log("[bench] CPU oracle baseline")
+        cpu = cpu_oracle_gather_slots(raw_np[:65536], w, 8192, args.cpu_budget, "the first 65,536 rows (32 MiB)")
+    res = base_result(
         args, value, wall,
         {"workload": f"dlrm: {n} rows x 128 fp32 U(-0.01,0.01), W=32, M=4096, T=0.9, slots in pinned host "
                      f"memory, {per_step} zero-copy gathers of {batch} random ids (with replacement) per step",
@@ -501,6 +583,9 @@ def run_dlrm(args) -> dict:
         savings, "ibp::k_decode_small<2, true, true, 1, false>", durs,
         link_roofline(link, durs, savings, None if args.small else "dlrm"),
         encode_GBps=round(n * L / t_enc / GB, 3), meta=ibp.ibp_meta_get_info(meta))
+    if cpu:
+        res["cpu_baseline"] = cpu
+    return res
 
 
 # ---------------------------------------------------------------------------
@@ -565,7 +650,13 @@ def run_llm_bf16(args) -> dict:
     durs = np.array([a.elapsed_time(b) / 1e3 for a, b in evs])
     link = float(stored_np.mean())
     value = args.steps * layers * L / wall / GB
-    return base_result(
+    cpu = None
+    if not args.no_cpu:
+        log("[bench] CPU oracle baseline")
+        # one tensor made of the first 256 rows of layer 0 (5.6 MB), its own sample
+        cpu = cpu_oracle_roundtrip(hv[0].reshape(1, -1)[:, : 256 * cols * 2], w, 1, args.cpu_budget,
+                                   "one 5.6 MB tensor: the first 256 rows of layer 0 (metadata from itself)")
+    res = base_result(
         args, value, wall,
         {"workload": f"llm_bf16: {layers} layers of {rows}x{cols} bf16 N(0,0.02) (0.1% columns x20), W=32, M=32, "
                      f"T=0.95, slots in pinned host memory, each layer decoded zero-copy into HBM on one stream "
@@ -574,6 +665,9 @@ def run_llm_bf16(args) -> dict:
         savings, "ibp::k_decode_tiles<3, true, true> (look-back)", durs,
         link_roofline(link, durs, savings, None if args.small else "llm_bf16"),
         encode_GBps=round(layers * L / t_enc / GB, 3), meta=ibp.ibp_meta_get_info(meta))
+    if cpu:
+        res["cpu_baseline"] = cpu
+    return res
 
 
 # ---------------------------------------------------------------------------
@@ -635,7 +729,12 @@ def run_sparse_gnn_cache(args) -> dict:
     raw_durs = queued_durations(lambda i: torch.index_select(table, 0, ids_dev[i], out=out[i & 1]), args.steps,
                                 args.warmup)
     del table
-    return base_result(
+    cpu = None
+    if not args.no_cpu:
+        log("[bench] CPU oracle baseline")
+        cpu = cpu_oracle_gather_slots(raw_np[:16384], w, 1024, args.cpu_budget, "the first 16,384 rows (16 MiB)",
+                                      packed=True, replace=False)
+    res = base_result(
         args, batch * L * args.steps / wall / GB, wall,
         {"workload": f"sparse_gnn_cache: {n} rows x 256 fp32 (97% zeros), W=1024, M=8192, T=0.95, all rows "
                      f"compressed into one packed HBM buffer (items back to back, 16-byte aligned), gather of "
@@ -648,6 +747,9 @@ def run_sparse_gnn_cache(args) -> dict:
         uncompressed_hbm_gather_GBps=round(batch * L * args.steps / raw_wall / GB, 3),
         uncompressed_gather_kernel_us=round(float(np.mean(raw_durs)) * 1e6, 2),
         meta=ibp.ibp_meta_get_info(meta))
+    if cpu:
+        res["cpu_baseline"] = cpu
+    return res
 
 
 # ---------------------------------------------------------------------------
