@@ -37,7 +37,14 @@
  * on the host before any launch and leave outputs untouched on error.  Errors
  * found by kernels (an id out of range, a corrupt record) are latched in the
  * handle and reported by ibp_check().  Calls on one handle may run on
- * different streams at once; calls on the same stream run in order.
+ * different streams at once; calls on the same stream run in order, also
+ * when several host threads issue them.
+ *
+ * Tensors longer than one tile (more than 8 KiB) are cut into tiles that
+ * find their start bit by a decoupled look-back over per-stream scratch of
+ * the handle.  ibp_compress, ibp_decompress and ibp_gather_decompress of
+ * such tensors, and ibp_packed_offsets, return IBP_ERR_UNSUPPORTED while
+ * `stream` is capturing a HIP graph; single-tile calls may be captured.
  */
 #ifndef IBP_H
 #define IBP_H
@@ -223,7 +230,10 @@ ibp_status ibp_gather_decompress_split(ibp_meta_t meta, const void* slots, uint6
                                        uint64_t n_ids, void* dst, hipStream_t stream);
 
 /* Waits for `stream`, returns the first error latched by a kernel of this
- * handle since the last ibp_check (IBP_OK if none) and clears it. */
+ * handle since the last ibp_check (IBP_OK if none) and clears it:
+ * IBP_ERR_RANGE, IBP_ERR_CORRUPT, or IBP_ERR_DEVICE when a tile gave up
+ * waiting for its predecessor in the look-back (its tensor's output is then
+ * unspecified). */
 ibp_status ibp_check(ibp_meta_t meta, hipStream_t stream);
 
 const char* ibp_status_string(ibp_status status);

@@ -28,13 +28,16 @@ constexpr uint32_t kMaxPeriodBits = 1u << 20;
 constexpr uint64_t kLineWords = 64;     // 256-byte first-read granule
 constexpr uint64_t kMemLineWords = 32;  // 128-byte line that memory reads move
 
+// Look-back scratch of one (handle, stream) pair.  The ticket counter is
+// zeroed on the stream before every launch; only the epoch, which keeps a
+// launch's status words apart from those of earlier launches, is counted on
+// the host.
 struct Scratch {
     unsigned long long* status = nullptr;
     uint64_t status_cap = 0;
     uint64_t* totals = nullptr;
     uint64_t totals_cap = 0;
     uint32_t* ticket = nullptr;
-    uint32_t ticket_base = 0;
     uint32_t epoch = 0;
 };
 
@@ -315,21 +318,38 @@ ibp_status sample_item_stats(ibp_meta_s* h, const void* sample, uint64_t n_sampl
     return IBP_OK;
 }
 
-// Look-back state for one launch of `waves` waves over `tiles` tiles on
-// stream s.  Grows the per-stream buffers when needed.
-ibp_status lookback_for(ibp_meta_s* h, hipStream_t s, uint64_t tiles, uint64_t waves, uint64_t tensors,
-                        LookBack* lb) {
-    std::lock_guard<std::mutex> lock(h->mu);
-    Scratch& sc = h->scratch[s];
-    if (!sc.ticket) {
-        IBP_TRY(hipMalloc(&sc.ticket, 256));
-        IBP_TRY(launch_fill_u32(sc.ticket, 1, 0, s));
-        sc.ticket_base = 0;
+// IBP_ERR_UNSUPPORTED while `s` is capturing a graph: a look-back launch
+// refers to its stream's scratch and epoch at the time of the call, which a
+// replay would not renew.
+ibp_status refuse_capture(hipStream_t s) {
+    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+    if (hipStreamIsCapturing(s, &cs) != hipSuccess) {
+        (void)hipGetLastError();
+        return IBP_ERR_DEVICE;
     }
+    return cs == hipStreamCaptureStatusNone ? IBP_OK : IBP_ERR_UNSUPPORTED;
+}
+
+// Look-back state for one launch over `tiles` tiles on stream s: grows the
+// per-stream buffers when needed and queues the zeroing of the ticket
+// counter on s.  Returns with `lock` holding the handle's mutex; the caller
+// queues its launch before releasing it, so launches on one stream from
+// several host threads reach the stream in the order of their reservations
+// and no buffer is replaced while a reserved launch is still to be queued.
+ibp_status lookback_for(ibp_meta_s* h, hipStream_t s, uint64_t tiles, uint64_t tensors, LookBack* lb,
+                        std::unique_lock<std::mutex>* lock) {
+    ibp_status st = refuse_capture(s);
+    if (st != IBP_OK) return st;
+    *lock = std::unique_lock<std::mutex>(h->mu);
+    Scratch& sc = h->scratch[s];
+    if (!sc.ticket) IBP_TRY(hipMalloc(&sc.ticket, 256));
     if (sc.status_cap < tiles) {
+        // earlier launches on s were queued under the mutex: once s is idle
+        // nothing refers to the old buffer
         IBP_TRY(hipStreamSynchronize(s));
         if (sc.status) IBP_TRY(hipFree(sc.status));
         sc.status = nullptr;
+        sc.status_cap = 0;
         IBP_TRY(hipMalloc(&sc.status, tiles * sizeof(unsigned long long)));
         IBP_TRY(launch_fill_u32(reinterpret_cast<uint32_t*>(sc.status), 2 * tiles, 0, s));
         sc.status_cap = tiles;
@@ -339,6 +359,7 @@ ibp_status lookback_for(ibp_meta_s* h, hipStream_t s, uint64_t tiles, uint64_t w
         IBP_TRY(hipStreamSynchronize(s));
         if (sc.totals) IBP_TRY(hipFree(sc.totals));
         sc.totals = nullptr;
+        sc.totals_cap = 0;
         IBP_TRY(hipMalloc(&sc.totals, tensors * sizeof(uint64_t)));
         sc.totals_cap = tensors;
     }
@@ -347,17 +368,13 @@ ibp_status lookback_for(ibp_meta_s* h, hipStream_t s, uint64_t tiles, uint64_t w
         IBP_TRY(launch_fill_u32(reinterpret_cast<uint32_t*>(sc.status), 2 * sc.status_cap, 0, s));
         sc.epoch = 1;
     }
+    IBP_TRY(launch_fill_u32(sc.ticket, 1, 0, s));
     lb->status = sc.status;
     lb->ticket = sc.ticket;
-    lb->ticket_base = sc.ticket_base;
     lb->epoch = sc.epoch;
     lb->totals = sc.totals;
-    sc.ticket_base += (uint32_t)waves;
+    lb->err = h->d_err;
     return IBP_OK;
-}
-
-uint64_t launched_waves(uint64_t tiles) {
-    return ((tiles + kWavesPerBlock - 1) / kWavesPerBlock) * kWavesPerBlock;
 }
 
 bool overlaps(const void* a, uint64_t na, const void* b, uint64_t nb) {
@@ -487,9 +504,9 @@ ibp_status ibp_compress(ibp_meta_t h, const void* src, uint64_t n_tensors, void*
     if (overlaps(src, n_tensors * L, dst_slots, n_tensors * L)) return IBP_ERR_INVALID_ARG;
     const Geo geo = make_geo(h, aligned16(L, {src, dst_slots}), kLongTileWordsEncode);
     LookBack lb{};
+    std::unique_lock<std::mutex> lock;
     if (geo.tiles_per_tensor > 1) {
-        const uint64_t tiles = n_tensors * geo.tiles_per_tensor;
-        ibp_status st = lookback_for(h, stream, tiles, launched_waves(tiles), n_tensors, &lb);
+        ibp_status st = lookback_for(h, stream, n_tensors * geo.tiles_per_tensor, n_tensors, &lb, &lock);
         if (st != IBP_OK) return st;
     }
     return from_hip(launch_encode(h->tabs, geo, h->sum.max_runs, h->sum.uniform != 0, src, n_tensors, dst_slots,
@@ -512,9 +529,9 @@ static ibp_status decode_common(ibp_meta_t h, const void* slots, uint64_t n_slot
     Geo geo = make_geo(h, aligned16(L, {slots, dst}), kLongTileWordsDecode);
     geo.src_in_hbm = slots_kind == Kind::Device;
     LookBack lb{};
+    std::unique_lock<std::mutex> lock;
     if (geo.tiles_per_tensor > 1) {
-        const uint64_t tiles = n_out * geo.tiles_per_tensor;
-        ibp_status st = lookback_for(h, stream, tiles, launched_waves(tiles), n_out, &lb);
+        ibp_status st = lookback_for(h, stream, n_out * geo.tiles_per_tensor, 0, &lb, &lock);
         if (st != IBP_OK) return st;
     }
     return from_hip(launch_decode(h->tabs, geo, h->sum.max_runs, h->sum.uniform != 0, slots, n_slots, bitmask,
@@ -549,13 +566,18 @@ ibp_status ibp_packed_offsets(ibp_meta_t h, const void* src, uint64_t n_tensors,
     if (!packed_supported(geo, h->sum.max_runs, uni) || !packed_decode_supported(geo, h->sum.max_runs, uni))
         return IBP_ERR_UNSUPPORTED;
     if (n_tensors) {
+        // the offsets scan below takes look-back scratch: refused under
+        // capture before anything is queued
+        ibp_status st = refuse_capture(stream);
+        if (st != IBP_OK) return st;
         IBP_TRY(launch_item_sizes(h->tabs, geo, h->sum.max_runs, uni, src, n_tensors, offsets + 1, h->cu_count,
                                   stream));
     }
     LookBack lb{};
+    std::unique_lock<std::mutex> lock;
     const uint64_t blocks = (n_tensors + kScanBlock - 1) / kScanBlock;
     if (n_tensors) {
-        ibp_status st = lookback_for(h, stream, blocks, scan_waves(n_tensors), 0, &lb);
+        ibp_status st = lookback_for(h, stream, blocks, 0, &lb, &lock);
         if (st != IBP_OK) return st;
     }
     return from_hip(launch_scan_sizes(offsets, n_tensors, lb, stream));
@@ -687,7 +709,8 @@ ibp_status ibp_check(ibp_meta_t h, hipStream_t stream) {
     if (v == kErrNone) return IBP_OK;
     IBP_TRY(launch_fill_u32(h->d_err, 1, 0, stream));
     IBP_TRY(hipStreamSynchronize(stream));
-    return v == kErrRange ? IBP_ERR_RANGE : IBP_ERR_CORRUPT;
+    if (v == kErrRange) return IBP_ERR_RANGE;
+    return v == kErrStall ? IBP_ERR_DEVICE : IBP_ERR_CORRUPT;
 }
 
 }  // extern "C"

@@ -449,7 +449,7 @@ __global__ __launch_bounds__(256) void k_decode_tiles(Tables t, Geo geo, const u
     if (MULTI) {
         uint32_t tk = 0;
         if (lane == 0) tk = atomicAdd(lb.ticket, 1u);
-        tile = (uint32_t)(uniform(tk) - lb.ticket_base);
+        tile = uniform(tk);
     } else {
         tile = (uint64_t)blockIdx.x * kWavesPerBlock + threadIdx.x / kWave;
     }
@@ -518,7 +518,7 @@ __global__ __launch_bounds__(256) void k_decode_tiles(Tables t, Geo geo, const u
     bool bad_pad;
     const uint32_t rem = header_removed_bits(t.planes, geo, hdr, hw0, hw_t, &bad_pad);
     const uint64_t agg = 32ull * nw - rem;
-    const uint64_t S = lookback_exclusive(lb.status, oi * tpt, local, agg, 32ull * geo.hdr_words, lb.epoch);
+    const uint64_t S = lookback_exclusive(lb.status, oi * tpt, local, agg, 32ull * geo.hdr_words, lb.epoch, err);
     const uint64_t E = S + agg;
     const bool last = local == tpt - 1;
     if (bad_pad || E > 8ull * geo.L || (last && 4 * ((E + 31) / 32) >= geo.L)) {

@@ -410,9 +410,11 @@ __device__ __forceinline__ unsigned long long status_load(unsigned long long* p)
 // Tile `local` of a tensor whose tiles use status[first .. first+n); returns
 // the sum of `base` and the aggregates of every earlier tile, and publishes
 // this tile's inclusive value.  Waits only on earlier tiles, which took their
-// tickets before this one and are therefore resident or finished.
+// tickets before this one and are therefore resident or finished.  A wait
+// that outlasts kLookbackPolls polls latches kErrStall in err and returns
+// (and publishes) kLookbackPoison, so every wave still exits.
 __device__ uint64_t lookback_exclusive(unsigned long long* status, uint64_t first, uint64_t local,
-                                       uint64_t agg, uint64_t base, uint32_t epoch) {
+                                       uint64_t agg, uint64_t base, uint32_t epoch, uint32_t* err) {
     const uint32_t lane = lane_id();
     unsigned long long* mine = status + first + local;
     if (local == 0) {
@@ -426,9 +428,10 @@ __device__ uint64_t lookback_exclusive(unsigned long long* status, uint64_t firs
         const bool inwin = (int64_t)lane <= j;
         uint64_t v = 0;
         uint32_t f = 0;
+        bool gave_up = false;
         if (inwin) {
             unsigned long long* p = status + first + (uint64_t)(j - (int64_t)lane);
-            while (true) {
+            for (uint32_t polls = 0;; ++polls) {
                 unsigned long long s = status_load(p);
                 uint32_t ep = (uint32_t)(s >> 42) & 0xFFFFFu;
                 f = (uint32_t)(s >> 62);
@@ -436,8 +439,17 @@ __device__ uint64_t lookback_exclusive(unsigned long long* status, uint64_t firs
                     v = s & kValMask;
                     break;
                 }
+                if (polls >= kLookbackPolls) {
+                    gave_up = true;
+                    break;
+                }
                 __builtin_amdgcn_s_sleep(1);
             }
+        }
+        if (ballot(gave_up)) {
+            latch_error(err, kErrStall);
+            if (lane == 0) status_store(mine, pack_status(kFlagIncl, epoch, kLookbackPoison));
+            return kLookbackPoison;
         }
         const uint64_t incl = ballot(inwin && f == kFlagIncl);
         if (incl) {

@@ -136,7 +136,7 @@ __global__ __launch_bounds__(256) void k_encode(Tables t, Geo geo, const uint8_t
     if (MULTI) {
         uint32_t tk = 0;
         if (lane == 0) tk = atomicAdd(lb.ticket, 1u);
-        tile = (uint32_t)(uniform(tk) - lb.ticket_base);
+        tile = uniform(tk);
     } else {
         tile = (uint64_t)blockIdx.x * kWavesPerBlock + threadIdx.x / kWave;
     }
@@ -179,7 +179,7 @@ __global__ __launch_bounds__(256) void k_encode(Tables t, Geo geo, const uint8_t
         return;
     }
 
-    const uint64_t S = lookback_exclusive(lb.status, ti * tpt, local, agg, 32ull * geo.hdr_words, lb.epoch);
+    const uint64_t S = lookback_exclusive(lb.status, ti * tpt, local, agg, 32ull * geo.hdr_words, lb.epoch, lb.err);
     const uint64_t E = S + agg;
     const bool last = local == tpt - 1;
     // header words of this tile (always inside the slot)
@@ -610,7 +610,7 @@ __global__ __launch_bounds__(256) void k_scan_sizes(uint64_t* __restrict__ offse
     const uint32_t lane = lane_id();
     uint32_t tk = 0;
     if (lane == 0) tk = atomicAdd(lb.ticket, 1u);
-    const uint64_t blk = (uint32_t)(uniform(tk) - lb.ticket_base);
+    const uint64_t blk = uniform(tk);
     const uint64_t n_blocks = (n + kScanBlock - 1) / kScanBlock;
     if (blk >= n_blocks) return;
     uint64_t* sz = offsets + 1;
@@ -624,7 +624,7 @@ __global__ __launch_bounds__(256) void k_scan_sizes(uint64_t* __restrict__ offse
     }
     const uint32_t incl = wave_incl_scan(run);
     const uint32_t agg = lane_value(incl, kWave - 1);
-    const uint64_t base = lookback_exclusive(lb.status, 0, blk, agg, 0, lb.epoch);
+    const uint64_t base = lookback_exclusive(lb.status, 0, blk, agg, 0, lb.epoch, lb.err);
     const uint64_t pre = base + (incl - run);
 #pragma unroll
     for (uint32_t j = 0; j < kScanPerLane; ++j)

@@ -48,16 +48,28 @@ struct Geo {
 };
 
 // Decoupled look-back state for multi-tile tensors.  A status word packs
-// flag (2 bits) | epoch (20 bits) | value (42 bits).
+// flag (2 bits) | epoch (20 bits) | value (42 bits).  The ticket counter is
+// set to zero by a fill kernel on the launch's stream right before each
+// launch, so the tiles of a launch take tickets 0, 1, 2, ... in stream order
+// and no counter state lives on the host.
 struct LookBack {
     unsigned long long* status;  // one per tile of the launch
-    uint32_t* ticket;            // dynamic tile counter
-    uint32_t ticket_base;        // counter value at launch
+    uint32_t* ticket;            // dynamic tile counter (zero at launch)
     uint32_t epoch;              // 1 .. 2^20-1, distinct from stale entries
     uint64_t* totals;            // per output tensor: record bits (encode)
+    uint32_t* err;               // error latch of the handle
 };
 
-enum DeviceError : uint32_t { kErrNone = 0, kErrCorrupt = 5, kErrRange = 6 };
+// A look-back wait gives up after this many polls of one predecessor's
+// status word (each poll is an atomic load and a short sleep, so several
+// seconds; a predecessor holds an earlier ticket and is resident or done, so
+// a legitimate wait lasts microseconds).  The tile then latches kErrStall and
+// publishes kLookbackPoison as its inclusive value, which every later tile
+// of the tensor rejects before it touches memory.
+constexpr uint32_t kLookbackPolls = 1u << 22;
+constexpr uint64_t kLookbackPoison = 1ull << 41;
+
+enum DeviceError : uint32_t { kErrNone = 0, kErrCorrupt = 5, kErrRange = 6, kErrStall = 7 };
 
 // Where tensor t's stored item lives.  offsets == nullptr: fixed slots, slot
 // t at byte t * L.  Otherwise the packed cache layout: item t spans bytes

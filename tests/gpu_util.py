@@ -66,6 +66,18 @@ class Result:
     pass
 
 
+def oracle_metadata(meta, sample: np.ndarray, W: int, M: int, T: float):
+    """Mask/Bitval from the oracle's own metadata build over `sample` (rows of
+    L bytes), asserted equal to the handle's; returned as the oracle's bytes,
+    so that an oracle encode that follows never takes the GPU's metadata."""
+    n_sample, L = sample.shape
+    o_mask, o_bitval = oracle.build_metadata(np.ascontiguousarray(sample), 8 * L, W, M, T, n_sample)
+    _, g_mask, g_bitval = ibp.ibp_meta_get(meta)
+    np.testing.assert_array_equal(g_mask.view(np.uint8), o_mask, err_msg="Mask differs from the oracle's")
+    np.testing.assert_array_equal(g_bitval.view(np.uint8), o_bitval, err_msg="Bitval differs from the oracle's")
+    return o_mask, o_bitval
+
+
 def compare_codec(raw: np.ndarray, W: int, M: int, T: float, n_sample: int, *, sample: np.ndarray | None = None,
                   src_pinned: bool = False, slots_pinned: bool = False, ids: np.ndarray | None = None,
                   check_slots: bool = True, label: str = "", misalign: int = 0) -> Result:

@@ -10,7 +10,7 @@ import torch
 from lossless_tensor_compression_ibp_amd import ibp
 from lossless_tensor_compression_ibp_amd import workloads as WL
 from oracle import oracle
-from tests.gpu_util import as_rows, device, say, to_gpu
+from tests.gpu_util import as_rows, device, oracle_metadata, say, to_gpu
 
 pytestmark = pytest.mark.gpu
 
@@ -38,8 +38,7 @@ def packed_case(raw: np.ndarray, W: int, M: int, T: float, n_sample: int, *, src
     say(f"[packed] {label} n={n} L={L} W={W} M={M} src_pinned={src_pinned} buf_pinned={buf_pinned}")
     src = to_gpu(raw, pinned=src_pinned)
     meta = ibp.ibp_build_metadata(src, n_sample, L, W, M, T)
-    _, m, b = ibp.ibp_meta_get(meta)
-    om, ob = m.view(np.uint8), b.view(np.uint8)
+    om, ob = oracle_metadata(meta, raw[:n_sample], W, M, T)
     # offsets
     off = torch.full((n + 1,), -1, dtype=torch.int64, device=dev)
     ibp.ibp_packed_offsets(meta, src, n, off)
@@ -183,13 +182,12 @@ def test_packed_sparse_gnn_full_size():
     bm = torch.zeros((n + 31) // 32, dtype=torch.int32, device=dev)
     ibp.ibp_compress_packed(meta, host, n, off, buf, bm)
     assert ibp.ibp_check(meta) == ibp.IBP_OK
-    _, m, b = ibp.ibp_meta_get(meta)
+    om, ob = oracle_metadata(meta, raw[: w.n_sample], w.chunk_bits, w.period_bits, w.threshold)
     rows = np.unique(np.concatenate([np.arange(300), np.random.default_rng(9).integers(0, n, 1500), [n - 1]]))
     sizes = np.diff(off_np.astype(np.int64))
     bnp = buf.cpu().numpy()
     for r in rows:
-        o_buf, o_off, _ = oracle.compress_packed(raw[r:r + 1], L, w.chunk_bits, w.period_bits, m.view(np.uint8),
-                                                 b.view(np.uint8), 1)
+        o_buf, o_off, _ = oracle.compress_packed(raw[r:r + 1], L, w.chunk_bits, w.period_bits, om, ob, 1)
         assert sizes[r] == int(o_off[1]), f"item size of row {r}"
         a = int(off_np[r])
         assert np.array_equal(bnp[a:a + sizes[r]], o_buf[: sizes[r]]), f"item of row {r}"

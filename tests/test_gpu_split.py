@@ -10,7 +10,7 @@ import torch
 from lossless_tensor_compression_ibp_amd import ibp
 from lossless_tensor_compression_ibp_amd import workloads as WL
 from oracle import oracle
-from tests.gpu_util import as_rows, device, say, to_gpu
+from tests.gpu_util import as_rows, device, oracle_metadata, say, to_gpu
 
 pytestmark = pytest.mark.gpu
 
@@ -27,8 +27,7 @@ def split_case(raw: np.ndarray, W: int, M: int, T: float, n_sample: int, *, pinn
     say(f"[split] {label} n={n} L={L} W={W} M={M} hw={hw} pinned={pinned}")
     src = to_gpu(raw, pinned=pinned)
     meta = ibp.ibp_build_metadata(src, n_sample, L, W, M, T)
-    _, m, b = ibp.ibp_meta_get(meta)
-    om, ob = m.view(np.uint8), b.view(np.uint8)
+    om, ob = oracle_metadata(meta, raw[:n_sample], W, M, T)
     if pinned:
         slots = torch.full((n, L), 0xEE, dtype=torch.uint8, pin_memory=True)
     else:
@@ -146,10 +145,9 @@ def test_split_sparse_gnn_full_size():
     stored = torch.zeros(n, dtype=torch.int64, device=dev)
     ibp.ibp_compress_split(meta, host, n, slots, headers, bm, stored)
     torch.cuda.synchronize()
-    _, m, b = ibp.ibp_meta_get(meta)
+    om, ob = oracle_metadata(meta, raw[: w.n_sample], w.chunk_bits, w.period_bits, w.threshold)
     rows = np.unique(np.concatenate([np.arange(256), np.random.default_rng(8).integers(0, n, 2048), [n - 1]]))
-    o_slots, o_hdr, o_bm, o_st = oracle.compress_split(raw[rows], L, w.chunk_bits, w.period_bits, m.view(np.uint8),
-                                                       b.view(np.uint8), len(rows))
+    o_slots, o_hdr, o_bm, o_st = oracle.compress_split(raw[rows], L, w.chunk_bits, w.period_bits, om, ob, len(rows))
     st = stored.cpu().numpy().astype(np.uint64)
     hd = headers.cpu().numpy().view(np.uint32)
     bits = (bm.cpu().numpy().view(np.uint32)[rows >> 5] >> (rows & 31)) & 1

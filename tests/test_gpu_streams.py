@@ -203,3 +203,169 @@ def test_two_threads_two_handles():
         assert torch.equal(outs_a[i], src_a[ids_dev[i]]), f"thread A call {i}"
         assert torch.equal(outs_b[i], src_b), f"thread B call {i}"
     say("[threads] two threads, two handles, two streams: ok")
+
+
+def _three_tile_tensors(n: int = 3):
+    """n bf16 tensors of 40 x 256 (20 KiB = 5,120 words): three decode tiles
+    of at most 2,048 words and five encode tiles of 1,024, so every call on
+    them takes the look-back path."""
+    raw = np.stack([WL.llm_layer(l, rows=40, cols=256).reshape(-1).view(np.uint8) for l in range(n)])
+    w = WL.LLM_BF16
+    return raw, w.chunk_bits, w.period_bits, w.threshold
+
+
+def test_look_back_calls_refused_under_capture():
+    """Multi-tile compress, decompress, gather and the packed offsets scan
+    are refused (IBP_ERR_UNSUPPORTED, nothing queued) while the stream
+    captures a graph; eager calls on the same stream afterwards are still
+    bit-exact against the oracle."""
+    from oracle import oracle
+    from tests.gpu_util import oracle_metadata
+
+    oracle.build(force=False)
+    dev = device()
+    raw, W, M, T = _three_tile_tensors()
+    n, L = raw.shape
+    src = torch.from_numpy(raw).to(dev)
+    meta = ibp.ibp_build_metadata(src, 1, L, W, M, T)
+    om, ob = oracle_metadata(meta, raw[:1], W, M, T)
+    o_slots, o_bm, o_st = oracle.compress(raw, L, W, M, om, ob, n)
+    assert np.unpackbits(o_bm.view(np.uint8), bitorder="little")[:n].all(), "every tensor compresses"
+    slots = torch.empty_like(src)
+    bm = torch.zeros(1, dtype=torch.int32, device=dev)
+    stored = torch.zeros(n, dtype=torch.int64, device=dev)
+    out = torch.empty_like(src)
+    ids = torch.tensor([2, 0, 2], dtype=torch.int64, device=dev)
+    gout = torch.empty((3, L), dtype=torch.uint8, device=dev)
+    offsets = torch.zeros(n + 1, dtype=torch.int64, device=dev)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        ibp.ibp_compress(meta, src, n, slots, bm, stored, stream=s)  # eager, before the capture
+    s.synchronize()
+    say("[capture] multi-tile calls under capture")
+    refused = []
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(s):
+        g.capture_begin()
+        try:
+            for name, call in (
+                    ("compress", lambda: ibp.ibp_compress(meta, src, n, slots, bm, stored, stream=s)),
+                    ("decompress", lambda: ibp.ibp_decompress(meta, slots, bm, n, out, stream=s)),
+                    ("gather", lambda: ibp.ibp_gather_decompress(meta, slots, n, bm, ids, gout, stream=s))):
+                try:
+                    call()
+                except ibp.IBPError as e:
+                    refused.append((name, e.status))
+        finally:
+            g.capture_end()
+    assert refused == [("compress", ibp.IBP_ERR_UNSUPPORTED), ("decompress", ibp.IBP_ERR_UNSUPPORTED),
+                       ("gather", ibp.IBP_ERR_UNSUPPORTED)], refused
+    del g
+    # packed offsets (look-back scan over item sizes): sparse rows
+    ws = WL.SPARSE_GNN
+    rows = as_rows(WL.sparse_gnn(600))
+    src_s = torch.from_numpy(rows).to(dev)
+    meta_s = ibp.ibp_build_metadata(src_s, 600, rows.shape[1], ws.chunk_bits, ws.period_bits, ws.threshold)
+    off_s = torch.zeros(601, dtype=torch.int64, device=dev)
+    g2 = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(s):
+        g2.capture_begin()
+        try:
+            with pytest.raises(ibp.IBPError) as e:
+                ibp.ibp_packed_offsets(meta_s, src_s, 600, off_s, stream=s)
+        finally:
+            g2.capture_end()
+    assert e.value.status == ibp.IBP_ERR_UNSUPPORTED
+    del g2
+    # eager calls on the same stream: bit-exact against the oracle
+    with torch.cuda.stream(s):
+        slots.fill_(0xEE)
+        ibp.ibp_compress(meta, src, n, slots, bm, stored, stream=s)
+        ibp.ibp_decompress(meta, torch.from_numpy(o_slots).to(dev), torch.from_numpy(o_bm.view(np.int32).copy()).to(dev),
+                           n, out, stream=s)
+        ibp.ibp_gather_decompress(meta, slots, n, bm, ids, gout, stream=s)
+        ibp.ibp_packed_offsets(meta_s, src_s, 600, off_s, stream=s)
+    s.synchronize()
+    assert ibp.ibp_check(meta, stream=s) == ibp.IBP_OK and ibp.ibp_check(meta_s, stream=s) == ibp.IBP_OK
+    st = stored.cpu().numpy().astype(np.uint64)
+    np.testing.assert_array_equal(st, o_st)
+    sl = slots.cpu().numpy()
+    for t in range(n):
+        k = int(o_st[t])
+        assert np.array_equal(sl[t, :k], o_slots[t, :k]), f"record {t} differs from the oracle's"
+    np.testing.assert_array_equal(out.cpu().numpy(), raw)
+    np.testing.assert_array_equal(gout.cpu().numpy(), raw[[2, 0, 2]])
+    om_s, ob_s = oracle_metadata(meta_s, rows, ws.chunk_bits, ws.period_bits, ws.threshold)
+    o_off = oracle.packed_offsets(rows, rows.shape[1], ws.chunk_bits, ws.period_bits, om_s, ob_s, 600)
+    np.testing.assert_array_equal(off_s.cpu().numpy().astype(np.uint64), o_off)
+    say("[capture] refused under capture, eager calls afterwards bit-exact: ok")
+
+
+def test_one_stream_two_threads_look_back():
+    """Two host threads queue multi-tile calls on ONE stream through one
+    handle (so they share its look-back scratch): thread A decodes and
+    gathers, thread B compresses into its own slots.  Every output is checked
+    against the source and the first compress."""
+    import threading
+
+    dev = device()
+    raw, W, M, T = _three_tile_tensors(4)
+    n, L = raw.shape
+    src = torch.from_numpy(raw).to(dev)
+    meta = ibp.ibp_build_metadata(src, 1, L, W, M, T)
+    slots = torch.empty_like(src)
+    bm = torch.zeros(1, dtype=torch.int32, device=dev)
+    stored = torch.zeros(n, dtype=torch.int64, device=dev)
+    ibp.ibp_compress(meta, src, n, slots, bm, stored)
+    torch.cuda.synchronize()
+    st_ref = stored.cpu().numpy()
+    s = torch.cuda.Stream()
+    k = 20
+    rng = np.random.default_rng(11)
+    id_sets = [torch.from_numpy(rng.integers(0, n, 5)).to(dev) for _ in range(k)]
+    outs_a = [torch.empty((n, L), dtype=torch.uint8, device=dev) for _ in range(k)]
+    gouts_a = [torch.empty((5, L), dtype=torch.uint8, device=dev) for _ in range(k)]
+    slots_b = [torch.empty_like(src) for _ in range(k)]
+    bms_b = [torch.zeros(1, dtype=torch.int32, device=dev) for _ in range(k)]
+    sts_b = [torch.zeros(n, dtype=torch.int64, device=dev) for _ in range(k)]
+    errors = []
+    start = threading.Barrier(2)
+
+    def run_a():
+        try:
+            start.wait()
+            for i in range(k):
+                ibp.ibp_decompress(meta, slots, bm, n, outs_a[i], stream=s)
+                ibp.ibp_gather_decompress(meta, slots, n, bm, id_sets[i], gouts_a[i], stream=s)
+        except Exception as e:  # reported by the main thread
+            errors.append(e)
+
+    def run_b():
+        try:
+            start.wait()
+            for i in range(k):
+                ibp.ibp_compress(meta, src, n, slots_b[i], bms_b[i], sts_b[i], stream=s)
+        except Exception as e:
+            errors.append(e)
+
+    say("[threads] two threads, one stream, multi-tile look-back")
+    ta, tb = threading.Thread(target=run_a), threading.Thread(target=run_b)
+    ta.start()
+    tb.start()
+    ta.join(timeout=60)
+    tb.join(timeout=60)
+    assert not ta.is_alive() and not tb.is_alive(), "a thread did not finish"
+    assert not errors, errors
+    s.synchronize()
+    assert ibp.ibp_check(meta, stream=s) == ibp.IBP_OK
+    ref = slots.cpu().numpy()
+    for i in range(k):
+        assert torch.equal(outs_a[i], src), f"decode {i}"
+        assert torch.equal(gouts_a[i], src[id_sets[i]]), f"gather {i}"
+        assert torch.equal(bms_b[i], bm), f"bitmask of compress {i}"
+        np.testing.assert_array_equal(sts_b[i].cpu().numpy(), st_ref)
+        sb = slots_b[i].cpu().numpy()
+        for t in range(n):
+            assert np.array_equal(sb[t, :st_ref[t]], ref[t, :st_ref[t]]), f"compress {i}, record {t}"
+    say("[threads] two threads, one stream: ok")

@@ -37,27 +37,46 @@ def test_unknown_key_is_an_error():
 
 
 @pytest.mark.gpu
-def test_ops_match_the_binding_on_the_gpu():
+def test_ops_match_the_oracle_on_the_gpu():
+    """torch.ops.ibp.compress / decompress / gather_decompress against the
+    oracle on the same rows: Mask/Bitval, bitmask, stored bytes, every
+    record prefix and raw slot, the decode and a gather with repeated ids."""
     from lossless_tensor_compression_ibp_amd import ibp
     from lossless_tensor_compression_ibp_amd import workloads as WL
+    from oracle import oracle
+    from tests.gpu_util import bitmask_bits, oracle_metadata
 
+    oracle.build(force=False)
     w = WL.DENSE_GNN
-    raw = np.ascontiguousarray(WL.dense_gnn(3000)).view(np.uint8).reshape(3000, -1)
+    n = 3000
+    raw = np.ascontiguousarray(WL.dense_gnn(n)).view(np.uint8).reshape(n, -1)
+    L = raw.shape[1]
     src = torch.from_numpy(raw).cuda()
-    meta = ibp.ibp_build_metadata(src, 1024, raw.shape[1], w.chunk_bits, w.period_bits, w.threshold)
+    meta = ibp.ibp_build_metadata(src, 1024, L, w.chunk_bits, w.period_bits, w.threshold)
+    om, ob = oracle_metadata(meta, raw[:1024], w.chunk_bits, w.period_bits, w.threshold)
     key = torch_ops.register(meta)
     slots, bm, stored = torch.ops.ibp.compress(key, src)
-    ref_slots = torch.empty_like(src)
-    ref_bm = torch.zeros_like(bm)
-    ref_st = torch.zeros_like(stored)
-    ibp.ibp_compress(meta, src, src.shape[0], ref_slots, ref_bm, ref_st)
-    assert torch.equal(bm, ref_bm) and torch.equal(stored, ref_st)
-    for t in range(0, 3000, 97):
-        k = int(ref_st[t])
-        assert torch.equal(slots[t, :k], ref_slots[t, :k])
-    assert torch.equal(torch.ops.ibp.decompress(key, slots, bm), src)
-    ids = torch.from_numpy(np.random.default_rng(2).integers(0, 3000, 999)).cuda()
-    assert torch.equal(torch.ops.ibp.gather_decompress(key, slots, bm, ids), src[ids])
+    o_slots, o_bm, o_stored = oracle.compress(raw, L, w.chunk_bits, w.period_bits, om, ob, n)
+    np.testing.assert_array_equal(bitmask_bits(bm.cpu().numpy().view(np.uint32), n), bitmask_bits(o_bm, n))
+    st = stored.cpu().numpy().astype(np.uint64)
+    np.testing.assert_array_equal(st, o_stored)
+    sl = slots.cpu().numpy()
+    comp = bitmask_bits(o_bm, n).astype(bool)
+    assert 0 < comp.sum() < n, "the rows hold both compressed and raw slots"
+    for t in range(n):
+        k = int(o_stored[t])
+        assert np.array_equal(sl[t, :k], o_slots[t, :k]), f"slot {t} differs from the oracle's"
+    assert np.array_equal(torch.ops.ibp.decompress(key, slots, bm).cpu().numpy(), raw)
+    ids_np = np.random.default_rng(2).integers(0, n, 999)
+    ids = torch.from_numpy(ids_np).cuda()
+    g = torch.ops.ibp.gather_decompress(key, slots, bm, ids).cpu().numpy()
+    o_g = oracle.gather_decompress(o_slots, n, o_bm, ids_np, L, w.chunk_bits, w.period_bits, om, ob)
+    np.testing.assert_array_equal(g, o_g)
+    np.testing.assert_array_equal(g, raw[ids_np])
+    # the ops decode the oracle's own slots too
+    o_slots_t = torch.from_numpy(np.ascontiguousarray(o_slots)).cuda()
+    o_bm_t = torch.from_numpy(o_bm.view(np.int32).copy()).cuda()
+    np.testing.assert_array_equal(torch.ops.ibp.gather_decompress(key, o_slots_t, o_bm_t, ids).cpu().numpy(), o_g)
     torch_ops.check(key)
     torch.library.opcheck(torch.ops.ibp.gather_decompress.default, (key, slots, bm, ids),
                           test_utils=("test_schema", "test_faketensor"))
