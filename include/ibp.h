@@ -63,7 +63,8 @@ typedef enum ibp_status {
     IBP_ERR_DEVICE = -3,      /* a HIP call failed */
     IBP_ERR_NOMEM = -4,       /* device or host allocation failed */
     IBP_ERR_CORRUPT = -5,     /* a compressed slot holds no valid record */
-    IBP_ERR_RANGE = -6        /* a gather id lies outside [0, n_slots) */
+    IBP_ERR_RANGE = -6,       /* a gather id lies outside [0, n_slots) */
+    IBP_ERR_TOO_LARGE = -7    /* more tiles than ibp_decompress_noalloc's static scratch holds */
 } ibp_status;
 
 typedef struct ibp_meta_s* ibp_meta_t; /* opaque, owned by the library */
@@ -148,6 +149,26 @@ ibp_status ibp_decompress(ibp_meta_t meta, const void* slots, const uint32_t* bi
 ibp_status ibp_gather_decompress(ibp_meta_t meta, const void* slots, uint64_t n_slots,
                                  const uint32_t* bitmask, const int64_t* ids, uint64_t n_ids,
                                  void* dst, hipStream_t stream);
+
+/* ibp_decompress for callers that cannot allocate device memory: code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.
+ * Same arguments, contract and output as ibp_decompress.  It calls no
+ * hipMalloc/hipFree: the look-back scratch of tensors longer than one tile
+ * (L > 8 KiB) lives in one static device array of IBP_NOALLOC_SCRATCH_BYTES
+ * per GPU, part of the library's code object and held until the process
+ * ends (its address is looked up with hipGetSymbolAddress on the first call
+ * on each device).  Each call zeroes the part it uses with fill kernels on
+ * `stream` (no memset), so a call may be captured and replayed.  At most
+ * IBP_NOALLOC_MAX_TILES tiles per call, a tile being 8 KiB of one tensor
+ * (n_tensors * ceil(L / 8192) when L > 8192); beyond that the call returns
+ * IBP_ERR_TOO_LARGE before anything is queued.  Every call on a GPU shares
+ * its array: calls that overlap in time on one GPU (other streams, other
+ * handles, other host threads) race on it and their outputs are then
+ * unspecified; calls queued on one stream run one after the other. */
+#define IBP_NOALLOC_SCRATCH_BYTES (1u << 20)
+#define IBP_NOALLOC_MAX_TILES (IBP_NOALLOC_SCRATCH_BYTES / 8u - 32u)
+ibp_status ibp_decompress_noalloc(ibp_meta_t meta, const void* slots, const uint32_t* bitmask,
+                                  uint64_t n_tensors, void* dst, hipStream_t stream);
 
 /* ---------------------------------------------------------------------------
  * Packed cache (FR/KO summary, "Intégration au système": in the GPU software

@@ -395,6 +395,7 @@ const char* ibp_status_string(ibp_status s) {
         case IBP_ERR_NOMEM: return "out of memory";
         case IBP_ERR_CORRUPT: return "corrupt record";
         case IBP_ERR_RANGE: return "id out of range";
+        case IBP_ERR_TOO_LARGE: return "more tiles than the static scratch of ibp_decompress_noalloc holds";
     }
     return "unknown status";
 }
@@ -513,13 +514,77 @@ ibp_status ibp_compress(ibp_meta_t h, const void* src, uint64_t n_tensors, void*
                                   bitmask, stored_bytes, &lb, h->cu_count, stream));
 }
 
+}  // extern "C"
+
+// ---------------------------------------------------------------------------
+// Static look-back scratch of ibp_decompress_noalloc: one array per GPU,
+// loaded with the library's code object and kept until the process ends.
+// Words [0, 32) hold the ticket counter, the status words of the tiles
+// follow.  Host code never passes the array's name to a kernel or a copy:
+// its device address comes from hipGetSymbolAddress, once per device.
+// ---------------------------------------------------------------------------
+namespace {
+constexpr uint64_t kNoAllocScratchWords = IBP_NOALLOC_SCRATCH_BYTES / 8;
+constexpr uint64_t kNoAllocHeadWords = 32;
+constexpr int kMaxDevices = 64;
+static_assert(IBP_NOALLOC_MAX_TILES == kNoAllocScratchWords - kNoAllocHeadWords, "scratch layout");
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+}  // namespace
+
+static __device__ __align__(256) unsigned long long scratch[kNoAllocScratchWords];
+
+// Device address of `scratch` on `dev` (the current device), looked up on
+// the first use on that device.
+static ibp_status noalloc_scratch(int dev, unsigned long long** out) {
+    if (dev < 0 || dev >= kMaxDevices) return IBP_ERR_DEVICE;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void* p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) {
+            (void)hipGetLastError();
+            return IBP_ERR_DEVICE;
+        }
+        g_scratch_ptr[dev] = p;
+    }
+    *out = static_cast<unsigned long long*>(g_scratch_ptr[dev]);
+    return IBP_OK;
+}
+
+// Look-back state of one launch over `tiles` tiles in the static scratch:
+// the ticket and the tiles' status words are zeroed by fill kernels on the
+// stream (no memset node, so the call may be captured in a graph), and the
+// epoch is always 1.
+static ibp_status noalloc_lookback(ibp_meta_s* h, hipStream_t s, uint64_t tiles, LookBack* lb) {
+    unsigned long long* base = nullptr;
+    ibp_status st = noalloc_scratch(h->device, &base);
+    if (st != IBP_OK) return st;
+    uint32_t* ticket = reinterpret_cast<uint32_t*>(base);
+    unsigned long long* status = base + kNoAllocHeadWords;
+    IBP_TRY(launch_fill_u32(ticket, 1, 0, s));
+    IBP_TRY(launch_fill_u32(reinterpret_cast<uint32_t*>(status), 2 * tiles, 0, s));
+    lb->status = status;
+    lb->ticket = ticket;
+    lb->epoch = 1;
+    lb->totals = nullptr;
+    lb->err = h->d_err;
+    return IBP_OK;
+}
+
+extern "C" {
+
 static ibp_status decode_common(ibp_meta_t h, const void* slots, uint64_t n_slots, const uint32_t* bitmask,
-                                const int64_t* ids, uint64_t n_out, void* dst, hipStream_t stream) {
+                                const int64_t* ids, uint64_t n_out, void* dst, hipStream_t stream,
+                                bool static_scratch = false) {
     if (!h) return IBP_ERR_INVALID_ARG;
     if (n_out == 0) return IBP_OK;
+    const uint64_t L = h->params.tensor_bytes;
+    if (static_scratch && L / 4 > kMaxTileWords) {
+        const uint64_t tpt = (L / 4 + kLongTileWordsDecode - 1) / kLongTileWordsDecode;
+        if (n_out > IBP_NOALLOC_MAX_TILES / tpt) return IBP_ERR_TOO_LARGE;
+    }
     DeviceGuard guard(h->device);
     if (!guard.ok) return IBP_ERR_DEVICE;
-    const uint64_t L = h->params.tensor_bytes;
     if (n_out > (~0ull) / L || n_slots > (~0ull) / L) return IBP_ERR_INVALID_ARG;
     const Kind slots_kind = pointer_kind(slots, h->device);
     if (slots_kind == Kind::Bad) return IBP_ERR_INVALID_ARG;
@@ -531,7 +596,9 @@ static ibp_status decode_common(ibp_meta_t h, const void* slots, uint64_t n_slot
     LookBack lb{};
     std::unique_lock<std::mutex> lock;
     if (geo.tiles_per_tensor > 1) {
-        ibp_status st = lookback_for(h, stream, n_out * geo.tiles_per_tensor, 0, &lb, &lock);
+        const uint64_t tiles = n_out * geo.tiles_per_tensor;
+        ibp_status st = static_scratch ? noalloc_lookback(h, stream, tiles, &lb)
+                                       : lookback_for(h, stream, tiles, 0, &lb, &lock);
         if (st != IBP_OK) return st;
     }
     return from_hip(launch_decode(h->tabs, geo, h->sum.max_runs, h->sum.uniform != 0, slots, n_slots, bitmask,
@@ -541,6 +608,11 @@ static ibp_status decode_common(ibp_meta_t h, const void* slots, uint64_t n_slot
 ibp_status ibp_decompress(ibp_meta_t h, const void* slots, const uint32_t* bitmask, uint64_t n_tensors,
                           void* dst, hipStream_t stream) {
     return decode_common(h, slots, n_tensors, bitmask, nullptr, n_tensors, dst, stream);
+}
+
+ibp_status ibp_decompress_noalloc(ibp_meta_t h, const void* slots, const uint32_t* bitmask, uint64_t n_tensors,
+                                  void* dst, hipStream_t stream) {
+    return decode_common(h, slots, n_tensors, bitmask, nullptr, n_tensors, dst, stream, true);
 }
 
 ibp_status ibp_gather_decompress(ibp_meta_t h, const void* slots, uint64_t n_slots, const uint32_t* bitmask,

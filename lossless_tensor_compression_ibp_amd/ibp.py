@@ -23,6 +23,11 @@ IBP_ERR_DEVICE = -3
 IBP_ERR_NOMEM = -4
 IBP_ERR_CORRUPT = -5
 IBP_ERR_RANGE = -6
+IBP_ERR_TOO_LARGE = -7
+
+# ibp_decompress_noalloc's static scratch (include/ibp.h)
+NOALLOC_SCRATCH_BYTES = 1 << 20
+NOALLOC_MAX_TILES = NOALLOC_SCRATCH_BYTES // 8 - 32
 
 # every function the header declares (checked by the tests)
 ABI_FUNCTIONS = (
@@ -31,6 +36,7 @@ ABI_FUNCTIONS = (
     "ibp_check", "ibp_status_string",
     "ibp_packed_offsets", "ibp_compress_packed", "ibp_decompress_packed", "ibp_gather_decompress_packed",
     "ibp_compress_split", "ibp_decompress_split", "ibp_gather_decompress_split",
+    "ibp_decompress_noalloc",
 )
 
 
@@ -71,6 +77,7 @@ def lib():
         L.ibp_meta_destroy.argtypes = [p]
         L.ibp_compress.argtypes = [p, p, u64, p, p, p, p]
         L.ibp_decompress.argtypes = [p, p, p, u64, p, p]
+        L.ibp_decompress_noalloc.argtypes = [p, p, p, u64, p, p]
         L.ibp_gather_decompress.argtypes = [p, p, u64, p, p, u64, p, p]
         L.ibp_check.argtypes = [p, p]
         L.ibp_packed_offsets.argtypes = [p, p, u64, p, p]
@@ -239,6 +246,18 @@ def ibp_decompress(meta: Meta, slots: torch.Tensor, bitmask: torch.Tensor, n_ten
     _need(dst, n * L, "dst")
     _check(lib().ibp_decompress(meta, _ptr(slots), _ptr(bitmask), int(n_tensors), _ptr(dst),
                                 _stream(stream)), "ibp_decompress")
+
+
+def ibp_decompress_noalloc(meta: Meta, slots: torch.Tensor, bitmask: torch.Tensor, n_tensors: int,
+                           dst: torch.Tensor, stream=None):
+    """ibp_decompress without device allocation (the library's static
+    scratch); the same output."""
+    L, n = meta.tensor_bytes, int(n_tensors)
+    _need(slots, n * L, "slots")
+    _need(bitmask, _bitmask_bytes(n), "bitmask")
+    _need(dst, n * L, "dst")
+    _check(lib().ibp_decompress_noalloc(meta, _ptr(slots), _ptr(bitmask), int(n_tensors), _ptr(dst),
+                                        _stream(stream)), "ibp_decompress_noalloc")
 
 
 def ibp_gather_decompress(meta: Meta, slots: torch.Tensor, n_slots: int, bitmask: torch.Tensor,
