@@ -1,23 +1,34 @@
 """IBP decode benchmark on one MI355X.
 
-Default workload: sparse GNN features, 1,048,576 rows x 256 fp32 (97 % exact
-zeros), chunk = 32 words (W = 1024), Mask/Bitval over the whole row
-(M = 8192 bits) from the first 1,024 rows at T = 0.95.  The rows are
-compressed once into fixed 1 KiB slots in pinned host memory; each step
-gathers one batch of 8,192 distinct random row ids, decoding on the GPU
-straight from host memory (zero copy over the host link) into HBM.
+Default (--workload all): every workload at its full size, one after the
+other, and ONE JSON line on stdout.  Its headline is the largest workload,
+llm_bf16 (32 layers of 4096 x 11008 bf16 weights, 2.89 GB per pass, held
+compressed in pinned host memory and decoded zero-copy into HBM one layer at
+a time while a consumer reads the previous layer); the other workloads
+(sparse_gnn, dlrm, kv_bf16, dense_gnn, sparse_gnn_cache) are nested under
+"workloads", each with its own decoded GB/s, space savings, roofline of its
+decode kernel and CPU oracle baseline.
 
-One JSON line on stdout: decoded GB/s of uncompressed output (the metric),
-space savings, the roofline of the decode kernel, the host-link ceiling
-measured in the same run, and the CPU oracle timed on a bounded sample.
-Other workloads: --workload dense_gnn | dlrm | llm_bf16 | kv_bf16.
+Per workload: decoded GB/s of uncompressed output (the metric), space
+savings, the decode kernel's algorithmic bytes per launch over its average
+launch duration (HIP events on its stream) against the roofline that bounds
+it (host link: PCIe 5.0 x16, 64 GB/s per direction, with the hipMemcpy H2D
+ceiling measured in the same run; HBM: 8 TB/s), the encode rate against the
+same bound, and the CPU oracle timed on a bounded sample, single-threaded and
+on every core the process may use.
+
+--workload NAME runs one workload alone (sparse_gnn, dlrm, kv_bf16,
+dense_gnn, sparse_gnn_cache, llm_bf16, or the W x T sweep).
 """
 from __future__ import annotations
 
 import argparse
+import copy
+import gc
 import json
 import os
 import sys
+import threading
 import time
 
 import numpy as np
@@ -33,6 +44,8 @@ from lossless_tensor_compression_ibp_amd import workloads as WL  # noqa: E402
 GB = 1e9
 PCIE5_X16_GBPS = 64.0   # PCIe 5.0 x16, one direction (MI355X host link)
 HBM_PEAK_GBPS = 8000.0  # MI355X HBM3E
+LINE = 128              # bytes a zero-copy read of pinned host memory moves at a time
+METRIC = "IBP decode GB/s (uncompressed out, 1 MI355X) + % of roofline + space savings %"
 
 
 def kernel_source_hash() -> str:
@@ -52,29 +65,33 @@ def kernel_source_hash() -> str:
     return h.hexdigest()[:16]
 
 
-TRAFFIC_NOTE_LINK = ("bytes per launch from rocprofv3 FETCH_SIZE (host reads over the link plus the few HBM "
-                     "reads of ids and bitmask) and WRITE_SIZE (decoded rows into HBM), each scaled by what the "
-                     "counter reads for a copy of known size with the same access pattern; zero-copy reads move "
-                     "whole 128-byte lines")
+TRAFFIC_SOURCE = ("copied from profiles/traffic.json: rocprofv3 --pmc FETCH_SIZE and --pmc WRITE_SIZE of a separate "
+                  "run of this workload (KiB per dispatch, one counter per run), each scaled by what the counter "
+                  "reads for a copy of known size with the same access pattern; null when the kernel sources changed "
+                  "since the counters were taken")
+TRAFFIC_SUMS_LINK = ("bytes per launch: reads over the host link (whole 128-byte lines) + HBM reads of ids, bitmask and "
+                     "header words + HBM writes of the decoded rows")
+TRAFFIC_SUMS_HBM = "bytes per launch: HBM reads + HBM writes"
 
 
 def measured_traffic(workload: str | None):
-    """Bytes per launch of the workload's decode kernel from the committed
-    rocprofv3 counter runs (FETCH_SIZE and WRITE_SIZE, each scaled by what it
-    reads for a copy kernel of known size), or None when the kernels changed
-    since the counters were taken."""
+    """(traffic bytes per launch, read bytes per launch) of the workload's
+    decode kernel from the committed rocprofv3 counter runs, or (None, None)
+    when the kernels changed since the counters were taken."""
     if workload is None:
-        return None
+        return None, None
     path = os.path.join(ROOT, "profiles", "traffic.json")
     try:
         with open(path) as f:
             t = json.load(f)
     except (OSError, ValueError):
-        return None
+        return None, None
     if t.get("source_hash") != kernel_source_hash():
-        return None
+        return None, None
     entry = t.get("workloads", {}).get(workload)
-    return None if entry is None else entry.get("traffic_bytes_per_launch")
+    if entry is None:
+        return None, None
+    return entry.get("traffic_bytes_per_launch"), entry.get("read_bytes_per_launch")
 
 
 def log(msg: str):
@@ -83,6 +100,12 @@ def log(msg: str):
 
 def pinned(shape, dtype):
     return torch.empty(shape, dtype=dtype, pin_memory=True)
+
+
+def line_bytes(stored: np.ndarray) -> int:
+    """Bytes a zero-copy read of these stored items moves: whole 128-byte
+    lines (every slot starts on a line boundary)."""
+    return int((LINE * ((np.asarray(stored, dtype=np.int64) + LINE - 1) // LINE)).sum())
 
 
 def h2d_ceiling(nbytes: int = 1 << 30, reps: int = 5) -> float:
@@ -118,13 +141,28 @@ def copy_kernel_ceiling(nbytes: int = 1 << 30, reps: int = 5) -> float:
     return 2 * nbytes / float(np.median(times[1:])) / GB
 
 
+RAMP_S = 0.25  # untimed calls before the warm-up, so the GPU's clocks have ramped up
+
+
+def ramp(fn, seconds: float = RAMP_S):
+    """Calls fn(0) until `seconds` of wall time have passed (synchronising
+    every call): short timed regions (a few ms) otherwise start on a GPU
+    whose clocks are still rising from idle."""
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < seconds:
+        fn(0)
+        torch.cuda.synchronize()
+
+
 def timed(fn, steps: int, warmup: int):
-    """Runs fn(i) warmup times, then times exactly `steps` calls between two
-    synchronisations.  Returns (wall seconds, launch durations in seconds):
-    one HIP event pair on the launching stream brackets the whole timed
-    region, and each launch is credited the region's GPU time / steps (events
-    around every launch would put their own gaps between the kernels)."""
+    """Runs fn(i) warmup times (after the untimed ramp), then times exactly
+    `steps` calls between two synchronisations.  Returns (wall seconds,
+    launch durations in seconds): one HIP event pair on the launching stream
+    brackets the whole timed region, and each launch is credited the region's
+    GPU time / steps (events around every launch would put their own gaps
+    between the kernels)."""
     stream = torch.cuda.current_stream()
+    ramp(fn)
     for i in range(warmup):
         fn(i)
     torch.cuda.synchronize()
@@ -170,97 +208,228 @@ def queued_durations(fn, steps: int, first: int = 0):
     return np.full(steps, start.elapsed_time(end) / 1e3 / steps)
 
 
-def cpu_oracle_gather(raw_rows: np.ndarray, w: WL.Workload, batch: int, budget_s: float,
-                      sample_rows: int) -> dict:
-    """The oracle, single-threaded, decoding random batches of rows (headers
-    in a separate array, as the GPU line does) from its own slots until the
-    time budget is spent (encode excluded)."""
-    from oracle import oracle
-
-    oracle.build(force=False)
-    sub = np.ascontiguousarray(raw_rows[:sample_rows])
-    L = sub.shape[1]
-    mask, bitval = oracle.build_metadata(sub[: w.n_sample], 8 * L, w.chunk_bits, w.period_bits,
-                                         w.threshold, min(w.n_sample, sub.shape[0]))
-    slots, headers, bm, _ = oracle.compress_split(sub, L, w.chunk_bits, w.period_bits, mask, bitval, sub.shape[0])
-    rng = np.random.default_rng(WL.ID_SEED)
-    rows = 0
-    t0 = time.perf_counter()
-    while time.perf_counter() - t0 < budget_s:
-        ids = rng.choice(sub.shape[0], batch, replace=False)
-        oracle.gather_decompress_split(slots, sub.shape[0], headers, bm, ids, L, w.chunk_bits, w.period_bits,
-                                       mask, bitval)
-        rows += batch
-    dt = time.perf_counter() - t0
-    return {"value": round(rows * L / dt / GB, 6), "unit": "GB/s", "cores": 1, "host_cores": os.cpu_count(),
-            "kind": "oracle",
-            "sample": f"{rows} rows decoded by gather in batches of {batch} ids from the oracle's slots of "
-                      f"the first {sample_rows} rows ({dt:.1f} s, single thread)"}
-
-
 # ---------------------------------------------------------------------------
-# Sparse GNN: zero-copy gather from pinned host slots (default workload)
-def cpu_oracle_roundtrip(rows: np.ndarray, w: WL.Workload, n_sample: int, budget_s: float, what: str) -> dict:
-    """The oracle, single-threaded: metadata from the first n_sample rows,
-    then compress and decompress of all the rows, repeated until the time
-    budget is spent.  value: GB/s of decoded tensor; encode_GBps beside it."""
+# CPU oracle baselines: the oracle as it stands, single-threaded, and the same
+# oracle on every core the process may use over disjoint tensor ranges
+# ---------------------------------------------------------------------------
+def oracle_threads() -> int:
+    """Threads for the all-cores baseline: the cores this process may run on,
+    at most 16 (the host share of one GPU)."""
+    try:
+        n = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        n = os.cpu_count() or 1
+    return max(1, min(16, n))
+
+
+def run_threads(work, n_threads: int, budget_s: float):
+    """work(k, deadline) -> bytes thread k decoded; the oracle's C calls
+    release the GIL, so the threads run on separate cores.  Returns (total
+    bytes, wall seconds)."""
+    out = [0] * n_threads
+    t0 = time.perf_counter()
+    deadline = t0 + budget_s
+
+    def one(k):
+        out[k] = work(k, deadline)
+
+    ts = [threading.Thread(target=one, args=(k,)) for k in range(n_threads)]
+    for t in ts:
+        t.start()
+    for t in ts:
+        t.join()
+    return sum(out), time.perf_counter() - t0
+
+
+def cpu_gather_baseline(rows: np.ndarray, w: WL.Workload, batch: int, budget_s: float, what: str,
+                        layout: str = "slots", replace: bool = True) -> dict:
+    """Gathers of random id batches decoded by the oracle from its own slots
+    ("slots"), slots with headers in a separate array ("split") or packed
+    items ("packed") of `rows` (encode excluded): single-threaded for
+    budget_s, then on every core over disjoint row ranges for budget_s / 2."""
     from oracle import oracle
 
     oracle.build(force=False)
     rows = np.ascontiguousarray(rows)
     n, L = rows.shape
-    mask, bitval = oracle.build_metadata(rows[:n_sample], 8 * L, w.chunk_bits, w.period_bits, w.threshold,
-                                         n_sample)
+    W, M = w.chunk_bits, w.period_bits
+    ns = min(w.n_sample, n)
+    mask, bitval = oracle.build_metadata(rows[:ns], 8 * L, W, M, w.threshold, ns)
+    if layout == "split":
+        slots, headers, bm, _ = oracle.compress_split(rows, L, W, M, mask, bitval, n)
+        gather = lambda ids: oracle.gather_decompress_split(slots, n, headers, bm, ids, L, W, M, mask, bitval)  # noqa: E731
+    elif layout == "packed":
+        buf, off, bm = oracle.compress_packed(rows, L, W, M, mask, bitval, n)
+        gather = lambda ids: oracle.gather_decompress_packed(buf, off, n, bm, ids, L, W, M, mask, bitval)  # noqa: E731
+    else:
+        slots, bm, _ = oracle.compress(rows, L, W, M, mask, bitval, n)
+        gather = lambda ids: oracle.gather_decompress(slots, n, bm, ids, L, W, M, mask, bitval)  # noqa: E731
+
+    def draw(rng, lo, hi, b):
+        return lo + (rng.choice(hi - lo, b, replace=False) if not replace else rng.integers(0, hi - lo, b))
+
+    rng = np.random.default_rng(WL.ID_SEED)
+    done = 0
+    t0 = time.perf_counter()
+    while done == 0 or time.perf_counter() - t0 < budget_s:
+        ids = draw(rng, 0, n, batch)
+        out = gather(ids)
+        done += batch
+    dt = time.perf_counter() - t0
+    if not np.array_equal(out, rows[ids]):
+        raise SystemExit("oracle gather differs from the source rows")
+    P = oracle_threads()
+
+    def work(k, deadline):
+        lo, hi = k * n // P, (k + 1) * n // P
+        b = min(batch, hi - lo)
+        r = np.random.default_rng([WL.ID_SEED, k])
+        got = 0
+        while got == 0 or time.perf_counter() < deadline:
+            gather(draw(r, lo, hi, b))
+            got += b * L
+        return got
+
+    tot, wall = run_threads(work, P, budget_s / 2)
+    return {"value": round(done * L / dt / GB, 6), "unit": "GB/s", "cores": 1, "host_cores": os.cpu_count(),
+            "kind": "oracle",
+            "sample": f"{done} rows decoded by gather in batches of {batch} ids from the oracle's "
+                      f"{ {'split': 'slots (headers in a separate array)', 'packed': 'packed items'}.get(layout, 'slots')} "
+                      f"of {what} ({dt:.1f} s, single thread)",
+            "all_cores": {"value": round(tot / wall / GB, 6), "unit": "GB/s", "cores": P, "kind": "oracle",
+                          "sample": f"the same gathers on {P} threads, thread k drawing ids from its own 1/{P} of the "
+                                    f"rows ({wall:.1f} s); a baseline only"}}
+
+
+def cpu_roundtrip_baseline(rows: np.ndarray, w: WL.Workload, n_sample: int, budget_s: float, what: str,
+                           single_n: int | None = None) -> dict:
+    """The oracle single-threaded: metadata from the first n_sample rows, then
+    compress and decompress of the first single_n rows (default all) until
+    budget_s is spent (value: decode GB/s, encode_GBps beside it); then decode
+    of its own slots of all the rows on every core, thread k on its own 1/P of
+    them, for budget_s / 2."""
+    from oracle import oracle
+
+    oracle.build(force=False)
+    rows = np.ascontiguousarray(rows)
+    n, L = rows.shape
+    W, M = w.chunk_bits, w.period_bits
+    mask, bitval = oracle.build_metadata(rows[:n_sample], 8 * L, W, M, w.threshold, n_sample)
+    n1 = n if single_n is None else single_n
     t_enc = t_dec = 0.0
     reps = 0
     t0 = time.perf_counter()
     while reps == 0 or time.perf_counter() - t0 < budget_s:
         a = time.perf_counter()
-        slots, bm, _ = oracle.compress(rows, L, w.chunk_bits, w.period_bits, mask, bitval, n)
+        slots, bm, _ = oracle.compress(rows[:n1], L, W, M, mask, bitval, n1)
         b = time.perf_counter()
-        out = oracle.decompress(slots, bm, L, w.chunk_bits, w.period_bits, mask, bitval, n)
+        out = oracle.decompress(slots, bm, L, W, M, mask, bitval, n1)
         t_enc += b - a
         t_dec += time.perf_counter() - b
         reps += 1
-    if not np.array_equal(out, rows):
+    if not np.array_equal(out, rows[:n1]):
         raise SystemExit("oracle round trip differs")
-    return {"value": round(reps * n * L / t_dec / GB, 6), "unit": "GB/s", "cores": 1, "host_cores": os.cpu_count(),
-            "kind": "oracle", "encode_GBps": round(reps * n * L / t_enc / GB, 6),
-            "sample": f"{what}: {reps} compress + decompress round trips ({t_enc + t_dec:.1f} s, single thread)"}
+    P = oracle_threads()
+    per = max(1, n // P)
+    parts = [(k * per, min(n, (k + 1) * per)) for k in range(min(P, n))]
+    enc = [None] * len(parts)
+
+    def encode_part(k, deadline):  # untimed set-up, on all threads too
+        lo, hi = parts[k]
+        enc[k] = oracle.compress(rows[lo:hi], L, W, M, mask, bitval, hi - lo)[:2]
+        return 0
+
+    run_threads(encode_part, len(parts), 0.0)
+
+    def work(k, deadline):
+        lo, hi = parts[k]
+        sl, bmk = enc[k]
+        got = 0
+        while got == 0 or time.perf_counter() < deadline:
+            oracle.decompress(sl, bmk, L, W, M, mask, bitval, hi - lo)
+            got += (hi - lo) * L
+        return got
+
+    tot, wall = run_threads(work, len(parts), budget_s / 2)
+    return {"value": round(reps * n1 * L / t_dec / GB, 6), "unit": "GB/s", "cores": 1, "host_cores": os.cpu_count(),
+            "kind": "oracle", "encode_GBps": round(reps * n1 * L / t_enc / GB, 6),
+            "sample": f"{what}: {reps} compress + decompress round trips ({t_enc + t_dec:.1f} s, single thread)",
+            "all_cores": {"value": round(tot / wall / GB, 6), "unit": "GB/s", "cores": len(parts), "kind": "oracle",
+                          "sample": f"decode of the oracle's own slots of all {n} tensors of the sample on "
+                                    f"{len(parts)} threads, thread k on its own 1/{len(parts)} of them ({wall:.1f} s); "
+                                    f"a baseline only"}}
 
 
-def cpu_oracle_gather_slots(rows: np.ndarray, w: WL.Workload, batch: int, budget_s: float, what: str,
-                            packed: bool = False, replace: bool = True) -> dict:
-    """The oracle, single-threaded, decoding random id batches from its own
-    slots (or packed items) of the sampled rows until the time budget is
-    spent (encode excluded)."""
-    from oracle import oracle
-
-    oracle.build(force=False)
-    rows = np.ascontiguousarray(rows)
-    n, L = rows.shape
-    ns = min(w.n_sample, n)
-    mask, bitval = oracle.build_metadata(rows[:ns], 8 * L, w.chunk_bits, w.period_bits, w.threshold, ns)
-    if packed:
-        buf, off, bm = oracle.compress_packed(rows, L, w.chunk_bits, w.period_bits, mask, bitval, n)
-    else:
-        slots, bm, _ = oracle.compress(rows, L, w.chunk_bits, w.period_bits, mask, bitval, n)
-    rng = np.random.default_rng(WL.ID_SEED)
-    done = 0
-    t0 = time.perf_counter()
-    while done == 0 or time.perf_counter() - t0 < budget_s:
-        ids = rng.choice(n, batch, replace=replace)
-        if packed:
-            oracle.gather_decompress_packed(buf, off, n, bm, ids, L, w.chunk_bits, w.period_bits, mask, bitval)
-        else:
-            oracle.gather_decompress(slots, n, bm, ids, L, w.chunk_bits, w.period_bits, mask, bitval)
-        done += batch
-    dt = time.perf_counter() - t0
-    return {"value": round(done * L / dt / GB, 6), "unit": "GB/s", "cores": 1, "host_cores": os.cpu_count(),
-            "kind": "oracle", "sample": f"{done} rows decoded by gather in batches of {batch} ids from the oracle's "
-                                        f"{'packed items' if packed else 'slots'} of {what} ({dt:.1f} s, single thread)"}
+# ---------------------------------------------------------------------------
+# Result assembly
+# ---------------------------------------------------------------------------
+def base_result(args, value, wall, config, savings, kernel, durs, roofline, **extra) -> dict:
+    res = {
+        "metric": METRIC, "value": round(value, 3), "unit": "GB/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(wall / args.steps * 1e3, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "u32", "data": "synthetic",
+        "config": config, "space_savings_pct": round(100 * savings, 3), "kernel": kernel,
+        "kernel_avg_us": round(float(np.mean(durs)) * 1e6, 2), "roofline": roofline,
+        "ramp_s": RAMP_S,
+    }
+    res.update(extra)
+    return res
 
 
+def hbm_roofline(bytes_per_launch: float, durs, workload: str | None) -> dict:
+    achieved = bytes_per_launch / float(np.mean(durs)) / GB
+    traffic, _ = measured_traffic(workload)
+    return {"bound": "hbm", "achieved": round(achieved, 3), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": traffic, "traffic_source": TRAFFIC_SOURCE,
+            "traffic_sums": TRAFFIC_SUMS_HBM, "copy_kernel_ceiling_measured": round(copy_kernel_ceiling(), 3),
+            "algorithmic_bytes_per_launch": int(bytes_per_launch)}
+
+
+def link_roofline(link_bytes_per_launch: float, durs, savings: float, workload: str | None, h2d: float,
+                  line_bytes_per_launch: float | None = None, out_bytes_per_launch: float | None = None) -> dict:
+    """Host-link roofline of a zero-copy decode: record bytes over the link
+    per launch / launch duration against 64 GB/s, with the same-run H2D
+    ceiling; the decoded roofline is H2D / compressed fraction, and, where
+    whole 128-byte lines are what the link moves, H2D x output / line bytes."""
+    achieved = link_bytes_per_launch / float(np.mean(durs)) / GB
+    traffic, read = measured_traffic(workload)
+    r = {"bound": "pcie", "achieved": round(achieved, 3), "peak": PCIE5_X16_GBPS, "unit": "GB/s",
+         "frac": round(achieved / PCIE5_X16_GBPS, 4), "traffic": traffic, "traffic_source": TRAFFIC_SOURCE,
+         "traffic_sums": TRAFFIC_SUMS_LINK, "traffic_read_bytes": read,
+         "link_ceiling_measured": round(h2d, 3), "frac_of_measured_ceiling": round(achieved / h2d, 4),
+         "algorithmic_bytes_per_launch": int(link_bytes_per_launch),
+         "decoded_roofline_GBps": round(h2d / (1.0 - savings), 3)}
+    if line_bytes_per_launch is not None and out_bytes_per_launch:
+        r["line_bytes_per_launch"] = int(line_bytes_per_launch)
+        r["line_granular_decoded_roofline_GBps"] = round(h2d * out_bytes_per_launch / line_bytes_per_launch, 3)
+    return r
+
+
+def decoded_fracs(res: dict):
+    """Decoded GB/s against the decoded rooflines of a link-bound line."""
+    roof = res["roofline"]
+    res["decoded_frac_of_roofline"] = round(res["value"] / roof["decoded_roofline_GBps"], 4)
+    res["decoded_frac_of_published_link_roofline"] = round(
+        res["value"] / (PCIE5_X16_GBPS / (1.0 - res["space_savings_pct"] / 100)), 4)
+    if "line_granular_decoded_roofline_GBps" in roof:
+        res["decoded_frac_of_line_granular_roofline"] = round(
+            res["value"] / roof["line_granular_decoded_roofline_GBps"], 4)
+
+
+def encode_link(in_bytes: float, seconds: float, h2d: float, note: str) -> dict:
+    gbps = in_bytes / seconds / GB
+    return {"GBps": round(gbps, 3), "bound": "pcie", "frac_of_measured_h2d": round(gbps / h2d, 4),
+            "frac_of_peak": round(gbps / PCIE5_X16_GBPS, 4), "note": note}
+
+
+def encode_hbm(in_bytes: float, hbm_bytes: float, seconds: float, note: str) -> dict:
+    return {"GBps": round(in_bytes / seconds / GB, 3), "bound": "hbm",
+            "hbm_GBps": round(hbm_bytes / seconds / GB, 3),
+            "frac_of_peak": round(hbm_bytes / seconds / GB / HBM_PEAK_GBPS, 4), "note": note}
+
+
+# ---------------------------------------------------------------------------
+# Sparse GNN: zero-copy gather from pinned host slots
 # ---------------------------------------------------------------------------
 def run_sparse_gnn(args) -> dict:
     """Zero-copy gathers of 8,192 random rows from pinned host slots.  The
@@ -290,12 +459,7 @@ def run_sparse_gnn(args) -> dict:
     headers = torch.zeros((n, hw), dtype=torch.int32, device=dev)
     bitmask = torch.zeros((n + 31) // 32, dtype=torch.int32, device=dev)
     stored = torch.zeros(n, dtype=torch.int64, device=dev)
-    enc_s = []
-    for _ in range(4):
-        t0 = time.perf_counter()
-        ibp.ibp_compress_split(meta, host, n, slots, headers, bitmask, stored)
-        torch.cuda.synchronize()
-        enc_s.append(time.perf_counter() - t0)
+    t_enc = encode_seconds(lambda: ibp.ibp_compress_split(meta, host, n, slots, headers, bitmask, stored))
     payload_np = stored.cpu().numpy()
     comp_np = (bitmask.cpu().numpy().view(np.uint32)[np.arange(n) >> 5] >> (np.arange(n) & 31)) & 1
     # compressed bytes: payload in the slots plus the header words kept in HBM
@@ -305,9 +469,9 @@ def run_sparse_gnn(args) -> dict:
     slots_plain = pinned((n, L), torch.uint8)
     bitmask_plain = torch.zeros_like(bitmask)
     stored_plain = torch.zeros(n, dtype=torch.int64, device=dev)
-    ibp.ibp_compress(meta, host, n, slots_plain, bitmask_plain, stored_plain)
-    torch.cuda.synchronize()
+    t_enc_plain = encode_seconds(lambda: ibp.ibp_compress(meta, host, n, slots_plain, bitmask_plain, stored_plain))
     stored_plain_np = stored_plain.cpu().numpy()
+    savings_plain = 1.0 - stored_plain_np.sum() / (n * L)
 
     ids_all = WL.batch_ids(n, batch, args.warmup + args.steps, replace=False)
     ids_dev = torch.from_numpy(ids_all).to(dev)
@@ -342,65 +506,44 @@ def run_sparse_gnn(args) -> dict:
     def raw_step(i):
         ibp.ibp_gather_decompress(meta, host, n, zero_bm, ids_dev[i], out[i & 1])
 
-    if args.no_raw:
-        raw_wall = float("nan")
-    else:
-        raw_wall, _ = timed(raw_step, args.steps, args.warmup)
+    raw_wall = float("nan") if args.no_raw else timed(raw_step, args.steps, args.warmup)[0]
     h2d = h2d_ceiling()
-    achieved = float(link_bytes.mean() / durs.mean() / GB)
-    comp_fraction = 1.0 - savings
-    res = {
-        "metric": "IBP decode GB/s (uncompressed out, 1 MI355X) + % of roofline + space savings %",
-        "value": round(value, 3),
-        "unit": "GB/s",
-        "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
-        "ms_per_step": round(wall / args.steps * 1e3, 4),
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": "u32",
-        "data": "synthetic",
-        "config": {"workload": f"sparse_gnn: {n} rows x 256 fp32 (97% zeros), W=1024, M=8192, T=0.95, "
-                               f"1 KiB slots in pinned host memory (payload only; each compressed row's header "
-                               f"word in HBM beside the bitmask), zero-copy gather of {batch} distinct random "
-                               f"row ids per step into HBM",
-                   "rows": n, "tensor_bytes": L, "batch_ids": batch, "chunk_bits": w.chunk_bits,
-                   "period_bits": w.period_bits, "threshold": w.threshold, "layout": "headers in HBM",
-                   "hbm_header_bytes": int(4 * hw * n), "hbm_bitmask_bytes": int(4 * ((n + 31) // 32))},
-        "space_savings_pct": round(100 * savings, 3),
-        "kernel": "ibp::k_decode_small<0, true, true, 1, true>",
-        "kernel_avg_us": round(float(durs.mean()) * 1e6, 2),
-        "roofline": {
-            "bound": "pcie",
-            "achieved": round(achieved, 3),
-            "peak": PCIE5_X16_GBPS,
-            "unit": "GB/s",
-            "frac": round(achieved / PCIE5_X16_GBPS, 4),
-            "traffic": None if args.small else measured_traffic("sparse_gnn"),
-            "traffic_note": TRAFFIC_NOTE_LINK,
-            "link_ceiling_measured": round(h2d, 3),
-            "frac_of_measured_ceiling": round(achieved / h2d, 4),
-            "algorithmic_bytes_per_launch": int(link_bytes.mean()),
-        },
-        # decoded throughput against link bandwidth / compressed fraction
-        "decoded_roofline_GBps": round(h2d / comp_fraction, 3),
-        "decoded_frac_of_roofline": round(value / (h2d / comp_fraction), 4),
-        "decoded_frac_of_published_link_roofline": round(value / (PCIE5_X16_GBPS / comp_fraction), 4),
-        "slot_layout": {"decoded_GBps": round(args.steps * out_bytes / plain_wall / GB, 3),
-                        "kernel_avg_us": round(float(plain_durs.mean()) * 1e6, 2),
-                        "link_bytes_per_launch": int(stored_plain_np[timed_ids].sum(axis=1).mean())},
-        "raw_zero_copy_gather_GBps": round(args.steps * out_bytes / raw_wall / GB, 3),
-        "speedup_vs_raw_zero_copy": round(raw_wall / wall, 3),
-        "encode_GBps": round(n * L / float(np.median(enc_s[1:])) / GB, 3),
-        "metadata_ms": round(t_meta * 1e3, 2),
-        "meta": info,
-    }
+    roof = link_roofline(float(link_bytes.mean()), durs, savings, None if args.small else "sparse_gnn", h2d,
+                         float(np.mean([line_bytes(payload_np[t]) for t in timed_ids])), out_bytes)
+    plain_link = float(stored_plain_np[timed_ids].sum(axis=1).mean())
+    plain_lines = float(np.mean([line_bytes(stored_plain_np[t]) for t in timed_ids]))
+    plain_value = args.steps * out_bytes / plain_wall / GB
+    plain_achieved = plain_link / float(plain_durs.mean()) / GB
+    res = base_result(
+        args, value, wall,
+        {"workload": f"sparse_gnn: {n} rows x 256 fp32 (97% zeros), W=1024, M=8192, T=0.95, 1 KiB slots in pinned "
+                     f"host memory (payload only; each compressed row's header word in HBM beside the bitmask), "
+                     f"zero-copy gather of {batch} distinct random row ids per step into HBM",
+         "rows": n, "tensor_bytes": L, "batch_ids": batch, "chunk_bits": w.chunk_bits,
+         "period_bits": w.period_bits, "threshold": w.threshold, "layout": "headers in HBM",
+         "hbm_header_bytes": int(4 * hw * n), "hbm_bitmask_bytes": int(4 * ((n + 31) // 32)),
+         "hbm_header_bytes_read_per_launch": int(4 * hw * batch)},
+        savings, "ibp::k_decode_small<0, true, true, 1, true>", durs, roof,
+        slot_layout={
+            "what": "the pages' own layout: the whole record (header word + payload) in the slot, only the bitmask "
+                    "in HBM; same rows, same ids, same run",
+            "decoded_GBps": round(plain_value, 3), "kernel_avg_us": round(float(plain_durs.mean()) * 1e6, 2),
+            "space_savings_pct": round(100 * savings_plain, 3),
+            "link_bytes_per_launch": int(plain_link), "line_bytes_per_launch": int(plain_lines),
+            "achieved_GBps": round(plain_achieved, 3), "frac_of_peak": round(plain_achieved / PCIE5_X16_GBPS, 4),
+            "frac_of_measured_ceiling": round(plain_achieved / h2d, 4),
+            "decoded_frac_of_roofline": round(plain_value / (h2d / (1.0 - savings_plain)), 4),
+            "decoded_frac_of_line_granular_roofline": round(plain_value / (h2d * out_bytes / plain_lines), 4),
+            "encode": encode_link(n * L, t_enc_plain, h2d, "host -> host, pinned source to pinned slots")},
+        raw_zero_copy_gather_GBps=round(args.steps * out_bytes / raw_wall / GB, 3),
+        speedup_vs_raw_zero_copy=round(raw_wall / wall, 3),
+        encode=encode_link(n * L, t_enc, h2d, "host -> host, pinned source to pinned slots, header words to HBM"),
+        metadata_ms=round(t_meta * 1e3, 2), meta=info)
+    decoded_fracs(res)
     if not args.no_cpu:
         log("[bench] CPU oracle baseline")
-        res["cpu_baseline"] = cpu_oracle_gather(raw_np, w, batch=1024, budget_s=args.cpu_budget,
-                                                sample_rows=16384)
+        res["cpu_baseline"] = cpu_gather_baseline(raw_np[:16384], w, 1024, args.cpu_budget,
+                                                  "the first 16,384 rows (16 MiB)", layout="split", replace=False)
     return res
 
 
@@ -427,6 +570,10 @@ def run_kv_bf16(args) -> dict:
     _, enc_durs = timed(lambda i: ibp.ibp_compress(meta, src, n, slots, bitmask, stored), 5, 1)
     stored_np = stored.cpu().numpy()
     savings = 1.0 - stored_np.sum() / (n * L)
+    # compressed pages, and the chunks that matched in them (header bits)
+    bits = np.unpackbits(bitmask.cpu().numpy().view(np.uint8), bitorder="little")[:n].astype(bool)
+    hdr = slots[torch.from_numpy(np.flatnonzero(bits)).to(dev), :128].cpu().numpy().view(np.uint32)
+    matched = int(np.bitwise_count(hdr).sum())
     out = torch.empty_like(src)
     wall, durs = timed(lambda i: ibp.ibp_decompress(meta, slots, bitmask, n, out), args.steps, args.warmup)
     assert ibp.ibp_check(meta) == ibp.IBP_OK
@@ -434,55 +581,22 @@ def run_kv_bf16(args) -> dict:
         raise SystemExit("decoded pages differ")
     hbm_bytes = float(stored_np.sum() + n * L + 4 * ((n + 31) // 32))
     roof = hbm_roofline(hbm_bytes, durs, None if args.small else "kv_bf16")
-    cpu = None
-    if not args.no_cpu:
-        log("[bench] CPU oracle baseline")
-        cpu = cpu_oracle_roundtrip(src[:2048].cpu().numpy(), w, w.n_sample, args.cpu_budget,
-                                   "the first 2,048 pages (8 MiB; metadata from their first 1,024)")
+    t_enc = float(np.mean(enc_durs))
     res = base_result(
         args, n * L * args.steps / wall / GB, wall,
         {"workload": f"kv_bf16: {layers} layers x 32 heads x 4096 tokens x 128 bf16, 4 KiB pages in HBM slots, "
                      f"W=32, M=32768, T=0.95, decode of all {n} pages per step", "pages": n, "tensor_bytes": L},
         savings, "ibp::k_decode_small<3, false, true, 4, false>", durs, roof,
-        encode_GBps=round(n * L / float(np.mean(enc_durs)) / GB, 3), metadata_ms=round(t_meta * 1e3, 2),
-        meta=ibp.ibp_meta_get_info(meta))
-    if cpu:
-        res["cpu_baseline"] = cpu
+        compressed_page_frac=round(float(bits.mean()), 6),
+        matched_chunk_frac_in_compressed_pages=round(matched / max(1, int(bits.sum()) * 1024), 6),
+        encode=encode_hbm(n * L, n * L + stored_np.sum(), t_enc, "HBM -> HBM, all pages per launch"),
+        metadata_ms=round(t_meta * 1e3, 2), meta=ibp.ibp_meta_get_info(meta))
+    if not args.no_cpu:
+        log("[bench] CPU oracle baseline")
+        res["cpu_baseline"] = cpu_roundtrip_baseline(
+            src[:2048].cpu().numpy(), w, w.n_sample, args.cpu_budget,
+            "the first 2,048 pages (8 MiB; metadata from their first 1,024)")
     return res
-
-
-METRIC = "IBP decode GB/s (uncompressed out, 1 MI355X) + % of roofline + space savings %"
-
-
-def base_result(args, value, wall, config, savings, kernel, durs, roofline, **extra) -> dict:
-    res = {
-        "metric": METRIC, "value": round(value, 3), "unit": "GB/s", "n_gpus": 1,
-        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(wall / args.steps * 1e3, 4),
-        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "u32", "data": "synthetic",
-        "config": config, "space_savings_pct": round(100 * savings, 3), "kernel": kernel,
-        "kernel_avg_us": round(float(np.mean(durs)) * 1e6, 2), "roofline": roofline,
-    }
-    res.update(extra)
-    return res
-
-
-def hbm_roofline(bytes_per_launch: float, durs, workload: str) -> dict:
-    achieved = bytes_per_launch / float(np.mean(durs)) / GB
-    return {"bound": "hbm", "achieved": round(achieved, 3), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-            "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": measured_traffic(workload),
-            "copy_kernel_ceiling_measured": round(copy_kernel_ceiling(), 3),
-            "algorithmic_bytes_per_launch": int(bytes_per_launch)}
-
-
-def link_roofline(link_bytes_per_launch: float, durs, savings: float, workload: str) -> dict:
-    achieved = link_bytes_per_launch / float(np.mean(durs)) / GB
-    h2d = h2d_ceiling()
-    return {"bound": "pcie", "achieved": round(achieved, 3), "peak": PCIE5_X16_GBPS, "unit": "GB/s",
-            "frac": round(achieved / PCIE5_X16_GBPS, 4), "traffic": measured_traffic(workload),
-            "traffic_note": TRAFFIC_NOTE_LINK,
-            "link_ceiling_measured": round(h2d, 3), "frac_of_measured_ceiling": round(achieved / h2d, 4),
-            "algorithmic_bytes_per_launch": int(link_bytes_per_launch),
-            "decoded_roofline_GBps": round(h2d / (1.0 - savings), 3)}
 
 
 # ---------------------------------------------------------------------------
@@ -499,7 +613,8 @@ def run_dense_gnn(args) -> dict:
     slots = torch.empty_like(src)
     bitmask = torch.zeros((n + 31) // 32, dtype=torch.int32, device=dev)
     stored = torch.zeros(n, dtype=torch.int64, device=dev)
-    _, enc_durs = timed(lambda i: ibp.ibp_compress(meta, src, n, slots, bitmask, stored), 20, 2)
+    timed(lambda i: ibp.ibp_compress(meta, src, n, slots, bitmask, stored), 20, 2)
+    enc_durs = queued_durations(lambda i: ibp.ibp_compress(meta, src, n, slots, bitmask, stored), 20)
     stored_np = stored.cpu().numpy()
     savings = 1.0 - stored_np.sum() / (n * L)
     out = torch.empty_like(src)
@@ -516,21 +631,18 @@ def run_dense_gnn(args) -> dict:
     raw_wall, _ = timed(lambda i: raw_copy.copy_(src), args.steps, args.warmup)
     raw_durs = queued_durations(lambda i: raw_copy.copy_(src), args.steps)
     del raw_copy
-    cpu = None
-    if not args.no_cpu:
-        log("[bench] CPU oracle baseline")
-        cpu = cpu_oracle_roundtrip(src.cpu().numpy(), w, w.n_sample, args.cpu_budget,
-                                   f"all {n} rows (8 MiB; metadata from the first 1,024)")
     res = base_result(
         args, n * L * args.steps / wall / GB, wall,
         {"workload": f"dense_gnn: {n} rows x 128 fp32 |N(0,0.5)| with 3% N(0,50) rows, W=32, M=4096, T=0.95, "
                      f"slots in HBM, contiguous decode of all rows per step", "rows": n, "tensor_bytes": L},
         savings, "ibp::k_decode_small<1, false, true, 1, false>", durs, hbm_roofline(hbm_bytes, durs, "dense_gnn"),
-        encode_GBps=round(n * L / float(np.mean(enc_durs)) / GB, 3),
+        encode=encode_hbm(n * L, n * L + stored_np.sum(), float(np.mean(enc_durs)), "HBM -> HBM, all rows per launch"),
         uncompressed_hbm_copy_GBps=round(n * L * args.steps / raw_wall / GB, 3),
         uncompressed_copy_kernel_us=round(float(np.mean(raw_durs)) * 1e6, 2), meta=ibp.ibp_meta_get_info(meta))
-    if cpu:
-        res["cpu_baseline"] = cpu
+    if not args.no_cpu:
+        log("[bench] CPU oracle baseline")
+        res["cpu_baseline"] = cpu_roundtrip_baseline(raw_np, w, w.n_sample, args.cpu_budget,
+                                                     f"all {n} rows (8 MiB; metadata from the first 1,024)")
     return res
 
 
@@ -558,6 +670,7 @@ def run_dlrm(args) -> dict:
     ids_np = WL.batch_ids(n, batch, n_batches, replace=True)
     ids = torch.from_numpy(ids_np).to(dev)
     out = torch.empty((2, batch, L), dtype=torch.uint8, device=dev)
+
     def step(i):
         for j in range(per_step):
             k = i * per_step + j
@@ -569,22 +682,27 @@ def run_dlrm(args) -> dict:
     if not np.array_equal(out[last & 1].cpu().numpy(), raw_np[ids_np[last]]):
         raise SystemExit("decoded rows differ")
     durs = np.full(args.steps * per_step, float(step_durs.mean()) / per_step)  # per gather launch
-    link = float(stored_np[ids_np[args.warmup * per_step:]].sum(axis=1).mean())
+    timed_ids = ids_np[args.warmup * per_step:]
+    link = float(stored_np[timed_ids].sum(axis=1).mean())
+    lines = float(np.mean([line_bytes(stored_np[t]) for t in timed_ids[:per_step]]))
     value = args.steps * per_step * batch * L / wall / GB
-    cpu = None
-    if not args.no_cpu:
-        log("[bench] CPU oracle baseline")
-        cpu = cpu_oracle_gather_slots(raw_np[:65536], w, 8192, args.cpu_budget, "the first 65,536 rows (32 MiB)")
+    h2d = h2d_ceiling()
     res = base_result(
         args, value, wall,
         {"workload": f"dlrm: {n} rows x 128 fp32 U(-0.01,0.01), W=32, M=4096, T=0.9, slots in pinned host "
                      f"memory, {per_step} zero-copy gathers of {batch} random ids (with replacement) per step",
          "rows": n, "tensor_bytes": L, "batch_ids": batch, "gathers_per_step": per_step},
         savings, "ibp::k_decode_small<2, true, true, 1, false>", durs,
-        link_roofline(link, durs, savings, None if args.small else "dlrm"),
-        encode_GBps=round(n * L / t_enc / GB, 3), meta=ibp.ibp_meta_get_info(meta))
-    if cpu:
-        res["cpu_baseline"] = cpu
+        link_roofline(link, durs, savings, None if args.small else "dlrm", h2d, lines, batch * L),
+        line_granular_note=("a 512-byte row whose record is about 465 bytes still spans 4 lines of 128 bytes, "
+                            "so at this saving the link moves the same lines as for raw rows"),
+        encode=encode_link(n * L, t_enc, h2d, "host -> host, pinned source to pinned slots"),
+        meta=ibp.ibp_meta_get_info(meta))
+    decoded_fracs(res)
+    if not args.no_cpu:
+        log("[bench] CPU oracle baseline")
+        res["cpu_baseline"] = cpu_gather_baseline(raw_np[:65536], w, 8192, args.cpu_budget,
+                                                  "the first 65,536 rows (32 MiB)")
     return res
 
 
@@ -614,28 +732,35 @@ def run_llm_bf16(args) -> dict:
     x = torch.randn((1, rows), dtype=torch.bfloat16, device=dev)
     y = torch.empty((1, cols), dtype=torch.bfloat16, device=dev)
     sa, sb = torch.cuda.Stream(), torch.cuda.Stream()
-    evs = []
+    marks = []
+    prev_freed = []  # the consumer's events of the previous pass
 
     def one_pass(record: bool):
         ready = [torch.cuda.Event() for _ in range(layers)]
         freed = [torch.cuda.Event() for _ in range(layers)]
+        if record:
+            e0 = torch.cuda.Event(enable_timing=True)
+            e0.record(sa)
         for l in range(layers):
             with torch.cuda.stream(sa):
+                # the buffer of layer l was last read by the consumer of layer l - 2
                 if l >= 2:
                     sa.wait_event(freed[l - 2])
-                if record:
-                    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-                    e0.record(sa)
+                elif prev_freed:
+                    sa.wait_event(prev_freed[layers - 2 + l])
                 ibp.ibp_gather_decompress(meta, slots, layers, bitmask, ids[l:l + 1], bufs[l & 1], stream=sa)
-                if record:
-                    e1.record(sa)
-                    evs.append((e0, e1))
                 ready[l].record(sa)
             with torch.cuda.stream(sb):
                 sb.wait_event(ready[l])
                 torch.matmul(x, bufs[l & 1].view(torch.bfloat16).view(rows, cols), out=y)
                 freed[l].record(sb)
+        if record:
+            e1 = torch.cuda.Event(enable_timing=True)
+            e1.record(sa)
+            marks.append((e0, e1))
+        prev_freed[:] = freed
 
+    ramp(lambda i: one_pass(False))
     for _ in range(args.warmup):
         one_pass(False)
     torch.cuda.synchronize()
@@ -647,15 +772,13 @@ def run_llm_bf16(args) -> dict:
     assert ibp.ibp_check(meta) == ibp.IBP_OK
     if not np.array_equal(bufs[(layers - 1) & 1].cpu().numpy(), hv[layers - 1]):
         raise SystemExit("decoded layer differs")
-    durs = np.array([a.elapsed_time(b) / 1e3 for a, b in evs])
+    # decode launch duration: the decode stream's span of a pass / layers (the
+    # decode of layer l waits only for the consumer of layer l - 2, which
+    # finishes long before; the launches run back to back)
+    durs = np.array([a.elapsed_time(b) / 1e3 / layers for a, b in marks])
     link = float(stored_np.mean())
     value = args.steps * layers * L / wall / GB
-    cpu = None
-    if not args.no_cpu:
-        log("[bench] CPU oracle baseline")
-        # one tensor made of the first 256 rows of layer 0 (5.6 MB), its own sample
-        cpu = cpu_oracle_roundtrip(hv[0].reshape(1, -1)[:, : 256 * cols * 2], w, 1, args.cpu_budget,
-                                   "one 5.6 MB tensor: the first 256 rows of layer 0 (metadata from itself)")
+    h2d = h2d_ceiling()
     res = base_result(
         args, value, wall,
         {"workload": f"llm_bf16: {layers} layers of {rows}x{cols} bf16 N(0,0.02) (0.1% columns x20), W=32, M=32, "
@@ -663,10 +786,17 @@ def run_llm_bf16(args) -> dict:
                      f"while a consumer (y = x @ W) reads the previous layer on another", "layers": layers,
          "tensor_bytes": L},
         savings, "ibp::k_decode_tiles<3, true, true> (look-back)", durs,
-        link_roofline(link, durs, savings, None if args.small else "llm_bf16"),
-        encode_GBps=round(layers * L / t_enc / GB, 3), meta=ibp.ibp_meta_get_info(meta))
-    if cpu:
-        res["cpu_baseline"] = cpu
+        link_roofline(link, durs, savings, None if args.small else "llm_bf16", h2d),
+        encode=encode_link(layers * L, t_enc, h2d, "host -> host, pinned source to pinned slots"),
+        meta=ibp.ibp_meta_get_info(meta))
+    decoded_fracs(res)
+    if not args.no_cpu:
+        log("[bench] CPU oracle baseline")
+        # layer 0 cut into 16 tensors of 256 rows (5.6 MB each), metadata from
+        # the first; one of them single-threaded, all 16 on every core
+        res["cpu_baseline"] = cpu_roundtrip_baseline(
+            hv[0].reshape(16, -1), w, 1, args.cpu_budget,
+            "one 5.6 MB tensor: the first 256 rows of layer 0 (metadata from itself)", single_n=1)
     return res
 
 
@@ -729,11 +859,8 @@ def run_sparse_gnn_cache(args) -> dict:
     raw_durs = queued_durations(lambda i: torch.index_select(table, 0, ids_dev[i], out=out[i & 1]), args.steps,
                                 args.warmup)
     del table
-    cpu = None
-    if not args.no_cpu:
-        log("[bench] CPU oracle baseline")
-        cpu = cpu_oracle_gather_slots(raw_np[:16384], w, 1024, args.cpu_budget, "the first 16,384 rows (16 MiB)",
-                                      packed=True, replace=False)
+    h2d = h2d_ceiling()
+    fill = float(np.median(fill_s))
     res = base_result(
         args, batch * L * args.steps / wall / GB, wall,
         {"workload": f"sparse_gnn_cache: {n} rows x 256 fp32 (97% zeros), W=1024, M=8192, T=0.95, all rows "
@@ -743,12 +870,16 @@ def run_sparse_gnn_cache(args) -> dict:
         1.0 - total / (n * L), "ibp::k_decode_small<0, true, true, 1, false> (packed items)", durs,
         hbm_roofline(hbm_bytes, durs, None if args.small else "sparse_gnn_cache"),
         cache_bytes=total, capacity_gain=round(n * L / total, 4),
-        fill_GBps=round(n * L / float(np.median(fill_s)) / GB, 3),
+        fill=dict(encode_link(2 * n * L, fill, h2d, "cache fill from pinned rows: the offsets pass, then the items "
+                                                    "pass (two reads of the source over the link)"),
+                  GBps=round(n * L / fill / GB, 3)),
         uncompressed_hbm_gather_GBps=round(batch * L * args.steps / raw_wall / GB, 3),
         uncompressed_gather_kernel_us=round(float(np.mean(raw_durs)) * 1e6, 2),
         meta=ibp.ibp_meta_get_info(meta))
-    if cpu:
-        res["cpu_baseline"] = cpu
+    if not args.no_cpu:
+        log("[bench] CPU oracle baseline")
+        res["cpu_baseline"] = cpu_gather_baseline(raw_np[:16384], w, 1024, args.cpu_budget,
+                                                  "the first 16,384 rows (16 MiB)", layout="packed", replace=False)
     return res
 
 
@@ -826,13 +957,55 @@ def run_sweep(args) -> dict:
                      f"thresholds T=0.9/0.95/0.99, pinned slots (plain layout), gathers of {batch} distinct ids; "
                      f"value at W=1024, T=0.95; plus dense_gnn rows as fp16 (16384 x 128 half, HBM)",
          "rows": n, "tensor_bytes": L, "batch_ids": batch},
-        savings_at, "ibp::k_decode_small", durs_at, link_roofline(link_at, durs_at, savings_at, None),
+        savings_at, "ibp::k_decode_small", durs_at, link_roofline(link_at, durs_at, savings_at, None, h2d_ceiling()),
         sweep=points, fp16_dense_gnn=fp16)
 
 
 WORKLOADS = {"sparse_gnn": run_sparse_gnn, "kv_bf16": run_kv_bf16, "dense_gnn": run_dense_gnn,
              "dlrm": run_dlrm, "llm_bf16": run_llm_bf16, "sparse_gnn_cache": run_sparse_gnn_cache,
              "sweep": run_sweep}
+# steps, warmup when the command line gives none
+DEFAULT_STEPS = {"sparse_gnn": (200, 10), "kv_bf16": (100, 5), "dense_gnn": (200, 10), "dlrm": (4, 1),
+                 "sparse_gnn_cache": (200, 10), "sweep": (30, 5), "llm_bf16": (3, 1)}
+# the default run: the headline (largest workload) last
+ALL_ORDER = ("dense_gnn", "sparse_gnn", "sparse_gnn_cache", "dlrm", "kv_bf16", "llm_bf16")
+HEADLINE = "llm_bf16"
+VERIFIED = "decoded output of the last timed step equal to the source, byte for byte; no device error"
+
+
+def release_memory():
+    gc.collect()
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    host_empty = getattr(torch._C, "_host_emptyCache", None)
+    if host_empty is not None:
+        host_empty()
+
+
+def run_one(name: str, args) -> dict:
+    a = copy.copy(args)
+    d_steps, d_warm = DEFAULT_STEPS[name]
+    a.steps = d_steps if args.steps is None else args.steps
+    a.warmup = d_warm if args.warmup is None else args.warmup
+    log(f"[bench] === {name}: {a.steps} timed steps, {a.warmup} warm-up ===")
+    t0 = time.perf_counter()
+    res = WORKLOADS[name](a)
+    # every workload exits before returning when a decoded output of its last
+    # timed step differs from the source or the library latched an error
+    res["output_verified"] = VERIFIED
+    res["run_s"] = round(time.perf_counter() - t0, 1)
+    release_memory()
+    return res
+
+
+def run_all(args) -> dict:
+    results = {name: run_one(name, args) for name in ALL_ORDER}
+    head = results.pop(HEADLINE)
+    head["config"]["headline"] = ("the largest workload that fits one GPU: 32 bf16 layers, 2.89 GB of weights per "
+                                  "pass; every other workload is nested under 'workloads'")
+    common = ("metric", "n_gpus", "higher_is_better", "scaling", "vs_baseline", "data")
+    head["workloads"] = {name: {k: v for k, v in r.items() if k not in common} for name, r in results.items()}
+    return head
 
 
 def main():
@@ -840,11 +1013,12 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=None, help="timed steps (default per workload)")
     ap.add_argument("--warmup", type=int, default=None)
-    ap.add_argument("--workload", default="sparse_gnn", choices=sorted(WORKLOADS))
-    ap.add_argument("--small", action="store_true", help="scaled-down table (quick check)")
-    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--workload", default="all", choices=["all"] + sorted(WORKLOADS))
+    ap.add_argument("--small", action="store_true", help="scaled-down tables (quick check)")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baselines")
     ap.add_argument("--no-raw", action="store_true", help="skip the raw zero-copy gather comparison")
-    ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle decode")
+    ap.add_argument("--cpu-budget", type=float, default=10.0,
+                    help="seconds of single-thread oracle decode per workload (half that on all cores)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on exactly one GPU; --gpus {args.gpus} is not supported "
@@ -854,17 +1028,8 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
-    defaults = {"sparse_gnn": (200, 10), "kv_bf16": (100, 5), "dense_gnn": (200, 10), "dlrm": (4, 1),
-                "sparse_gnn_cache": (200, 10), "sweep": (30, 5),
-                "llm_bf16": (3, 1)}
-    d_steps, d_warm = defaults[args.workload]
-    args.steps = d_steps if args.steps is None else args.steps
-    args.warmup = d_warm if args.warmup is None else args.warmup
     ibp.lib()
-    res = WORKLOADS[args.workload](args)
-    # every workload exits before printing when a decoded output of its last
-    # timed step differs from the source or the library latched an error
-    res["output_verified"] = "decoded output of the last timed step equal to the source, byte for byte; no device error"
+    res = run_all(args) if args.workload == "all" else run_one(args.workload, args)
     print(json.dumps(res), flush=True)
 
 
