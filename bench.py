@@ -778,6 +778,21 @@ def run_llm_bf16(args) -> dict:
     durs = np.array([a.elapsed_time(b) / 1e3 / layers for a, b in marks])
     link = float(stored_np.mean())
     value = args.steps * layers * L / wall / GB
+    del bufs
+    # the same records already resident in HBM: one decode of all layers per
+    # step, HBM -> HBM (no host link in the timed region)
+    log("[bench] llm_bf16: the same layers decoded from HBM-resident slots")
+    dslots = slots.to(dev)
+    dout = torch.empty((layers, L), dtype=torch.uint8, device=dev)
+    hbm_wall, hbm_durs = timed(lambda i: ibp.ibp_decompress(meta, dslots, bitmask, layers, dout), args.steps,
+                               args.warmup)
+    assert ibp.ibp_check(meta) == ibp.IBP_OK
+    if not np.array_equal(dout[layers - 1].cpu().numpy(), hv[layers - 1]):
+        raise SystemExit("decoded layer (HBM-resident slots) differs")
+    hbm_bytes = float(stored_np.sum() + layers * L + 4 * ((layers + 31) // 32))
+    hbm_value = args.steps * layers * L / hbm_wall / GB
+    hbm_roof = hbm_roofline(hbm_bytes, hbm_durs, None)
+    del dslots, dout
     h2d = h2d_ceiling()
     res = base_result(
         args, value, wall,
@@ -787,6 +802,11 @@ def run_llm_bf16(args) -> dict:
          "tensor_bytes": L},
         savings, "ibp::k_decode_tiles<3, true, true> (look-back)", durs,
         link_roofline(link, durs, savings, None if args.small else "llm_bf16", h2d),
+        hbm_resident={"what": f"the same {layers} compressed layers held in HBM slots, all of them decoded by one "
+                              f"ibp_decompress per step into HBM (inputs resident in HBM, no host link)",
+                      "decoded_GBps": round(hbm_value, 3), "ms_per_step": round(hbm_wall / args.steps * 1e3, 4),
+                      "kernel": "ibp::k_decode_tiles<3, true, true> (look-back)",
+                      "kernel_avg_us": round(float(np.mean(hbm_durs)) * 1e6, 2), "roofline": hbm_roof},
         encode=encode_link(layers * L, t_enc, h2d, "host -> host, pinned source to pinned slots"),
         meta=ibp.ibp_meta_get_info(meta))
     decoded_fracs(res)

@@ -330,9 +330,10 @@ ibp_status refuse_capture(hipStream_t s) {
     return cs == hipStreamCaptureStatusNone ? IBP_OK : IBP_ERR_UNSUPPORTED;
 }
 
-// Look-back state for one launch over `tiles` tiles on stream s: grows the
-// per-stream buffers when needed and queues the zeroing of the ticket
-// counter on s.  Returns with `lock` holding the handle's mutex; the caller
+// Look-back state for one launch with `tiles` status words (one per tile of
+// the multi-tile encode, per group of tiles of the decode, per block of the
+// offsets scan) on stream s: grows the per-stream buffers when needed and
+// queues the zeroing of the ticket counter on s.  Returns with `lock` holding the handle's mutex; the caller
 // queues its launch before releasing it, so launches on one stream from
 // several host threads reach the stream in the order of their reservations
 // and no buffer is replaced while a reserved launch is still to be queued.
@@ -551,18 +552,18 @@ static ibp_status noalloc_scratch(int dev, unsigned long long** out) {
     return IBP_OK;
 }
 
-// Look-back state of one launch over `tiles` tiles in the static scratch:
-// the ticket and the tiles' status words are zeroed by fill kernels on the
-// stream (no memset node, so the call may be captured in a graph), and the
-// epoch is always 1.
-static ibp_status noalloc_lookback(ibp_meta_s* h, hipStream_t s, uint64_t tiles, LookBack* lb) {
+// Look-back state of one launch with `entries` status words (one per group of
+// tiles) in the static scratch: the ticket and the status words are zeroed
+// by fill kernels on the stream (no memset node, so the call may be captured
+// in a graph), and the epoch is always 1.
+static ibp_status noalloc_lookback(ibp_meta_s* h, hipStream_t s, uint64_t entries, LookBack* lb) {
     unsigned long long* base = nullptr;
     ibp_status st = noalloc_scratch(h->device, &base);
     if (st != IBP_OK) return st;
     uint32_t* ticket = reinterpret_cast<uint32_t*>(base);
     unsigned long long* status = base + kNoAllocHeadWords;
     IBP_TRY(launch_fill_u32(ticket, 1, 0, s));
-    IBP_TRY(launch_fill_u32(reinterpret_cast<uint32_t*>(status), 2 * tiles, 0, s));
+    IBP_TRY(launch_fill_u32(reinterpret_cast<uint32_t*>(status), 2 * entries, 0, s));
     lb->status = status;
     lb->ticket = ticket;
     lb->epoch = 1;
@@ -596,9 +597,10 @@ static ibp_status decode_common(ibp_meta_t h, const void* slots, uint64_t n_slot
     LookBack lb{};
     std::unique_lock<std::mutex> lock;
     if (geo.tiles_per_tensor > 1) {
-        const uint64_t tiles = n_out * geo.tiles_per_tensor;
-        ibp_status st = static_scratch ? noalloc_lookback(h, stream, tiles, &lb)
-                                       : lookback_for(h, stream, tiles, 0, &lb, &lock);
+        // one look-back status word per group of tiles
+        const uint64_t groups = n_out * decode_groups(geo.tiles_per_tensor);
+        ibp_status st = static_scratch ? noalloc_lookback(h, stream, groups, &lb)
+                                       : lookback_for(h, stream, groups, 0, &lb, &lock);
         if (st != IBP_OK) return st;
     }
     return from_hip(launch_decode(h->tabs, geo, h->sum.max_runs, h->sum.uniform != 0, slots, n_slots, bitmask,

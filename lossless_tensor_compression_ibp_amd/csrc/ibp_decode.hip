@@ -18,6 +18,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <algorithm>
+
 #include "ibp_device.hpp"
 #include "ibp_internal.hpp"
 
@@ -389,9 +391,10 @@ __global__ __launch_bounds__(256) void k_decode_small(Tables t, Geo geo, const u
                 // The whole slot (or the whole packed item, whose length the
                 // offsets give) is in LDS already, so the record length is
                 // needed only to validate it: the rebuild returns the payload
-                // bits it consumed (its reads stay inside the slot-sized
-                // buffer even for a corrupt header), and only the last header
-                // word can hold padding bits.
+                // bits it consumed (its reads stay inside this wave's buffer,
+                // sized hw + n_words + 1 words or more, even for a corrupt
+                // header whose chunks all claim to be verbatim), and only the
+                // last header word can hold padding bits.
                 const uint32_t valid = (uint32_t)(geo.n_chunks - 32ull * (hw - 1));
                 const bool bad_pad = valid < 32 && (buf[hw - 1] >> valid) != 0;
                 if (lane == 0) buf[4 * n4_first] = 0;
@@ -427,6 +430,119 @@ __global__ __launch_bounds__(256) void k_decode_small(Tables t, Geo geo, const u
                 decode_tile<RUNS, MW4, (STAGE >= 4)>(ta, geo, buf, buf + hw, 0, 0, nwords, out, true);
             __builtin_amdgcn_wave_barrier();
         }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Tensors longer than one tile (decoupled look-back).  A wave takes a group
+// of up to kDecodeTilesPerGroup consecutive tiles of one tensor; thread 0 of
+// a workgroup takes one ticket for its four waves, whose groups follow each
+// other, so groups are numbered in the order their workgroups started and a
+// group waits only on groups that are resident or done.  The wave reads the
+// header words of its whole group at once, publishes the group's payload
+// bits, finds where the group's payload starts by look-back over earlier
+// groups of the tensor, then reads and rebuilds its tiles one after another
+// (each tile's start bit is the group's plus the earlier tiles' bits, from
+// their header words).  One atomic and one look-back per group instead of
+// per tile.
+// ---------------------------------------------------------------------------
+template <int RUNS, bool UNI>
+__global__ __launch_bounds__(256) void k_decode_groups(Tables t, Geo geo, const uint8_t* __restrict__ slots,
+                                                       uint64_t n_slots, const uint32_t* __restrict__ bitmask,
+                                                       const int64_t* __restrict__ ids, uint64_t n_out,
+                                                       uint8_t* __restrict__ dst, uint32_t* err, LookBack lb,
+                                                       uint32_t lds_words) {
+    extern __shared__ uint32_t smem[];
+    __shared__ uint32_t block_ticket;
+    const uint32_t lane = lane_id();
+    const uint32_t wib = uniform(threadIdx.x / kWave);
+    uint32_t* lds = smem + wib * lds_words;
+    if (threadIdx.x == 0) block_ticket = atomicAdd(lb.ticket, 1u);
+    __syncthreads();
+    const uint64_t group = (uint64_t)uniform(block_ticket) * kWavesPerBlock + wib;
+    const uint64_t tpt = geo.tiles_per_tensor;
+    const uint64_t gpt = decode_groups(tpt);
+    if (group >= n_out * gpt) return;
+    const uint64_t oi = group / gpt;
+    const uint64_t lg = group - oi * gpt;
+    const uint64_t t0 = lg * kDecodeTilesPerGroup;
+    const uint32_t n_tiles = (uint32_t)min((uint64_t)kDecodeTilesPerGroup, tpt - t0);
+
+    // every group of a tensor sees the same id and bitmask bit, so a bad id
+    // or a raw tensor ends all of them before the look-back
+    const int64_t tensor = ids ? (int64_t)uniform64((uint64_t)ids[oi]) : (int64_t)oi;
+    if (tensor < 0 || (uint64_t)tensor >= n_slots) {
+        latch_error(err, kErrRange);
+        return;
+    }
+    const uint32_t* src = reinterpret_cast<const uint32_t*>(slots + (uint64_t)tensor * geo.L);
+    uint32_t* out = reinterpret_cast<uint32_t*>(dst + oi * geo.L);
+    const uint32_t tw = geo.tile_words;
+    const uint64_t w0 = t0 * tw;
+    const uint64_t wend = min(w0 + (uint64_t)n_tiles * tw, geo.n_words);
+    const bool vec = geo.aligned16 != 0;
+    const bool comp = (uniform(bitmask[(uint64_t)tensor >> 5]) >> ((uint64_t)tensor & 31)) & 1u;
+    if (!comp) {
+        copy_words(src, out, w0, (uint32_t)(wend - w0), vec);
+        return;
+    }
+    TabArrays ta{t.b, t.kd, t.dx, t.r, geo.Mw};
+    TabUniform<RUNS> tu;
+    if (UNI) tu = load_uniform<RUNS>(t, geo.Mw);
+
+    // header words of the group (a tile's chunks start on a header word)
+    const uint32_t hw_tile = (tw >> geo.log2g) / 32;
+    const uint64_t hw0 = (w0 >> geo.log2g) >> 5;
+    const uint32_t hw_g = (uint32_t)((((wend - w0) >> geo.log2g) + 31) / 32);
+    uint32_t* hdr = lds;
+    uint32_t* pay = lds + kDecodeTilesPerGroup * 64;
+    for (uint32_t j = lane; j < hw_g; j += kWave) hdr[j] = src[hw0 + j];
+    __builtin_amdgcn_wave_barrier();
+    uint32_t agg[kDecodeTilesPerGroup];
+    uint64_t agg_all = 0;
+    bool bad_pad = false;
+#pragma unroll
+    for (uint32_t r = 0; r < kDecodeTilesPerGroup; ++r) {
+        agg[r] = 0;
+        if (r < n_tiles) {
+            const uint32_t nw = (uint32_t)min((uint64_t)tw, wend - (w0 + (uint64_t)r * tw));
+            const uint32_t hw_t = ((nw >> geo.log2g) + 31) / 32;
+            bool bad;
+            const uint32_t rem = header_removed_bits(t.planes, geo, hdr + r * hw_tile, hw0 + r * hw_tile, hw_t, &bad);
+            bad_pad = bad_pad || bad;
+            agg[r] = 32u * nw - rem;
+            agg_all += agg[r];
+        }
+    }
+    const uint64_t S = lookback_exclusive(lb.status, oi * gpt, lg, agg_all, 32ull * geo.hdr_words, lb.epoch, err);
+    const uint64_t E = S + agg_all;
+    const bool last = lg == gpt - 1;
+    if (bad_pad || E > 8ull * geo.L || (last && 4 * ((E + 31) / 32) >= geo.L)) {
+        latch_error(err, kErrCorrupt);
+        return;
+    }
+    uint64_t St = S;
+    for (uint32_t r = 0; r < n_tiles; ++r) {
+        const uint64_t wt = w0 + (uint64_t)r * tw;
+        const uint32_t nw = (uint32_t)min((uint64_t)tw, wend - wt);
+        const uint64_t Et = St + agg[r];
+        uint64_t a = St >> 5, b = (Et + 31) >> 5;
+        if (vec) {
+            a &= ~3ull;
+            b = (b + 3) & ~3ull;
+        }
+        b = min(b, geo.n_words);
+        __builtin_amdgcn_wave_barrier();  // the previous tile's reads of pay are done
+        load_words_to_lds(src, a, b, pay, vec);
+        if (lane == 0) pay[b - a] = 0;
+        __builtin_amdgcn_wave_barrier();
+        if (UNI)
+            decode_tile<RUNS, false, true>(tu, geo, hdr + r * hw_tile, pay, (uint32_t)(St - 32 * a), wt, nw, out,
+                                           vec && (wt & 3) == 0);
+        else
+            decode_tile<RUNS, false, true>(ta, geo, hdr + r * hw_tile, pay, (uint32_t)(St - 32 * a), wt, nw, out,
+                                           vec && (wt & 3) == 0);
+        St = Et;
     }
 }
 
@@ -552,7 +668,11 @@ static uint32_t runs_bucket(uint32_t runs) {
 // LDS k_decode_small shares per workgroup (tables, planes) and needs per
 // wave (record buffer); false when the tables do not fit.
 static bool small_lds(const Geo& geo, int runs, bool uni, uint32_t* buf_words, size_t* head, size_t* wave) {
-    *buf_words = ((uint32_t)geo.n_words + 8 + 3) & ~3u;
+    // a rebuild from a whole slot reads at most word hw + n_words of the
+    // buffer (a corrupt header whose chunks all claim to be verbatim), and
+    // the header-in-GPU-memory layout puts hw <= 4 words after n_words + 4
+    const uint32_t tail = std::max<uint32_t>(8u, (uint32_t)geo.hdr_words + 1);
+    *buf_words = ((uint32_t)geo.n_words + tail + 3) & ~3u;
     const uint64_t tab = uni ? 0 : (uint64_t)tab_rows(runs) * geo.Mw * 4;
     const uint64_t planes = (uint64_t)(geo.Pc / geo.G) * kPlanes * 4;
     if (tab > kMaxLdsTableBytes || planes > kMaxLdsPlaneBytes) return false;
@@ -631,6 +751,24 @@ static hipError_t launch_tiles(const Tables& t, const Geo& geo, const void* slot
     return hipGetLastError();
 }
 
+// Tensors longer than one tile: one wave per group of tiles; lb holds one
+// status word per group (n_out * decode_groups(tiles_per_tensor)).
+template <int RUNS, bool UNI>
+static hipError_t launch_groups(const Tables& t, const Geo& geo, const void* slots, uint64_t n_slots,
+                                const uint32_t* bitmask, const int64_t* ids, uint64_t n_out, void* dst,
+                                uint32_t* err, const LookBack& lb, hipStream_t s) {
+    // header words of a group, then one tile's payload (up to 8 words of
+    // 16-byte rounding and the zero word after it)
+    const uint32_t lds_words = kDecodeTilesPerGroup * 64 + geo.tile_words + 8;
+    const uint64_t groups = n_out * decode_groups(geo.tiles_per_tensor);
+    const dim3 grid((uint32_t)((groups + kWavesPerBlock - 1) / kWavesPerBlock));
+    const dim3 block(kWave * kWavesPerBlock);
+    const size_t shm = (size_t)lds_words * 4 * kWavesPerBlock;
+    hipLaunchKernelGGL((k_decode_groups<RUNS, UNI>), grid, block, shm, s, t, geo, static_cast<const uint8_t*>(slots),
+                       n_slots, bitmask, ids, n_out, static_cast<uint8_t*>(dst), err, lb, lds_words);
+    return hipGetLastError();
+}
+
 template <int RUNS, bool UNI>
 static hipError_t launch_decode_r(const Tables& t, const Geo& geo, const void* slots, uint64_t n_slots,
                                   const uint32_t* bitmask, const int64_t* ids, uint64_t n_out, void* dst,
@@ -638,7 +776,7 @@ static hipError_t launch_decode_r(const Tables& t, const Geo& geo, const void* s
                                   const Items& items, const uint32_t* headers) {
     if (geo.tiles_per_tensor > 1) {
         if (items.offsets || headers) return hipErrorInvalidValue;
-        return launch_tiles<RUNS, UNI, true>(t, geo, slots, n_slots, bitmask, ids, n_out, dst, err, *lb, s);
+        return launch_groups<RUNS, UNI>(t, geo, slots, n_slots, bitmask, ids, n_out, dst, err, *lb, s);
     }
     uint32_t buf_words = 0;
     size_t head = 0, wave = 0;

@@ -69,6 +69,15 @@ struct LookBack {
 constexpr uint32_t kLookbackPolls = 1u << 22;
 constexpr uint64_t kLookbackPoison = 1ull << 41;
 
+// The decode of a tensor longer than one tile gives each wave a group of up
+// to this many consecutive tiles of one tensor, and the look-back chains
+// groups (one status word per group); a workgroup takes one ticket for its
+// waves' groups.
+constexpr uint32_t kDecodeTilesPerGroup = 4;
+__host__ __device__ constexpr uint64_t decode_groups(uint64_t tiles_per_tensor) {
+    return (tiles_per_tensor + kDecodeTilesPerGroup - 1) / kDecodeTilesPerGroup;
+}
+
 enum DeviceError : uint32_t { kErrNone = 0, kErrCorrupt = 5, kErrRange = 6, kErrStall = 7 };
 
 // Where tensor t's stored item lives.  offsets == nullptr: fixed slots, slot

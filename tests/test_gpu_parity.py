@@ -52,6 +52,28 @@ def test_kv_pages_small():
     compare_codec(raw, w.chunk_bits, w.period_bits, w.threshold, 1024, label="kv_pages")
 
 
+def test_kv_page_with_corrupt_long_header():
+    """4 KiB pages carry 32 header words and are read whole in one pass: a
+    page whose header claims every chunk verbatim (a record longer than the
+    slot) latches IBP_ERR_CORRUPT, its rebuild stays inside its own buffer,
+    and every other page of the launch still decodes exactly."""
+    kv = WL.kv_cache(n_layers=1, n_heads=4, n_tokens=2048)
+    raw = kv.reshape(-1, 2048).view(np.uint8).reshape(-1, 4096)
+    w = WL.KV_BF16
+    r = compare_codec(raw, w.chunk_bits, w.period_bits, w.threshold, raw.shape[0], label="kv corrupt setup")
+    n, L = raw.shape
+    comp = np.flatnonzero(np.unpackbits(r.bm.cpu().numpy().view(np.uint8), bitorder="little")[:n])
+    assert comp.size > 2
+    bad = r.slots.clone()
+    for t in comp[[0, comp.size // 2]]:
+        bad[int(t), :128] = 0  # 32 header words, no participating chunk
+    out = torch.empty((n, L), dtype=torch.uint8, device=device())
+    ibp.ibp_decompress(r.meta, bad, r.bm, n, out)
+    assert ibp.ibp_check(r.meta) == ibp.IBP_ERR_CORRUPT
+    keep = np.setdiff1d(np.arange(n), comp[[0, comp.size // 2]])
+    np.testing.assert_array_equal(out.cpu().numpy()[keep], raw[keep])
+
+
 def test_llm_layer_multi_tile():
     """A scaled layer (64 x 11008 bf16, 1.4 MB): 344 tiles of look-back."""
     layers = [WL.llm_layer(l, rows=64) for l in range(3)]
