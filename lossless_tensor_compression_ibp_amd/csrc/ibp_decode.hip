@@ -547,33 +547,21 @@ __global__ __launch_bounds__(256) void k_decode_groups(Tables t, Geo geo, const 
 }
 
 // ---------------------------------------------------------------------------
-// General tiles: tensors longer than one tile (decoupled look-back between
-// the tiles of a tensor) and single-tile tensors whose slots or output are
-// not 16-byte aligned.  One wave per tile, tables read from global memory.
+// Single-tile tensors the persistent kernel does not take: slots or output
+// not 16-byte aligned, or tables too large for LDS.  One wave per tensor,
+// tables read from global memory; the record's first read, then (once the
+// header gives its length) the rest.
 // ---------------------------------------------------------------------------
-template <int RUNS, bool UNI, bool MULTI>
+template <int RUNS, bool UNI>
 __global__ __launch_bounds__(256) void k_decode_tiles(Tables t, Geo geo, const uint8_t* __restrict__ slots,
                                                       uint64_t n_slots, const uint32_t* __restrict__ bitmask,
                                                       const int64_t* __restrict__ ids, uint64_t n_out,
-                                                      uint8_t* __restrict__ dst, uint32_t* err, LookBack lb,
-                                                      uint32_t lds_words) {
+                                                      uint8_t* __restrict__ dst, uint32_t* err, uint32_t lds_words) {
     extern __shared__ uint32_t smem[];
     const uint32_t lane = lane_id();
     uint32_t* lds = smem + (threadIdx.x / kWave) * lds_words;
-
-    uint64_t tile;
-    if (MULTI) {
-        uint32_t tk = 0;
-        if (lane == 0) tk = atomicAdd(lb.ticket, 1u);
-        tile = uniform(tk);
-    } else {
-        tile = (uint64_t)blockIdx.x * kWavesPerBlock + threadIdx.x / kWave;
-    }
-    const uint64_t tpt = MULTI ? geo.tiles_per_tensor : 1;
-    if (tile >= n_out * tpt) return;
-    const uint64_t oi = MULTI ? tile / tpt : tile;
-    const uint64_t local = MULTI ? tile - oi * tpt : 0;
-
+    const uint64_t oi = (uint64_t)blockIdx.x * kWavesPerBlock + threadIdx.x / kWave;
+    if (oi >= n_out) return;
     const int64_t tensor = ids ? (int64_t)uniform64((uint64_t)ids[oi]) : (int64_t)oi;
     if (tensor < 0 || (uint64_t)tensor >= n_slots) {
         latch_error(err, kErrRange);
@@ -581,79 +569,40 @@ __global__ __launch_bounds__(256) void k_decode_tiles(Tables t, Geo geo, const u
     }
     const uint32_t* src = reinterpret_cast<const uint32_t*>(slots + (uint64_t)tensor * geo.L);
     uint32_t* out = reinterpret_cast<uint32_t*>(dst + oi * geo.L);
-    const uint64_t w0 = local * geo.tile_words;
-    const uint32_t nw = (uint32_t)min((uint64_t)geo.tile_words, geo.n_words - w0);
+    const uint32_t nw = (uint32_t)geo.n_words;
     const bool vec = geo.aligned16 != 0;
     const bool comp = (uniform(bitmask[(uint64_t)tensor >> 5]) >> ((uint64_t)tensor & 31)) & 1u;
     if (!comp) {
-        copy_words(src, out, w0, nw, vec);
+        copy_words(src, out, 0, nw, vec);
         return;
     }
     TabArrays ta{t.b, t.kd, t.dx, t.r, geo.Mw};
     TabUniform<RUNS> tu;
     if (UNI) tu = load_uniform<RUNS>(t, geo.Mw);
-
-    if (!MULTI) {
-        const uint32_t hw = (uint32_t)geo.hdr_words;
-        const uint32_t cap = (uint32_t)geo.n_words;
-        uint32_t have = geo.spec_words;
-        load_words_to_lds(src, 0, have, lds, vec);
-        __builtin_amdgcn_wave_barrier();
-        bool bad_pad;
-        const uint32_t rem = header_removed_bits(t.planes, geo, lds, 0, hw, &bad_pad);
-        const uint64_t R = 32ull * hw + 32ull * geo.n_words - rem;
-        const uint64_t words = (R + 31) / 32;
-        if (bad_pad || 4 * words >= geo.L) {
-            latch_error(err, kErrCorrupt);
-            return;
-        }
-        if (words > have) {
-            const uint32_t need = vec ? (uint32_t)((words + 3) & ~3ull) : (uint32_t)words;
-            const uint32_t upto = min(need, cap);
-            load_words_to_lds(src, have, upto, lds + have, vec);
-            have = upto;
-        }
-        if (lane == 0) lds[have] = 0;
-        __builtin_amdgcn_wave_barrier();
-        if (UNI)
-            decode_tile<RUNS, false, false>(tu, geo, lds, lds + hw, 0, 0, nw, out, vec);
-        else
-            decode_tile<RUNS, false, false>(ta, geo, lds, lds + hw, 0, 0, nw, out, vec);
-        return;
-    }
-
-    // Tile of a long tensor: header slice, look-back, then the payload slice.
-    const uint64_t c0 = w0 >> geo.log2g;
-    const uint32_t nch = nw >> geo.log2g;
-    const uint32_t hw_t = (nch + 31) / 32;
-    const uint64_t hw0 = c0 >> 5;
-    uint32_t* hdr = lds;
-    uint32_t* pay = lds + 64;
-    for (uint32_t j = lane; j < hw_t; j += kWave) hdr[j] = src[hw0 + j];
+    const uint32_t hw = (uint32_t)geo.hdr_words;
+    uint32_t have = geo.spec_words;
+    load_words_to_lds(src, 0, have, lds, vec);
     __builtin_amdgcn_wave_barrier();
     bool bad_pad;
-    const uint32_t rem = header_removed_bits(t.planes, geo, hdr, hw0, hw_t, &bad_pad);
-    const uint64_t agg = 32ull * nw - rem;
-    const uint64_t S = lookback_exclusive(lb.status, oi * tpt, local, agg, 32ull * geo.hdr_words, lb.epoch, err);
-    const uint64_t E = S + agg;
-    const bool last = local == tpt - 1;
-    if (bad_pad || E > 8ull * geo.L || (last && 4 * ((E + 31) / 32) >= geo.L)) {
+    const uint32_t rem = header_removed_bits(t.planes, geo, lds, 0, hw, &bad_pad);
+    const uint64_t R = 32ull * hw + 32ull * geo.n_words - rem;
+    const uint64_t words = (R + 31) / 32;
+    if (bad_pad || 4 * words >= geo.L) {
         latch_error(err, kErrCorrupt);
         return;
     }
-    uint64_t a = S >> 5, b = (E + 31) >> 5;
-    if (vec) {
-        a &= ~3ull;
-        b = (b + 3) & ~3ull;
+    if (words > have) {
+        const uint32_t need = vec ? (uint32_t)((words + 3) & ~3ull) : (uint32_t)words;
+        const uint32_t upto = min(need, nw);
+        load_words_to_lds(src, have, upto, lds + have, vec);
+        have = upto;
     }
-    b = min(b, geo.n_words);
-    load_words_to_lds(src, a, b, pay, vec);
-    if (lane == 0) pay[b - a] = 0;
+    if (lane == 0) lds[have] = 0;
     __builtin_amdgcn_wave_barrier();
     if (UNI)
-        decode_tile<RUNS, false, MULTI>(tu, geo, hdr, pay, (uint32_t)(S - 32 * a), w0, nw, out, vec && (w0 & 3) == 0);
+        decode_tile<RUNS, false, false>(tu, geo, lds, lds + hw, 0, 0, nw, out, vec);
     else
-        decode_tile<RUNS, false, MULTI>(ta, geo, hdr, pay, (uint32_t)(S - 32 * a), w0, nw, out, vec && (w0 & 3) == 0);
+        decode_tile<RUNS, false, false>(ta, geo, lds, lds + hw, 0, 0, nw, out, vec);
 }
 
 // ---------------------------------------------------------------------------
@@ -736,18 +685,17 @@ static hipError_t launch_small(const Tables& t, const Geo& geo, const void* slot
 #undef IBP_SMALL_X
 }
 
-template <int RUNS, bool UNI, bool MULTI>
+template <int RUNS, bool UNI>
 static hipError_t launch_tiles(const Tables& t, const Geo& geo, const void* slots, uint64_t n_slots,
                                const uint32_t* bitmask, const int64_t* ids, uint64_t n_out, void* dst,
-                               uint32_t* err, const LookBack& lb, hipStream_t s) {
-    const uint32_t lds_words = MULTI ? 64 + geo.tile_words + 8 : (uint32_t)geo.n_words + 8;
-    const uint64_t tiles = n_out * geo.tiles_per_tensor;
-    const dim3 grid((uint32_t)((tiles + kWavesPerBlock - 1) / kWavesPerBlock));
+                               uint32_t* err, hipStream_t s) {
+    // the record (up to the slot) and the zero word after it
+    const uint32_t lds_words = (uint32_t)geo.n_words + 8;
+    const dim3 grid((uint32_t)((n_out + kWavesPerBlock - 1) / kWavesPerBlock));
     const dim3 block(kWave * kWavesPerBlock);
     const size_t shm = (size_t)lds_words * 4 * kWavesPerBlock;
-    hipLaunchKernelGGL((k_decode_tiles<RUNS, UNI, MULTI>), grid, block, shm, s, t, geo,
-                       static_cast<const uint8_t*>(slots), n_slots, bitmask, ids, n_out,
-                       static_cast<uint8_t*>(dst), err, lb, lds_words);
+    hipLaunchKernelGGL((k_decode_tiles<RUNS, UNI>), grid, block, shm, s, t, geo, static_cast<const uint8_t*>(slots),
+                       n_slots, bitmask, ids, n_out, static_cast<uint8_t*>(dst), err, lds_words);
     return hipGetLastError();
 }
 
@@ -788,7 +736,7 @@ static hipError_t launch_decode_r(const Tables& t, const Geo& geo, const void* s
     }
     // the packed and header-in-GPU-memory layouts run on k_decode_small only
     if (items.offsets || headers) return hipErrorInvalidValue;
-    return launch_tiles<RUNS, UNI, false>(t, geo, slots, n_slots, bitmask, ids, n_out, dst, err, LookBack{}, s);
+    return launch_tiles<RUNS, UNI>(t, geo, slots, n_slots, bitmask, ids, n_out, dst, err, s);
 }
 
 bool packed_decode_supported(const Geo& geo, uint32_t runs, bool uniform_meta) {
