@@ -521,19 +521,58 @@ __global__ __launch_bounds__(256) void k_decode_groups(Tables t, Geo geo, const 
         latch_error(err, kErrCorrupt);
         return;
     }
+    // payload words [a, b) of tile r, whose fields start at bit St (16-byte
+    // rounded when vec)
+    auto tile_range = [&](uint64_t St, uint32_t r, uint64_t* a, uint64_t* b) __attribute__((always_inline)) {
+        *a = St >> 5;
+        *b = (St + agg[r] + 31) >> 5;
+        if (vec) {
+            *a &= ~3ull;
+            *b = (*b + 3) & ~3ull;
+        }
+        *b = min(*b, geo.n_words);
+    };
+    // Records in HBM, with 16-byte vectors: the next tile's payload (at most
+    // 2,048 + 8 words, so kPre vectors per lane) is read into registers while
+    // the current tile is rebuilt from LDS (32 llm_bf16 layers from HBM:
+    // 1,355 -> 1,172 us).  Over the host link the reads in flight of many
+    // waves already fill the link, and this prefetch measured slower
+    // (1,272 -> 1,302 us per layer), so there each tile is read when due.
+    const bool pipelined = vec && geo.src_in_hbm;
+    constexpr uint32_t kPre = (kMaxTileWords + 8 + 4 * kWave - 1) / (4 * kWave);
+    u32x4 pre[kPre];
+    const u32x4* src4 = reinterpret_cast<const u32x4*>(src);
+    auto issue = [&](uint64_t a, uint64_t b) __attribute__((always_inline)) {
+        const uint32_t n4 = (uint32_t)((b - a) >> 2);
+#pragma unroll
+        for (uint32_t i = 0; i < kPre; ++i)
+            if (lane + i * kWave < n4) pre[i] = __builtin_nontemporal_load(src4 + (a >> 2) + lane + i * kWave);
+    };
     uint64_t St = S;
+    uint64_t a_next = 0, b_next = 0;
+    if (pipelined) {
+        tile_range(St, 0, &a_next, &b_next);
+        issue(a_next, b_next);
+    }
     for (uint32_t r = 0; r < n_tiles; ++r) {
         const uint64_t wt = w0 + (uint64_t)r * tw;
         const uint32_t nw = (uint32_t)min((uint64_t)tw, wend - wt);
         const uint64_t Et = St + agg[r];
-        uint64_t a = St >> 5, b = (Et + 31) >> 5;
-        if (vec) {
-            a &= ~3ull;
-            b = (b + 3) & ~3ull;
-        }
-        b = min(b, geo.n_words);
+        uint64_t a, b;
+        tile_range(St, r, &a, &b);
         __builtin_amdgcn_wave_barrier();  // the previous tile's reads of pay are done
-        load_words_to_lds(src, a, b, pay, vec);
+        if (pipelined) {
+            const uint32_t n4 = (uint32_t)((b - a) >> 2);
+#pragma unroll
+            for (uint32_t i = 0; i < kPre; ++i)
+                if (lane + i * kWave < n4) reinterpret_cast<u32x4*>(pay)[lane + i * kWave] = pre[i];
+            if (r + 1 < n_tiles) {
+                tile_range(Et, r + 1, &a_next, &b_next);
+                issue(a_next, b_next);
+            }
+        } else {
+            load_words_to_lds(src, a, b, pay, vec);
+        }
         if (lane == 0) pay[b - a] = 0;
         __builtin_amdgcn_wave_barrier();
         if (UNI)
