@@ -141,15 +141,15 @@ def copy_kernel_ceiling(nbytes: int = 1 << 30, reps: int = 5) -> float:
     return 2 * nbytes / float(np.median(times[1:])) / GB
 
 
-RAMP_S = 0.25  # untimed calls before the warm-up, so the GPU's clocks have ramped up
+RAMP_S = 0.25  # untimed calls before the warm-up, so the GPU's clocks have ramped up (--ramp)
 
 
-def ramp(fn, seconds: float = RAMP_S):
-    """Calls fn(0) until `seconds` of wall time have passed (synchronising
-    every call): short timed regions (a few ms) otherwise start on a GPU
-    whose clocks are still rising from idle."""
+def ramp(fn):
+    """Calls fn(0) until RAMP_S seconds of wall time have passed
+    (synchronising every call): short timed regions (a few ms) otherwise
+    start on a GPU whose clocks are still rising from idle."""
     t0 = time.perf_counter()
-    while time.perf_counter() - t0 < seconds:
+    while time.perf_counter() - t0 < RAMP_S:
         fn(0)
         torch.cuda.synchronize()
 
@@ -711,6 +711,9 @@ def run_dlrm(args) -> dict:
 # prefetch: decode of layer i+1 (stream A) overlaps a consumer of layer i
 # (stream B, y = x @ W on the decoded layer)
 # ---------------------------------------------------------------------------
+LLM_KERNEL = "ibp::k_decode_groups<3, true> (look-back over groups of 8 tiles of 8 KiB)"
+
+
 def run_llm_bf16(args) -> dict:
     w = WL.LLM_BF16
     layers = 32 if not args.small else 4
@@ -779,20 +782,27 @@ def run_llm_bf16(args) -> dict:
     link = float(stored_np.mean())
     value = args.steps * layers * L / wall / GB
     del bufs
-    # the same records already resident in HBM: one decode of all layers per
-    # step, HBM -> HBM (no host link in the timed region)
-    log("[bench] llm_bf16: the same layers decoded from HBM-resident slots")
-    dslots = slots.to(dev)
-    dout = torch.empty((layers, L), dtype=torch.uint8, device=dev)
-    hbm_wall, hbm_durs = timed(lambda i: ibp.ibp_decompress(meta, dslots, bitmask, layers, dout), args.steps,
-                               args.warmup)
-    assert ibp.ibp_check(meta) == ibp.IBP_OK
-    if not np.array_equal(dout[layers - 1].cpu().numpy(), hv[layers - 1]):
-        raise SystemExit("decoded layer (HBM-resident slots) differs")
-    hbm_bytes = float(stored_np.sum() + layers * L + 4 * ((layers + 31) // 32))
-    hbm_value = args.steps * layers * L / hbm_wall / GB
-    hbm_roof = hbm_roofline(hbm_bytes, hbm_durs, None)
-    del dslots, dout
+    hbm_resident = None
+    if not args.no_hbm_resident:
+        # the same records already resident in HBM: one decode of all layers
+        # per step, HBM -> HBM (no host link in the timed region)
+        log("[bench] llm_bf16: the same layers decoded from HBM-resident slots")
+        dslots = slots.to(dev)
+        dout = torch.empty((layers, L), dtype=torch.uint8, device=dev)
+        hbm_wall, hbm_durs = timed(lambda i: ibp.ibp_decompress(meta, dslots, bitmask, layers, dout), args.steps,
+                                   args.warmup)
+        assert ibp.ibp_check(meta) == ibp.IBP_OK
+        if not np.array_equal(dout[layers - 1].cpu().numpy(), hv[layers - 1]):
+            raise SystemExit("decoded layer (HBM-resident slots) differs")
+        hbm_bytes = float(stored_np.sum() + layers * L + 4 * ((layers + 31) // 32))
+        hbm_resident = {
+            "what": f"the same {layers} compressed layers held in HBM slots, all of them decoded by one "
+                    f"ibp_decompress per step into HBM (inputs resident in HBM, no host link)",
+            "decoded_GBps": round(args.steps * layers * L / hbm_wall / GB, 3),
+            "ms_per_step": round(hbm_wall / args.steps * 1e3, 4), "kernel": LLM_KERNEL,
+            "kernel_avg_us": round(float(np.mean(hbm_durs)) * 1e6, 2),
+            "roofline": hbm_roofline(hbm_bytes, hbm_durs, None)}
+        del dslots, dout
     h2d = h2d_ceiling()
     res = base_result(
         args, value, wall,
@@ -800,13 +810,9 @@ def run_llm_bf16(args) -> dict:
                      f"T=0.95, slots in pinned host memory, each layer decoded zero-copy into HBM on one stream "
                      f"while a consumer (y = x @ W) reads the previous layer on another", "layers": layers,
          "tensor_bytes": L},
-        savings, "ibp::k_decode_tiles<3, true, true> (look-back)", durs,
+        savings, LLM_KERNEL, durs,
         link_roofline(link, durs, savings, None if args.small else "llm_bf16", h2d),
-        hbm_resident={"what": f"the same {layers} compressed layers held in HBM slots, all of them decoded by one "
-                              f"ibp_decompress per step into HBM (inputs resident in HBM, no host link)",
-                      "decoded_GBps": round(hbm_value, 3), "ms_per_step": round(hbm_wall / args.steps * 1e3, 4),
-                      "kernel": "ibp::k_decode_tiles<3, true, true> (look-back)",
-                      "kernel_avg_us": round(float(np.mean(hbm_durs)) * 1e6, 2), "roofline": hbm_roof},
+        hbm_resident=hbm_resident,
         encode=encode_link(layers * L, t_enc, h2d, "host -> host, pinned source to pinned slots"),
         meta=ibp.ibp_meta_get_info(meta))
     decoded_fracs(res)
@@ -1039,7 +1045,12 @@ def main():
     ap.add_argument("--no-raw", action="store_true", help="skip the raw zero-copy gather comparison")
     ap.add_argument("--cpu-budget", type=float, default=10.0,
                     help="seconds of single-thread oracle decode per workload (half that on all cores)")
+    ap.add_argument("--no-hbm-resident", action="store_true",
+                    help="llm_bf16: skip the decode of the same layers from HBM-resident slots")
+    ap.add_argument("--ramp", type=float, default=RAMP_S,
+                    help="seconds of untimed calls before each warm-up (clock ramp; 0 under a profiler)")
     args = ap.parse_args()
+    globals()["RAMP_S"] = args.ramp
     if args.gpus != 1:
         print(f"bench.py runs on exactly one GPU; --gpus {args.gpus} is not supported "
               "(the codec path is single-GPU; how it would shard across GPUs is a design note only)",
