@@ -251,6 +251,7 @@ Geo make_geo(const ibp_meta_s* h, bool aligned16, uint32_t long_tile_words) {
     g.G = h->G;
     g.np = bit_length(h->sum.max_chunk_k);
     if (g.np > (uint32_t)kPlanes) g.np = kPlanes;
+    g.k1 = g.Pc == 1 ? h->sum.max_chunk_k : 0;
     g.aligned16 = aligned16 ? 1u : 0u;
     if (g.n_words <= kMaxTileWords) {
         g.tile_words = (uint32_t)g.n_words;

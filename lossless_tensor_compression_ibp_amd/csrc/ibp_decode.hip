@@ -161,6 +161,30 @@ __device__ __forceinline__ uint32_t decode_tile(const Tab& tab, const Geo& geo, 
 
 // LDS image of the tables: b, kd, dx rows, r rows (stride Mw), then the
 // header bit planes.  Copied once per workgroup.
+// A whole tile of kMaxTileWords words (every step full, output 16-byte
+// aligned, w0 a multiple of 4): decode_tile with a compile-time step count,
+// so the steps unroll into one block with one store each.
+template <int RUNS, class Tab>
+__device__ __forceinline__ void decode_full_tile(const Tab& tab, const Geo& geo, const uint32_t* hdr,
+                                                 const uint32_t* pay, uint32_t bit0, uint64_t w0,
+                                                 uint32_t* __restrict__ out) {
+    constexpr bool UNI = IsUniformTab<Tab>::value;
+    const uint32_t lane = lane_id();
+    const uint32_t Mw = geo.Mw;
+    const uint32_t step_inc = (uint32_t)(4 * kWave) % Mw;
+    uint32_t pos0 = UNI ? 0u : (uint32_t)((w0 + 4ull * lane) % Mw);
+    uint32_t carry = bit0;
+#pragma unroll
+    for (uint32_t s = 0; s < kMaxTileWords / (4 * kWave); ++s) {
+        decode_step<RUNS, false, true>(tab, geo, hdr, pay, s * (4 * kWave) + 4 * lane, pos0, kMaxTileWords, &carry,
+                                       out + w0, true);
+        if (!UNI) {
+            pos0 += step_inc;
+            if (pos0 >= Mw) pos0 -= Mw;
+        }
+    }
+}
+
 template <int RUNS>
 __device__ __forceinline__ void stage_tables(const Tables& t, uint32_t Mw, uint32_t n_planes_words,
                                              bool per_position, uint32_t* lds) {
@@ -434,32 +458,191 @@ __global__ __launch_bounds__(256) void k_decode_small(Tables t, Geo geo, const u
 }
 
 // ---------------------------------------------------------------------------
-// Tensors longer than one tile (decoupled look-back).  A wave takes a group
-// of up to kDecodeTilesPerGroup consecutive tiles of one tensor; thread 0 of
-// a workgroup takes one ticket for its four waves, whose groups follow each
+// Start bits of the groups of tiles without look-back, for records already in
+// HBM, where a second read of the header words (1/W of the tensor's bits)
+// costs less than a look-back wait per group.  k_group_bits: a wave takes
+// kGroupsPerWave groups and writes each group's payload bits (its chunks'
+// widths from its participation bits and the bit planes); k_group_scan: one
+// workgroup per tensor turns them into exclusive start bits, the header words
+// first.
+// Groups of raw tensors or bad ids get 0; the decode reports those itself.
+// ---------------------------------------------------------------------------
+constexpr uint32_t kGroupsPerWave = 4;
+
+__global__ __launch_bounds__(kWave * kWavesPerBlock) void k_group_bits(Tables t, Geo geo,
+                                                                       const uint8_t* __restrict__ slots,
+                                                                       uint64_t n_slots,
+                                                                       const uint32_t* __restrict__ bitmask,
+                                                                       const int64_t* __restrict__ ids,
+                                                                       uint64_t n_out, uint64_t* bits) {
+    // The bit planes of one entry (the same for every header word) are kept
+    // in registers; more entries go to LDS when they fit (every header word
+    // reads np of them).
+    __shared__ uint32_t lds_planes[kMaxLdsPlaneBytes / 4];
+    const uint32_t n_plane_words = (geo.Pc / geo.G) * (uint32_t)kPlanes;
+    const bool one_entry = n_plane_words == (uint32_t)kPlanes;
+    const bool staged = !one_entry && 4ull * n_plane_words <= kMaxLdsPlaneBytes;
+    if (staged) {
+        for (uint32_t i = threadIdx.x; i < n_plane_words; i += blockDim.x) lds_planes[i] = t.planes[i];
+        __syncthreads();
+    }
+    const uint32_t lane = lane_id();
+    const uint64_t gpt = decode_groups(geo.tiles_per_tensor);
+    const uint64_t first = ((uint64_t)blockIdx.x * kWavesPerBlock + uniform(threadIdx.x / kWave)) * kGroupsPerWave;
+    // A group has at most kDecodeTilesPerGroup * 64 = 512 header words: 8 per
+    // lane, read for all kGroupsPerWave groups before any is summed.  Word u
+    // of a lane is header word j(u) of its group (16-byte vectors when the
+    // slots are aligned).
+    constexpr uint32_t kU = kDecodeTilesPerGroup * 64 / kWave;
+    const bool vec = geo.aligned16 != 0;
+    auto j_of = [&](uint32_t u) __attribute__((always_inline)) {
+        return vec ? 4 * lane + 4 * kWave * (u / 4) + (u & 3) : lane + kWave * u;
+    };
+    const uint64_t total = n_out * gpt;
+    // the tensor of each group, then its bitmask bit, then its header words,
+    // each step for all groups before the next
+    int64_t tensor[kGroupsPerWave];
+#pragma unroll
+    for (uint32_t k = 0; k < kGroupsPerWave; ++k) {
+        const uint64_t oi = min(first + k, total - 1) / gpt;
+        tensor[k] = ids ? (int64_t)uniform64((uint64_t)ids[oi]) : (int64_t)oi;
+    }
+    bool live[kGroupsPerWave];
+#pragma unroll
+    for (uint32_t k = 0; k < kGroupsPerWave; ++k) {
+        live[k] = first + k < total && tensor[k] >= 0 && (uint64_t)tensor[k] < n_slots;
+        if (live[k]) live[k] = (uniform(bitmask[(uint64_t)tensor[k] >> 5]) >> ((uint64_t)tensor[k] & 31)) & 1u;
+    }
+    uint32_t h[kGroupsPerWave][kU];
+    uint64_t hw0[kGroupsPerWave], span[kGroupsPerWave];
+    uint32_t hw_g[kGroupsPerWave];
+#pragma unroll
+    for (uint32_t k = 0; k < kGroupsPerWave; ++k) {
+        const uint64_t group = min(first + k, total - 1);
+        const uint64_t w0 = (group % gpt) * kDecodeTilesPerGroup * geo.tile_words;
+        span[k] = min(w0 + (uint64_t)kDecodeTilesPerGroup * geo.tile_words, geo.n_words) - w0;
+        hw0[k] = (w0 >> geo.log2g) >> 5;
+        hw_g[k] = (uint32_t)(((span[k] >> geo.log2g) + 31) / 32);
+        if (!live[k]) continue;
+        const uint32_t* hs = reinterpret_cast<const uint32_t*>(slots + (uint64_t)tensor[k] * geo.L) + hw0[k];
+        // loads past the group's header words read its first word again
+        if (vec) {
+#pragma unroll
+            for (uint32_t i = 0; i < kU / 4; ++i) {
+                const uint32_t jv = j_of(4 * i) < hw_g[k] ? j_of(4 * i) : 0u;
+                const u32x4 x = *reinterpret_cast<const u32x4*>(hs + jv);
+#pragma unroll
+                for (uint32_t c = 0; c < 4; ++c) h[k][4 * i + c] = x[c];
+            }
+        } else {
+#pragma unroll
+            for (uint32_t u = 0; u < kU; ++u) h[k][u] = hs[j_of(u) < hw_g[k] ? j_of(u) : 0u];
+        }
+    }
+    // removed(gj, h): removed bits of header word gj holding h
+    auto sum_groups = [&](auto removed) __attribute__((always_inline)) {
+#pragma unroll
+        for (uint32_t k = 0; k < kGroupsPerWave; ++k) {
+            if (first + k >= total) break;
+            uint32_t rem = 0;
+            if (live[k]) {
+#pragma unroll
+                for (uint32_t u = 0; u < kU; ++u) {
+                    const uint64_t gj = hw0[k] + j_of(u);
+                    uint32_t hw = j_of(u) < hw_g[k] ? h[k][u] : 0u;
+                    if (gj == geo.hdr_words - 1) {  // bits past the last chunk count nothing
+                        const uint32_t valid = (uint32_t)(geo.n_chunks - 32ull * gj);
+                        if (valid < 32) hw &= (1u << valid) - 1u;
+                    }
+                    rem += removed(gj, hw);
+                }
+            }
+            const uint32_t tot = wave_sum(rem);
+            if (lane == 0) bits[first + k] = live[k] ? 32 * span[k] - tot : 0;
+        }
+    };
+    if (geo.Pc == 1) {
+        // one chunk per period: every chunk removes the same k bits
+        sum_groups([&](uint64_t, uint32_t hw) __attribute__((always_inline)) {
+            return (uint32_t)__builtin_popcount(hw) * geo.k1;
+        });
+    } else if (one_entry) {
+        // planes past np are zero
+        uint32_t pl[kPlanes];
+#pragma unroll
+        for (int q = 0; q < kPlanes; ++q) pl[q] = t.planes[q];
+        sum_groups([&](uint64_t, uint32_t hw) __attribute__((always_inline)) {
+            uint32_t r = 0;
+#pragma unroll
+            for (int q = 0; q < kPlanes; ++q) r += (uint32_t)__builtin_popcount(hw & pl[q]) << q;
+            return r;
+        });
+    } else if (staged) {
+        sum_groups([&](uint64_t gj, uint32_t hw) __attribute__((always_inline)) {
+            return removed_bits_pl(lds_planes, geo, gj, hw);
+        });
+    } else {
+        sum_groups([&](uint64_t gj, uint32_t hw) __attribute__((always_inline)) {
+            return removed_bits_pl(t.planes, geo, gj, hw);
+        });
+    }
+}
+
+__global__ __launch_bounds__(256) void k_group_scan(uint64_t gpt, uint64_t base, uint64_t* bits) {
+    __shared__ uint64_t part[256];
+    uint64_t* v = bits + (uint64_t)blockIdx.x * gpt;
+    const uint32_t tid = threadIdx.x;
+    const uint64_t per = (gpt + 255) / 256;
+    const uint64_t lo = min(tid * per, gpt), hi = min(lo + per, gpt);
+    uint64_t sum = 0;
+    for (uint64_t i = lo; i < hi; ++i) sum += v[i];
+    part[tid] = sum;
+    __syncthreads();
+    // inclusive scan of the 256 partial sums (Hillis-Steele)
+    for (uint32_t d = 1; d < 256; d <<= 1) {
+        const uint64_t add = tid >= d ? part[tid - d] : 0;
+        __syncthreads();
+        part[tid] += add;
+        __syncthreads();
+    }
+    uint64_t run = base + part[tid] - sum;
+    for (uint64_t i = lo; i < hi; ++i) {
+        const uint64_t x = v[i];
+        v[i] = run;
+        run += x;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Tensors longer than one tile.  A wave takes a group of up to
+// kDecodeTilesPerGroup consecutive tiles of one tensor and reads the header
+// words of its whole group at once.  With `starts` (from k_group_bits and
+// k_group_scan) the group's start bit is read from there and groups follow
+// the block index.  Otherwise it is found by decoupled look-back: thread 0
+// of a workgroup takes one ticket for its waves, whose groups follow each
 // other, so groups are numbered in the order their workgroups started and a
-// group waits only on groups that are resident or done.  The wave reads the
-// header words of its whole group at once, publishes the group's payload
-// bits, finds where the group's payload starts by look-back over earlier
-// groups of the tensor, then reads and rebuilds its tiles one after another
-// (each tile's start bit is the group's plus the earlier tiles' bits, from
-// their header words).  One atomic and one look-back per group instead of
-// per tile.
+// group waits only on groups that are resident or done; the wave publishes
+// its group's payload bits and sums those of earlier groups of the tensor
+// (one atomic and one look-back per group instead of per tile).  It then
+// reads and rebuilds its tiles one after another (each tile's start bit is
+// the group's plus the earlier tiles' bits, from their header words).
 // ---------------------------------------------------------------------------
 template <int RUNS, bool UNI>
-__global__ __launch_bounds__(256) void k_decode_groups(Tables t, Geo geo, const uint8_t* __restrict__ slots,
+__global__ __launch_bounds__(kWave * kGroupWaves) void k_decode_groups(Tables t, Geo geo, const uint8_t* __restrict__ slots,
                                                        uint64_t n_slots, const uint32_t* __restrict__ bitmask,
                                                        const int64_t* __restrict__ ids, uint64_t n_out,
                                                        uint8_t* __restrict__ dst, uint32_t* err, LookBack lb,
-                                                       uint32_t lds_words) {
+                                                       const uint64_t* __restrict__ starts, uint32_t lds_words) {
     extern __shared__ uint32_t smem[];
     __shared__ uint32_t block_ticket;
     const uint32_t lane = lane_id();
     const uint32_t wib = uniform(threadIdx.x / kWave);
     uint32_t* lds = smem + wib * lds_words;
-    if (threadIdx.x == 0) block_ticket = atomicAdd(lb.ticket, 1u);
-    __syncthreads();
-    const uint64_t group = (uint64_t)uniform(block_ticket) * kWavesPerBlock + wib;
+    if (!starts) {
+        if (threadIdx.x == 0) block_ticket = atomicAdd(lb.ticket, 1u);
+        __syncthreads();
+    }
+    const uint64_t group = (uint64_t)(starts ? blockIdx.x : uniform(block_ticket)) * kGroupWaves + wib;
     const uint64_t tpt = geo.tiles_per_tensor;
     const uint64_t gpt = decode_groups(tpt);
     if (group >= n_out * gpt) return;
@@ -514,7 +697,9 @@ __global__ __launch_bounds__(256) void k_decode_groups(Tables t, Geo geo, const 
             agg_all += agg[r];
         }
     }
-    const uint64_t S = lookback_exclusive(lb.status, oi * gpt, lg, agg_all, 32ull * geo.hdr_words, lb.epoch, err);
+    const uint64_t S = starts ? uniform64(starts[group])
+                              : lookback_exclusive(lb.status, oi * gpt, lg, agg_all, 32ull * geo.hdr_words, lb.epoch,
+                                                   err);
     const uint64_t E = S + agg_all;
     const bool last = lg == gpt - 1;
     if (bad_pad || E > 8ull * geo.L || (last && 4 * ((E + 31) / 32) >= geo.L)) {
@@ -535,52 +720,103 @@ __global__ __launch_bounds__(256) void k_decode_groups(Tables t, Geo geo, const 
     // Records in HBM, with 16-byte vectors: the next tile's payload (at most
     // 2,048 + 8 words, so kPre vectors per lane) is read into registers while
     // the current tile is rebuilt from LDS (32 llm_bf16 layers from HBM:
-    // 1,355 -> 1,172 us).  Over the host link the reads in flight of many
-    // waves already fill the link, and this prefetch measured slower
-    // (1,272 -> 1,302 us per layer), so there each tile is read when due.
+    // 1,355 -> 1,172 us, and 1,100 us with the buffer loads below).  Over the
+    // host link the reads in flight of many waves already fill the link, and
+    // this prefetch measured slower (1,272 -> 1,302 us per layer), so there
+    // each tile is read when due.
     const bool pipelined = vec && geo.src_in_hbm;
     constexpr uint32_t kPre = (kMaxTileWords + 8 + 4 * kWave - 1) / (4 * kWave);
     u32x4 pre[kPre];
-    const u32x4* src4 = reinterpret_cast<const u32x4*>(src);
+    // kPre buffer loads per lane whose range is payload words [a, b): vectors
+    // past it return zero without touching memory, so every tile issues the
+    // same number of loads whatever its length.  Word 3 of the descriptor is
+    // the gfx9 raw-buffer format (32-bit data, no swizzle); cache policy 2 is
+    // the non-temporal hint.
     auto issue = [&](uint64_t a, uint64_t b) __attribute__((always_inline)) {
+        const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+            (void*)(src + uniform64(a)), (short)0, (int)uniform((uint32_t)(4 * (b - a))), 0x00020000);
+#pragma unroll
+        for (uint32_t i = 0; i < kPre; ++i)
+            pre[i] = __builtin_amdgcn_raw_buffer_load_b128(rs, (int)(16 * (lane + i * kWave)), 0, 2);
+    };
+    // the loaded words [a, b) into pay, and the zero word after them
+    auto stage = [&](uint64_t a, uint64_t b) __attribute__((always_inline)) {
         const uint32_t n4 = (uint32_t)((b - a) >> 2);
 #pragma unroll
         for (uint32_t i = 0; i < kPre; ++i)
-            if (lane + i * kWave < n4) pre[i] = __builtin_nontemporal_load(src4 + (a >> 2) + lane + i * kWave);
+            if (lane + i * kWave < n4) reinterpret_cast<u32x4*>(pay)[lane + i * kWave] = pre[i];
+        if (lane == 0) pay[b - a] = 0;
     };
     uint64_t St = S;
-    uint64_t a_next = 0, b_next = 0;
-    if (pipelined) {
-        tile_range(St, 0, &a_next, &b_next);
-        issue(a_next, b_next);
-    }
-    for (uint32_t r = 0; r < n_tiles; ++r) {
+    // the rebuild of tile r from pay (any length)
+    auto rebuild = [&](uint32_t r, uint64_t a) __attribute__((always_inline)) {
         const uint64_t wt = w0 + (uint64_t)r * tw;
         const uint32_t nw = (uint32_t)min((uint64_t)tw, wend - wt);
-        const uint64_t Et = St + agg[r];
-        uint64_t a, b;
-        tile_range(St, r, &a, &b);
-        __builtin_amdgcn_wave_barrier();  // the previous tile's reads of pay are done
-        if (pipelined) {
-            const uint32_t n4 = (uint32_t)((b - a) >> 2);
-#pragma unroll
-            for (uint32_t i = 0; i < kPre; ++i)
-                if (lane + i * kWave < n4) reinterpret_cast<u32x4*>(pay)[lane + i * kWave] = pre[i];
-            if (r + 1 < n_tiles) {
-                tile_range(Et, r + 1, &a_next, &b_next);
-                issue(a_next, b_next);
-            }
-        } else {
-            load_words_to_lds(src, a, b, pay, vec);
-        }
-        if (lane == 0) pay[b - a] = 0;
-        __builtin_amdgcn_wave_barrier();
         if (UNI)
             decode_tile<RUNS, false, true>(tu, geo, hdr + r * hw_tile, pay, (uint32_t)(St - 32 * a), wt, nw, out,
                                            vec && (wt & 3) == 0);
         else
             decode_tile<RUNS, false, true>(ta, geo, hdr + r * hw_tile, pay, (uint32_t)(St - 32 * a), wt, nw, out,
                                            vec && (wt & 3) == 0);
+    };
+    const uint32_t n_full = (uint32_t)((wend - w0) / tw);
+    if (pipelined && n_full > 0 && tw == kMaxTileWords) {
+        // Each iteration rebuilds full tile r (kMaxTileWords / 256 unrolled
+        // steps, one store each), then writes tile r + 1's prefetched vectors
+        // to LDS and issues tile r + 2's loads.  The loop is entered with
+        // tile 0 staged and tile 1's loads in flight, the same pattern its
+        // back edge carries, so before each LDS write the compiler waits for
+        // that vector's load alone and leaves the tile's stores in flight.
+        // (A second register buffer, two tiles ahead, measured no faster.)
+        uint64_t a, b;
+        tile_range(St, 0, &a, &b);
+        issue(a, b);
+        stage(a, b);
+        if (n_tiles > 1) {
+            uint64_t an, bn;
+            tile_range(St + agg[0], 1, &an, &bn);
+            issue(an, bn);
+        }
+        for (uint32_t r = 0; r < n_full; ++r) {
+            __builtin_amdgcn_wave_barrier();  // the staged words are written
+            if (UNI)
+                decode_full_tile<RUNS>(tu, geo, hdr + r * hw_tile, pay, (uint32_t)(St - 32 * a), w0 + (uint64_t)r * tw,
+                                       out);
+            else
+                decode_full_tile<RUNS>(ta, geo, hdr + r * hw_tile, pay, (uint32_t)(St - 32 * a), w0 + (uint64_t)r * tw,
+                                       out);
+            St += agg[r];
+            if (r + 1 < n_tiles) {
+                tile_range(St, r + 1, &a, &b);
+                __builtin_amdgcn_wave_barrier();  // this tile's reads of pay are done
+                stage(a, b);
+                if (r + 2 < n_tiles) {
+                    uint64_t an, bn;
+                    tile_range(St + agg[r + 1], r + 2, &an, &bn);
+                    issue(an, bn);
+                }
+            }
+        }
+        if (n_full < n_tiles) {  // the tensor's ragged last tile, staged by the loop
+            __builtin_amdgcn_wave_barrier();
+            rebuild(n_full, a);
+        }
+        return;
+    }
+    for (uint32_t r = 0; r < n_tiles; ++r) {
+        const uint64_t Et = St + agg[r];
+        uint64_t a, b;
+        tile_range(St, r, &a, &b);
+        __builtin_amdgcn_wave_barrier();  // the previous tile's reads of pay are done
+        if (pipelined) {  // a single ragged tile
+            issue(a, b);
+            stage(a, b);
+        } else {
+            load_words_to_lds(src, a, b, pay, vec);
+            if (lane == 0) pay[b - a] = 0;
+        }
+        __builtin_amdgcn_wave_barrier();
+        rebuild(r, a);
         St = Et;
     }
 }
@@ -747,12 +983,28 @@ static hipError_t launch_groups(const Tables& t, const Geo& geo, const void* slo
     // header words of a group, then one tile's payload (up to 8 words of
     // 16-byte rounding and the zero word after it)
     const uint32_t lds_words = kDecodeTilesPerGroup * 64 + geo.tile_words + 8;
-    const uint64_t groups = n_out * decode_groups(geo.tiles_per_tensor);
-    const dim3 grid((uint32_t)((groups + kWavesPerBlock - 1) / kWavesPerBlock));
-    const dim3 block(kWave * kWavesPerBlock);
-    const size_t shm = (size_t)lds_words * 4 * kWavesPerBlock;
+    const uint64_t gpt = decode_groups(geo.tiles_per_tensor);
+    const uint64_t groups = n_out * gpt;
+    uint64_t* starts = nullptr;
+    if (geo.src_in_hbm) {
+        // records in HBM: start bits from two short passes over the header
+        // words, into the look-back status words
+        starts = reinterpret_cast<uint64_t*>(lb.status);
+        const uint64_t waves = (groups + kGroupsPerWave - 1) / kGroupsPerWave;
+        hipLaunchKernelGGL(k_group_bits, dim3((uint32_t)((waves + kWavesPerBlock - 1) / kWavesPerBlock)),
+                           dim3(kWave * kWavesPerBlock), 0, s, t, geo, static_cast<const uint8_t*>(slots), n_slots,
+                           bitmask, ids, n_out, starts);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        hipLaunchKernelGGL(k_group_scan, dim3((uint32_t)n_out), dim3(256), 0, s, gpt, 32ull * geo.hdr_words, starts);
+        e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    const dim3 grid((uint32_t)((groups + kGroupWaves - 1) / kGroupWaves));
+    const dim3 block(kWave * kGroupWaves);
+    const size_t shm = (size_t)lds_words * 4 * kGroupWaves;
     hipLaunchKernelGGL((k_decode_groups<RUNS, UNI>), grid, block, shm, s, t, geo, static_cast<const uint8_t*>(slots),
-                       n_slots, bitmask, ids, n_out, static_cast<uint8_t*>(dst), err, lb, lds_words);
+                       n_slots, bitmask, ids, n_out, static_cast<uint8_t*>(dst), err, lb, starts, lds_words);
     return hipGetLastError();
 }
 

@@ -354,9 +354,10 @@ __device__ __forceinline__ void latch_error(uint32_t* err, uint32_t code) {
 
 // Removed bits of header word `hword` (global header word index j): the sum
 // over its set participation bits of that chunk's k, from the bit planes of
-// entry ((32 j) mod Pc) / G.
+// entry ((32 j) mod Pc) / G (with one chunk per period, every chunk's k).
 __device__ __forceinline__ uint32_t removed_bits_pl(const uint32_t* planes, const Geo& g, uint64_t j,
                                                     uint32_t hword) {
+    if (g.Pc == 1) return (uint32_t)__builtin_popcount(hword) * g.k1;
     const uint32_t e = (uint32_t)(((32ull * j) % g.Pc) / g.G);
     const uint32_t* pl = planes + e * (uint32_t)kPlanes;
     uint32_t s = 0;

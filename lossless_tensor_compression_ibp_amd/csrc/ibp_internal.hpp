@@ -40,6 +40,7 @@ struct Geo {
     uint32_t log2g;          // log2(W / 32)
     uint32_t G;              // gcd(32, Pc)
     uint32_t np;             // bit planes worth scanning (<= kPlanes)
+    uint32_t k1;             // Pc == 1: the k every chunk removes
     uint32_t tile_words;     // words per tile (multiple of 64 * 32 >> ... see host)
     uint64_t tiles_per_tensor;
     uint32_t spec_words;     // first-read words of a single-tile record (multiple of 4)
@@ -80,6 +81,11 @@ constexpr uint64_t kLookbackPoison = 1ull << 41;
 #define IBP_DECODE_TILES_PER_GROUP 8
 #endif
 constexpr uint32_t kDecodeTilesPerGroup = IBP_DECODE_TILES_PER_GROUP;
+// Waves per workgroup of the group decode.
+#ifndef IBP_DECODE_GROUP_WAVES
+#define IBP_DECODE_GROUP_WAVES 4
+#endif
+constexpr int kGroupWaves = IBP_DECODE_GROUP_WAVES;
 __host__ __device__ constexpr uint64_t decode_groups(uint64_t tiles_per_tensor) {
     return (tiles_per_tensor + kDecodeTilesPerGroup - 1) / kDecodeTilesPerGroup;
 }

@@ -109,6 +109,10 @@ def _structured(rng, n, L, flip=0.01):
     (32, 32, 8192 + 16, 33),           # smallest two-tile tensor, ragged tail
     (64, 128, 65536 + 48, 9),          # many tiles, W = 64
     (1024, 1024, 3 * 4096 + 1024, 7),  # tiles of W = 1024 chunks
+    (32, 96 * 32, 3 * 8192, 12),       # three full tiles, period of 96 words
+    (128, 4096, 3 * 8192 + 4096 + 512, 6),  # ragged fourth tile, period of 128 words
+    (32, 256, 17 * 8192 + 64, 5),      # three groups of tiles, the last one ragged
+    (32, 375 * 32, 12 * 1500, 6),      # 375 header-word phases: bit planes too many for LDS
 ])
 def test_shapes(W, M, L, n):
     rng = np.random.default_rng(W + M + L)
