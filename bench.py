@@ -712,6 +712,8 @@ def run_dlrm(args) -> dict:
 # (stream B, y = x @ W on the decoded layer)
 # ---------------------------------------------------------------------------
 LLM_KERNEL = "ibp::k_decode_groups<3, true> (look-back over groups of 8 tiles of 8 KiB)"
+LLM_HBM_KERNELS = ("ibp::k_group_bits + ibp::k_group_scan + ibp::k_decode_groups<3, true> (group start bits from a "
+                   "pass over the header words, then groups of 8 tiles of 8 KiB; kernel_avg_us spans all three)")
 
 
 def run_llm_bf16(args) -> dict:
@@ -799,9 +801,9 @@ def run_llm_bf16(args) -> dict:
             "what": f"the same {layers} compressed layers held in HBM slots, all of them decoded by one "
                     f"ibp_decompress per step into HBM (inputs resident in HBM, no host link)",
             "decoded_GBps": round(args.steps * layers * L / hbm_wall / GB, 3),
-            "ms_per_step": round(hbm_wall / args.steps * 1e3, 4), "kernel": LLM_KERNEL,
+            "ms_per_step": round(hbm_wall / args.steps * 1e3, 4), "kernel": LLM_HBM_KERNELS,
             "kernel_avg_us": round(float(np.mean(hbm_durs)) * 1e6, 2),
-            "roofline": hbm_roofline(hbm_bytes, hbm_durs, None)}
+            "roofline": hbm_roofline(hbm_bytes, hbm_durs, "llm_bf16_hbm")}
         del dslots, dout
     h2d = h2d_ceiling()
     res = base_result(
