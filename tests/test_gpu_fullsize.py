@@ -164,6 +164,22 @@ def test_llm_bf16_full():
         assert ibp.ibp_check(meta) == ibp.IBP_OK
         assert torch.equal(buf[0], host[l].to(DEV)), f"layer {l} differs"
     say("[full] llm_bf16 ok")
+    # the same records in HBM slots: every layer in one call (header pass,
+    # scan, group decode), then a gather with repeated ids
+    say("[full] llm_bf16 from HBM slots (start bits from the header pass)")
+    del buf
+    dsl = slots.to(DEV)
+    out = torch.empty((layers, L), dtype=torch.uint8, device=DEV)
+    ibp.ibp_decompress(meta, dsl, bm, layers, out)
+    assert ibp.ibp_check(meta) == ibp.IBP_OK
+    for l in range(layers):
+        assert torch.equal(out[l], host[l].to(DEV)), f"layer {l} differs (HBM slots)"
+    ids = torch.tensor([layers - 1, 0, layers - 1], dtype=torch.int64, device=DEV)
+    ibp.ibp_gather_decompress(meta, dsl, layers, bm, ids, out[:3])
+    assert ibp.ibp_check(meta) == ibp.IBP_OK
+    for i, l in enumerate([layers - 1, 0, layers - 1]):
+        assert torch.equal(out[i], host[l].to(DEV)), f"gathered layer {l} differs (HBM slots)"
+    say("[full] llm_bf16 HBM slots ok")
 
 
 def test_kv_bf16_full():

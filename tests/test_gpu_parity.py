@@ -325,6 +325,43 @@ def test_device_errors_are_latched():
     assert ibp.ibp_check(r2.meta) == ibp.IBP_ERR_CORRUPT
 
 
+@pytest.mark.parametrize("pinned", [False, True], ids=["hbm_two_pass", "pinned_look_back"])
+def test_multi_tile_errors_are_latched(pinned):
+    """Tensors of 22 tiles (records in HBM: start bits from the header pass
+    and scan; pinned: look-back): bad ids latch IBP_ERR_RANGE while the good
+    ids of the same gather decode exactly; a record whose header claims every
+    chunk verbatim latches IBP_ERR_CORRUPT, and the other tensors of that
+    launch still decode exactly."""
+    dev = device()
+    w = WL.LLM_BF16
+    # five scaled layers (8 x 11008 bf16, 176 KB: 22 tiles, three groups)
+    raw = np.stack([WL.llm_layer(l, rows=8).reshape(-1).view(np.uint8) for l in range(5)])
+    n, L = raw.shape
+    r = compare_codec(raw, w.chunk_bits, w.period_bits, w.threshold, 1, slots_pinned=pinned,
+                      label="multi-tile errors setup")
+    meta = r.meta
+    out = torch.zeros((4, L), dtype=torch.uint8, device=dev)
+    ids = torch.tensor([0, n, 3, -1], dtype=torch.int64, device=dev)
+    ibp.ibp_gather_decompress(meta, r.slots, n, r.bm, ids, out)
+    assert ibp.ibp_check(meta) == ibp.IBP_ERR_RANGE
+    assert ibp.ibp_check(meta) == ibp.IBP_OK
+    np.testing.assert_array_equal(out[0].cpu().numpy(), raw[0])
+    np.testing.assert_array_equal(out[2].cpu().numpy(), raw[3])
+    comp = np.flatnonzero(np.unpackbits(r.bm.cpu().numpy().view(np.uint8), bitorder="little")[:n])
+    assert comp.size >= 2
+    t = int(comp[0])
+    bad = r.slots.clone()
+    if pinned:
+        bad = bad.pin_memory()
+    hw = (8 * L // 32 + 31) // 32
+    bad[t, : 4 * hw] = 0  # no participating chunk: a record longer than the slot
+    full = torch.zeros((n, L), dtype=torch.uint8, device=dev)
+    ibp.ibp_decompress(meta, bad, r.bm, n, full)
+    assert ibp.ibp_check(meta) == ibp.IBP_ERR_CORRUPT
+    others = [i for i in range(n) if i != t]
+    np.testing.assert_array_equal(full.cpu().numpy()[others], raw[others])
+
+
 def test_pageable_host_memory_is_rejected():
     dev = device()
     L, n = 512, 8
