@@ -1,6 +1,6 @@
 """Seeded random formats against the oracle, bit for bit: chunk widths 32 to
-1024, periods, tensor lengths (one tile and several, 16-byte multiples and
-not), Mask words with 0 to 16 runs of kept bits (uniform and per-position),
+1024, periods, tensor lengths (one tile, several, and several groups of eight
+tiles; 16-byte multiples and not), Mask words with 0 to 16 runs of kept bits (uniform and per-position),
 chunk match rates from none to all, slots in HBM or pinned host memory, and
 gathers with repeated ids.  Metadata comes from ibp_meta_create so that the
 run structure and the match rate are controlled; everything the kernels
@@ -53,7 +53,9 @@ def _format(rng, layout):
     if layout is None:
         shape = rng.choice(["small", "small", "small", "multi"])
         if shape == "multi":
-            n_chunks = int(rng.integers(2049 // g + 1, 9000 // g + 2))
+            # up to 4 tiles (one group of the decode), or up to 26 (four groups)
+            top = 9000 if rng.random() < 0.5 else 53000
+            n_chunks = int(rng.integers(2049 // g + 1, top // g + 2))
         else:
             n_chunks = int(rng.integers(1, max(2, 2048 // g) + 1))
         max_m = 1 << 20
