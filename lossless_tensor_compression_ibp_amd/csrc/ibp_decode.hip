@@ -922,7 +922,8 @@ static hipError_t launch_small_s(const Tables& t, const Geo& geo, const void* sl
     const void* fn = reinterpret_cast<const void*>(&k_decode_small<RUNS, UNI, MW4, S, SPLIT>);
     PersistentPlan plan;
     *launched = false;
-    if (!plan_persistent(fn, head, wave, cu_count, n_out, &plan, geo.src_in_hbm ? kSmallDecodeWavesPerSimdHbm : 8u))
+    if (!plan_persistent(fn, head, wave, cu_count, n_out, &plan, geo.src_in_hbm ? kSmallDecodeWavesPerSimdHbm : 8u,
+                         kDecodeItemsPerWave))
         return hipSuccess;
     hipLaunchKernelGGL((k_decode_small<RUNS, UNI, MW4, S, SPLIT>), dim3(plan.blocks), dim3(kWave * plan.wpb),
                        plan.shm, s, t, geo, static_cast<const uint8_t*>(slots), n_slots, bitmask, ids, n_out,

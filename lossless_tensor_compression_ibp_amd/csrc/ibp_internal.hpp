@@ -125,19 +125,31 @@ struct PersistentPlan {
 // VGPR count, the LDS limits of the device and at most max_waves_per_simd
 // resident waves per SIMD.
 // blocks = min(items / wpb, max(workgroups that fill the device,
-// items / (wpb * kMaxItemsPerWave))).  Returns false when no shape fits.
+// items / (wpb * max_items))).  Returns false when no shape fits.
 //
-// kMaxItemsPerWave: a wave of a persistent launch takes at most this many
-// items; longer launches get more workgroups than fit at once.  Measured on
-// MI355X with the 262,144 4 KiB KV pages in HBM (64 pages per resident wave
-// otherwise): decode 384 -> 368 us and encode 2.34 -> 2.54 TB/s at 8 pages
-// per wave, against 372 and 374 us at 4 and 16, 408 us at 2 and 493 us at
-// one page per wave, where every workgroup stages 21 KiB of tables for four
-// pages.  A plain copy of 4 KiB pages shows the same: persistent waves
-// striding over the pages move 5.7-5.9 TB/s, one wave per page 6.3 TB/s.
-constexpr uint64_t kMaxItemsPerWave = 8;
+// max_items: a wave of a persistent launch takes at most this many items;
+// longer launches get more workgroups than fit at once.  Measured on MI355X
+// with the 262,144 4 KiB KV pages in HBM (64 pages per resident wave
+// otherwise): the encode moves 2.20 / 2.36 / 2.53-2.56 / 2.57 / 2.52 TB/s of
+// input at 2 / 4 / 8 / 16 / 32 pages per wave (kMaxItemsPerWave, 8); the
+// decode takes 474 / 369 / 359-361 / 354-357 / 360 / 363 / 361 us at
+// 1 / 2 / 3 / 4 / 5 / 6 / 8 pages per wave (kDecodeItemsPerWave, 4), where
+// every workgroup stages 21 KiB of tables for its waves' pages.  512-byte
+// and 1 KiB rows in HBM (dense_gnn, the packed cache) and zero-copy gathers
+// of 65,536 rows of 512 bytes decode alike at 4 to 8.  A plain copy of 4 KiB pages shows
+// the same trade: persistent waves striding over the pages move
+// 5.7-5.9 TB/s, one wave per page 6.3 TB/s.
+#ifndef IBP_MAX_ITEMS_PER_WAVE
+#define IBP_MAX_ITEMS_PER_WAVE 8
+#endif
+constexpr uint64_t kMaxItemsPerWave = IBP_MAX_ITEMS_PER_WAVE;
+#ifndef IBP_DECODE_ITEMS_PER_WAVE
+#define IBP_DECODE_ITEMS_PER_WAVE 4
+#endif
+constexpr uint64_t kDecodeItemsPerWave = IBP_DECODE_ITEMS_PER_WAVE;
 bool plan_persistent(const void* kernel, size_t head_bytes, size_t wave_bytes, uint32_t cu_count,
-                     uint64_t n_items, PersistentPlan* plan, uint32_t max_waves_per_simd = 8);
+                     uint64_t n_items, PersistentPlan* plan, uint32_t max_waves_per_simd = 8,
+                     uint64_t max_items = kMaxItemsPerWave);
 
 // Kernel launchers.  All return hipError_t of the launch.
 hipError_t launch_fill_u32(uint32_t* p, uint64_t n, uint32_t v, hipStream_t s);

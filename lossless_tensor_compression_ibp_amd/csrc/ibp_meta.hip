@@ -255,7 +255,7 @@ static bool plan_uncached(const void* kernel, size_t head_bytes, size_t wave_byt
 }
 
 bool plan_persistent(const void* kernel, size_t head_bytes, size_t wave_bytes, uint32_t cu_count,
-                     uint64_t n_items, PersistentPlan* plan, uint32_t max_waves_per_simd) {
+                     uint64_t n_items, PersistentPlan* plan, uint32_t max_waves_per_simd, uint64_t max_items) {
     static std::mutex mu;
     static std::unordered_map<PlanKey, std::pair<bool, PersistentPlan>, PlanKeyHash> cache;
     int dev = 0;
@@ -274,11 +274,12 @@ bool plan_persistent(const void* kernel, size_t head_bytes, size_t wave_bytes, u
     }
     if (!entry.first) return false;
     PersistentPlan p = entry.second;
-    // Beyond kMaxItemsPerWave items per resident wave the launch adds
-    // workgroups past the resident fill; the hardware dispatches them as
-    // earlier ones retire, and each re-stages the tables once.
+    // Beyond max_items items per resident wave the launch adds workgroups
+    // past the resident fill; the hardware dispatches them as earlier ones
+    // retire, and each re-stages the tables once.
+    if (max_items == 0) max_items = 1;
     const uint64_t want = (n_items + p.wpb - 1) / p.wpb;
-    const uint64_t cap = (n_items + (uint64_t)p.wpb * kMaxItemsPerWave - 1) / ((uint64_t)p.wpb * kMaxItemsPerWave);
+    const uint64_t cap = (n_items + (uint64_t)p.wpb * max_items - 1) / ((uint64_t)p.wpb * max_items);
     uint64_t blocks = cap > p.blocks ? cap : (uint64_t)p.blocks;
     if (blocks > want) blocks = want;
     if (blocks > 0x7fffffffull) blocks = 0x7fffffffull;
