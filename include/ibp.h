@@ -40,11 +40,14 @@
  * different streams at once; calls on the same stream run in order, also
  * when several host threads issue them.
  *
- * Tensors longer than one tile (more than 8 KiB) are cut into tiles that
- * find their start bit by a decoupled look-back over per-stream scratch of
- * the handle.  ibp_compress, ibp_decompress and ibp_gather_decompress of
- * such tensors, and ibp_packed_offsets, return IBP_ERR_UNSUPPORTED while
- * `stream` is capturing a HIP graph; single-tile calls may be captured.
+ * Tensors longer than one tile (more than 8 KiB) are cut into tiles whose
+ * start bits need per-stream scratch of the handle: the encode, and a decode
+ * of records read over the host link, find them by a decoupled look-back; a
+ * decode of records in device memory computes them first from the header
+ * words (a pass over them and a scan per tensor).  ibp_compress,
+ * ibp_decompress and ibp_gather_decompress of such tensors, and
+ * ibp_packed_offsets, return IBP_ERR_UNSUPPORTED while `stream` is capturing
+ * a HIP graph; single-tile calls may be captured.
  */
 #ifndef IBP_H
 #define IBP_H
@@ -153,7 +156,7 @@ ibp_status ibp_gather_decompress(ibp_meta_t meta, const void* slots, uint64_t n_
 /* ibp_decompress for callers that cannot allocate device memory: code under
  * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.
  * Same arguments, contract and output as ibp_decompress.  It calls no
- * hipMalloc/hipFree: the look-back scratch of tensors longer than one tile
+ * hipMalloc/hipFree: the start-bit scratch of tensors longer than one tile
  * (L > 8 KiB) lives in one static device array of IBP_NOALLOC_SCRATCH_BYTES
  * per GPU, part of the library's code object and held until the process
  * ends (its address is looked up with hipGetSymbolAddress on the first call

@@ -976,7 +976,9 @@ static hipError_t launch_tiles(const Tables& t, const Geo& geo, const void* slot
 }
 
 // Tensors longer than one tile: one wave per group of tiles; lb holds one
-// status word per group (n_out * decode_groups(tiles_per_tensor)).
+// status word per group (n_out * decode_groups(tiles_per_tensor)), which the
+// look-back uses over the host link and the start bits of the header pass
+// and scan use for records in HBM.
 template <int RUNS, bool UNI>
 static hipError_t launch_groups(const Tables& t, const Geo& geo, const void* slots, uint64_t n_slots,
                                 const uint32_t* bitmask, const int64_t* ids, uint64_t n_out, void* dst,
