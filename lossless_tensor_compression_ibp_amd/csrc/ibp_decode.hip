@@ -722,8 +722,8 @@ __global__ __launch_bounds__(kWave * kGroupWaves) void k_decode_groups(Tables t,
     // the current tile is rebuilt from LDS (32 llm_bf16 layers from HBM:
     // 1,355 -> 1,172 us, and 1,100 us with the buffer loads below).  Over the
     // host link the reads in flight of many waves already fill the link, and
-    // this prefetch measured slower (1,272 -> 1,302 us per layer), so there
-    // each tile is read when due.
+    // this prefetch measured slower (1,252 -> 1,267 us per layer alone), so
+    // there each tile is read when due.
     const bool pipelined = vec && geo.src_in_hbm;
     constexpr uint32_t kPre = (kMaxTileWords + 8 + 4 * kWave - 1) / (4 * kWave);
     u32x4 pre[kPre];
