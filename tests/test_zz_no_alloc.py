@@ -1,6 +1,8 @@
 """ibp_decompress_noalloc, the decode entry point for callers that cannot
-allocate device memory (its look-back scratch is a static device array of
-the library), against ibp_decompress through the C ABI: the same bytes on
+allocate device memory (the start-bit scratch of its long tensors is a
+static device array of the library), against ibp_decompress through the C
+ABI, with the slots in device memory (header pass, scan and group decode):
+the same bytes on
 two calls in a row, the second with a smaller input, and inside a captured
 HIP graph replayed between eager calls."""
 from __future__ import annotations
