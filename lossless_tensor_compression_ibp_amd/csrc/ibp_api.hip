@@ -600,7 +600,7 @@ static ibp_status decode_common(ibp_meta_t h, const void* slots, uint64_t n_slot
     if (geo.tiles_per_tensor > 1) {
         // one status word per group of tiles (look-back entries, or the
         // group start bits when the records are in HBM)
-        const uint64_t groups = n_out * decode_groups(geo.tiles_per_tensor);
+        const uint64_t groups = n_out * decode_groups(geo.tiles_per_tensor, decode_group_tiles(geo.src_in_hbm));
         ibp_status st = static_scratch ? noalloc_lookback(h, stream, groups, &lb)
                                        : lookback_for(h, stream, groups, 0, &lb, &lock);
         if (st != IBP_OK) return st;

@@ -469,6 +469,7 @@ __global__ __launch_bounds__(256) void k_decode_small(Tables t, Geo geo, const u
 // ---------------------------------------------------------------------------
 constexpr uint32_t kGroupsPerWave = 4;
 
+template <uint32_t TPG>
 __global__ __launch_bounds__(kWave * kWavesPerBlock) void k_group_bits(Tables t, Geo geo,
                                                                        const uint8_t* __restrict__ slots,
                                                                        uint64_t n_slots,
@@ -487,14 +488,15 @@ __global__ __launch_bounds__(kWave * kWavesPerBlock) void k_group_bits(Tables t,
         __syncthreads();
     }
     const uint32_t lane = lane_id();
-    const uint64_t gpt = decode_groups(geo.tiles_per_tensor);
+    const uint64_t gpt = decode_groups(geo.tiles_per_tensor, TPG);
     const uint64_t first = ((uint64_t)blockIdx.x * kWavesPerBlock + uniform(threadIdx.x / kWave)) * kGroupsPerWave;
-    // A group has at most kDecodeTilesPerGroup * 64 = 512 header words: 8 per
-    // lane, read for all kGroupsPerWave groups before any is summed.  Word u
-    // of a lane is header word j(u) of its group (16-byte vectors when the
-    // slots are aligned).
-    constexpr uint32_t kU = kDecodeTilesPerGroup * 64 / kWave;
-    const bool vec = geo.aligned16 != 0;
+    // A group has at most TPG * 64 header words: TPG per lane, read for all
+    // kGroupsPerWave groups before any is summed.  Word u of a lane is header
+    // word j(u) of its group (16-byte vectors when the slots are aligned and
+    // a lane's words make whole vectors).
+    constexpr uint32_t kU = TPG * 64 / kWave;
+    static_assert(kU >= 1, "a group has at least one tile of 64 header words at most");
+    const bool vec = (kU % 4 == 0) && geo.aligned16 != 0;  // whole vectors per lane
     auto j_of = [&](uint32_t u) __attribute__((always_inline)) {
         return vec ? 4 * lane + 4 * kWave * (u / 4) + (u & 3) : lane + kWave * u;
     };
@@ -519,8 +521,8 @@ __global__ __launch_bounds__(kWave * kWavesPerBlock) void k_group_bits(Tables t,
 #pragma unroll
     for (uint32_t k = 0; k < kGroupsPerWave; ++k) {
         const uint64_t group = min(first + k, total - 1);
-        const uint64_t w0 = (group % gpt) * kDecodeTilesPerGroup * geo.tile_words;
-        span[k] = min(w0 + (uint64_t)kDecodeTilesPerGroup * geo.tile_words, geo.n_words) - w0;
+        const uint64_t w0 = (group % gpt) * TPG * geo.tile_words;
+        span[k] = min(w0 + (uint64_t)TPG * geo.tile_words, geo.n_words) - w0;
         hw0[k] = (w0 >> geo.log2g) >> 5;
         hw_g[k] = (uint32_t)(((span[k] >> geo.log2g) + 31) / 32);
         if (!live[k]) continue;
@@ -615,7 +617,7 @@ __global__ __launch_bounds__(256) void k_group_scan(uint64_t gpt, uint64_t base,
 
 // ---------------------------------------------------------------------------
 // Tensors longer than one tile.  A wave takes a group of up to
-// kDecodeTilesPerGroup consecutive tiles of one tensor and reads the header
+// TPG consecutive tiles of one tensor and reads the header
 // words of its whole group at once.  With `starts` (from k_group_bits and
 // k_group_scan) the group's start bit is read from there and groups follow
 // the block index.  Otherwise it is found by decoupled look-back: thread 0
@@ -627,7 +629,7 @@ __global__ __launch_bounds__(256) void k_group_scan(uint64_t gpt, uint64_t base,
 // reads and rebuilds its tiles one after another (each tile's start bit is
 // the group's plus the earlier tiles' bits, from their header words).
 // ---------------------------------------------------------------------------
-template <int RUNS, bool UNI>
+template <int RUNS, bool UNI, uint32_t TPG>
 __global__ __launch_bounds__(kWave * kGroupWaves) void k_decode_groups(Tables t, Geo geo, const uint8_t* __restrict__ slots,
                                                        uint64_t n_slots, const uint32_t* __restrict__ bitmask,
                                                        const int64_t* __restrict__ ids, uint64_t n_out,
@@ -644,12 +646,12 @@ __global__ __launch_bounds__(kWave * kGroupWaves) void k_decode_groups(Tables t,
     }
     const uint64_t group = (uint64_t)(starts ? blockIdx.x : uniform(block_ticket)) * kGroupWaves + wib;
     const uint64_t tpt = geo.tiles_per_tensor;
-    const uint64_t gpt = decode_groups(tpt);
+    const uint64_t gpt = decode_groups(tpt, TPG);
     if (group >= n_out * gpt) return;
     const uint64_t oi = group / gpt;
     const uint64_t lg = group - oi * gpt;
-    const uint64_t t0 = lg * kDecodeTilesPerGroup;
-    const uint32_t n_tiles = (uint32_t)min((uint64_t)kDecodeTilesPerGroup, tpt - t0);
+    const uint64_t t0 = lg * TPG;
+    const uint32_t n_tiles = (uint32_t)min((uint64_t)TPG, tpt - t0);
 
     // every group of a tensor sees the same id and bitmask bit, so a bad id
     // or a raw tensor ends all of them before the look-back
@@ -678,14 +680,14 @@ __global__ __launch_bounds__(kWave * kGroupWaves) void k_decode_groups(Tables t,
     const uint64_t hw0 = (w0 >> geo.log2g) >> 5;
     const uint32_t hw_g = (uint32_t)((((wend - w0) >> geo.log2g) + 31) / 32);
     uint32_t* hdr = lds;
-    uint32_t* pay = lds + kDecodeTilesPerGroup * 64;
+    uint32_t* pay = lds + TPG * 64;
     for (uint32_t j = lane; j < hw_g; j += kWave) hdr[j] = src[hw0 + j];
     __builtin_amdgcn_wave_barrier();
-    uint32_t agg[kDecodeTilesPerGroup];
+    uint32_t agg[TPG];
     uint64_t agg_all = 0;
     bool bad_pad = false;
 #pragma unroll
-    for (uint32_t r = 0; r < kDecodeTilesPerGroup; ++r) {
+    for (uint32_t r = 0; r < TPG; ++r) {
         agg[r] = 0;
         if (r < n_tiles) {
             const uint32_t nw = (uint32_t)min((uint64_t)tw, wend - (w0 + (uint64_t)r * tw));
@@ -976,17 +978,17 @@ static hipError_t launch_tiles(const Tables& t, const Geo& geo, const void* slot
 }
 
 // Tensors longer than one tile: one wave per group of tiles; lb holds one
-// status word per group (n_out * decode_groups(tiles_per_tensor)), which the
+// status word per group (n_out * decode_groups(tiles_per_tensor, TPG)), which the
 // look-back uses over the host link and the start bits of the header pass
 // and scan use for records in HBM.
-template <int RUNS, bool UNI>
-static hipError_t launch_groups(const Tables& t, const Geo& geo, const void* slots, uint64_t n_slots,
-                                const uint32_t* bitmask, const int64_t* ids, uint64_t n_out, void* dst,
-                                uint32_t* err, const LookBack& lb, hipStream_t s) {
+template <int RUNS, bool UNI, uint32_t TPG>
+static hipError_t launch_groups_t(const Tables& t, const Geo& geo, const void* slots, uint64_t n_slots,
+                                  const uint32_t* bitmask, const int64_t* ids, uint64_t n_out, void* dst,
+                                  uint32_t* err, const LookBack& lb, hipStream_t s) {
     // header words of a group, then one tile's payload (up to 8 words of
     // 16-byte rounding and the zero word after it)
-    const uint32_t lds_words = kDecodeTilesPerGroup * 64 + geo.tile_words + 8;
-    const uint64_t gpt = decode_groups(geo.tiles_per_tensor);
+    const uint32_t lds_words = TPG * 64 + geo.tile_words + 8;
+    const uint64_t gpt = decode_groups(geo.tiles_per_tensor, TPG);
     const uint64_t groups = n_out * gpt;
     uint64_t* starts = nullptr;
     if (geo.src_in_hbm) {
@@ -994,7 +996,7 @@ static hipError_t launch_groups(const Tables& t, const Geo& geo, const void* slo
         // words, into the look-back status words
         starts = reinterpret_cast<uint64_t*>(lb.status);
         const uint64_t waves = (groups + kGroupsPerWave - 1) / kGroupsPerWave;
-        hipLaunchKernelGGL(k_group_bits, dim3((uint32_t)((waves + kWavesPerBlock - 1) / kWavesPerBlock)),
+        hipLaunchKernelGGL(k_group_bits<TPG>, dim3((uint32_t)((waves + kWavesPerBlock - 1) / kWavesPerBlock)),
                            dim3(kWave * kWavesPerBlock), 0, s, t, geo, static_cast<const uint8_t*>(slots), n_slots,
                            bitmask, ids, n_out, starts);
         hipError_t e = hipGetLastError();
@@ -1006,9 +1008,23 @@ static hipError_t launch_groups(const Tables& t, const Geo& geo, const void* slo
     const dim3 grid((uint32_t)((groups + kGroupWaves - 1) / kGroupWaves));
     const dim3 block(kWave * kGroupWaves);
     const size_t shm = (size_t)lds_words * 4 * kGroupWaves;
-    hipLaunchKernelGGL((k_decode_groups<RUNS, UNI>), grid, block, shm, s, t, geo, static_cast<const uint8_t*>(slots),
-                       n_slots, bitmask, ids, n_out, static_cast<uint8_t*>(dst), err, lb, starts, lds_words);
+    hipLaunchKernelGGL((k_decode_groups<RUNS, UNI, TPG>), grid, block, shm, s, t, geo,
+                       static_cast<const uint8_t*>(slots), n_slots, bitmask, ids, n_out, static_cast<uint8_t*>(dst),
+                       err, lb, starts, lds_words);
     return hipGetLastError();
+}
+
+// Tensors longer than one tile, with the group size of where their records
+// are (decode_group_tiles).
+template <int RUNS, bool UNI>
+static hipError_t launch_groups(const Tables& t, const Geo& geo, const void* slots, uint64_t n_slots,
+                                const uint32_t* bitmask, const int64_t* ids, uint64_t n_out, void* dst,
+                                uint32_t* err, const LookBack& lb, hipStream_t s) {
+    if (geo.src_in_hbm)
+        return launch_groups_t<RUNS, UNI, decode_group_tiles(true)>(t, geo, slots, n_slots, bitmask, ids, n_out, dst,
+                                                                     err, lb, s);
+    return launch_groups_t<RUNS, UNI, decode_group_tiles(false)>(t, geo, slots, n_slots, bitmask, ids, n_out, dst,
+                                                                  err, lb, s);
 }
 
 template <int RUNS, bool UNI>

@@ -71,23 +71,36 @@ constexpr uint32_t kLookbackPolls = 1u << 22;
 constexpr uint64_t kLookbackPoison = 1ull << 41;
 
 // The decode of a tensor longer than one tile gives each wave a group of up
-// to this many consecutive tiles of one tensor, and the look-back chains
-// groups (one status word per group); a workgroup takes one ticket for its
-// waves' groups.  Measured on MI355X (32 llm_bf16 layers of 90 MB, 8 KiB
-// tiles): 2 / 4 / 8 / 16 tiles per group decode a layer zero-copy from
-// pinned memory in 1,277 / 1,268 / 1,255 / 1,270 us, and all 32 layers from
-// HBM in 1,658 / 1,390 / 1,350 / 1,379 us.
+// to this many consecutive tiles of one tensor (one status word per group).
+// Records read over the host link: the look-back chains groups, and a
+// workgroup takes one ticket for its waves' groups; measured on MI355X (32
+// llm_bf16 layers of 90 MB, 8 KiB tiles) 2 / 4 / 8 / 16 tiles per group
+// decode a layer zero-copy from pinned memory in 1,277 / 1,268 / 1,255 /
+// 1,270 us, and 8 is kept (1,263 / 1,251 us at 4 / 8 with the current
+// kernel).  Records in HBM take their start bits from a header pass instead;
+// there 2 / 3 / 4 / 8 / 16 tiles per group decode all 32 layers in
+// 918 / 950 / 899-909 / 955-961 / 1,046 us: groups of 4 keep 16 waves per CU
+// resident (LDS: a 1 KiB header area and an 8 KiB payload buffer per wave)
+// against 12 with groups of 8.
 #ifndef IBP_DECODE_TILES_PER_GROUP
 #define IBP_DECODE_TILES_PER_GROUP 8
 #endif
+#ifndef IBP_DECODE_TILES_PER_GROUP_HBM
+#define IBP_DECODE_TILES_PER_GROUP_HBM 4
+#endif
 constexpr uint32_t kDecodeTilesPerGroup = IBP_DECODE_TILES_PER_GROUP;
+constexpr uint32_t kDecodeTilesPerGroupHbm = IBP_DECODE_TILES_PER_GROUP_HBM;
 // Waves per workgroup of the group decode.
 #ifndef IBP_DECODE_GROUP_WAVES
 #define IBP_DECODE_GROUP_WAVES 4
 #endif
 constexpr int kGroupWaves = IBP_DECODE_GROUP_WAVES;
-__host__ __device__ constexpr uint64_t decode_groups(uint64_t tiles_per_tensor) {
-    return (tiles_per_tensor + kDecodeTilesPerGroup - 1) / kDecodeTilesPerGroup;
+__host__ __device__ constexpr uint64_t decode_groups(uint64_t tiles_per_tensor, uint32_t tiles_per_group) {
+    return (tiles_per_tensor + tiles_per_group - 1) / tiles_per_group;
+}
+// Tiles per group of a decode whose stored records are (not) in device memory.
+__host__ __device__ constexpr uint32_t decode_group_tiles(bool src_in_hbm) {
+    return src_in_hbm ? kDecodeTilesPerGroupHbm : kDecodeTilesPerGroup;
 }
 
 enum DeviceError : uint32_t { kErrNone = 0, kErrCorrupt = 5, kErrRange = 6, kErrStall = 7 };
