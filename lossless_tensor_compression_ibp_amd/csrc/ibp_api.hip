@@ -20,9 +20,9 @@ using namespace ibp;
 
 namespace {
 
-// Tile of a tensor longer than kMaxTileWords.  Decode measured fastest with
-// the largest tile (fewer look-back hops per tensor), encode with half of it.
-constexpr uint32_t kLongTileWordsDecode = 2048;
+// Tile of a tensor longer than kMaxTileWords.  Decode over the host link
+// measured fastest with the largest tile (fewer look-back hops per tensor;
+// kLongTileWordsDecode), encode with half of it.
 constexpr uint32_t kLongTileWordsEncode = 1024;
 constexpr uint32_t kMaxPeriodBits = 1u << 20;
 constexpr uint64_t kLineWords = 64;     // 256-byte first-read granule
@@ -581,6 +581,11 @@ static ibp_status decode_common(ibp_meta_t h, const void* slots, uint64_t n_slot
     if (!h) return IBP_ERR_INVALID_ARG;
     if (n_out == 0) return IBP_OK;
     const uint64_t L = h->params.tensor_bytes;
+    // the static scratch holds one status word per group, and a group spans
+    // at least one 2,048-word tile's worth of words on either path
+    static_assert(kDecodeTilesPerGroupHbm * kLongTileWordsDecodeHbm >= kLongTileWordsDecode &&
+                      kDecodeTilesPerGroup >= 1,
+                  "groups per tensor must not exceed its 2,048-word tiles");
     if (static_scratch && L / 4 > kMaxTileWords) {
         const uint64_t tpt = (L / 4 + kLongTileWordsDecode - 1) / kLongTileWordsDecode;
         if (n_out > IBP_NOALLOC_MAX_TILES / tpt) return IBP_ERR_TOO_LARGE;
@@ -593,7 +598,7 @@ static ibp_status decode_common(ibp_meta_t h, const void* slots, uint64_t n_slot
     if (!device_only(bitmask, h->device) || !device_only(dst, h->device)) return IBP_ERR_INVALID_ARG;
     if (ids && !device_only(ids, h->device)) return IBP_ERR_INVALID_ARG;
     if (overlaps(slots, n_slots * L, dst, n_out * L)) return IBP_ERR_INVALID_ARG;
-    Geo geo = make_geo(h, aligned16(L, {slots, dst}), kLongTileWordsDecode);
+    Geo geo = make_geo(h, aligned16(L, {slots, dst}), decode_tile_words(slots_kind == Kind::Device));
     geo.src_in_hbm = slots_kind == Kind::Device;
     LookBack lb{};
     std::unique_lock<std::mutex> lock;

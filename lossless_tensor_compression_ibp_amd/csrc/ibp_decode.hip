@@ -161,10 +161,10 @@ __device__ __forceinline__ uint32_t decode_tile(const Tab& tab, const Geo& geo, 
 
 // LDS image of the tables: b, kd, dx rows, r rows (stride Mw), then the
 // header bit planes.  Copied once per workgroup.
-// A whole tile of kMaxTileWords words (every step full, output 16-byte
-// aligned, w0 a multiple of 4): decode_tile with a compile-time step count,
-// so the steps unroll into one block with one store each.
-template <int RUNS, class Tab>
+// A whole tile of TW words (every step full, output 16-byte aligned, w0 a
+// multiple of 4): decode_tile with a compile-time step count, so the steps
+// unroll into one block with one store each.
+template <int RUNS, uint32_t TW, class Tab>
 __device__ __forceinline__ void decode_full_tile(const Tab& tab, const Geo& geo, const uint32_t* hdr,
                                                  const uint32_t* pay, uint32_t bit0, uint64_t w0,
                                                  uint32_t* __restrict__ out) {
@@ -175,9 +175,9 @@ __device__ __forceinline__ void decode_full_tile(const Tab& tab, const Geo& geo,
     uint32_t pos0 = UNI ? 0u : (uint32_t)((w0 + 4ull * lane) % Mw);
     uint32_t carry = bit0;
 #pragma unroll
-    for (uint32_t s = 0; s < kMaxTileWords / (4 * kWave); ++s) {
-        decode_step<RUNS, false, true>(tab, geo, hdr, pay, s * (4 * kWave) + 4 * lane, pos0, kMaxTileWords, &carry,
-                                       out + w0, true);
+    for (uint32_t s = 0; s < TW / (4 * kWave); ++s) {
+        decode_step<RUNS, false, true>(tab, geo, hdr, pay, s * (4 * kWave) + 4 * lane, pos0, TW, &carry, out + w0,
+                                       true);
         if (!UNI) {
             pos0 += step_inc;
             if (pos0 >= Mw) pos0 -= Mw;
@@ -469,7 +469,7 @@ __global__ __launch_bounds__(256) void k_decode_small(Tables t, Geo geo, const u
 // ---------------------------------------------------------------------------
 constexpr uint32_t kGroupsPerWave = 4;
 
-template <uint32_t TPG>
+template <uint32_t TPG, uint32_t TW>
 __global__ __launch_bounds__(kWave * kWavesPerBlock) void k_group_bits(Tables t, Geo geo,
                                                                        const uint8_t* __restrict__ slots,
                                                                        uint64_t n_slots,
@@ -490,11 +490,12 @@ __global__ __launch_bounds__(kWave * kWavesPerBlock) void k_group_bits(Tables t,
     const uint32_t lane = lane_id();
     const uint64_t gpt = decode_groups(geo.tiles_per_tensor, TPG);
     const uint64_t first = ((uint64_t)blockIdx.x * kWavesPerBlock + uniform(threadIdx.x / kWave)) * kGroupsPerWave;
-    // A group has at most TPG * 64 header words: TPG per lane, read for all
-    // kGroupsPerWave groups before any is summed.  Word u of a lane is header
-    // word j(u) of its group (16-byte vectors when the slots are aligned and
-    // a lane's words make whole vectors).
-    constexpr uint32_t kU = TPG * 64 / kWave;
+    // A group has at most TPG * TW / 32 header words (one chunk per word at
+    // most): kU per lane, read for all kGroupsPerWave groups before any is
+    // summed.  Word u of a lane is header word j(u) of its group (16-byte
+    // vectors when the slots are aligned and a lane's words make whole
+    // vectors).
+    constexpr uint32_t kU = (TPG * TW / 32 + kWave - 1) / kWave;
     static_assert(kU >= 1, "a group has at least one tile of 64 header words at most");
     const bool vec = (kU % 4 == 0) && geo.aligned16 != 0;  // whole vectors per lane
     auto j_of = [&](uint32_t u) __attribute__((always_inline)) {
@@ -629,7 +630,7 @@ __global__ __launch_bounds__(256) void k_group_scan(uint64_t gpt, uint64_t base,
 // reads and rebuilds its tiles one after another (each tile's start bit is
 // the group's plus the earlier tiles' bits, from their header words).
 // ---------------------------------------------------------------------------
-template <int RUNS, bool UNI, uint32_t TPG>
+template <int RUNS, bool UNI, uint32_t TPG, uint32_t TW>
 __global__ __launch_bounds__(kWave * kGroupWaves) void k_decode_groups(Tables t, Geo geo, const uint8_t* __restrict__ slots,
                                                        uint64_t n_slots, const uint32_t* __restrict__ bitmask,
                                                        const int64_t* __restrict__ ids, uint64_t n_out,
@@ -680,7 +681,7 @@ __global__ __launch_bounds__(kWave * kGroupWaves) void k_decode_groups(Tables t,
     const uint64_t hw0 = (w0 >> geo.log2g) >> 5;
     const uint32_t hw_g = (uint32_t)((((wend - w0) >> geo.log2g) + 31) / 32);
     uint32_t* hdr = lds;
-    uint32_t* pay = lds + TPG * 64;
+    uint32_t* pay = lds + TPG * (TW / 32);
     for (uint32_t j = lane; j < hw_g; j += kWave) hdr[j] = src[hw0 + j];
     __builtin_amdgcn_wave_barrier();
     uint32_t agg[TPG];
@@ -727,7 +728,7 @@ __global__ __launch_bounds__(kWave * kGroupWaves) void k_decode_groups(Tables t,
     // this prefetch measured slower (1,252 -> 1,267 us per layer alone), so
     // there each tile is read when due.
     const bool pipelined = vec && geo.src_in_hbm;
-    constexpr uint32_t kPre = (kMaxTileWords + 8 + 4 * kWave - 1) / (4 * kWave);
+    constexpr uint32_t kPre = (TW + 8 + 4 * kWave - 1) / (4 * kWave);
     u32x4 pre[kPre];
     // kPre buffer loads per lane whose range is payload words [a, b): vectors
     // past it return zero without touching memory, so every tile issues the
@@ -762,8 +763,8 @@ __global__ __launch_bounds__(kWave * kGroupWaves) void k_decode_groups(Tables t,
                                            vec && (wt & 3) == 0);
     };
     const uint32_t n_full = (uint32_t)((wend - w0) / tw);
-    if (pipelined && n_full > 0 && tw == kMaxTileWords) {
-        // Each iteration rebuilds full tile r (kMaxTileWords / 256 unrolled
+    if (pipelined && n_full > 0 && tw == TW) {
+        // Each iteration rebuilds full tile r (TW / 256 unrolled
         // steps, one store each), then writes tile r + 1's prefetched vectors
         // to LDS and issues tile r + 2's loads.  The loop is entered with
         // tile 0 staged and tile 1's loads in flight, the same pattern its
@@ -782,10 +783,10 @@ __global__ __launch_bounds__(kWave * kGroupWaves) void k_decode_groups(Tables t,
         for (uint32_t r = 0; r < n_full; ++r) {
             __builtin_amdgcn_wave_barrier();  // the staged words are written
             if (UNI)
-                decode_full_tile<RUNS>(tu, geo, hdr + r * hw_tile, pay, (uint32_t)(St - 32 * a), w0 + (uint64_t)r * tw,
+                decode_full_tile<RUNS, TW>(tu, geo, hdr + r * hw_tile, pay, (uint32_t)(St - 32 * a), w0 + (uint64_t)r * tw,
                                        out);
             else
-                decode_full_tile<RUNS>(ta, geo, hdr + r * hw_tile, pay, (uint32_t)(St - 32 * a), w0 + (uint64_t)r * tw,
+                decode_full_tile<RUNS, TW>(ta, geo, hdr + r * hw_tile, pay, (uint32_t)(St - 32 * a), w0 + (uint64_t)r * tw,
                                        out);
             St += agg[r];
             if (r + 1 < n_tiles) {
@@ -981,13 +982,14 @@ static hipError_t launch_tiles(const Tables& t, const Geo& geo, const void* slot
 // status word per group (n_out * decode_groups(tiles_per_tensor, TPG)), which the
 // look-back uses over the host link and the start bits of the header pass
 // and scan use for records in HBM.
-template <int RUNS, bool UNI, uint32_t TPG>
+template <int RUNS, bool UNI, uint32_t TPG, uint32_t TW>
 static hipError_t launch_groups_t(const Tables& t, const Geo& geo, const void* slots, uint64_t n_slots,
                                   const uint32_t* bitmask, const int64_t* ids, uint64_t n_out, void* dst,
                                   uint32_t* err, const LookBack& lb, hipStream_t s) {
+    if (geo.tile_words != TW) return hipErrorInvalidValue;
     // header words of a group, then one tile's payload (up to 8 words of
     // 16-byte rounding and the zero word after it)
-    const uint32_t lds_words = TPG * 64 + geo.tile_words + 8;
+    const uint32_t lds_words = TPG * (TW / 32) + TW + 8;
     const uint64_t gpt = decode_groups(geo.tiles_per_tensor, TPG);
     const uint64_t groups = n_out * gpt;
     uint64_t* starts = nullptr;
@@ -996,7 +998,7 @@ static hipError_t launch_groups_t(const Tables& t, const Geo& geo, const void* s
         // words, into the look-back status words
         starts = reinterpret_cast<uint64_t*>(lb.status);
         const uint64_t waves = (groups + kGroupsPerWave - 1) / kGroupsPerWave;
-        hipLaunchKernelGGL(k_group_bits<TPG>, dim3((uint32_t)((waves + kWavesPerBlock - 1) / kWavesPerBlock)),
+        hipLaunchKernelGGL((k_group_bits<TPG, TW>), dim3((uint32_t)((waves + kWavesPerBlock - 1) / kWavesPerBlock)),
                            dim3(kWave * kWavesPerBlock), 0, s, t, geo, static_cast<const uint8_t*>(slots), n_slots,
                            bitmask, ids, n_out, starts);
         hipError_t e = hipGetLastError();
@@ -1008,23 +1010,23 @@ static hipError_t launch_groups_t(const Tables& t, const Geo& geo, const void* s
     const dim3 grid((uint32_t)((groups + kGroupWaves - 1) / kGroupWaves));
     const dim3 block(kWave * kGroupWaves);
     const size_t shm = (size_t)lds_words * 4 * kGroupWaves;
-    hipLaunchKernelGGL((k_decode_groups<RUNS, UNI, TPG>), grid, block, shm, s, t, geo,
+    hipLaunchKernelGGL((k_decode_groups<RUNS, UNI, TPG, TW>), grid, block, shm, s, t, geo,
                        static_cast<const uint8_t*>(slots), n_slots, bitmask, ids, n_out, static_cast<uint8_t*>(dst),
                        err, lb, starts, lds_words);
     return hipGetLastError();
 }
 
-// Tensors longer than one tile, with the group size of where their records
-// are (decode_group_tiles).
+// Tensors longer than one tile, with the group and tile sizes of where their
+// records are (decode_group_tiles, decode_tile_words).
 template <int RUNS, bool UNI>
 static hipError_t launch_groups(const Tables& t, const Geo& geo, const void* slots, uint64_t n_slots,
                                 const uint32_t* bitmask, const int64_t* ids, uint64_t n_out, void* dst,
                                 uint32_t* err, const LookBack& lb, hipStream_t s) {
     if (geo.src_in_hbm)
-        return launch_groups_t<RUNS, UNI, decode_group_tiles(true)>(t, geo, slots, n_slots, bitmask, ids, n_out, dst,
-                                                                     err, lb, s);
-    return launch_groups_t<RUNS, UNI, decode_group_tiles(false)>(t, geo, slots, n_slots, bitmask, ids, n_out, dst,
-                                                                  err, lb, s);
+        return launch_groups_t<RUNS, UNI, decode_group_tiles(true), decode_tile_words(true)>(
+            t, geo, slots, n_slots, bitmask, ids, n_out, dst, err, lb, s);
+    return launch_groups_t<RUNS, UNI, decode_group_tiles(false), decode_tile_words(false)>(
+        t, geo, slots, n_slots, bitmask, ids, n_out, dst, err, lb, s);
 }
 
 template <int RUNS, bool UNI>

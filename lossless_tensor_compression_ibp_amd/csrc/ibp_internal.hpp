@@ -102,6 +102,22 @@ __host__ __device__ constexpr uint64_t decode_groups(uint64_t tiles_per_tensor, 
 __host__ __device__ constexpr uint32_t decode_group_tiles(bool src_in_hbm) {
     return src_in_hbm ? kDecodeTilesPerGroupHbm : kDecodeTilesPerGroup;
 }
+// Words per tile of a tensor longer than kMaxTileWords, for a decode whose
+// records are read over the host link, and for one whose records are in
+// device memory.  The record format does not depend on the tile size.  From
+// HBM, 1,024-word tiles (fewer prefetch registers, half the LDS per wave)
+// decoded the 32 llm_bf16 layers in 937-940 us in groups of 4 or 8 and
+// 1,002 us in groups of 16, against 895 us with 2,048-word tiles in groups
+// of 4 (916 us in groups of 2).
+#ifndef IBP_DECODE_TILE_WORDS_HBM
+#define IBP_DECODE_TILE_WORDS_HBM 2048
+#endif
+constexpr uint32_t kLongTileWordsDecode = 2048;
+constexpr uint32_t kLongTileWordsDecodeHbm = IBP_DECODE_TILE_WORDS_HBM;
+static_assert(kLongTileWordsDecodeHbm % 256 == 0 && kLongTileWordsDecodeHbm <= kMaxTileWords, "tile words");
+__host__ __device__ constexpr uint32_t decode_tile_words(bool src_in_hbm) {
+    return src_in_hbm ? kLongTileWordsDecodeHbm : kLongTileWordsDecode;
+}
 
 enum DeviceError : uint32_t { kErrNone = 0, kErrCorrupt = 5, kErrRange = 6, kErrStall = 7 };
 
