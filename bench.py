@@ -711,9 +711,10 @@ def run_dlrm(args) -> dict:
 # prefetch: decode of layer i+1 (stream A) overlaps a consumer of layer i
 # (stream B, y = x @ W on the decoded layer)
 # ---------------------------------------------------------------------------
-LLM_KERNEL = "ibp::k_decode_groups<3, true> (look-back over groups of 8 tiles of 8 KiB)"
-LLM_HBM_KERNELS = ("ibp::k_group_bits + ibp::k_group_scan + ibp::k_decode_groups<3, true> (group start bits from a "
-                   "pass over the header words, then groups of 8 tiles of 8 KiB; kernel_avg_us spans all three)")
+LLM_KERNEL = "ibp::k_decode_groups<3, true, 8u, 2048u> (look-back over groups of 8 tiles of 8 KiB)"
+LLM_HBM_KERNELS = ("ibp::k_group_bits<4u, 2048u> + ibp::k_group_scan + ibp::k_decode_groups<3, true, 4u, 2048u> "
+                   "(group start bits from a pass over the header words, then groups of 4 tiles of 8 KiB; "
+                   "kernel_avg_us spans all three)")
 
 
 def run_llm_bf16(args) -> dict:
