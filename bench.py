@@ -48,9 +48,19 @@ LINE = 128              # bytes a zero-copy read of pinned host memory moves at 
 METRIC = "IBP decode GB/s (uncompressed out, 1 MI355X) + % of roofline + space savings %"
 
 
+def _code_only(text: str) -> str:
+    """C/C++ source without its comments and with runs of white space
+    collapsed (string literals are kept as they are)."""
+    import re
+
+    token = re.compile(r'"(?:\\.|[^"\\])*"|//[^\n]*|/\*.*?\*/', re.S)
+    text = token.sub(lambda m: m.group(0) if m.group(0).startswith('"') else " ", text)
+    return " ".join(text.split())
+
+
 def kernel_source_hash() -> str:
-    """Hash of the kernel sources; counter readings in profiles/traffic.json
-    apply only while it matches."""
+    """Hash of the kernel sources' code (comments and layout ignored); counter
+    readings in profiles/traffic.json apply only while it matches."""
     import glob
     import hashlib
 
@@ -60,8 +70,8 @@ def kernel_source_hash() -> str:
     h = hashlib.sha256()
     for f in sorted(files, key=os.path.basename):
         h.update(os.path.basename(f).encode())
-        with open(f, "rb") as fh:
-            h.update(fh.read())
+        with open(f, encoding="utf-8") as fh:
+            h.update(_code_only(fh.read()).encode())
     return h.hexdigest()[:16]
 
 
