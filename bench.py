@@ -808,13 +808,28 @@ def run_llm_bf16(args) -> dict:
         if not np.array_equal(dout[layers - 1].cpu().numpy(), hv[layers - 1]):
             raise SystemExit("decoded layer (HBM-resident slots) differs")
         hbm_bytes = float(stored_np.sum() + layers * L + 4 * ((layers + 31) // 32))
+        # the same layers encoded with source and slots in HBM; records equal
+        # to those written to the pinned slots
+        log("[bench] llm_bf16: the same layers encoded HBM -> HBM")
+        dsrc = host.to(dev)
+        eslots = torch.empty((layers, L), dtype=torch.uint8, device=dev)
+        ebm, estored = torch.zeros_like(bitmask), torch.zeros_like(stored)
+        t_enc_hbm = encode_seconds(lambda: ibp.ibp_compress(meta, dsrc, layers, eslots, ebm, estored))
+        if not (torch.equal(ebm, bitmask) and torch.equal(estored, stored)) or not all(
+                torch.equal(eslots[l, :int(stored_np[l])], dslots[l, :int(stored_np[l])]) for l in range(layers)):
+            raise SystemExit("HBM -> HBM encode differs from the pinned-slot records")
+        del dsrc, eslots
         hbm_resident = {
             "what": f"the same {layers} compressed layers held in HBM slots, all of them decoded by one "
                     f"ibp_decompress per step into HBM (inputs resident in HBM, no host link)",
             "decoded_GBps": round(args.steps * layers * L / hbm_wall / GB, 3),
             "ms_per_step": round(hbm_wall / args.steps * 1e3, 4), "kernel": LLM_HBM_KERNELS,
             "kernel_avg_us": round(float(np.mean(hbm_durs)) * 1e6, 2),
-            "roofline": hbm_roofline(hbm_bytes, hbm_durs, "llm_bf16_hbm")}
+            "roofline": hbm_roofline(hbm_bytes, hbm_durs, "llm_bf16_hbm"),
+            "encode": encode_hbm(layers * L, layers * L + float(stored_np.sum()), t_enc_hbm,
+                                 "HBM -> HBM, source and slots in device memory: a first pass sums each group of "
+                                 "4 tiles' payload bits, a scan gives the start bits, then one wave encodes a "
+                                 "group")}
         del dslots, dout
     h2d = h2d_ceiling()
     res = base_result(

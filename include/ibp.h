@@ -41,10 +41,12 @@
  * when several host threads issue them.
  *
  * Tensors longer than one tile (more than 8 KiB) are cut into tiles whose
- * start bits need per-stream scratch of the handle: the encode, and a decode
- * of records read over the host link, find them by a decoupled look-back; a
- * decode of records in device memory computes them first from the header
- * words (a pass over them and a scan per tensor).  ibp_compress,
+ * start bits need per-stream scratch of the handle: an encode of a source in
+ * pinned host memory, and a decode of records read over the host link, find
+ * them by a decoupled look-back; an encode of a 16-byte aligned source in
+ * device memory computes them first from the source (a pass over it and a
+ * scan per tensor), and a decode of records in device memory from the header
+ * words (likewise).  ibp_compress,
  * ibp_decompress and ibp_gather_decompress of such tensors, and
  * ibp_packed_offsets, return IBP_ERR_UNSUPPORTED while `stream` is capturing
  * a HIP graph; single-tile calls may be captured.

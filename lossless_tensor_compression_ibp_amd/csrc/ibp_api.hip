@@ -20,10 +20,6 @@ using namespace ibp;
 
 namespace {
 
-// Tile of a tensor longer than kMaxTileWords.  Decode over the host link
-// measured fastest with the largest tile (fewer look-back hops per tensor;
-// kLongTileWordsDecode), encode with half of it.
-constexpr uint32_t kLongTileWordsEncode = 1024;
 constexpr uint32_t kMaxPeriodBits = 1u << 20;
 constexpr uint64_t kLineWords = 64;     // 256-byte first-read granule
 constexpr uint64_t kMemLineWords = 32;  // 128-byte line that memory reads move
@@ -505,11 +501,12 @@ ibp_status ibp_compress(ibp_meta_t h, const void* src, uint64_t n_tensors, void*
     if (!device_only(bitmask, h->device)) return IBP_ERR_INVALID_ARG;
     if (stored_bytes && !device_only(stored_bytes, h->device)) return IBP_ERR_INVALID_ARG;
     if (overlaps(src, n_tensors * L, dst_slots, n_tensors * L)) return IBP_ERR_INVALID_ARG;
-    const Geo geo = make_geo(h, aligned16(L, {src, dst_slots}), kLongTileWordsEncode);
+    Geo geo = make_geo(h, aligned16(L, {src, dst_slots}), kLongTileWordsEncode);
+    geo.src_in_hbm = pointer_kind(src, h->device) == Kind::Device;
     LookBack lb{};
     std::unique_lock<std::mutex> lock;
     if (geo.tiles_per_tensor > 1) {
-        ibp_status st = lookback_for(h, stream, n_tensors * geo.tiles_per_tensor, n_tensors, &lb, &lock);
+        ibp_status st = lookback_for(h, stream, encode_status_words(geo, n_tensors), n_tensors, &lb, &lock);
         if (st != IBP_OK) return st;
     }
     return from_hip(launch_encode(h->tabs, geo, h->sum.max_runs, h->sum.uniform != 0, src, n_tensors, dst_slots,
@@ -605,7 +602,7 @@ static ibp_status decode_common(ibp_meta_t h, const void* slots, uint64_t n_slot
     if (geo.tiles_per_tensor > 1) {
         // one status word per group of tiles (look-back entries, or the
         // group start bits when the records are in HBM)
-        const uint64_t groups = n_out * decode_groups(geo.tiles_per_tensor, decode_group_tiles(geo.src_in_hbm));
+        const uint64_t groups = n_out * tile_groups(geo.tiles_per_tensor, decode_group_tiles(geo.src_in_hbm));
         ibp_status st = static_scratch ? noalloc_lookback(h, stream, groups, &lb)
                                        : lookback_for(h, stream, groups, 0, &lb, &lock);
         if (st != IBP_OK) return st;

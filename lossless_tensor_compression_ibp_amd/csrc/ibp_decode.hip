@@ -488,7 +488,7 @@ __global__ __launch_bounds__(kWave * kWavesPerBlock) void k_group_bits(Tables t,
         __syncthreads();
     }
     const uint32_t lane = lane_id();
-    const uint64_t gpt = decode_groups(geo.tiles_per_tensor, TPG);
+    const uint64_t gpt = tile_groups(geo.tiles_per_tensor, TPG);
     const uint64_t first = ((uint64_t)blockIdx.x * kWavesPerBlock + uniform(threadIdx.x / kWave)) * kGroupsPerWave;
     // A group has at most TPG * TW / 32 header words (one chunk per word at
     // most): kU per lane, read for all kGroupsPerWave groups before any is
@@ -616,6 +616,18 @@ __global__ __launch_bounds__(256) void k_group_scan(uint64_t gpt, uint64_t base,
     }
 }
 
+hipError_t launch_group_scan(uint64_t n_tensors, uint64_t gpt, uint64_t base, uint64_t* bits, hipStream_t s) {
+    // one workgroup per tensor, at most 2^20 workgroups per launch
+    constexpr uint64_t kMaxBlocks = 1ull << 20;
+    for (uint64_t t0 = 0; t0 < n_tensors; t0 += kMaxBlocks) {
+        const uint64_t nb = min(n_tensors - t0, kMaxBlocks);
+        hipLaunchKernelGGL(k_group_scan, dim3((uint32_t)nb), dim3(256), 0, s, gpt, base, bits + t0 * gpt);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
+}
+
 // ---------------------------------------------------------------------------
 // Tensors longer than one tile.  A wave takes a group of up to
 // TPG consecutive tiles of one tensor and reads the header
@@ -647,7 +659,7 @@ __global__ __launch_bounds__(kWave * kGroupWaves) void k_decode_groups(Tables t,
     }
     const uint64_t group = (uint64_t)(starts ? blockIdx.x : uniform(block_ticket)) * kGroupWaves + wib;
     const uint64_t tpt = geo.tiles_per_tensor;
-    const uint64_t gpt = decode_groups(tpt, TPG);
+    const uint64_t gpt = tile_groups(tpt, TPG);
     if (group >= n_out * gpt) return;
     const uint64_t oi = group / gpt;
     const uint64_t lg = group - oi * gpt;
@@ -979,7 +991,7 @@ static hipError_t launch_tiles(const Tables& t, const Geo& geo, const void* slot
 }
 
 // Tensors longer than one tile: one wave per group of tiles; lb holds one
-// status word per group (n_out * decode_groups(tiles_per_tensor, TPG)), which the
+// status word per group (n_out * tile_groups(tiles_per_tensor, TPG)), which the
 // look-back uses over the host link and the start bits of the header pass
 // and scan use for records in HBM.
 template <int RUNS, bool UNI, uint32_t TPG, uint32_t TW>
@@ -990,7 +1002,7 @@ static hipError_t launch_groups_t(const Tables& t, const Geo& geo, const void* s
     // header words of a group, then one tile's payload (up to 8 words of
     // 16-byte rounding and the zero word after it)
     const uint32_t lds_words = TPG * (TW / 32) + TW + 8;
-    const uint64_t gpt = decode_groups(geo.tiles_per_tensor, TPG);
+    const uint64_t gpt = tile_groups(geo.tiles_per_tensor, TPG);
     const uint64_t groups = n_out * gpt;
     uint64_t* starts = nullptr;
     if (geo.src_in_hbm) {
@@ -1003,8 +1015,7 @@ static hipError_t launch_groups_t(const Tables& t, const Geo& geo, const void* s
                            bitmask, ids, n_out, starts);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
-        hipLaunchKernelGGL(k_group_scan, dim3((uint32_t)n_out), dim3(256), 0, s, gpt, 32ull * geo.hdr_words, starts);
-        e = hipGetLastError();
+        e = launch_group_scan(n_out, gpt, 32ull * geo.hdr_words, starts, s);
         if (e != hipSuccess) return e;
     }
     const dim3 grid((uint32_t)((groups + kGroupWaves - 1) / kGroupWaves));

@@ -4,9 +4,23 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "ibp_internal.hpp"
 
 namespace ibp {
+
+// f(std::integral_constant<int, I>{}) for I = 0 .. N-1, each index a
+// compile-time constant from the start, so a register array indexed by it is
+// never turned into one vector that every partial update copies (which a
+// loop that is unrolled only later can lead to).
+template <int N, int I = 0, class F>
+__device__ __forceinline__ void static_for(F&& f) {
+    if constexpr (I < N) {
+        f(std::integral_constant<int, I>{});
+        static_for<N, I + 1>(static_cast<F&&>(f));
+    }
+}
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 

@@ -209,6 +209,150 @@ __global__ __launch_bounds__(256) void k_encode(Tables t, Geo geo, const uint8_t
     if (last && lane == 0) lb.totals[ti] = E;
 }
 
+// Tables one encode step reads: the Mask row and the per-position arrays (in
+// LDS or global memory), or for uniform metadata the position-0 entries in
+// registers.
+template <int RUNS, bool UNI>
+struct EncTabs {
+    const uint32_t* mrow;
+    TabArrays ta;
+    TabUniform<RUNS> tu;
+    uint32_t mu;
+};
+
+template <int RUNS, bool UNI>
+__device__ __forceinline__ EncTabs<RUNS, UNI> enc_tabs_global(const Tables& t, uint32_t Mw) {
+    EncTabs<RUNS, UNI> e{};
+    e.mrow = t.m;
+    e.ta = TabArrays{t.b, t.kd, t.dx, t.r, Mw};
+    if constexpr (UNI) {
+        e.tu = load_uniform<RUNS>(t, Mw);
+        e.mu = uniform(t.m[0]);
+    }
+    return e;
+}
+
+// One lane's share of an encode step: the match test, participation and
+// removal of its four consecutive words x, at positions pos0.. of the period
+// (all four live or none).  With HDR the lane's participation bits are OR-ed
+// into hdr from chunk c0, its first word's; each word's field goes to f and
+// its width to size; returns the widths' sum.  Every lane of the wave calls it
+// (chunks of more than 4 words take a ballot).
+template <int RUNS, bool UNI, bool MW4, bool HDR>
+__device__ __forceinline__ uint32_t encode_lane4(const EncTabs<RUNS, UNI>& et, uint32_t Mw, uint32_t lg, bool live,
+                                                 uint32_t pos0, const uint32_t (&x)[4], uint32_t* hdr, uint32_t c0,
+                                                 uint32_t (&f)[4], uint32_t (&size)[4]) {
+    const uint32_t lane = lane_id();
+    const uint32_t g = 1u << lg;
+    const uint32_t* mrow = et.mrow;
+    const TabArrays& ta = et.ta;
+    const TabUniform<RUNS>& tu = et.tu;
+    const uint32_t mu = et.mu;
+    uint32_t m[4], bv[4], kd[4], pos[4];
+    if constexpr (UNI) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            pos[j] = 0;
+            m[j] = mu;
+            bv[j] = tu.bw(0);
+            kd[j] = tu.kdw(0);
+        }
+    } else if constexpr (MW4) {
+        const u32x4 m4 = *reinterpret_cast<const u32x4*>(mrow + pos0);
+        const u32x4 b4 = ta.bw4(pos0), k4 = ta.kdw4(pos0);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            pos[j] = pos0 + j;
+            m[j] = m4[j];
+            bv[j] = b4[j];
+            kd[j] = k4[j];
+        }
+    } else {
+        pos[0] = pos0;
+#pragma unroll
+        for (int j = 1; j < 4; ++j) pos[j] = (pos[j - 1] + 1 == Mw) ? 0u : pos[j - 1] + 1;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            m[j] = mrow[pos[j]];
+            bv[j] = ta.bw(pos[j]);
+            kd[j] = ta.kdw(pos[j]);
+        }
+    }
+    bool mis[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) mis[j] = live && ((x[j] ^ bv[j]) & m[j]) != 0;
+    // participation: a chunk matches when none of its words mismatches
+    bool p[4];
+    uint32_t hbits;  // the lane's header bits from chunk c0 on
+    if (g == 1) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) p[j] = !mis[j];
+        hbits = (uint32_t)p[0] | ((uint32_t)p[1] << 1) | ((uint32_t)p[2] << 2) | ((uint32_t)p[3] << 3);
+    } else if (g == 2) {
+        const bool pa = !(mis[0] || mis[1]), pb = !(mis[2] || mis[3]);
+        p[0] = p[1] = pa;
+        p[2] = p[3] = pb;
+        hbits = (uint32_t)pa | ((uint32_t)pb << 1);
+    } else {
+        const uint32_t q = g >> 2;  // lanes per chunk
+        const uint64_t bal = ballot(mis[0] || mis[1] || mis[2] || mis[3]);
+        const uint32_t gs = lane & ~(q - 1u);
+        const uint64_t qmask = (q >= 64) ? ~0ull : ((1ull << q) - 1ull);
+        const bool pc = ((bal >> gs) & qmask) == 0;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) p[j] = pc;
+        hbits = (lane & (q - 1u)) == 0 ? (uint32_t)pc : 0u;
+    }
+    if (HDR && live && hbits) atomicOr(&hdr[c0 >> 5], hbits << (c0 & 31u));
+    // run masks of the lane's four positions: one 16-byte read per run
+    uint32_t rr[RUNS > 0 ? RUNS : 1][4];
+    if constexpr (MW4 && !UNI) {
+#pragma unroll
+        for (int r = 0; r < RUNS; ++r) {
+            const u32x4 v = ta.rw4(r, pos0);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) rr[r][j] = v[j];
+        }
+    }
+    uint32_t tot = 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        uint32_t e;
+        if constexpr (UNI) {
+            e = extract_t<RUNS>(tu, 0, kd[j], x[j]);
+        } else if constexpr (MW4) {
+            e = 0;
+#pragma unroll
+            for (int r = 0; r < RUNS; ++r) e |= (x[j] & rr[r][j]) >> (ta.dw(r, pos[j], kd[j]) & 31u);
+        } else {
+            e = extract_t<RUNS>(ta, pos[j], kd[j], x[j]);
+        }
+        f[j] = p[j] ? e : x[j];
+        size[j] = live ? (p[j] ? 32u - (kd[j] & 63u) : 32u) : 0u;
+        tot += size[j];
+    }
+    return tot;
+}
+
+// Places one step's fields after the record's first `carry` payload bits (a
+// wave scan of the lanes' widths gives each lane its offset) and advances
+// carry by the step's total.
+__device__ __forceinline__ void or_fields(uint32_t* pay, uint32_t& carry, const uint32_t (&f)[4],
+                                          const uint32_t (&size)[4], uint32_t tot) {
+    const uint32_t incl = wave_incl_scan(tot);
+    uint32_t off = carry + incl - tot;
+    carry += lane_value(incl, kWave - 1);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        if (size[j]) {
+            const uint32_t q = off >> 5, sh = off & 31u;
+            atomicOr(&pay[q], f[j] << sh);
+            if (sh + size[j] > 32) atomicOr(&pay[q + 1], f[j] >> (32 - sh));
+        }
+        off += size[j];
+    }
+}
+
 // ---------------------------------------------------------------------------
 // Tensors of at most kMaxTileWords words with 16-byte aligned source and
 // slots: persistent workgroups, tables staged once in LDS, four words per lane
@@ -241,20 +385,18 @@ __global__ __launch_bounds__(1024) void k_encode_small(Tables t, Geo geo, const 
     stage_table_image<dx_rows(RUNS)>(t, 0, rows, Mw, nullptr, 0, smem);
     __syncthreads();
     uint32_t* buf = smem + ((rows * Mw + 3u) & ~3u) + wib * buf_words;
-    const uint32_t* mrow = smem;
-    const TabArrays ta{smem + Mw, smem + 2 * Mw, smem + 3 * Mw, smem + (3 + dx_rows(RUNS)) * Mw, Mw};
-    TabUniform<RUNS> tu;
-    uint32_t mu = 0;
-    if (UNI) {
-        tu = load_uniform<RUNS>(t, Mw);
-        mu = uniform(t.m[0]);
+    EncTabs<RUNS, UNI> et{};
+    et.mrow = smem;
+    et.ta = TabArrays{smem + Mw, smem + 2 * Mw, smem + 3 * Mw, smem + (3 + dx_rows(RUNS)) * Mw, Mw};
+    if constexpr (UNI) {
+        et.tu = load_uniform<RUNS>(t, Mw);
+        et.mu = uniform(t.m[0]);
     }
 
     const uint32_t nw = (uint32_t)geo.n_words;
     const uint32_t n4 = nw >> 2;
     const uint32_t hw = (uint32_t)geo.hdr_words;
     const uint32_t lg = geo.log2g;
-    const uint32_t g = 1u << lg;
     const uint32_t step_inc = (uint32_t)(4 * kWave) % Mw;
     const uint32_t wpb = blockDim.x / kWave;
     const uint64_t stride = (uint64_t)gridDim.x * wpb;
@@ -267,11 +409,11 @@ __global__ __launch_bounds__(1024) void k_encode_small(Tables t, Geo geo, const 
     u32x4 cur[STAGE];
     {
         const u32x4* s4 = reinterpret_cast<const u32x4*>(src + ti * geo.L);
-#pragma unroll
-        for (int r = 0; r < STAGE; ++r) {
+        static_for<STAGE>([&](auto rc) {
+            constexpr int r = decltype(rc)::value;
             const uint32_t i = lane + (uint32_t)r * kWave;
             if (i < n4) cur[r] = __builtin_nontemporal_load(s4 + i);
-        }
+        });
     }
     for (; ti < n_tensors; ti += stride) {
         const uint64_t tnext = ti + stride;
@@ -291,121 +433,26 @@ __global__ __launch_bounds__(1024) void k_encode_small(Tables t, Geo geo, const 
         uint32_t* pay = buf + (headers ? 4u : hw);
         uint32_t carry = 0;
         uint32_t pos0 = UNI ? 0u : (4u * lane) % Mw;
-#pragma unroll
-        for (int s = 0; s < STAGE; ++s) {
+        static_for<STAGE>([&](auto sc) {
+            constexpr int s = decltype(sc)::value;
             const uint32_t lw0 = (uint32_t)s * (4 * kWave) + 4 * lane;
-            if ((uint32_t)s * (4 * kWave) >= nw) break;  // wave-uniform
+            if ((uint32_t)s * (4 * kWave) >= nw) return;  // wave-uniform, and so for every later step
             const bool live = lw0 < nw;  // nw % 4 == 0: a live lane owns four words
             const u32x4 xv = cur[s];
             if (tnext < n_tensors && live) cur[s] = __builtin_nontemporal_load(nx4 + lane + (uint32_t)s * kWave);
-            uint32_t x[4], m[4], bv[4], kd[4], pos[4];
-#pragma unroll
-            for (int j = 0; j < 4; ++j) x[j] = xv[j];
-            if constexpr (UNI) {
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    pos[j] = 0;
-                    m[j] = mu;
-                    bv[j] = tu.bw(0);
-                    kd[j] = tu.kdw(0);
-                }
-            } else if constexpr (MW4) {
-                const u32x4 m4 = *reinterpret_cast<const u32x4*>(mrow + pos0);
-                const u32x4 b4 = ta.bw4(pos0), k4 = ta.kdw4(pos0);
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    pos[j] = pos0 + j;
-                    m[j] = m4[j];
-                    bv[j] = b4[j];
-                    kd[j] = k4[j];
-                }
-            } else {
-                pos[0] = pos0;
-#pragma unroll
-                for (int j = 1; j < 4; ++j) pos[j] = (pos[j - 1] + 1 == Mw) ? 0u : pos[j - 1] + 1;
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    m[j] = mrow[pos[j]];
-                    bv[j] = ta.bw(pos[j]);
-                    kd[j] = ta.kdw(pos[j]);
-                }
-            }
-            bool mis[4];
-#pragma unroll
-            for (int j = 0; j < 4; ++j) mis[j] = live && ((x[j] ^ bv[j]) & m[j]) != 0;
-            // participation: a chunk matches when none of its words mismatches
-            bool p[4];
-            uint32_t hbits;  // this lane's header bits, already at their bit position
-            const uint32_t c0 = lw0 >> lg;
-            if (g == 1) {
-#pragma unroll
-                for (int j = 0; j < 4; ++j) p[j] = !mis[j];
-                hbits = (uint32_t)p[0] | ((uint32_t)p[1] << 1) | ((uint32_t)p[2] << 2) | ((uint32_t)p[3] << 3);
-            } else if (g == 2) {
-                const bool pa = !(mis[0] || mis[1]), pb = !(mis[2] || mis[3]);
-                p[0] = p[1] = pa;
-                p[2] = p[3] = pb;
-                hbits = (uint32_t)pa | ((uint32_t)pb << 1);
-            } else {
-                const uint32_t q = g >> 2;  // lanes per chunk
-                const uint64_t bal = ballot(mis[0] || mis[1] || mis[2] || mis[3]);
-                const uint32_t gs = lane & ~(q - 1u);
-                const uint64_t qmask = (q >= 64) ? ~0ull : ((1ull << q) - 1ull);
-                const bool pc = ((bal >> gs) & qmask) == 0;
-#pragma unroll
-                for (int j = 0; j < 4; ++j) p[j] = pc;
-                hbits = (lane & (q - 1u)) == 0 ? (uint32_t)pc : 0u;
-            }
-            if (!SIZES && live && hbits) atomicOr(&buf[c0 >> 5], hbits << (c0 & 31u));
-            // run masks of the lane's four positions: one 16-byte read per run
-            uint32_t rr[RUNS > 0 ? RUNS : 1][4];
-            if constexpr (MW4 && !UNI) {
-#pragma unroll
-                for (int r = 0; r < RUNS; ++r) {
-                    const u32x4 v = ta.rw4(r, pos0);
-#pragma unroll
-                    for (int j = 0; j < 4; ++j) rr[r][j] = v[j];
-                }
-            }
+            const uint32_t x[4] = {xv[0], xv[1], xv[2], xv[3]};
             uint32_t f[4], size[4];
-            uint32_t tot = 0;
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                uint32_t e;
-                if constexpr (UNI) {
-                    e = extract_t<RUNS>(tu, 0, kd[j], x[j]);
-                } else if constexpr (MW4) {
-                    e = 0;
-#pragma unroll
-                    for (int r = 0; r < RUNS; ++r) e |= (x[j] & rr[r][j]) >> (ta.dw(r, pos[j], kd[j]) & 31u);
-                } else {
-                    e = extract_t<RUNS>(ta, pos[j], kd[j], x[j]);
-                }
-                f[j] = p[j] ? e : x[j];
-                size[j] = live ? (p[j] ? 32u - (kd[j] & 63u) : 32u) : 0u;
-                tot += size[j];
-            }
-            if constexpr (SIZES) {
+            const uint32_t tot =
+                encode_lane4<RUNS, UNI, MW4, !SIZES>(et, Mw, lg, live, pos0, x, buf, lw0 >> lg, f, size);
+            if constexpr (SIZES)
                 carry += wave_sum(tot);
-            } else {
-                const uint32_t incl = wave_incl_scan(tot);
-                uint32_t off = carry + incl - tot;
-                carry += lane_value(incl, kWave - 1);
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    if (size[j]) {
-                        const uint32_t q = off >> 5, sh = off & 31u;
-                        atomicOr(&pay[q], f[j] << sh);
-                        if (sh + size[j] > 32) atomicOr(&pay[q + 1], f[j] >> (32 - sh));
-                    }
-                    off += size[j];
-                }
-            }
+            else
+                or_fields(pay, carry, f, size, tot);
             if constexpr (!UNI) {
                 pos0 += step_inc;
                 if (pos0 >= Mw) pos0 -= Mw;
             }
-        }
+        });
         __builtin_amdgcn_wave_barrier();
         const uint64_t R = 32ull * hw + carry;
         const uint32_t words = (uint32_t)((R + 31) / 32);
@@ -475,6 +522,230 @@ __global__ __launch_bounds__(256) void k_encode_finalize(Geo geo, const uint8_t*
     for (uint64_t i = (uint64_t)bi * blockDim.x + threadIdx.x; i < geo.n_words;
          i += (uint64_t)blocks_per_tensor * blockDim.x)
         slot[i] = x[i];
+}
+
+// ---------------------------------------------------------------------------
+// Tensors longer than one tile whose source is in device memory (16-byte
+// aligned): start bits without look-back.  A look-back chain moves its
+// inclusive prefix by at most one wave's window of tiles per memory round
+// trip, which holds an HBM-resident encode far below the memory bound; a
+// second read of the source costs less.  k_enc_group_bits: one wave per group
+// of TPG tiles runs the match test over the group's words and writes the
+// group's payload bits; launch_group_scan turns them into each group's start
+// bit.  k_encode_groups: one wave per group encodes its tiles in order, four
+// words per lane per step (each step's words of the next tile are loaded as
+// the step consumes the current one), and writes each tile's header words
+// and the payload words whose last bit falls in it.  The bits of the previous
+// tile that share its first word are carried over in a register within the
+// group and rebuilt from the source at the group's first tile.
+// ---------------------------------------------------------------------------
+template <int RUNS, bool UNI, bool MW4, uint32_t TPG>
+__global__ __launch_bounds__(kWave * kWavesPerBlock) void k_enc_group_bits(Tables t, Geo geo,
+                                                                           const uint8_t* __restrict__ src,
+                                                                           uint64_t n_tensors, uint64_t* bits) {
+    constexpr uint32_t kBatch = 4;  // steps whose loads are issued together
+    const uint32_t lane = lane_id();
+    const uint64_t gpt = tile_groups(geo.tiles_per_tensor, TPG);
+    const uint64_t group = (uint64_t)blockIdx.x * kWavesPerBlock + uniform(threadIdx.x / kWave);
+    if (group >= n_tensors * gpt) return;
+    const uint64_t ti = group / gpt;
+    const uint64_t w0 = (group - ti * gpt) * TPG * kLongTileWordsEncode;
+    const uint32_t nw = (uint32_t)min((uint64_t)TPG * kLongTileWordsEncode, geo.n_words - w0);
+    const uint32_t n4 = nw >> 2;
+    const u32x4* x4 = reinterpret_cast<const u32x4*>(src + ti * geo.L) + (w0 >> 2);
+    const EncTabs<RUNS, UNI> et = enc_tabs_global<RUNS, UNI>(t, geo.Mw);
+    const uint32_t Mw = geo.Mw;
+    const uint32_t step_inc = (uint32_t)(4 * kWave) % Mw;
+    uint32_t pos0 = UNI ? 0u : (uint32_t)((w0 + 4 * lane) % Mw);
+    const uint32_t steps = (n4 + kWave - 1) / kWave;
+    uint32_t acc = 0;
+    for (uint32_t s0 = 0; s0 < steps; s0 += kBatch) {
+        u32x4 v[kBatch];
+        static_for<kBatch>([&](auto uc) {
+            constexpr uint32_t u = decltype(uc)::value;
+            // past the group's end: its last vector again (all loads in flight together)
+            const uint32_t i = min((s0 + u) * kWave + lane, n4 - 1);
+            v[u] = __builtin_nontemporal_load(x4 + i);
+        });
+        static_for<kBatch>([&](auto uc) {
+            constexpr uint32_t u = decltype(uc)::value;
+            if (s0 + u >= steps) return;  // wave-uniform
+            const bool live = (s0 + u) * kWave + lane < n4;
+            const uint32_t x[4] = {v[u][0], v[u][1], v[u][2], v[u][3]};
+            uint32_t f[4], size[4];
+            acc += encode_lane4<RUNS, UNI, MW4, false>(et, Mw, geo.log2g, live, pos0, x, nullptr, 0, f, size);
+            if constexpr (!UNI) {
+                pos0 += step_inc;
+                if (pos0 >= Mw) pos0 -= Mw;
+            }
+        });
+    }
+    const uint32_t tot = wave_sum(acc);
+    if (lane == 0) bits[group] = tot;
+}
+
+template <int RUNS, bool UNI, bool MW4, uint32_t TPG>
+__global__ __launch_bounds__(kWave * kWavesPerBlock) void k_encode_groups(Tables t, Geo geo,
+                                                                          const uint8_t* __restrict__ src,
+                                                                          uint64_t n_tensors,
+                                                                          uint8_t* __restrict__ slots,
+                                                                          const uint64_t* __restrict__ starts,
+                                                                          uint64_t* __restrict__ totals,
+                                                                          uint32_t lds_words) {
+    extern __shared__ uint32_t smem[];
+    constexpr uint32_t TW = kLongTileWordsEncode;
+    constexpr uint32_t kSteps = TW / (4 * kWave);
+    const uint32_t lane = lane_id();
+    const uint32_t wib = uniform(threadIdx.x / kWave);
+    const uint64_t gpt = tile_groups(geo.tiles_per_tensor, TPG);
+    const uint64_t group = (uint64_t)blockIdx.x * kWavesPerBlock + wib;
+    if (group >= n_tensors * gpt) return;
+    const uint64_t ti = group / gpt;
+    const uint64_t tile0 = (group - ti * gpt) * TPG;
+    const uint32_t ntiles = (uint32_t)min((uint64_t)TPG, geo.tiles_per_tensor - tile0);
+    const uint32_t* x = reinterpret_cast<const uint32_t*>(src + ti * geo.L);
+    const u32x4* x4 = reinterpret_cast<const u32x4*>(x);
+    uint32_t* slot = reinterpret_cast<uint32_t*>(slots + ti * geo.L);
+    // LDS of the wave: 64 header words, then the tile's payload bits
+    uint32_t* hdr = smem + wib * lds_words;
+    uint32_t* pay = hdr + 64;
+    const EncTabs<RUNS, UNI> et = enc_tabs_global<RUNS, UNI>(t, geo.Mw);
+    const uint32_t Mw = geo.Mw, lg = geo.log2g;
+    const uint32_t step_inc = (uint32_t)(4 * kWave) % Mw;
+
+    uint64_t S = uniform64(starts[group]);
+    uint64_t w0 = tile0 * TW;
+    // bits [32 * (S >> 5), S) of the record: the end of the previous tile
+    uint32_t tail = 0;
+    if (tile0 > 0 && (S & 31)) tail = bits_before_tile<RUNS>(t, geo, x, w0, (uint32_t)(S & 31));
+
+    // Tile k's words are in cur; the next tile's are loaded into nxt as the
+    // tile starts, with range-checked buffer loads: every tile issues the same
+    // number, and those past the next tile (all of them when the group has no
+    // next tile) return zero without touching memory.  The arrays swap roles
+    // from tile to tile, so no register that a load in flight writes is
+    // copied (a copy waits for its load).
+    u32x4 buf_a[kSteps], buf_b[kSteps];
+    {
+        const uint32_t n4 = (uint32_t)min((uint64_t)TW, geo.n_words - w0) >> 2;
+        static_for<kSteps>([&](auto sc) {
+            constexpr uint32_t s = decltype(sc)::value;
+            if (s * kWave + lane < n4) buf_a[s] = __builtin_nontemporal_load(x4 + (w0 >> 2) + s * kWave + lane);
+        });
+    }
+    auto one_tile = [&](u32x4(&cur)[kSteps], u32x4(&nxt)[kSteps], uint32_t k) __attribute__((always_inline)) {
+        const uint32_t nw = (uint32_t)min((uint64_t)TW, geo.n_words - w0);
+        const uint64_t wn = w0 + TW;
+        const uint32_t nn4 = k + 1 < ntiles ? (uint32_t)min((uint64_t)TW, geo.n_words - wn) >> 2 : 0u;
+        const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+            (void*)(x4 + (k + 1 < ntiles ? wn >> 2 : 0)), (short)0, (int)(16 * nn4), 0x00020000);
+        u32x4* z4 = reinterpret_cast<u32x4*>(hdr);
+        for (uint32_t i = lane; i < (lds_words >> 2); i += kWave) z4[i] = u32x4{0u, 0u, 0u, 0u};
+        __builtin_amdgcn_wave_barrier();
+        static_for<kSteps>([&](auto sc) {
+            constexpr uint32_t s = decltype(sc)::value;
+            nxt[s] = __builtin_amdgcn_raw_buffer_load_b128(rs, (int)(16 * (s * kWave + lane)), 0, 2);
+        });
+        uint32_t carry = 0;
+        uint32_t pos0 = UNI ? 0u : (uint32_t)((w0 + 4 * lane) % Mw);
+        static_for<kSteps>([&](auto sc) {
+            constexpr uint32_t s = decltype(sc)::value;
+            if (s * 4 * kWave >= nw) return;  // wave-uniform, and so for every later step
+            const uint32_t lw0 = s * 4 * kWave + 4 * lane;
+            const bool live = lw0 < nw;
+            const u32x4 xv = cur[s];
+            const uint32_t x[4] = {xv[0], xv[1], xv[2], xv[3]};
+            uint32_t f[4], size[4];
+            const uint32_t tot = encode_lane4<RUNS, UNI, MW4, true>(et, Mw, lg, live, pos0, x, hdr, lw0 >> lg, f, size);
+            or_fields(pay, carry, f, size, tot);
+            if constexpr (!UNI) {
+                pos0 += step_inc;
+                if (pos0 >= Mw) pos0 -= Mw;
+            }
+        });
+        __builtin_amdgcn_wave_barrier();
+        const uint64_t E = S + carry;
+        const bool last = tile0 + k == geo.tiles_per_tensor - 1;
+        // the tile's header words (always inside the slot)
+        const uint64_t hw0 = (w0 >> lg) >> 5;
+        const uint32_t hw_t = ((nw >> lg) + 31) / 32;
+        for (uint32_t j = lane; j < hw_t; j += kWave) slot[hw0 + j] = hdr[j];
+        // Payload words whose last bit lies in [S, E); the tensor's last tile
+        // also writes the final partial word, zero padded.  A record longer
+        // than the slot is cut off here and replaced by the raw tensor later.
+        // Word q0 + i is bits [32 i, 32 i + 32) of the tile's payload shifted
+        // up by r, below them the open bits of the previous tile: with those
+        // bits in the word before the payload (shifted to its top), word i is
+        // a funnel shift of two neighbouring LDS words, 16-byte stores from
+        // the first aligned word on.
+        const uint64_t q0 = S >> 5;
+        uint64_t q1 = E >> 5;
+        if (last && (E & 31)) q1 += 1;
+        q1 = min(q1, geo.n_words);
+        const uint32_t r = (uint32_t)(S & 31);
+        const uint32_t sh = (32u - r) & 31u;
+        if (lane == 0) pay[-1] = r ? tail << (32u - r) : 0u;
+        __builtin_amdgcn_wave_barrier();
+        const uint32_t* P = r ? pay - 1 : pay;
+        const uint32_t n = q1 > q0 ? (uint32_t)(q1 - q0) : 0u;
+        const uint32_t head = min((4u - (uint32_t)(q0 & 3)) & 3u, n);
+        const uint32_t nv = (n - head) >> 2;
+        const uint32_t rest = head + 4 * nv;  // words [rest, n) after the last vector
+        uint32_t* sq = slot + q0;
+        if (lane < head) {
+            sq[lane] = funnel(P[lane + 1], P[lane], sh);
+        } else if (lane >= 4 && lane - 4 < n - rest) {
+            const uint32_t i = rest + lane - 4;
+            sq[i] = funnel(P[i + 1], P[i], sh);
+        }
+        for (uint32_t v = lane; v < nv; v += kWave) {
+            const uint32_t i = head + 4 * v;
+            u32x4 w;
+    #pragma unroll
+            for (uint32_t c = 0; c < 4; ++c) w[c] = funnel(P[i + c + 1], P[i + c], sh);
+            *reinterpret_cast<u32x4*>(sq + i) = w;
+        }
+        // bits [32 * (E >> 5), E) for the next tile
+        const uint32_t iE = (uint32_t)((E >> 5) - q0);
+        tail = uniform(funnel(P[iE + 1], P[iE], sh));
+        if (last && lane == 0) totals[ti] = E;
+        S = E;
+        w0 = wn;
+        __builtin_amdgcn_wave_barrier();
+    };
+    for (uint32_t k = 0; k < ntiles; k += 2) {
+        one_tile(buf_a, buf_b, k);
+        if (k + 1 < ntiles) one_tile(buf_b, buf_a, k + 1);
+    }
+}
+
+template <int RUNS, bool UNI, bool MW4>
+static hipError_t launch_encode_groups_s(const Tables& t, const Geo& geo, const void* src, uint64_t n_tensors,
+                                         void* slots, const LookBack& lb, hipStream_t s) {
+    constexpr uint32_t TPG = kEncodeTilesPerGroupHbm;
+    const uint64_t groups = n_tensors * tile_groups(geo.tiles_per_tensor, TPG);
+    uint64_t* starts = reinterpret_cast<uint64_t*>(lb.status);  // one word per group
+    const dim3 grid((uint32_t)((groups + kWavesPerBlock - 1) / kWavesPerBlock));
+    const dim3 block(kWave * kWavesPerBlock);
+    const uint8_t* sr = static_cast<const uint8_t*>(src);
+    hipLaunchKernelGGL((k_enc_group_bits<RUNS, UNI, MW4, TPG>), grid, block, 0, s, t, geo, sr, n_tensors, starts);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    e = launch_group_scan(n_tensors, tile_groups(geo.tiles_per_tensor, TPG), 32ull * geo.hdr_words, starts, s);
+    if (e != hipSuccess) return e;
+    // 64 header words, the tile's payload and the zero words after it
+    const uint32_t lds_words = 64 + kLongTileWordsEncode + 8;
+    hipLaunchKernelGGL((k_encode_groups<RUNS, UNI, MW4, TPG>), grid, block, (size_t)lds_words * 4 * kWavesPerBlock, s,
+                       t, geo, sr, n_tensors, static_cast<uint8_t*>(slots), starts, lb.totals, lds_words);
+    return hipGetLastError();
+}
+
+template <int RUNS>
+static hipError_t launch_encode_groups(const Tables& t, const Geo& geo, bool uniform_meta, const void* src,
+                                       uint64_t n_tensors, void* slots, const LookBack& lb, hipStream_t s) {
+    if (uniform_meta) return launch_encode_groups_s<RUNS, true, false>(t, geo, src, n_tensors, slots, lb, s);
+    if (geo.Mw % 4 == 0) return launch_encode_groups_s<RUNS, false, true>(t, geo, src, n_tensors, slots, lb, s);
+    return launch_encode_groups_s<RUNS, false, false>(t, geo, src, n_tensors, slots, lb, s);
 }
 
 template <bool MULTI>
@@ -588,7 +859,9 @@ static hipError_t launch_encode_r(const Tables& t, const Geo& geo, bool uniform_
         return launch_encode_t<false>(t, geo, RUNS, src, n_tensors, slots, bitmask, stored, LookBack{}, lds_words,
                                       s);
     }
-    hipError_t e = launch_encode_t<true>(t, geo, RUNS, src, n_tensors, slots, bitmask, stored, *lb, lds_words, s);
+    hipError_t e = encode_two_pass(geo)
+                       ? launch_encode_groups<RUNS>(t, geo, uniform_meta, src, n_tensors, slots, *lb, s)
+                       : launch_encode_t<true>(t, geo, RUNS, src, n_tensors, slots, bitmask, stored, *lb, lds_words, s);
     if (e != hipSuccess) return e;
     uint64_t per = (geo.n_words + 256ull * 64 - 1) / (256ull * 64);  // ~64 words per thread
     if (per > 1024) per = 1024;

@@ -45,7 +45,7 @@ struct Geo {
     uint64_t tiles_per_tensor;
     uint32_t spec_words;     // first-read words of a single-tile record (multiple of 4)
     uint32_t aligned16;      // slot base and L allow 16-byte vector access
-    uint32_t src_in_hbm;     // decode: stored items in device memory (not read over the host link)
+    uint32_t src_in_hbm;     // what the launch reads (stored items, or the encode's source) is in device memory
 };
 
 // Decoupled look-back state for multi-tile tensors.  A status word packs
@@ -95,7 +95,7 @@ constexpr uint32_t kDecodeTilesPerGroupHbm = IBP_DECODE_TILES_PER_GROUP_HBM;
 #define IBP_DECODE_GROUP_WAVES 4
 #endif
 constexpr int kGroupWaves = IBP_DECODE_GROUP_WAVES;
-__host__ __device__ constexpr uint64_t decode_groups(uint64_t tiles_per_tensor, uint32_t tiles_per_group) {
+__host__ __device__ constexpr uint64_t tile_groups(uint64_t tiles_per_tensor, uint32_t tiles_per_group) {
     return (tiles_per_tensor + tiles_per_group - 1) / tiles_per_group;
 }
 // Tiles per group of a decode whose stored records are (not) in device memory.
@@ -118,6 +118,29 @@ static_assert(kLongTileWordsDecodeHbm % 256 == 0 && kLongTileWordsDecodeHbm <= k
 __host__ __device__ constexpr uint32_t decode_tile_words(bool src_in_hbm) {
     return src_in_hbm ? kLongTileWordsDecodeHbm : kLongTileWordsDecode;
 }
+// Words per tile of a tensor longer than kMaxTileWords, for the encode (over
+// the host link it measured faster than 2,048-word tiles).
+constexpr uint32_t kLongTileWordsEncode = 1024;
+// Tiles per group of an encode whose source is in device memory: a first pass
+// sums each group's payload bits, a per-tensor scan turns the sums into start
+// bits, and one wave then encodes the group's tiles in order.
+#ifndef IBP_ENCODE_TILES_PER_GROUP_HBM
+#define IBP_ENCODE_TILES_PER_GROUP_HBM 4
+#endif
+constexpr uint32_t kEncodeTilesPerGroupHbm = IBP_ENCODE_TILES_PER_GROUP_HBM;
+
+// Whether an encode of tensors longer than one tile takes the two-pass path
+// (source in device memory, 16-byte aligned) rather than look-back per tile;
+// it needs one status word per group instead of one per tile.
+inline bool encode_two_pass(const Geo& g) { return g.src_in_hbm && g.aligned16; }
+inline uint64_t encode_status_words(const Geo& g, uint64_t n_tensors) {
+    return n_tensors * (encode_two_pass(g) ? tile_groups(g.tiles_per_tensor, kEncodeTilesPerGroupHbm)
+                                           : g.tiles_per_tensor);
+}
+
+// Exclusive start bits, `base` first, of the n_tensors * gpt group bit counts
+// in `bits` (in place; gpt consecutive groups per tensor).
+hipError_t launch_group_scan(uint64_t n_tensors, uint64_t gpt, uint64_t base, uint64_t* bits, hipStream_t s);
 
 enum DeviceError : uint32_t { kErrNone = 0, kErrCorrupt = 5, kErrRange = 6, kErrStall = 7 };
 

@@ -1,8 +1,8 @@
 """Seeded random formats against the oracle, bit for bit: chunk widths 32 to
 1024, periods, tensor lengths (one tile, several, and several groups of eight
-tiles; 16-byte multiples and not), Mask words with 0 to 16 runs of kept bits (uniform and per-position),
-chunk match rates from none to all, slots in HBM or pinned host memory, and
-gathers with repeated ids.  Metadata comes from ibp_meta_create so that the
+tiles; 16-byte multiples and not), Mask words with 0 to 16 runs of kept bits
+(uniform and per-position), chunk match rates from none to all, source and
+slots in HBM or pinned host memory, and gathers with repeated ids.  Metadata comes from ibp_meta_create so that the
 run structure and the match rate are controlled; everything the kernels
 produce (stored bytes, bitmask, records, raw slots, decoded tensors, gathers)
 is compared with the oracle's."""
@@ -117,18 +117,23 @@ def make_case(seed: int, layout: str | None = None):
     raw = x.view(np.uint8).reshape(n, L)
     pinned = bool(rng.random() < 0.3)
     ids = rng.integers(0, n, size=int(rng.integers(1, 2 * n + 2)))
-    return dict(W=W, M=M, L=L, n=n, mask=mask, bitval=bitval, raw=raw, pinned=pinned, ids=ids, kind=kind, q=q)
+    # the encode's source in pinned host memory (look-back per tile) or in HBM
+    # (a first pass over groups of tiles for long tensors)
+    src_pinned = bool(rng.random() < 0.3)
+    return dict(W=W, M=M, L=L, n=n, mask=mask, bitval=bitval, raw=raw, pinned=pinned, ids=ids, kind=kind, q=q,
+                src_pinned=src_pinned)
 
 
 @pytest.mark.parametrize("seed", range(N_CASES))
 def test_random_format(seed):
     c = make_case(seed)
     W, M, L, n, raw = c["W"], c["M"], c["L"], c["n"], c["raw"]
-    say(f"[fuzz] seed={seed} W={W} M={M} L={L} n={n} mask={c['kind']} q={c['q']} pinned={c['pinned']}")
+    say(f"[fuzz] seed={seed} W={W} M={M} L={L} n={n} mask={c['kind']} q={c['q']} pinned={c['pinned']} "
+        f"src_pinned={c['src_pinned']}")
     dev = device()
     meta = ibp.ibp_meta_create(L, W, M, c["mask"], c["bitval"])
     mb, bb = c["mask"].view(np.uint8), c["bitval"].view(np.uint8)
-    src = to_gpu(raw)
+    src = to_gpu(raw, pinned=c["src_pinned"])
     slots = empty_like_loc((n, L), torch.uint8, c["pinned"])
     bm = torch.zeros((n + 31) // 32, dtype=torch.int32, device=dev)
     stored = torch.zeros(n, dtype=torch.int64, device=dev)

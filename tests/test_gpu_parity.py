@@ -9,7 +9,7 @@ import torch
 from lossless_tensor_compression_ibp_amd import ibp
 from lossless_tensor_compression_ibp_amd import workloads as WL
 from oracle import oracle
-from tests.gpu_util import as_rows, compare_codec, device, say, to_gpu
+from tests.gpu_util import as_rows, bitmask_bits, compare_codec, device, say, to_gpu
 
 pytestmark = pytest.mark.gpu
 
@@ -119,6 +119,84 @@ def test_shapes(W, M, L, n):
     raw = _structured(rng, n, L)
     ids = rng.integers(0, n, size=2 * n)
     compare_codec(raw, W, M, 0.9, min(n, 64), ids=ids, label=f"shape W={W} M={M} L={L}")
+
+
+def _multi_tile_case(name):
+    """Tensors longer than one 8 KiB tile with their format: (W, M, mask,
+    bitval, rows).  Encode tiles are 1,024 words; from HBM a wave encodes a
+    group of 8 of them."""
+    rng = np.random.default_rng(sum(map(ord, name)))
+    if name == "zero_payload_tiles":
+        # period = the whole 16-tile tensor; tiles 3-9 hold only fully
+        # invariant words (k = 32), so a matching tile adds no payload bit and
+        # the open last word of tile 2 is carried across them and across the
+        # group boundary at tile 8; the other tiles keep 4 bits per word (one
+        # word of tile 0 keeps 12)
+        L, W = 16 * 4096, 32
+        Mw = L // 4
+        mask = np.full(Mw, 0xFFFFFFF0, np.uint32)
+        mask[3 * 1024:10 * 1024] = 0xFFFFFFFF
+        mask[1000] = 0xFFFF00F0  # tile 0 ends 7 bits into a word
+        bitval = np.zeros(Mw, np.uint32)
+        x = (rng.integers(0, 16, size=(5, Mw), dtype=np.uint64).astype(np.uint32)) & ~mask
+        x[1, 5 * 1024 + 7] ^= 1 << 20     # one mismatching word inside the zero-payload tiles
+        x[2, 9 * 1024 + 1023] ^= 1 << 31  # and one at the last word of tile 9
+        x[3, 2 * 1024 + 5] ^= 1 << 9      # and one in tile 2
+        return W, 32 * Mw, mask, bitval, x.view(np.uint8).reshape(5, L)
+    W, M, L, n = {"two_tiles": (32, 32, 8192 + 16, 9),         # 1,024 + 1,024 + 4 words
+                  "one_group": (32, 96 * 32, 85 * 384, 6),      # 8 tiles (the last of 992 words), period of 96 words
+                  "group_plus_one": (64, 128, 9 * 4096, 5),     # a second group of one tile
+                  "ragged": (32, 256, 16 * 4096 + 1056, 5),     # 17 tiles, the last of 264 words
+                  "wide_chunks": (1024, 2048, 20 * 4096, 3),    # W = 1,024, three groups
+                  "noise": (32, 32, 9 * 4096 + 16, 3)}[name]    # records longer than the slot: raw
+    if name == "noise":
+        raw = rng.integers(0, 256, size=(n, L), dtype=np.uint8)
+    else:
+        # words that repeat with the period M, low 20 bits and a few whole words random
+        Mw = M // 32
+        base = np.tile(rng.integers(0, 2**32, size=Mw, dtype=np.uint64).astype(np.uint32), (n, L // 4 // Mw))
+        base ^= rng.integers(0, 2**20, size=base.shape, dtype=np.uint64).astype(np.uint32)
+        noise = rng.random(base.shape) < 0.01
+        base[noise] ^= rng.integers(0, 2**32, size=int(noise.sum()), dtype=np.uint64).astype(np.uint32)
+        raw = base.view(np.uint8).reshape(n, L)
+    # metadata from the oracle over the rows themselves
+    o_mask, o_bitval = oracle.build_metadata(raw, 8 * L, W, M, 0.9, n)
+    return W, M, np.frombuffer(o_mask.tobytes(), np.uint32), np.frombuffer(o_bitval.tobytes(), np.uint32), raw
+
+
+@pytest.mark.parametrize("src_pinned", [False, True], ids=["hbm_two_pass", "pinned_look_back"])
+@pytest.mark.parametrize("name", ["two_tiles", "one_group", "group_plus_one", "ragged", "wide_chunks",
+                                  "zero_payload_tiles", "noise"])
+def test_multi_tile_encode(name, src_pinned):
+    """Long tensors encoded from HBM (first pass over groups of tiles, scan,
+    group encode) and from pinned host memory (look-back per tile), into
+    HBM slots: records, bitmask and stored bytes equal the oracle's."""
+    W, M, mask, bitval, raw = _multi_tile_case(name)
+    n, L = raw.shape
+    say(f"[parity] multi-tile encode {name} W={W} M={M} L={L} n={n} src_pinned={src_pinned}")
+    dev = device()
+    meta = ibp.ibp_meta_create(L, W, M, mask, bitval)
+    src = to_gpu(raw, pinned=src_pinned)
+    slots = torch.full((n, L), 0xEE, dtype=torch.uint8, device=dev)
+    bm = torch.zeros((n + 31) // 32, dtype=torch.int32, device=dev)
+    stored = torch.zeros(n, dtype=torch.int64, device=dev)
+    ibp.ibp_compress(meta, src, n, slots, bm, stored)
+    torch.cuda.synchronize()
+    o_slots, o_bm, o_stored = oracle.compress(raw, L, W, M, mask.view(np.uint8), bitval.view(np.uint8), n)
+    np.testing.assert_array_equal(bitmask_bits(bm.cpu().numpy().view(np.uint32), n), bitmask_bits(o_bm, n))
+    np.testing.assert_array_equal(stored.cpu().numpy().astype(np.uint64), o_stored)
+    g_slots = slots.cpu().numpy()
+    comp = bitmask_bits(o_bm, n).astype(bool)
+    assert comp.any() == (name != "noise")
+    for t in range(n):
+        k = int(o_stored[t])
+        np.testing.assert_array_equal(g_slots[t, :k], o_slots[t, :k] if comp[t] else raw[t],
+                                      err_msg=f"slot {t} differs")
+    out = torch.empty((n, L), dtype=torch.uint8, device=dev)
+    ibp.ibp_decompress(meta, slots, bm, n, out)
+    assert ibp.ibp_check(meta) == ibp.IBP_OK
+    np.testing.assert_array_equal(out.cpu().numpy(), raw)
+    meta.close()
 
 
 @pytest.mark.parametrize("W,M,L,n", [
