@@ -110,12 +110,14 @@ def test_soak_encode_paths():
         return torch.zeros((n + 31) // 32, dtype=torch.int32, device=dev)
 
     def enc_plain(m, src):
+        # slots and output in HBM whether the source is in HBM or pinned
         n = src.shape[0]
-        sl, bm, st = torch.empty_like(src), bitmask(n), torch.zeros(n, dtype=torch.int64, device=dev)
+        sl = torch.empty(src.shape, dtype=src.dtype, device=dev)
+        bm, st = bitmask(n), torch.zeros(n, dtype=torch.int64, device=dev)
         ibp.ibp_compress(m, src, n, sl, bm, st)
-        out = torch.empty_like(src)
+        out = torch.empty(src.shape, dtype=src.dtype, device=dev)
         ibp.ibp_decompress(m, sl, bm, n, out)
-        return bm, st, torch.equal(out, src)
+        return bm, st, torch.equal(out.cpu(), src.cpu()) if src.device.type == "cpu" else torch.equal(out, src)
 
     def enc_split(m, src):
         n = src.shape[0]
@@ -136,7 +138,9 @@ def test_soak_encode_paths():
         ibp.ibp_decompress_packed(m, buf, off, bm, n, out)
         return bm, off, torch.equal(out, src)
 
+    src_ll_pinned = src_ll.cpu().pin_memory()  # long tensors: look-back from pinned memory, two passes from HBM
     cases = [("kv", enc_plain, m_kv, src_kv), ("dense", enc_plain, m_dg, src_dg), ("llm", enc_plain, m_ll, src_ll),
+             ("llm_pinned_source", enc_plain, m_ll, src_ll_pinned),
              ("split", enc_split, m_sp, src_sp), ("packed", enc_packed, m_sp, src_sp)]
     first = {name: f(m, s) for name, f, m, s in cases}
     assert all(v[2] for v in first.values()), "a first encode does not round-trip"
@@ -152,4 +156,4 @@ def test_soak_encode_paths():
             say(f"[soak encode] {it} iterations exact after {last - t0:.0f} s")
     for m in (m_kv, m_dg, m_ll, m_sp):
         assert ibp.ibp_check(m) == ibp.IBP_OK
-    say(f"[soak encode] {it} iterations of 5 encodes, all exact")
+    say(f"[soak encode] {it} iterations of {len(cases)} encodes, all exact")

@@ -1,6 +1,6 @@
 """Concurrency and capture: one handle used from two streams at once (the
-multi-tile look-back keeps its scratch per stream), and single-tile decode
-captured in a HIP graph and replayed."""
+multi-tile look-back and the long-tensor start bits keep their scratch per
+stream), and single-tile decode captured in a HIP graph and replayed."""
 from __future__ import annotations
 
 import numpy as np
@@ -42,6 +42,44 @@ def test_one_handle_two_streams():
         assert torch.equal(outs1[i], src), f"stream 1 launch {i}"
         assert torch.equal(outs2[i], src[ids]), f"stream 2 launch {i}"
     say("[streams] two streams, multi-tile look-back: ok")
+
+
+def test_multi_tile_encodes_on_two_streams():
+    """Long-tensor encodes from HBM (size pass and scan) on one stream and
+    from pinned memory (look-back) on another, interleaved through one
+    handle: every record equals the one a lone encode writes."""
+    dev = device()
+    layers = [WL.llm_layer(l, rows=48, cols=1024) for l in range(4)]
+    raw = np.stack([x.reshape(-1).view(np.uint8) for x in layers])
+    n, L = raw.shape
+    src_d = torch.from_numpy(raw).to(dev)
+    src_h = torch.from_numpy(raw).pin_memory()
+    w = WL.LLM_BF16
+    meta = ibp.ibp_build_metadata(src_d, 1, L, w.chunk_bits, w.period_bits, w.threshold)
+    ref = torch.empty_like(src_d)
+    ref_bm = torch.zeros(1, dtype=torch.int32, device=dev)
+    ref_st = torch.zeros(n, dtype=torch.int64, device=dev)
+    ibp.ibp_compress(meta, src_d, n, ref, ref_bm, ref_st)
+    torch.cuda.synchronize()
+    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+    outs = {k: [(torch.empty_like(src_d), torch.zeros(1, dtype=torch.int32, device=dev),
+                 torch.zeros(n, dtype=torch.int64, device=dev)) for _ in range(5)] for k in ("hbm", "pinned")}
+    for i in range(5):
+        with torch.cuda.stream(s1):
+            sl, bm, st = outs["hbm"][i]
+            ibp.ibp_compress(meta, src_d, n, sl, bm, st, stream=s1)
+        with torch.cuda.stream(s2):
+            sl, bm, st = outs["pinned"][i]
+            ibp.ibp_compress(meta, src_h, n, sl, bm, st, stream=s2)
+    torch.cuda.synchronize()
+    assert ibp.ibp_check(meta) == ibp.IBP_OK
+    for k, runs in outs.items():
+        for i, (sl, bm, st) in enumerate(runs):
+            assert torch.equal(bm, ref_bm) and torch.equal(st, ref_st), f"{k} launch {i}"
+            for t in range(n):
+                b = int(ref_st[t])
+                assert torch.equal(sl[t, :b], ref[t, :b]), f"{k} launch {i}, record {t}"
+    say("[streams] two streams, long-tensor encodes from HBM and pinned memory: ok")
 
 
 def test_single_tile_decode_in_a_graph():
