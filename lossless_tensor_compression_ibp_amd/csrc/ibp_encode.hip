@@ -10,8 +10,10 @@
 // fixed-size slots and a GPU bitmask says which slots hold a record.
 //
 // One wave64 encodes one tile (all of a tensor of at most 2048 words, or a
-// 1024-word tile of a longer one); tiles of one tensor find their start bit
-// by decoupled look-back.
+// 1024-word tile of a longer one).  The tiles of a longer tensor find their
+// start bits by decoupled look-back when the source is in pinned host memory;
+// a source in HBM is read twice instead (a pass summing each group of tiles'
+// payload bits, a scan per tensor), and one wave encodes a group of tiles.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
