@@ -25,6 +25,9 @@
 
 namespace ibp {
 
+// Step shapes of decode_tile.
+constexpr int kTileOneStep = 0, kTileMultiStep = 1, kTileHalfStep = 2;
+
 // One step of decode_tile: lane words lw0 .. lw0+3 (256 words per wave).
 // FULL: every lane's four words lie inside the tile, so the step needs no
 // bounds checks (every step but a ragged last one).
@@ -111,17 +114,102 @@ __device__ __forceinline__ void decode_step(const Tab& tab, const Geo& geo, cons
     }
 }
 
+// The same step for tensors of at most 128 words: lane words lw0, lw0 + 1
+// (128 words per wave), so no lane idles on a 512-byte row as it would with
+// four words per lane.  MW4: Mw is a multiple of 4, so a lane's two positions
+// are consecutive and read as one 8-byte vector.
+template <int RUNS, bool MW4, class Tab>
+__device__ __forceinline__ void decode_step2(const Tab& tab, const Geo& geo, const uint32_t* hdr,
+                                             const uint32_t* pay, uint32_t lw0, uint32_t pos0, uint32_t nw,
+                                             uint32_t* carry, uint32_t* __restrict__ out, bool vec) {
+    constexpr bool UNI = IsUniformTab<Tab>::value;
+    const uint32_t Mw = geo.Mw;
+    const uint32_t lg = geo.log2g;
+    uint32_t pos[2], kd[2], bv[2];
+    uint32_t rr[RUNS > 0 ? RUNS : 1][2];
+    if constexpr (UNI) {
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            pos[j] = 0;
+            kd[j] = tab.kdw(0);
+            bv[j] = tab.bw(0);
+        }
+    } else if constexpr (MW4) {
+        const u32x2 k2 = tab.kdw2(pos0), b2 = tab.bw2(pos0);
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            pos[j] = pos0 + j;
+            kd[j] = k2[j];
+            bv[j] = b2[j];
+        }
+    } else {
+        pos[0] = pos0;
+        pos[1] = (pos0 + 1 == Mw) ? 0u : pos0 + 1;
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            kd[j] = tab.kdw(pos[j]);
+            bv[j] = tab.bw(pos[j]);
+        }
+    }
+    const uint32_t c0 = lw0 >> lg;
+    const uint32_t hsh = hdr[c0 >> 5] >> (c0 & 31u);
+    uint32_t p[2], size[2];
+    uint32_t tot = 0;
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+        p[j] = (hsh >> ((uint32_t)j >> lg)) & 1u;
+        size[j] = lw0 + j < nw ? (p[j] ? 32u - (kd[j] & 63u) : 32u) : 0u;
+        tot += size[j];
+    }
+    const uint32_t incl = wave_incl_scan(tot);
+    uint32_t off = *carry + incl - tot;
+    *carry += lane_value(incl, kWave - 1);
+    if constexpr (MW4 && !UNI) {
+#pragma unroll
+        for (int r = 0; r < RUNS; ++r) {
+            const u32x2 v = tab.rw2(r, pos0);
+            rr[r][0] = v[0];
+            rr[r][1] = v[1];
+        }
+    } else {
+#pragma unroll
+        for (int r = 0; r < RUNS; ++r)
+#pragma unroll
+            for (int j = 0; j < 2; ++j) rr[r][j] = tab.rw(r, pos[j]);
+    }
+    uint32_t x[2];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+        const uint32_t q = off >> 5;
+        const uint32_t f = funnel(pay[q + 1], pay[q], off);
+        uint32_t dep = bv[j];
+#pragma unroll
+        for (int r = 0; r < RUNS; ++r) dep |= (f << (tab.dw(r, pos[j], kd[j]) & 31u)) & rr[r][j];
+        x[j] = p[j] ? dep : f;
+        off += size[j];
+    }
+    if (vec && lw0 + 1 < nw) {
+        __builtin_nontemporal_store(u32x2{x[0], x[1]}, reinterpret_cast<u32x2*>(out + lw0));
+    } else {
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+            if (lw0 + j < nw) out[lw0 + j] = x[j];
+    }
+}
+
 // Rebuild words [w0, w0 + nw) of a tensor into out.  hdr: participation bits
 // of the tile (bit 0 = the tile's first chunk); pay: LDS words holding the
 // tile's kept bits, the first at bit `bit0` of pay[0].  Lanes past the end
 // contribute size 0.  With `vec`, out + w0 is 16-byte aligned.  MW4: the
 // period Mw is a multiple of 4 (and w0 too), so a lane's four positions are
 // consecutive and their table entries are read as one 16-byte vector.
-// MULTI_STEP: tiles of several 256-word steps get a step body compiled
-// without bounds checks (measured 2 % faster on 4 KiB pages); one-step tiles
-// keep a single body, whose lower register count keeps more waves resident
-// (measured 2.5 % faster on 512-byte and 1 KiB rows).
-template <int RUNS, bool MW4, bool MULTI_STEP, class Tab>
+// MODE kTileMultiStep: tiles of several 256-word steps get a step body
+// compiled without bounds checks (measured 2 % faster on 4 KiB pages);
+// kTileOneStep: tiles of at most a few steps keep a single body, whose lower
+// register count keeps more waves resident (measured 2.5 % faster on 512-byte
+// and 1 KiB rows); kTileHalfStep: tiles of at most 128 words (w0 even) take
+// one step of two words per lane.
+template <int RUNS, bool MW4, int MODE, class Tab>
 __device__ __forceinline__ uint32_t decode_tile(const Tab& tab, const Geo& geo, const uint32_t* hdr,
                                                 const uint32_t* pay, uint32_t bit0, uint64_t w0,
                                                 uint32_t nw, uint32_t* __restrict__ out, bool vec) {
@@ -132,7 +220,12 @@ __device__ __forceinline__ uint32_t decode_tile(const Tab& tab, const Geo& geo, 
     uint32_t pos0 = UNI ? 0u : (uint32_t)((w0 + 4ull * lane) % Mw);
     uint32_t carry = bit0;
     uint32_t* o = out + w0;
-    if constexpr (!MULTI_STEP) {
+    if constexpr (MODE == kTileHalfStep) {
+        decode_step2<RUNS, MW4>(tab, geo, hdr, pay, 2 * lane, UNI ? 0u : (uint32_t)((w0 + 2ull * lane) % Mw), nw,
+                                &carry, o, vec);
+        return carry;
+    }
+    if constexpr (MODE == kTileOneStep) {
         const uint32_t steps = (nw + 4 * kWave - 1) / (4 * kWave);
         for (uint32_t s = 0; s < steps; ++s) {
             const bool full = (s + 1) * (4 * kWave) <= nw;  // wave-uniform: no lane runs past the end
@@ -246,7 +339,11 @@ __global__ __launch_bounds__(256) void k_decode_small(Tables t, Geo geo, const u
     const uint32_t hw = (uint32_t)geo.hdr_words;
     if (first >= n_out) return;
 
-    u32x4 st[STAGE];
+    // STAGE 0: tensors of at most 128 words (one 16-byte vector per lane is
+    // read, and the rebuild takes two words per lane)
+    constexpr int kSt = STAGE > 0 ? STAGE : 1;
+    constexpr int kTileMode = STAGE >= 4 ? kTileMultiStep : (STAGE == 0 ? kTileHalfStep : kTileOneStep);
+    u32x4 st[kSt];
     for (uint64_t base = 0; base < my_tiles; base += kWave) {
         const uint32_t cnt = (uint32_t)min((uint64_t)kWave, my_tiles - base);
         // lane k: id of tile base + k; the first read of tile 0 (the same
@@ -349,7 +446,7 @@ __global__ __launch_bounds__(256) void k_decode_small(Tables t, Geo geo, const u
             uint32_t n4_first;
             const u32x4* s4 = reinterpret_cast<const u32x4*>(slots + where_of(k, tn, &n4_first));
 #pragma unroll
-            for (int r = 0; r < STAGE; ++r) {
+            for (int r = 0; r < kSt; ++r) {
                 const uint32_t i = lane + (uint32_t)r * kWave;
                 if (i < n4_first) st[r] = __builtin_nontemporal_load(s4 + i);
             }
@@ -374,7 +471,7 @@ __global__ __launch_bounds__(256) void k_decode_small(Tables t, Geo geo, const u
                 len = packed ? lane_value(my_len, k) : (uint32_t)geo.L;
                 if (comp) {
 #pragma unroll
-                    for (int r = 0; r < STAGE; ++r) {
+                    for (int r = 0; r < kSt; ++r) {
                         const uint32_t i = lane + (uint32_t)r * kWave;
                         if (i < n4_first) reinterpret_cast<u32x4*>(buf)[i] = st[r];
                     }
@@ -383,7 +480,7 @@ __global__ __launch_bounds__(256) void k_decode_small(Tables t, Geo geo, const u
                 } else {
                     // raw slot: the prefix from registers, the rest copied
 #pragma unroll
-                    for (int r = 0; r < STAGE; ++r) {
+                    for (int r = 0; r < kSt; ++r) {
                         const uint32_t i = lane + (uint32_t)r * kWave;
                         if (i < n4_first) __builtin_nontemporal_store(st[r], reinterpret_cast<u32x4*>(out) + i);
                     }
@@ -404,9 +501,9 @@ __global__ __launch_bounds__(256) void k_decode_small(Tables t, Geo geo, const u
                 if (lane == 0) buf[4 * n4_first] = 0;
                 __builtin_amdgcn_wave_barrier();
                 if (UNI)
-                    decode_tile<RUNS, MW4, (STAGE >= 4)>(tu, geo, hdr, buf, 0, 0, nwords, out, true);
+                    decode_tile<RUNS, MW4, kTileMode>(tu, geo, hdr, buf, 0, 0, nwords, out, true);
                 else
-                    decode_tile<RUNS, MW4, (STAGE >= 4)>(ta, geo, hdr, buf, 0, 0, nwords, out, true);
+                    decode_tile<RUNS, MW4, kTileMode>(ta, geo, hdr, buf, 0, 0, nwords, out, true);
                 __builtin_amdgcn_wave_barrier();
                 continue;
             }
@@ -425,9 +522,9 @@ __global__ __launch_bounds__(256) void k_decode_small(Tables t, Geo geo, const u
                 __builtin_amdgcn_wave_barrier();
                 uint32_t pbits;
                 if (UNI)
-                    pbits = decode_tile<RUNS, MW4, (STAGE >= 4)>(tu, geo, buf, buf + hw, 0, 0, nwords, out, true);
+                    pbits = decode_tile<RUNS, MW4, kTileMode>(tu, geo, buf, buf + hw, 0, 0, nwords, out, true);
                 else
-                    pbits = decode_tile<RUNS, MW4, (STAGE >= 4)>(ta, geo, buf, buf + hw, 0, 0, nwords, out, true);
+                    pbits = decode_tile<RUNS, MW4, kTileMode>(ta, geo, buf, buf + hw, 0, 0, nwords, out, true);
                 const uint64_t words = hw + (pbits + 31) / 32;
                 if (bad_pad || 4ull * words >= geo.L || 4ull * words > len) latch_error(err, kErrCorrupt);
                 __builtin_amdgcn_wave_barrier();
@@ -449,9 +546,9 @@ __global__ __launch_bounds__(256) void k_decode_small(Tables t, Geo geo, const u
             if (lane == 0) buf[have] = 0;
             __builtin_amdgcn_wave_barrier();
             if (UNI)
-                decode_tile<RUNS, MW4, (STAGE >= 4)>(tu, geo, buf, buf + hw, 0, 0, nwords, out, true);
+                decode_tile<RUNS, MW4, kTileMode>(tu, geo, buf, buf + hw, 0, 0, nwords, out, true);
             else
-                decode_tile<RUNS, MW4, (STAGE >= 4)>(ta, geo, buf, buf + hw, 0, 0, nwords, out, true);
+                decode_tile<RUNS, MW4, kTileMode>(ta, geo, buf, buf + hw, 0, 0, nwords, out, true);
             __builtin_amdgcn_wave_barrier();
         }
     }
@@ -768,10 +865,10 @@ __global__ __launch_bounds__(kWave * kGroupWaves) void k_decode_groups(Tables t,
         const uint64_t wt = w0 + (uint64_t)r * tw;
         const uint32_t nw = (uint32_t)min((uint64_t)tw, wend - wt);
         if (UNI)
-            decode_tile<RUNS, false, true>(tu, geo, hdr + r * hw_tile, pay, (uint32_t)(St - 32 * a), wt, nw, out,
+            decode_tile<RUNS, false, kTileMultiStep>(tu, geo, hdr + r * hw_tile, pay, (uint32_t)(St - 32 * a), wt, nw, out,
                                            vec && (wt & 3) == 0);
         else
-            decode_tile<RUNS, false, true>(ta, geo, hdr + r * hw_tile, pay, (uint32_t)(St - 32 * a), wt, nw, out,
+            decode_tile<RUNS, false, kTileMultiStep>(ta, geo, hdr + r * hw_tile, pay, (uint32_t)(St - 32 * a), wt, nw, out,
                                            vec && (wt & 3) == 0);
     };
     const uint32_t n_full = (uint32_t)((wend - w0) / tw);
@@ -890,9 +987,9 @@ __global__ __launch_bounds__(256) void k_decode_tiles(Tables t, Geo geo, const u
     if (lane == 0) lds[have] = 0;
     __builtin_amdgcn_wave_barrier();
     if (UNI)
-        decode_tile<RUNS, false, false>(tu, geo, lds, lds + hw, 0, 0, nw, out, vec);
+        decode_tile<RUNS, false, kTileOneStep>(tu, geo, lds, lds + hw, 0, 0, nw, out, vec);
     else
-        decode_tile<RUNS, false, false>(ta, geo, lds, lds + hw, 0, 0, nw, out, vec);
+        decode_tile<RUNS, false, kTileOneStep>(ta, geo, lds, lds + hw, 0, 0, nw, out, vec);
 }
 
 // ---------------------------------------------------------------------------
@@ -968,6 +1065,7 @@ static hipError_t launch_small(const Tables& t, const Geo& geo, const void* slot
         }                          \
         IBP_SMALL_X(S, false);     \
     } while (0)
+    if (geo.n_words <= 2 * kWave) IBP_SMALL(0);
     if (stage <= 1) IBP_SMALL(1);
     if (stage <= 2) IBP_SMALL(2);
     if (stage <= 4) IBP_SMALL(4);

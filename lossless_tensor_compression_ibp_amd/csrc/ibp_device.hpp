@@ -23,6 +23,7 @@ __device__ __forceinline__ void static_for(F&& f) {
 }
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ uint32_t lane_id() { return threadIdx.x & (kWave - 1); }
 
@@ -158,6 +159,12 @@ struct TabArrays {
     }
     __device__ __forceinline__ u32x4 dxw4(int q, uint32_t pos) const {
         return *reinterpret_cast<const u32x4*>(dx + (uint32_t)q * Mw + pos);
+    }
+    // two consecutive positions starting at an even one (Mw % 4 == 0)
+    __device__ __forceinline__ u32x2 kdw2(uint32_t pos) const { return *reinterpret_cast<const u32x2*>(kd + pos); }
+    __device__ __forceinline__ u32x2 bw2(uint32_t pos) const { return *reinterpret_cast<const u32x2*>(b + pos); }
+    __device__ __forceinline__ u32x2 rw2(int j, uint32_t pos) const {
+        return *reinterpret_cast<const u32x2*>(r + (uint32_t)j * Mw + pos);
     }
 };
 

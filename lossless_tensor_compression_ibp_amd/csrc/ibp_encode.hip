@@ -17,6 +17,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "ibp_device.hpp"
 #include "ibp_internal.hpp"
 
@@ -234,91 +236,106 @@ __device__ __forceinline__ EncTabs<RUNS, UNI> enc_tabs_global(const Tables& t, u
     return e;
 }
 
+// NW consecutive table words from p (p 4 * NW-byte aligned).
+template <int NW>
+__device__ __forceinline__ void load_vec(const uint32_t* p, uint32_t (&v)[NW]) {
+    if constexpr (NW == 4) {
+        const u32x4 w = *reinterpret_cast<const u32x4*>(p);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) v[j] = w[j];
+    } else {
+        const u32x2 w = *reinterpret_cast<const u32x2*>(p);
+        v[0] = w[0];
+        v[1] = w[1];
+    }
+}
+
 // One lane's share of an encode step: the match test, participation and
-// removal of its four consecutive words x, at positions pos0.. of the period
-// (all four live or none).  With HDR the lane's participation bits are OR-ed
-// into hdr from chunk c0, its first word's; each word's field goes to f and
-// its width to size; returns the widths' sum.  Every lane of the wave calls it
-// (chunks of more than 4 words take a ballot).
-template <int RUNS, bool UNI, bool MW4, bool HDR>
-__device__ __forceinline__ uint32_t encode_lane4(const EncTabs<RUNS, UNI>& et, uint32_t Mw, uint32_t lg, bool live,
-                                                 uint32_t pos0, const uint32_t (&x)[4], uint32_t* hdr, uint32_t c0,
-                                                 uint32_t (&f)[4], uint32_t (&size)[4]) {
+// removal of its NW (4, or 2 for tensors of at most 128 words) consecutive
+// words x, at positions pos0.. of the period (all live or none).  With HDR the
+// lane's participation bits are OR-ed into hdr from chunk c0, its first
+// word's; each word's field goes to f and its width to size; returns the
+// widths' sum.  Every lane of the wave calls it (chunks longer than a lane's
+// words take a ballot).
+template <int NW, int RUNS, bool UNI, bool MW4, bool HDR>
+__device__ __forceinline__ uint32_t encode_lane(const EncTabs<RUNS, UNI>& et, uint32_t Mw, uint32_t lg, bool live,
+                                                uint32_t pos0, const uint32_t (&x)[NW], uint32_t* hdr, uint32_t c0,
+                                                uint32_t (&f)[NW], uint32_t (&size)[NW]) {
+    static_assert(NW == 2 || NW == 4, "two or four words per lane");
     const uint32_t lane = lane_id();
     const uint32_t g = 1u << lg;
     const uint32_t* mrow = et.mrow;
     const TabArrays& ta = et.ta;
     const TabUniform<RUNS>& tu = et.tu;
     const uint32_t mu = et.mu;
-    uint32_t m[4], bv[4], kd[4], pos[4];
+    uint32_t m[NW], bv[NW], kd[NW], pos[NW];
     if constexpr (UNI) {
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
+        for (int j = 0; j < NW; ++j) {
             pos[j] = 0;
             m[j] = mu;
             bv[j] = tu.bw(0);
             kd[j] = tu.kdw(0);
         }
     } else if constexpr (MW4) {
-        const u32x4 m4 = *reinterpret_cast<const u32x4*>(mrow + pos0);
-        const u32x4 b4 = ta.bw4(pos0), k4 = ta.kdw4(pos0);
+        load_vec<NW>(mrow + pos0, m);
+        load_vec<NW>(ta.b + pos0, bv);
+        load_vec<NW>(ta.kd + pos0, kd);
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            pos[j] = pos0 + j;
-            m[j] = m4[j];
-            bv[j] = b4[j];
-            kd[j] = k4[j];
-        }
+        for (int j = 0; j < NW; ++j) pos[j] = pos0 + j;
     } else {
         pos[0] = pos0;
 #pragma unroll
-        for (int j = 1; j < 4; ++j) pos[j] = (pos[j - 1] + 1 == Mw) ? 0u : pos[j - 1] + 1;
+        for (int j = 1; j < NW; ++j) pos[j] = (pos[j - 1] + 1 == Mw) ? 0u : pos[j - 1] + 1;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
+        for (int j = 0; j < NW; ++j) {
             m[j] = mrow[pos[j]];
             bv[j] = ta.bw(pos[j]);
             kd[j] = ta.kdw(pos[j]);
         }
     }
-    bool mis[4];
+    bool mis[NW];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) mis[j] = live && ((x[j] ^ bv[j]) & m[j]) != 0;
+    for (int j = 0; j < NW; ++j) mis[j] = live && ((x[j] ^ bv[j]) & m[j]) != 0;
     // participation: a chunk matches when none of its words mismatches
-    bool p[4];
+    bool p[NW];
     uint32_t hbits;  // the lane's header bits from chunk c0 on
     if (g == 1) {
+        hbits = 0;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) p[j] = !mis[j];
-        hbits = (uint32_t)p[0] | ((uint32_t)p[1] << 1) | ((uint32_t)p[2] << 2) | ((uint32_t)p[3] << 3);
-    } else if (g == 2) {
-        const bool pa = !(mis[0] || mis[1]), pb = !(mis[2] || mis[3]);
-        p[0] = p[1] = pa;
-        p[2] = p[3] = pb;
+        for (int j = 0; j < NW; ++j) {
+            p[j] = !mis[j];
+            hbits |= (uint32_t)p[j] << j;
+        }
+    } else if (NW == 4 && g == 2) {
+        // two chunks per lane (words 0-1 and 2-3)
+        const bool pa = !(mis[0] || mis[1 % NW]), pb = !(mis[2 % NW] || mis[3 % NW]);
+#pragma unroll
+        for (int j = 0; j < NW; ++j) p[j] = j < 2 ? pa : pb;
         hbits = (uint32_t)pa | ((uint32_t)pb << 1);
     } else {
-        const uint32_t q = g >> 2;  // lanes per chunk
-        const uint64_t bal = ballot(mis[0] || mis[1] || mis[2] || mis[3]);
+        const uint32_t q = g / NW;  // lanes per chunk
+        bool any = false;
+#pragma unroll
+        for (int j = 0; j < NW; ++j) any = any || mis[j];
+        const uint64_t bal = ballot(any);
         const uint32_t gs = lane & ~(q - 1u);
         const uint64_t qmask = (q >= 64) ? ~0ull : ((1ull << q) - 1ull);
         const bool pc = ((bal >> gs) & qmask) == 0;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) p[j] = pc;
+        for (int j = 0; j < NW; ++j) p[j] = pc;
         hbits = (lane & (q - 1u)) == 0 ? (uint32_t)pc : 0u;
     }
     if (HDR && live && hbits) atomicOr(&hdr[c0 >> 5], hbits << (c0 & 31u));
-    // run masks of the lane's four positions: one 16-byte read per run
-    uint32_t rr[RUNS > 0 ? RUNS : 1][4];
+    // run masks of the lane's positions: one vector read per run
+    uint32_t rr[RUNS > 0 ? RUNS : 1][NW];
     if constexpr (MW4 && !UNI) {
 #pragma unroll
-        for (int r = 0; r < RUNS; ++r) {
-            const u32x4 v = ta.rw4(r, pos0);
-#pragma unroll
-            for (int j = 0; j < 4; ++j) rr[r][j] = v[j];
-        }
+        for (int r = 0; r < RUNS; ++r) load_vec<NW>(ta.r + (uint32_t)r * Mw + pos0, rr[r]);
     }
     uint32_t tot = 0;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
+    for (int j = 0; j < NW; ++j) {
         uint32_t e;
         if constexpr (UNI) {
             e = extract_t<RUNS>(tu, 0, kd[j], x[j]);
@@ -339,13 +356,14 @@ __device__ __forceinline__ uint32_t encode_lane4(const EncTabs<RUNS, UNI>& et, u
 // Places one step's fields after the record's first `carry` payload bits (a
 // wave scan of the lanes' widths gives each lane its offset) and advances
 // carry by the step's total.
-__device__ __forceinline__ void or_fields(uint32_t* pay, uint32_t& carry, const uint32_t (&f)[4],
-                                          const uint32_t (&size)[4], uint32_t tot) {
+template <int NW>
+__device__ __forceinline__ void or_fields(uint32_t* pay, uint32_t& carry, const uint32_t (&f)[NW],
+                                          const uint32_t (&size)[NW], uint32_t tot) {
     const uint32_t incl = wave_incl_scan(tot);
     uint32_t off = carry + incl - tot;
     carry += lane_value(incl, kWave - 1);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
+    for (int j = 0; j < NW; ++j) {
         if (size[j]) {
             const uint32_t q = off >> 5, sh = off & 31u;
             atomicOr(&pay[q], f[j] << sh);
@@ -379,9 +397,13 @@ __global__ __launch_bounds__(1024) void k_encode_small(Tables t, Geo geo, const 
                                                       uint32_t buf_words, Items items, uint64_t* __restrict__ sizes,
                                                       uint32_t* err, uint32_t* __restrict__ headers) {
     extern __shared__ uint32_t smem[];
+    // bitmask bits of the workgroup's tensors: set (compressed) and touched
+    // (written at all), one bit per tensor from bit b0 % 32 of word 0
+    __shared__ uint32_t bm_set[kEncBlockBitWords], bm_touched[kEncBlockBitWords];
     const uint32_t lane = lane_id();
     const uint32_t wib = uniform(threadIdx.x / kWave);
     const uint32_t Mw = geo.Mw;
+    if (threadIdx.x < kEncBlockBitWords) bm_set[threadIdx.x] = bm_touched[threadIdx.x] = 0u;
     // LDS: [m row + per-position tables (not for uniform metadata)][wave buffers]
     const uint32_t rows = UNI ? 0u : 1u + tab_rows(RUNS);
     stage_table_image<dx_rows(RUNS)>(t, 0, rows, Mw, nullptr, 0, smem);
@@ -395,31 +417,42 @@ __global__ __launch_bounds__(1024) void k_encode_small(Tables t, Geo geo, const 
         et.mu = uniform(t.m[0]);
     }
 
+    // STAGE 0: tensors of at most 128 words, two words per lane in one step
+    // (four would leave half the lanes idle on a 512-byte row)
+    constexpr int NW = STAGE == 0 ? 2 : 4;
+    constexpr int kSt = STAGE == 0 ? 1 : STAGE;
+    using Vec = std::conditional_t<NW == 4, u32x4, u32x2>;
     const uint32_t nw = (uint32_t)geo.n_words;
-    const uint32_t n4 = nw >> 2;
+    const uint32_t nvec = nw / NW;
     const uint32_t hw = (uint32_t)geo.hdr_words;
     const uint32_t lg = geo.log2g;
-    const uint32_t step_inc = (uint32_t)(4 * kWave) % Mw;
+    const uint32_t step_inc = (uint32_t)(NW * kWave) % Mw;
+    // The workgroup takes tensors [b0, b1), its waves every wpb-th of them,
+    // so that their bitmask bits gather in LDS: a bitmask word then takes one
+    // store, or an atomic or two where neighbouring ranges share it (an
+    // atomic per tensor, 32 to a word, cost 512-byte rows 2.4x the encode).
     const uint32_t wpb = blockDim.x / kWave;
-    const uint64_t stride = (uint64_t)gridDim.x * wpb;
-    uint64_t ti = (uint64_t)blockIdx.x * wpb + wib;
-    if (ti >= n_tensors) return;
+    const uint64_t stride = wpb;
+    const uint64_t per_block = (n_tensors + gridDim.x - 1) / gridDim.x;
+    const uint64_t b0 = min((uint64_t)blockIdx.x * per_block, n_tensors);
+    const uint64_t b1 = min(b0 + per_block, n_tensors);
+    uint64_t ti = b0 + wib;
 
-    // cur[s]: the lane's four words of step s.  Once step s has taken them,
-    // the same registers receive step s of the wave's next tensor, so the
+    // cur[s]: the lane's words of step s.  Once step s has taken them, the
+    // same registers receive step s of the wave's next tensor, so the
     // prefetch costs no registers beyond one step's words.
-    u32x4 cur[STAGE];
-    {
-        const u32x4* s4 = reinterpret_cast<const u32x4*>(src + ti * geo.L);
-        static_for<STAGE>([&](auto rc) {
+    Vec cur[kSt];
+    if (ti < b1) {
+        const Vec* sv = reinterpret_cast<const Vec*>(src + ti * geo.L);
+        static_for<kSt>([&](auto rc) {
             constexpr int r = decltype(rc)::value;
             const uint32_t i = lane + (uint32_t)r * kWave;
-            if (i < n4) cur[r] = __builtin_nontemporal_load(s4 + i);
+            if (i < nvec) cur[r] = __builtin_nontemporal_load(sv + i);
         });
     }
-    for (; ti < n_tensors; ti += stride) {
+    for (; ti < b1; ti += stride) {
         const uint64_t tnext = ti + stride;
-        const u32x4* nx4 = reinterpret_cast<const u32x4*>(src + (tnext < n_tensors ? tnext : ti) * geo.L);
+        const Vec* nxv = reinterpret_cast<const Vec*>(src + (tnext < b1 ? tnext : ti) * geo.L);
         // packed placement: this tensor's item span, needed once the record is built
         uint64_t item_a = 0, item_b = 0;
         if (!SIZES && items.offsets) {
@@ -434,18 +467,20 @@ __global__ __launch_bounds__(1024) void k_encode_small(Tables t, Geo geo, const 
         __builtin_amdgcn_wave_barrier();
         uint32_t* pay = buf + (headers ? 4u : hw);
         uint32_t carry = 0;
-        uint32_t pos0 = UNI ? 0u : (4u * lane) % Mw;
-        static_for<STAGE>([&](auto sc) {
+        uint32_t pos0 = UNI ? 0u : ((uint32_t)NW * lane) % Mw;
+        static_for<kSt>([&](auto sc) {
             constexpr int s = decltype(sc)::value;
-            const uint32_t lw0 = (uint32_t)s * (4 * kWave) + 4 * lane;
-            if ((uint32_t)s * (4 * kWave) >= nw) return;  // wave-uniform, and so for every later step
-            const bool live = lw0 < nw;  // nw % 4 == 0: a live lane owns four words
-            const u32x4 xv = cur[s];
-            if (tnext < n_tensors && live) cur[s] = __builtin_nontemporal_load(nx4 + lane + (uint32_t)s * kWave);
-            const uint32_t x[4] = {xv[0], xv[1], xv[2], xv[3]};
-            uint32_t f[4], size[4];
+            const uint32_t lw0 = (uint32_t)s * (NW * kWave) + NW * lane;
+            if ((uint32_t)s * (NW * kWave) >= nw) return;  // wave-uniform, and so for every later step
+            const bool live = lw0 < nw;  // nw % 4 == 0: a live lane owns all its words
+            const Vec xv = cur[s];
+            if (tnext < b1 && live) cur[s] = __builtin_nontemporal_load(nxv + lane + (uint32_t)s * kWave);
+            uint32_t x[NW];
+#pragma unroll
+            for (int j = 0; j < NW; ++j) x[j] = xv[j];
+            uint32_t f[NW], size[NW];
             const uint32_t tot =
-                encode_lane4<RUNS, UNI, MW4, !SIZES>(et, Mw, lg, live, pos0, x, buf, lw0 >> lg, f, size);
+                encode_lane<NW, RUNS, UNI, MW4, !SIZES>(et, Mw, lg, live, pos0, x, buf, lw0 >> lg, f, size);
             if constexpr (SIZES)
                 carry += wave_sum(tot);
             else
@@ -486,14 +521,26 @@ __global__ __launch_bounds__(1024) void k_encode_small(Tables t, Geo geo, const 
                        nw, true);
         }
         if (lane == 0) {
-            const uint32_t bit = 1u << (ti & 31);
-            if (comp)
-                atomicOr(&bitmask[ti >> 5], bit);
-            else
-                atomicAnd(&bitmask[ti >> 5], ~bit);
+            const uint32_t j = (uint32_t)((ti >> 5) - (b0 >> 5)), bit = 1u << (ti & 31);
+            atomicOr(&bm_touched[j], bit);
+            if (comp) atomicOr(&bm_set[j], bit);
             if (stored) stored[ti] = comp ? 4ull * (headers ? words - hw : words) : geo.L;
         }
         __builtin_amdgcn_wave_barrier();
+    }
+    if constexpr (!SIZES) {
+        __syncthreads();
+        const uint32_t n_bw = b1 > b0 ? (uint32_t)(((b1 - 1) >> 5) - (b0 >> 5) + 1) : 0u;
+        if (threadIdx.x < n_bw) {
+            const uint32_t set = bm_set[threadIdx.x], touched = bm_touched[threadIdx.x];
+            uint32_t* w = bitmask + (b0 >> 5) + threadIdx.x;
+            if (touched == ~0u) {
+                *w = set;  // every tensor of the word is this workgroup's
+            } else {
+                if (set) atomicOr(w, set);
+                if (touched & ~set) atomicAnd(w, ~(touched & ~set));
+            }
+        }
     }
 }
 
@@ -575,7 +622,7 @@ __global__ __launch_bounds__(kWave * kWavesPerBlock) void k_enc_group_bits(Table
             const bool live = (s0 + u) * kWave + lane < n4;
             const uint32_t x[4] = {v[u][0], v[u][1], v[u][2], v[u][3]};
             uint32_t f[4], size[4];
-            acc += encode_lane4<RUNS, UNI, MW4, false>(et, Mw, geo.log2g, live, pos0, x, nullptr, 0, f, size);
+            acc += encode_lane<4, RUNS, UNI, MW4, false>(et, Mw, geo.log2g, live, pos0, x, nullptr, 0, f, size);
             if constexpr (!UNI) {
                 pos0 += step_inc;
                 if (pos0 >= Mw) pos0 -= Mw;
@@ -658,7 +705,7 @@ __global__ __launch_bounds__(kWave * kWavesPerBlock) void k_encode_groups(Tables
             const u32x4 xv = cur[s];
             const uint32_t x[4] = {xv[0], xv[1], xv[2], xv[3]};
             uint32_t f[4], size[4];
-            const uint32_t tot = encode_lane4<RUNS, UNI, MW4, true>(et, Mw, lg, live, pos0, x, hdr, lw0 >> lg, f, size);
+            const uint32_t tot = encode_lane<4, RUNS, UNI, MW4, true>(et, Mw, lg, live, pos0, x, hdr, lw0 >> lg, f, size);
             or_fields(pay, carry, f, size, tot);
             if constexpr (!UNI) {
                 pos0 += step_inc;
@@ -809,6 +856,9 @@ static hipError_t launch_encode_small_s(const Tables& t, const Geo& geo, const v
     PersistentPlan plan;
     *launched = false;
     if (!plan_persistent(fn, head, SIZES ? 0 : wave, cu_count, n_tensors, &plan)) return hipSuccess;
+    // a workgroup's tensors must span at most kEncBlockBitWords bitmask words
+    const uint64_t per_block = (n_tensors + plan.blocks - 1) / plan.blocks;
+    if (per_block + 31 > 32ull * kEncBlockBitWords) return hipErrorInvalidValue;
     hipLaunchKernelGGL((k_encode_small<RUNS, UNI, MW4, S, SIZES>), dim3(plan.blocks), dim3(kWave * plan.wpb),
                        plan.shm, s, t, geo, static_cast<const uint8_t*>(src), n_tensors,
                        static_cast<uint8_t*>(slots), bitmask, stored, SIZES ? 0u : buf_words, xa.items, xa.sizes,
@@ -831,6 +881,7 @@ static hipError_t launch_encode_small(const Tables& t, const Geo& geo, const voi
                : launch_encode_small_s<RUNS, UNI, false, S, SIZES>(t, geo, src, n_tensors, slots, bitmask,      \
                                                                    stored, cu_count, head, wave, buf_words, xa, \
                                                                    s, launched)
+    if (geo.n_words <= 2 * kWave) IBP_ENC_SMALL(0);
     if (stage <= 1) IBP_ENC_SMALL(1);
     if (stage <= 2) IBP_ENC_SMALL(2);
     if (stage <= 4) IBP_ENC_SMALL(4);

@@ -118,6 +118,11 @@ static_assert(kLongTileWordsDecodeHbm % 256 == 0 && kLongTileWordsDecodeHbm <= k
 __host__ __device__ constexpr uint32_t decode_tile_words(bool src_in_hbm) {
     return src_in_hbm ? kLongTileWordsDecodeHbm : kLongTileWordsDecode;
 }
+// Bitmask words one workgroup of the small-tensor encode can cover: it takes
+// at most 16 waves x kMaxItemsPerWave tensors (the launch plan guarantees it),
+// which span at most 5 words.
+constexpr uint32_t kEncBlockBitWords = 8;
+
 // Words per tile of a tensor longer than kMaxTileWords, for the encode (over
 // the host link it measured faster than 2,048-word tiles).
 constexpr uint32_t kLongTileWordsEncode = 1024;
@@ -195,6 +200,8 @@ struct PersistentPlan {
 #define IBP_MAX_ITEMS_PER_WAVE 8
 #endif
 constexpr uint64_t kMaxItemsPerWave = IBP_MAX_ITEMS_PER_WAVE;
+static_assert(16 * kMaxItemsPerWave + 31 <= 32ull * kEncBlockBitWords,
+              "a workgroup's tensors must fit the encode's LDS bitmask words");
 #ifndef IBP_DECODE_ITEMS_PER_WAVE
 #define IBP_DECODE_ITEMS_PER_WAVE 4
 #endif

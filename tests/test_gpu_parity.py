@@ -83,6 +83,35 @@ def test_llm_layer_multi_tile():
                   slots_pinned=True, label="llm_multi_tile")
 
 
+@pytest.mark.parametrize("fill", [0, -1], ids=["zeroed", "all_ones"])
+def test_bitmask_words_rewritten(fill):
+    """Enough 512-byte rows (70,001) that each workgroup of the encode takes
+    whole bitmask words (written with one store) as well as words it shares
+    with its neighbours (atomics): every bit of the rows equals the oracle's
+    whatever the bitmask held, and the bits past the last row keep their
+    value."""
+    w = WL.DENSE_GNN
+    raw = as_rows(WL.dense_gnn(70001))
+    n, L = raw.shape
+    say(f"[parity] bitmask words n={n} L={L} fill={fill}")
+    dev = device()
+    g_sample = to_gpu(raw[:1024])
+    meta = ibp.ibp_build_metadata(g_sample, 1024, L, w.chunk_bits, w.period_bits, w.threshold)
+    o_mask, o_bitval = oracle.build_metadata(raw[:1024], 8 * L, w.chunk_bits, w.period_bits, w.threshold, 1024)
+    src = to_gpu(raw)
+    slots = torch.empty_like(src)
+    bm = torch.full(((n + 31) // 32,), fill, dtype=torch.int32, device=dev)
+    stored = torch.zeros(n, dtype=torch.int64, device=dev)
+    ibp.ibp_compress(meta, src, n, slots, bm, stored)
+    _, o_bm, o_stored = oracle.compress(raw, L, w.chunk_bits, w.period_bits, o_mask, o_bitval, n)
+    bits = np.unpackbits(bm.cpu().numpy().view(np.uint8), bitorder="little")
+    np.testing.assert_array_equal(bits[:n], bitmask_bits(o_bm, n))
+    assert (bits[n:] == (1 if fill == -1 else 0)).all(), "bits past n_tensors must be left as they were"
+    np.testing.assert_array_equal(stored.cpu().numpy().astype(np.uint64), o_stored)
+    assert 0 < bits[:n].sum() < n  # both compressed and raw rows
+    meta.close()
+
+
 # --------------------------------------------------------------------------
 # Chunk widths, periods, tails
 # --------------------------------------------------------------------------
