@@ -645,7 +645,7 @@ def run_dense_gnn(args) -> dict:
         args, n * L * args.steps / wall / GB, wall,
         {"workload": f"dense_gnn: {n} rows x 128 fp32 |N(0,0.5)| with 3% N(0,50) rows, W=32, M=4096, T=0.95, "
                      f"slots in HBM, contiguous decode of all rows per step", "rows": n, "tensor_bytes": L},
-        savings, "ibp::k_decode_small<1, false, true, 1, false>", durs, hbm_roofline(hbm_bytes, durs, "dense_gnn"),
+        savings, "ibp::k_decode_small<1, false, true, 0, false>", durs, hbm_roofline(hbm_bytes, durs, "dense_gnn"),
         encode=encode_hbm(n * L, n * L + stored_np.sum(), float(np.mean(enc_durs)), "HBM -> HBM, all rows per launch"),
         uncompressed_hbm_copy_GBps=round(n * L * args.steps / raw_wall / GB, 3),
         uncompressed_copy_kernel_us=round(float(np.mean(raw_durs)) * 1e6, 2), meta=ibp.ibp_meta_get_info(meta))
@@ -702,7 +702,7 @@ def run_dlrm(args) -> dict:
         {"workload": f"dlrm: {n} rows x 128 fp32 U(-0.01,0.01), W=32, M=4096, T=0.9, slots in pinned host "
                      f"memory, {per_step} zero-copy gathers of {batch} random ids (with replacement) per step",
          "rows": n, "tensor_bytes": L, "batch_ids": batch, "gathers_per_step": per_step},
-        savings, "ibp::k_decode_small<2, true, true, 1, false>", durs,
+        savings, "ibp::k_decode_small<2, true, true, 0, false>", durs,
         link_roofline(link, durs, savings, None if args.small else "dlrm", h2d, lines, batch * L),
         line_granular_note=("a 512-byte row whose record is about 465 bytes still spans 4 lines of 128 bytes, "
                             "so at this saving the link moves the same lines as for raw rows"),
