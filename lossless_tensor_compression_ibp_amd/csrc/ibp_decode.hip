@@ -290,7 +290,9 @@ __device__ __forceinline__ void stage_tables(const Tables& t, uint32_t Mw, uint3
 // software pipeline over its tiles.  All ids and bitmask bits of a wave's
 // next 64 tiles are fetched first (one lane per tile); then the first read of
 // tile k+1 (the whole slot of a raw tensor, the first spec_words of a record)
-// is in flight in registers while tile k is decoded.
+// is in flight in registers while tile k is decoded.  STAGE: 16-byte vectors
+// per lane of that read; STAGE 0 for tensors of at most 128 words, which one
+// vector per lane covers and whose rebuild takes two words per lane.
 //
 // Packed cache layout (items.offsets set): each lane also fetches its tile's
 // item span; every read stays inside that span, and an item whose span does

@@ -375,11 +375,13 @@ __device__ __forceinline__ void or_fields(uint32_t* pay, uint32_t& carry, const 
 
 // ---------------------------------------------------------------------------
 // Tensors of at most kMaxTileWords words with 16-byte aligned source and
-// slots: persistent workgroups, tables staged once in LDS, four words per lane
-// per step, and each step's words of the wave's next tensor in flight in the
-// registers the current step has just consumed.  The record is assembled in
-// LDS (header words, then the kept bits) and written with 16-byte stores; an
-// incompressible tensor is copied from its source again.
+// slots: persistent workgroups, each taking a contiguous range of tensors,
+// tables staged once in LDS, four words per lane per step (two for tensors of
+// at most 128 words), and each step's words of the wave's next tensor in
+// flight in the registers the current step has just consumed.  The record is
+// assembled in LDS (header words, then the kept bits) and written with
+// 16-byte stores; an incompressible tensor is copied from its source again.
+// The range's bitmask bits are gathered in LDS and written once per word.
 //
 // Item placement: fixed slots (items.offsets == nullptr) or the packed cache
 // layout, where the item goes to its offset once its length has been checked
