@@ -1026,7 +1026,10 @@ static bool small_lds(const Geo& geo, int runs, bool uni, uint32_t* buf_words, s
 // 512-byte and 1 KiB rows in HBM decoded 10-25 % slower than with 4 to 6
 // (measured on MI355X).  Items read over the host link keep every wave the
 // registers allow, since there the reads in flight set the rate.
-constexpr uint32_t kSmallDecodeWavesPerSimdHbm = 5;
+#ifndef IBP_SMALL_DECODE_WAVES_HBM
+#define IBP_SMALL_DECODE_WAVES_HBM 5
+#endif
+constexpr uint32_t kSmallDecodeWavesPerSimdHbm = IBP_SMALL_DECODE_WAVES_HBM;
 
 template <int RUNS, bool UNI, bool MW4, int S, bool SPLIT>
 static hipError_t launch_small_s(const Tables& t, const Geo& geo, const void* slots, uint64_t n_slots,
