@@ -1,12 +1,13 @@
 """Soak of every decode and encode path (opt-in: set IBP_SOAK_SECONDS).
 
 Repeats, until the time is spent: the decode of KV pages in HBM, gathers of
-header-in-GPU-memory rows from pinned slots and of the packed HBM cache, the
-multi-tile (look-back) decode of layers from pinned slots; and the encodes of
-KV pages, dense rows, multi-tile layers, headers in GPU memory and the packed
-cache.  Every decoded output must equal its source, and every repetition of
-an encode must give the first run's bitmask and stored bytes (or offsets) and
-decode exactly.  Races between waves (look-back, bitmask atomics, persistent
+header-in-GPU-memory rows from pinned slots, of the packed HBM cache and of
+512-byte rows in HBM, the multi-tile (look-back) decode of layers from pinned
+slots; and the encodes of KV pages, dense rows, multi-tile layers (from HBM
+and from pinned memory), headers in GPU memory and the packed cache.  Every
+decoded output must equal its source, and every repetition of an encode must
+give the first run's bitmask and stored bytes (or offsets) and decode
+exactly.  Races between waves (look-back, bitmask words, persistent
 pipelines) that a single pass could miss would show up as a mismatch."""
 from __future__ import annotations
 
@@ -65,6 +66,15 @@ def test_soak_decode_paths():
     bm_ll = torch.zeros(1, dtype=torch.int32, device=dev)
     ibp.ibp_compress(m_ll, src_ll, n_ll, sl_ll, bm_ll)
     out_ll = torch.empty_like(src_ll)
+    # 512-byte rows (the two-words-per-lane stage) in HBM, gathered with repeats
+    w = WL.DENSE_GNN
+    src_dg = _rows(WL.dense_gnn(16384), dev)
+    n_dg = src_dg.shape[0]
+    m_dg = ibp.ibp_build_metadata(src_dg, 1024, 512, w.chunk_bits, w.period_bits, w.threshold)
+    sl_dg = torch.empty_like(src_dg)
+    bm_dg = torch.zeros((n_dg + 31) // 32, dtype=torch.int32, device=dev)
+    ibp.ibp_compress(m_dg, src_dg, n_dg, sl_dg, bm_dg)
+    out_dg = torch.empty((8192, 512), dtype=torch.uint8, device=dev)
     out_sp = torch.empty((8192, 1024), dtype=torch.uint8, device=dev)
     out_pk = torch.empty_like(out_sp)
     g = torch.Generator(device=dev).manual_seed(9)
@@ -75,7 +85,10 @@ def test_soak_decode_paths():
         ibp.ibp_gather_decompress_split(m_sp, sl_sp, n_sp, hd_sp, bm_sp, ids, out_sp)
         ibp.ibp_gather_decompress_packed(m_sp, buf, off, n_sp, bm_pk, ids, out_pk)
         ibp.ibp_decompress(m_ll, sl_ll, bm_ll, n_ll, out_ll)
+        ids_dg = ids % n_dg
+        ibp.ibp_gather_decompress(m_dg, sl_dg, n_dg, bm_dg, ids_dg, out_dg)
         assert torch.equal(out_kv, src_kv), f"KV pages, iteration {it}"
+        assert torch.equal(out_dg, src_dg[ids_dg]), f"512-byte rows, iteration {it}"
         assert torch.equal(out_sp, src_sp[ids]), f"split gather, iteration {it}"
         assert torch.equal(out_pk, src_sp[ids]), f"packed gather, iteration {it}"
         assert torch.equal(out_ll, src_ll), f"multi-tile layers, iteration {it}"
@@ -83,9 +96,9 @@ def test_soak_decode_paths():
         if time.time() - last > 20:
             last = time.time()
             say(f"[soak decode] {it} iterations exact after {last - t0:.0f} s")
-    for m in (m_kv, m_sp, m_ll):
+    for m in (m_kv, m_sp, m_ll, m_dg):
         assert ibp.ibp_check(m) == ibp.IBP_OK
-    say(f"[soak decode] {it} iterations of 4 decodes, all exact")
+    say(f"[soak decode] {it} iterations of 5 decodes, all exact")
 
 
 def test_soak_encode_paths():
