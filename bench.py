@@ -921,7 +921,7 @@ def run_sparse_gnn_cache(args) -> dict:
                      f"compressed into one packed HBM buffer (items back to back, 16-byte aligned), gather of "
                      f"{batch} distinct random row ids per step into HBM", "rows": n, "tensor_bytes": L,
          "batch_ids": batch},
-        1.0 - total / (n * L), "ibp::k_decode_small<0, true, true, 1, false> (packed items)", durs,
+        1.0 - total / (n * L), "ibp::k_decode_rows<0, true, 4, true> (packed items, one wave per row)", durs,
         hbm_roofline(hbm_bytes, durs, None if args.small else "sparse_gnn_cache"),
         cache_bytes=total, capacity_gain=round(n * L / total, 4),
         fill=dict(encode_link(2 * n * L, fill, h2d, "cache fill from pinned rows: the offsets pass, then the items "

@@ -224,8 +224,7 @@ __device__ __forceinline__ uint32_t decode_tile(const Tab& tab, const Geo& geo, 
         decode_step2<RUNS, MW4>(tab, geo, hdr, pay, 2 * lane, UNI ? 0u : (uint32_t)((w0 + 2ull * lane) % Mw), nw,
                                 &carry, o, vec);
         return carry;
-    }
-    if constexpr (MODE == kTileOneStep) {
+    } else if constexpr (MODE == kTileOneStep) {
         const uint32_t steps = (nw + 4 * kWave - 1) / (4 * kWave);
         for (uint32_t s = 0; s < steps; ++s) {
             const bool full = (s + 1) * (4 * kWave) <= nw;  // wave-uniform: no lane runs past the end
@@ -237,19 +236,20 @@ __device__ __forceinline__ uint32_t decode_tile(const Tab& tab, const Geo& geo, 
             }
         }
         return carry;
-    }
-    const uint32_t full_steps = nw / (4 * kWave);
-    for (uint32_t s = 0; s < full_steps; ++s) {
-        decode_step<RUNS, MW4, true>(tab, geo, hdr, pay, s * (4 * kWave) + 4 * lane, pos0, nw, &carry, o, vec);
-        if constexpr (!UNI) {
-            pos0 += step_inc;
-            if (pos0 >= Mw) pos0 -= Mw;
+    } else {
+        const uint32_t full_steps = nw / (4 * kWave);
+        for (uint32_t s = 0; s < full_steps; ++s) {
+            decode_step<RUNS, MW4, true>(tab, geo, hdr, pay, s * (4 * kWave) + 4 * lane, pos0, nw, &carry, o, vec);
+            if constexpr (!UNI) {
+                pos0 += step_inc;
+                if (pos0 >= Mw) pos0 -= Mw;
+            }
         }
+        if (full_steps * (4 * kWave) < nw)
+            decode_step<RUNS, MW4, false>(tab, geo, hdr, pay, full_steps * (4 * kWave) + 4 * lane, pos0, nw, &carry,
+                                          o, vec);
+        return carry;
     }
-    if (full_steps * (4 * kWave) < nw)
-        decode_step<RUNS, MW4, false>(tab, geo, hdr, pay, full_steps * (4 * kWave) + 4 * lane, pos0, nw, &carry, o,
-                                      vec);
-    return carry;
 }
 
 // LDS image of the tables: b, kd, dx rows, r rows (stride Mw), then the
@@ -995,6 +995,112 @@ __global__ __launch_bounds__(256) void k_decode_tiles(Tables t, Geo geo, const u
 }
 
 // ---------------------------------------------------------------------------
+// Short launches from GPU memory: tensors of at most 1 KiB (one 16-byte
+// vector per lane holds the whole slot or item) and at most a few rows per
+// CU.  One wave per output row, four to a workgroup, nothing staged: the
+// wave's record, its bitmask word and the table entries of its lanes'
+// positions (or the few wave-uniform words of uniform metadata) are loaded at
+// once, straight into registers, so a row costs one round trip to memory
+// after its id (and, in the packed layout, its item span).  A fixed slot is
+// read whole; the persistent kernel, which stages the tables per workgroup
+// and reads only the record, keeps the longer launches, where its waves
+// decode several rows each.
+// ---------------------------------------------------------------------------
+
+// Table entries of one lane's NW consecutive positions (Mw a multiple of 4),
+// loaded once into registers; the accessors decode_step / decode_step2 use.
+template <int RUNS, int NW>
+struct TabRegs {
+    static_assert(RUNS <= 3, "run shifts past the third live in the dx rows");
+    using V = std::conditional_t<NW == 4, u32x4, u32x2>;
+    V kd, b;
+    V r[RUNS > 0 ? RUNS : 1];
+    __device__ __forceinline__ void load(const Tables& t, uint32_t Mw, uint32_t pos0) {
+        kd = *reinterpret_cast<const V*>(t.kd + pos0);
+        b = *reinterpret_cast<const V*>(t.b + pos0);
+#pragma unroll
+        for (int j = 0; j < RUNS; ++j) r[j] = *reinterpret_cast<const V*>(t.r + (uint32_t)j * Mw + pos0);
+    }
+    __device__ __forceinline__ V kdw4(uint32_t) const { return kd; }
+    __device__ __forceinline__ V bw4(uint32_t) const { return b; }
+    __device__ __forceinline__ V rw4(int j, uint32_t) const { return r[j]; }
+    __device__ __forceinline__ V kdw2(uint32_t) const { return kd; }
+    __device__ __forceinline__ V bw2(uint32_t) const { return b; }
+    __device__ __forceinline__ V rw2(int j, uint32_t) const { return r[j]; }
+    __device__ __forceinline__ uint32_t dw(int j, uint32_t, uint32_t kdv) const { return kdv >> (8 * (j + 1)); }
+};
+
+// NW: words per lane of the rebuild (2 for tensors of at most 128 words, else
+// 4).  PACKED: items at items.offsets (else fixed slots of L bytes).
+template <int RUNS, bool UNI, int NW, bool PACKED>
+__global__ __launch_bounds__(256) void k_decode_rows(Tables t, Geo geo, const uint8_t* __restrict__ base,
+                                                     uint64_t n_slots, const uint32_t* __restrict__ bitmask,
+                                                     const int64_t* __restrict__ ids, uint64_t n_out,
+                                                     uint8_t* __restrict__ dst, uint32_t* err, uint32_t buf_words,
+                                                     Items items) {
+    extern __shared__ uint32_t smem[];
+    const uint32_t lane = lane_id();
+    const uint32_t wib = uniform(threadIdx.x / kWave);
+    const uint64_t oi = (uint64_t)blockIdx.x * (blockDim.x / kWave) + wib;
+    if (oi >= n_out) return;
+    const int64_t id = ids ? (int64_t)uniform64((uint64_t)ids[oi]) : (int64_t)oi;
+    if (id < 0 || (uint64_t)id >= n_slots) {
+        latch_error(err, kErrRange);
+        return;
+    }
+    uint64_t a = (uint64_t)id * geo.L, len = geo.L;
+    if constexpr (PACKED) {
+        const uint64_t b = uniform64(items.offsets[id + 1]);
+        a = uniform64(items.offsets[id]);
+        if (b < a || b > items.bytes || ((a | b) & 15) || b - a > ((geo.L + 15) & ~15ull)) {
+            latch_error(err, kErrCorrupt);
+            return;
+        }
+        len = b - a;
+    }
+    const uint32_t comp = (uniform(bitmask[(uint64_t)id >> 5]) >> ((uint64_t)id & 31)) & 1u;
+    const uint32_t n4 = (uint32_t)(len >> 4);
+    u32x4 v = u32x4{0u, 0u, 0u, 0u};
+    if (lane < n4) v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(base + a) + lane);
+    const uint32_t Mw = geo.Mw;
+    TabUniform<RUNS> tu;
+    TabRegs<UNI ? 0 : RUNS, NW> tr;
+    if constexpr (UNI)
+        tu = load_uniform<RUNS>(t, Mw);
+    else
+        tr.load(t, Mw, ((uint32_t)NW * lane) % Mw);
+    uint32_t* out = reinterpret_cast<uint32_t*>(dst + oi * geo.L);
+    const uint32_t nwords = (uint32_t)geo.n_words;
+    if (!comp) {
+        // a raw slot or item holds the tensor's bytes
+        if (len < geo.L) {
+            latch_error(err, kErrCorrupt);
+            return;
+        }
+        if (lane < (nwords >> 2)) __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(out) + lane);
+        return;
+    }
+    uint32_t* buf = smem + wib * buf_words;
+    if (lane < n4) reinterpret_cast<u32x4*>(buf)[lane] = v;
+    if (lane == 0) buf[4 * n4] = 0;
+    __builtin_amdgcn_wave_barrier();
+    // The whole record is in LDS, so its length only validates it: the
+    // rebuild returns the payload bits it consumed, and its reads stay inside
+    // the buffer (hw + n_words + 1 words or more) whatever the header says.
+    const uint32_t hw = (uint32_t)geo.hdr_words;
+    const uint32_t valid = (uint32_t)(geo.n_chunks - 32ull * (hw - 1));
+    const bool bad_pad = valid < 32 && (buf[hw - 1] >> valid) != 0;
+    constexpr int kMode = NW == 2 ? kTileHalfStep : kTileOneStep;
+    uint32_t pbits;
+    if constexpr (UNI)
+        pbits = decode_tile<RUNS, true, kMode>(tu, geo, buf, buf + hw, 0, 0, nwords, out, true);
+    else
+        pbits = decode_tile<RUNS, true, kMode>(tr, geo, buf, buf + hw, 0, 0, nwords, out, true);
+    const uint64_t words = hw + (pbits + 31) / 32;
+    if (bad_pad || 4ull * words >= geo.L || 4ull * words > len) latch_error(err, kErrCorrupt);
+}
+
+// ---------------------------------------------------------------------------
 // Launch.
 // ---------------------------------------------------------------------------
 static uint32_t runs_bucket(uint32_t runs) {
@@ -1079,6 +1185,56 @@ static hipError_t launch_small(const Tables& t, const Geo& geo, const void* slot
 #undef IBP_SMALL_X
 }
 
+// Single-tile tensors of at most 1 KiB in GPU memory, 16-byte aligned, at
+// most three runs per position unless the metadata is uniform, and at most
+// 128 rows per CU: one wave per row (k_decode_rows).  Measured on MI355X with
+// 1 KiB sparse_gnn rows in the packed layout: 1,024 / 8,192 / 32,768 /
+// 65,536 / 262,144 ids gathered in 3.4 / 5.9 / 16.9 / 31.1 / 116.4 us,
+// against 4.4 / 7.7 / 19.0 / 31.5 / 111.3 us for the persistent kernel, which
+// also decodes all 1,048,576 items 5 % faster.  0 sends every call to the
+// persistent kernel.
+#ifndef IBP_DECODE_ROWS
+#define IBP_DECODE_ROWS 1
+#endif
+
+static bool decode_rows(const Geo& geo, int runs, bool uni, uint64_t n_out, uint32_t cu_count) {
+    return IBP_DECODE_ROWS && geo.src_in_hbm && geo.aligned16 && geo.n_words <= 4 * kWave &&
+           (uni || (runs <= 3 && geo.Mw % 4 == 0)) && n_out <= 128ull * cu_count;
+}
+
+template <int RUNS, bool UNI, int NW, bool PACKED>
+static hipError_t launch_rows_t(const Tables& t, const Geo& geo, const void* base, uint64_t n_slots,
+                                const uint32_t* bitmask, const int64_t* ids, uint64_t n_out, void* dst,
+                                uint32_t* err, uint32_t buf_words, const Items& items, hipStream_t s) {
+    constexpr uint32_t kRowWaves = 4;
+    const dim3 grid((uint32_t)((n_out + kRowWaves - 1) / kRowWaves));
+    const size_t shm = (size_t)buf_words * 4 * kRowWaves;
+    hipLaunchKernelGGL((k_decode_rows<RUNS, UNI, NW, PACKED>), grid, dim3(kWave * kRowWaves), shm, s, t, geo,
+                       static_cast<const uint8_t*>(base), n_slots, bitmask, ids, n_out, static_cast<uint8_t*>(dst),
+                       err, buf_words, items);
+    return hipGetLastError();
+}
+
+template <int RUNS, bool UNI>
+static hipError_t launch_rows(const Tables& t, const Geo& geo, const void* base, uint64_t n_slots,
+                              const uint32_t* bitmask, const int64_t* ids, uint64_t n_out, void* dst, uint32_t* err,
+                              uint32_t buf_words, const Items& items, hipStream_t s) {
+    if constexpr (!UNI && RUNS > 3) {
+        return hipErrorInvalidValue;
+    } else {
+        const bool half = geo.n_words <= 2 * kWave;
+        if (items.offsets)
+            return half ? launch_rows_t<RUNS, UNI, 2, true>(t, geo, base, n_slots, bitmask, ids, n_out, dst, err,
+                                                            buf_words, items, s)
+                        : launch_rows_t<RUNS, UNI, 4, true>(t, geo, base, n_slots, bitmask, ids, n_out, dst, err,
+                                                            buf_words, items, s);
+        return half ? launch_rows_t<RUNS, UNI, 2, false>(t, geo, base, n_slots, bitmask, ids, n_out, dst, err,
+                                                         buf_words, items, s)
+                    : launch_rows_t<RUNS, UNI, 4, false>(t, geo, base, n_slots, bitmask, ids, n_out, dst, err,
+                                                         buf_words, items, s);
+    }
+}
+
 template <int RUNS, bool UNI>
 static hipError_t launch_tiles(const Tables& t, const Geo& geo, const void* slots, uint64_t n_slots,
                                const uint32_t* bitmask, const int64_t* ids, uint64_t n_out, void* dst,
@@ -1155,6 +1311,9 @@ static hipError_t launch_decode_r(const Tables& t, const Geo& geo, const void* s
     uint32_t buf_words = 0;
     size_t head = 0, wave = 0;
     if (geo.aligned16 && small_lds(geo, RUNS, UNI, &buf_words, &head, &wave)) {
+        if (!headers && decode_rows(geo, RUNS, UNI, n_out, cu_count))
+            return launch_rows<RUNS, UNI>(t, geo, slots, n_slots, bitmask, ids, n_out, dst, err, buf_words, items,
+                                          s);
         bool launched = false;
         const hipError_t e = launch_small<RUNS, UNI>(t, geo, slots, n_slots, bitmask, ids, n_out, dst, err, cu_count,
                                                      head, wave, buf_words, items, headers, s, &launched);

@@ -101,12 +101,34 @@ def test_packed_shapes_and_edges(W, M, L, n):
     packed_case(rows.view(np.uint8).reshape(n, L), W, M, 0.9, n, label=f"W={W} M={M} L={L}")
 
 
-def test_packed_errors():
-    w = WL.DENSE_GNN
-    raw = _rows("dense_gnn", 300)
+@pytest.mark.parametrize("W,M,L", [(32, 32, 64), (64, 512, 256)], ids=["uniform", "per_position"])
+def test_packed_past_the_row_kernel_bound(W, M, L):
+    """More items than 128 per CU: the decode of all items and the gather of
+    2n + 5 ids take the persistent kernel, smaller launches one wave per row."""
+    rng = np.random.default_rng(L)
+    n = 128 * torch.cuda.get_device_properties(0).multi_processor_count + 37
+    base = rng.integers(0, 2**32, size=L // 4, dtype=np.uint64).astype(np.uint32)
+    rows = np.tile(base, (n, 1)) ^ rng.integers(0, 2**12, size=(n, L // 4), dtype=np.uint64).astype(np.uint32)
+    rows[::5] = rng.integers(0, 2**32, size=rows[::5].shape, dtype=np.uint64).astype(np.uint32)
+    meta, src, off, buf, bm, cap = packed_case(rows.view(np.uint8).reshape(n, L), W, M, 0.9, 1024,
+                                               label=f"past the row bound W={W} M={M} L={L}")
+    ids = rng.integers(0, n, 3000)
+    g = torch.empty((ids.size, L), dtype=torch.uint8, device=device())
+    ibp.ibp_gather_decompress_packed(meta, buf, off, n, bm, torch.from_numpy(ids).to(device()), g, buf_bytes=cap)
+    assert ibp.ibp_check(meta) == ibp.IBP_OK
+    np.testing.assert_array_equal(g.cpu().numpy(), rows.view(np.uint8).reshape(n, L)[ids])
+
+
+@pytest.mark.parametrize("wl", ["dense_gnn", "sparse_gnn"])
+def test_packed_errors(wl):
+    """dense_gnn has per-position metadata (the persistent kernel), sparse_gnn
+    the same word at every position (one wave per gathered row)."""
+    w = WL.ALL[wl]
+    raw = _rows(wl, 300)
     n, L = raw.shape
     dev = device()
-    meta, src, off, buf, bm, cap = packed_case(raw, w.chunk_bits, w.period_bits, w.threshold, 300, label="errors")
+    meta, src, off, buf, bm, cap = packed_case(raw, w.chunk_bits, w.period_bits, w.threshold, 300,
+                                               label=f"errors {wl}")
     total = int(off[-1].item())
     # capacity one item short: the last item is not written, range error
     small = torch.full((total,), 0xEE, dtype=torch.uint8, device=dev)
@@ -123,8 +145,9 @@ def test_packed_errors():
     out = torch.empty((4, L), dtype=torch.uint8, device=dev)
     ibp.ibp_gather_decompress_packed(meta, buf, off, n, bm, torch.tensor([0, n, 1, 2], device=dev), out)
     assert ibp.ibp_check(meta) == ibp.IBP_ERR_RANGE
-    comp_ids = np.nonzero(np.unpackbits(bm.cpu().numpy().view(np.uint8), bitorder="little")[:n])[0]
-    t = int(comp_ids[0])
+    comp = np.unpackbits(bm.cpu().numpy().view(np.uint8), bitorder="little")[:n].astype(bool)
+    sizes = np.diff(off.cpu().numpy())
+    t = int(np.nonzero(comp & (sizes > 16))[0][0])
     bad = off.clone()
     bad[t + 1] = bad[t] + 16  # 16 bytes cannot hold this record
     ibp.ibp_gather_decompress_packed(meta, buf, bad, n, bm, torch.tensor([t], device=dev), out[:1])
@@ -133,6 +156,14 @@ def test_packed_errors():
     bad[t] += 4
     ibp.ibp_gather_decompress_packed(meta, buf, bad, n, bm, torch.tensor([t], device=dev), out[:1])
     assert ibp.ibp_check(meta) == ibp.IBP_ERR_CORRUPT
+    # a raw item cut shorter than the tensor
+    raw_ids = np.nonzero(~comp)[0]
+    if raw_ids.size:
+        r = int(raw_ids[0])
+        bad = off.clone()
+        bad[r + 1] = bad[r] + L - 16
+        ibp.ibp_gather_decompress_packed(meta, buf, bad, n, bm, torch.tensor([r], device=dev), out[:1])
+        assert ibp.ibp_check(meta) == ibp.IBP_ERR_CORRUPT
     # offsets past the buffer
     ibp.ibp_gather_decompress_packed(meta, buf, off, n, bm, torch.tensor([n - 1], device=dev), out[:1],
                                      buf_bytes=int(off[-2].item()))

@@ -74,6 +74,52 @@ def test_kv_page_with_corrupt_long_header():
     np.testing.assert_array_equal(out.cpu().numpy()[keep], raw[keep])
 
 
+def _cu_count() -> int:
+    return torch.cuda.get_device_properties(0).multi_processor_count
+
+
+@pytest.mark.parametrize("W,M,L", [(32, 4096, 512), (32, 32, 1024), (1024, 8192, 1024), (64, 512, 256)],
+                         ids=["per_position_512B", "uniform_1KiB", "sparse_W1024", "per_position_256B"])
+def test_short_rows_both_launch_shapes(W, M, L):
+    """Rows of at most 1 KiB in HBM decode one wave per row in launches of at
+    most 128 rows per CU and on the persistent kernel above that: a decode of
+    all rows and a gather just past that bound take the persistent kernel, a
+    gather of 3,000 ids the one-wave-per-row kernel, all bit-exact."""
+    rng = np.random.default_rng(W + M + L)
+    n = 128 * _cu_count() + 37
+    raw = _structured(rng, n, L)
+    raw[::7] = rng.integers(0, 256, size=raw[::7].shape, dtype=np.uint8)  # raw slots
+    r = compare_codec(raw, W, M, 0.9, 1024, ids=rng.integers(0, n, 3000), label=f"short rows W={W} M={M} L={L}")
+    big = rng.integers(0, n, 128 * _cu_count() + 1)
+    out = torch.empty((big.size, L), dtype=torch.uint8, device=device())
+    ibp.ibp_gather_decompress(r.meta, r.slots, n, r.bm, torch.from_numpy(big).to(device()), out)
+    assert ibp.ibp_check(r.meta) == ibp.IBP_OK
+    np.testing.assert_array_equal(out.cpu().numpy(), raw[big])
+    r.meta.close()
+
+
+def test_short_rows_corrupt_header():
+    """512-byte rows decoded one wave per row: a row whose header words claim
+    every chunk verbatim latches IBP_ERR_CORRUPT, and every other row of the
+    launch still decodes exactly."""
+    raw = as_rows(WL.dense_gnn(300))
+    w = WL.DENSE_GNN
+    r = compare_codec(raw, w.chunk_bits, w.period_bits, w.threshold, 300, label="short rows corrupt setup")
+    n, L = raw.shape
+    comp = np.flatnonzero(np.unpackbits(r.bm.cpu().numpy().view(np.uint8), bitorder="little")[:n])
+    assert comp.size > 2
+    hw = (8 * L // w.chunk_bits + 31) // 32
+    bad = r.slots.clone()
+    for t in comp[[0, comp.size // 2]]:
+        bad[int(t), :4 * hw] = 0
+    out = torch.empty((n, L), dtype=torch.uint8, device=device())
+    ibp.ibp_decompress(r.meta, bad, r.bm, n, out)
+    assert ibp.ibp_check(r.meta) == ibp.IBP_ERR_CORRUPT
+    keep = np.setdiff1d(np.arange(n), comp[[0, comp.size // 2]])
+    np.testing.assert_array_equal(out.cpu().numpy()[keep], raw[keep])
+    r.meta.close()
+
+
 def test_llm_layer_multi_tile():
     """A scaled layer (64 x 11008 bf16, 1.4 MB): 344 tiles of look-back."""
     layers = [WL.llm_layer(l, rows=64) for l in range(3)]
