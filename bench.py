@@ -645,7 +645,8 @@ def run_dense_gnn(args) -> dict:
         args, n * L * args.steps / wall / GB, wall,
         {"workload": f"dense_gnn: {n} rows x 128 fp32 |N(0,0.5)| with 3% N(0,50) rows, W=32, M=4096, T=0.95, "
                      f"slots in HBM, contiguous decode of all rows per step", "rows": n, "tensor_bytes": L},
-        savings, "ibp::k_decode_small<1, false, true, 0, false>", durs, hbm_roofline(hbm_bytes, durs, "dense_gnn"),
+        savings, "ibp::k_decode_rows<1, false, 2, false, 2> (two rows per wave)", durs,
+        hbm_roofline(hbm_bytes, durs, "dense_gnn"),
         encode=encode_hbm(n * L, n * L + stored_np.sum(), float(np.mean(enc_durs)), "HBM -> HBM, all rows per launch"),
         uncompressed_hbm_copy_GBps=round(n * L * args.steps / raw_wall / GB, 3),
         uncompressed_copy_kernel_us=round(float(np.mean(raw_durs)) * 1e6, 2), meta=ibp.ibp_meta_get_info(meta))
@@ -921,7 +922,7 @@ def run_sparse_gnn_cache(args) -> dict:
                      f"compressed into one packed HBM buffer (items back to back, 16-byte aligned), gather of "
                      f"{batch} distinct random row ids per step into HBM", "rows": n, "tensor_bytes": L,
          "batch_ids": batch},
-        1.0 - total / (n * L), "ibp::k_decode_rows<0, true, 4, true> (packed items, one wave per row)", durs,
+        1.0 - total / (n * L), "ibp::k_decode_rows<0, true, 4, true, 2> (packed items, two rows per wave)", durs,
         hbm_roofline(hbm_bytes, durs, None if args.small else "sparse_gnn_cache"),
         cache_bytes=total, capacity_gain=round(n * L / total, 4),
         fill=dict(encode_link(2 * n * L, fill, h2d, "cache fill from pinned rows: the offsets pass, then the items "

@@ -997,14 +997,14 @@ __global__ __launch_bounds__(256) void k_decode_tiles(Tables t, Geo geo, const u
 // ---------------------------------------------------------------------------
 // Short launches from GPU memory: tensors of at most 1 KiB (one 16-byte
 // vector per lane holds the whole slot or item) and at most a few rows per
-// CU.  One wave per output row, four to a workgroup, nothing staged: the
-// wave's record, its bitmask word and the table entries of its lanes'
-// positions (or the few wave-uniform words of uniform metadata) are loaded at
-// once, straight into registers, so a row costs one round trip to memory
-// after its id (and, in the packed layout, its item span).  A fixed slot is
-// read whole; the persistent kernel, which stages the tables per workgroup
-// and reads only the record, keeps the longer launches, where its waves
-// decode several rows each.
+// CU.  A wave takes RPW output rows, four waves to a workgroup, nothing
+// staged: the rows' records, their bitmask words and the table entries of
+// the lanes' positions (or the few wave-uniform words of uniform metadata)
+// are loaded at once, straight into registers, so the rows cost one round
+// trip to memory after their ids (and, in the packed layout, their item
+// spans).  A fixed slot is read whole; the persistent kernel, which stages
+// the tables per workgroup and reads only the record, keeps the longer
+// launches, where its waves decode several rows each.
 // ---------------------------------------------------------------------------
 
 // Table entries of one lane's NW consecutive positions (Mw a multiple of 4),
@@ -1031,8 +1031,9 @@ struct TabRegs {
 };
 
 // NW: words per lane of the rebuild (2 for tensors of at most 128 words, else
-// 4).  PACKED: items at items.offsets (else fixed slots of L bytes).
-template <int RUNS, bool UNI, int NW, bool PACKED>
+// 4).  PACKED: items at items.offsets (else fixed slots of L bytes).  RPW:
+// rows per wave, whose loads are all in flight before the first is rebuilt.
+template <int RUNS, bool UNI, int NW, bool PACKED, int RPW>
 __global__ __launch_bounds__(256) void k_decode_rows(Tables t, Geo geo, const uint8_t* __restrict__ base,
                                                      uint64_t n_slots, const uint32_t* __restrict__ bitmask,
                                                      const int64_t* __restrict__ ids, uint64_t n_out,
@@ -1041,27 +1042,61 @@ __global__ __launch_bounds__(256) void k_decode_rows(Tables t, Geo geo, const ui
     extern __shared__ uint32_t smem[];
     const uint32_t lane = lane_id();
     const uint32_t wib = uniform(threadIdx.x / kWave);
-    const uint64_t oi = (uint64_t)blockIdx.x * (blockDim.x / kWave) + wib;
-    if (oi >= n_out) return;
-    const int64_t id = ids ? (int64_t)uniform64((uint64_t)ids[oi]) : (int64_t)oi;
-    if (id < 0 || (uint64_t)id >= n_slots) {
+    const uint64_t oi0 = ((uint64_t)blockIdx.x * (blockDim.x / kWave) + wib) * RPW;
+    if (oi0 >= n_out) return;
+    if (n_slots == 0) {
         latch_error(err, kErrRange);
         return;
     }
-    uint64_t a = (uint64_t)id * geo.L, len = geo.L;
-    if constexpr (PACKED) {
-        const uint64_t b = uniform64(items.offsets[id + 1]);
-        a = uniform64(items.offsets[id]);
-        if (b < a || b > items.bytes || ((a | b) & 15) || b - a > ((geo.L + 15) & ~15ull)) {
-            latch_error(err, kErrCorrupt);
-            return;
+    // Each round of loads (ids; item spans and bitmask words; records) is
+    // issued for all the wave's rows before any of them is waited for.  A row
+    // that is past the launch or has a bad id or span keeps id 0 and reads
+    // nothing.
+    int64_t raw_id[RPW];
+    static_for<RPW>([&](auto rc) {
+        constexpr int r = decltype(rc)::value;
+        raw_id[r] = ids ? ids[min(oi0 + r, n_out - 1)] : (int64_t)(oi0 + r);
+    });
+    int64_t id[RPW];
+    bool live[RPW];
+    static_for<RPW>([&](auto rc) {
+        constexpr int r = decltype(rc)::value;
+        const int64_t v = (int64_t)uniform64((uint64_t)raw_id[r]);
+        const bool in_launch = oi0 + r < n_out;
+        live[r] = in_launch && v >= 0 && (uint64_t)v < n_slots;
+        if (in_launch && !live[r]) latch_error(err, kErrRange);
+        id[r] = live[r] ? v : 0;
+    });
+    uint64_t a[RPW], b[RPW];
+    uint32_t bw[RPW];
+    static_for<RPW>([&](auto rc) {
+        constexpr int r = decltype(rc)::value;
+        if constexpr (PACKED) {
+            a[r] = items.offsets[id[r]];
+            b[r] = items.offsets[id[r] + 1];
+        } else {
+            a[r] = (uint64_t)id[r] * geo.L;
+            b[r] = a[r] + geo.L;
         }
-        len = b - a;
-    }
-    const uint32_t comp = (uniform(bitmask[(uint64_t)id >> 5]) >> ((uint64_t)id & 31)) & 1u;
-    const uint32_t n4 = (uint32_t)(len >> 4);
-    u32x4 v = u32x4{0u, 0u, 0u, 0u};
-    if (lane < n4) v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(base + a) + lane);
+        bw[r] = bitmask[(uint64_t)id[r] >> 5];
+    });
+    uint32_t len[RPW];
+    u32x4 v[RPW];
+    static_for<RPW>([&](auto rc) {
+        constexpr int r = decltype(rc)::value;
+        a[r] = uniform64(a[r]);
+        b[r] = uniform64(b[r]);
+        if (PACKED && live[r] &&
+            (b[r] < a[r] || b[r] > items.bytes || ((a[r] | b[r]) & 15) || b[r] - a[r] > ((geo.L + 15) & ~15ull))) {
+            latch_error(err, kErrCorrupt);
+            live[r] = false;
+        }
+        len[r] = live[r] ? (uint32_t)(b[r] - a[r]) : 0u;
+        // range-checked: lanes past the record read zeros
+        const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+            (void*)(base + (live[r] ? a[r] : 0)), (short)0, (int)len[r], 0x00020000);
+        v[r] = __builtin_amdgcn_raw_buffer_load_b128(rs, (int)(16 * lane), 0, 2);
+    });
     const uint32_t Mw = geo.Mw;
     TabUniform<RUNS> tu;
     TabRegs<UNI ? 0 : RUNS, NW> tr;
@@ -1069,35 +1104,42 @@ __global__ __launch_bounds__(256) void k_decode_rows(Tables t, Geo geo, const ui
         tu = load_uniform<RUNS>(t, Mw);
     else
         tr.load(t, Mw, ((uint32_t)NW * lane) % Mw);
-    uint32_t* out = reinterpret_cast<uint32_t*>(dst + oi * geo.L);
     const uint32_t nwords = (uint32_t)geo.n_words;
-    if (!comp) {
-        // a raw slot or item holds the tensor's bytes
-        if (len < geo.L) {
-            latch_error(err, kErrCorrupt);
+    const uint32_t hw = (uint32_t)geo.hdr_words;
+    uint32_t* buf = smem + wib * buf_words;
+    static_for<RPW>([&](auto rc) {
+        constexpr int r = decltype(rc)::value;
+        if (!live[r]) return;
+        const uint32_t comp = (uniform(bw[r]) >> ((uint64_t)id[r] & 31)) & 1u;
+        uint32_t* out = reinterpret_cast<uint32_t*>(dst + (oi0 + r) * geo.L);
+        if (!comp) {
+            // a raw slot or item holds the tensor's bytes
+            if (len[r] < geo.L)
+                latch_error(err, kErrCorrupt);
+            else if (lane < (nwords >> 2))
+                __builtin_nontemporal_store(v[r], reinterpret_cast<u32x4*>(out) + lane);
             return;
         }
-        if (lane < (nwords >> 2)) __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(out) + lane);
-        return;
-    }
-    uint32_t* buf = smem + wib * buf_words;
-    if (lane < n4) reinterpret_cast<u32x4*>(buf)[lane] = v;
-    if (lane == 0) buf[4 * n4] = 0;
-    __builtin_amdgcn_wave_barrier();
-    // The whole record is in LDS, so its length only validates it: the
-    // rebuild returns the payload bits it consumed, and its reads stay inside
-    // the buffer (hw + n_words + 1 words or more) whatever the header says.
-    const uint32_t hw = (uint32_t)geo.hdr_words;
-    const uint32_t valid = (uint32_t)(geo.n_chunks - 32ull * (hw - 1));
-    const bool bad_pad = valid < 32 && (buf[hw - 1] >> valid) != 0;
-    constexpr int kMode = NW == 2 ? kTileHalfStep : kTileOneStep;
-    uint32_t pbits;
-    if constexpr (UNI)
-        pbits = decode_tile<RUNS, true, kMode>(tu, geo, buf, buf + hw, 0, 0, nwords, out, true);
-    else
-        pbits = decode_tile<RUNS, true, kMode>(tr, geo, buf, buf + hw, 0, 0, nwords, out, true);
-    const uint64_t words = hw + (pbits + 31) / 32;
-    if (bad_pad || 4ull * words >= geo.L || 4ull * words > len) latch_error(err, kErrCorrupt);
+        const uint32_t n4 = len[r] >> 4;
+        if (lane < n4) reinterpret_cast<u32x4*>(buf)[lane] = v[r];
+        if (lane == 0) buf[4 * n4] = 0;
+        __builtin_amdgcn_wave_barrier();
+        // The whole record is in LDS, so its length only validates it: the
+        // rebuild returns the payload bits it consumed, and its reads stay
+        // inside the buffer (hw + n_words + 1 words or more) whatever the
+        // header says.
+        const uint32_t valid = (uint32_t)(geo.n_chunks - 32ull * (hw - 1));
+        const bool bad_pad = valid < 32 && (buf[hw - 1] >> valid) != 0;
+        constexpr int kMode = NW == 2 ? kTileHalfStep : kTileOneStep;
+        uint32_t pbits;
+        if constexpr (UNI)
+            pbits = decode_tile<RUNS, true, kMode>(tu, geo, buf, buf + hw, 0, 0, nwords, out, true);
+        else
+            pbits = decode_tile<RUNS, true, kMode>(tr, geo, buf, buf + hw, 0, 0, nwords, out, true);
+        const uint64_t words = hw + (pbits + 31) / 32;
+        if (bad_pad || 4ull * words >= geo.L || 4ull * words > len[r]) latch_error(err, kErrCorrupt);
+        __builtin_amdgcn_wave_barrier();
+    });
 }
 
 // ---------------------------------------------------------------------------
@@ -1187,8 +1229,8 @@ static hipError_t launch_small(const Tables& t, const Geo& geo, const void* slot
 
 // Single-tile tensors of at most 1 KiB in GPU memory, 16-byte aligned, at
 // most three runs per position unless the metadata is uniform, and at most
-// 128 rows per CU: one wave per row (k_decode_rows).  Measured on MI355X with
-// 1 KiB sparse_gnn rows in the packed layout: 1,024 / 8,192 / 32,768 /
+// 128 rows per CU: k_decode_rows.  Measured on MI355X with 1 KiB sparse_gnn
+// rows in the packed layout and one row per wave: 1,024 / 8,192 / 32,768 /
 // 65,536 / 262,144 ids gathered in 3.4 / 5.9 / 16.9 / 31.1 / 116.4 us,
 // against 4.4 / 7.7 / 19.0 / 31.5 / 111.3 us for the persistent kernel, which
 // also decodes all 1,048,576 items 5 % faster.  0 sends every call to the
@@ -1202,14 +1244,24 @@ static bool decode_rows(const Geo& geo, int runs, bool uni, uint64_t n_out, uint
            (uni || (runs <= 3 && geo.Mw % 4 == 0)) && n_out <= 128ull * cu_count;
 }
 
+// Rows per wave of k_decode_rows.  Measured on MI355X (16,384 dense_gnn rows
+// of 512 bytes / 8,192-id packed-cache gathers of 1 KiB rows): 1 row 5.9-6.8
+// / 6.2-6.4 us, 2 rows 5.5-5.9 / 5.8 us, 4 rows 6.2-6.5 / 6.9 us.
+#ifndef IBP_DECODE_ROWS_PER_WAVE
+#define IBP_DECODE_ROWS_PER_WAVE 2
+#endif
+constexpr int kDecodeRowsPerWave = IBP_DECODE_ROWS_PER_WAVE;
+
 template <int RUNS, bool UNI, int NW, bool PACKED>
 static hipError_t launch_rows_t(const Tables& t, const Geo& geo, const void* base, uint64_t n_slots,
                                 const uint32_t* bitmask, const int64_t* ids, uint64_t n_out, void* dst,
                                 uint32_t* err, uint32_t buf_words, const Items& items, hipStream_t s) {
     constexpr uint32_t kRowWaves = 4;
-    const dim3 grid((uint32_t)((n_out + kRowWaves - 1) / kRowWaves));
+    constexpr uint64_t kRows = kRowWaves * kDecodeRowsPerWave;
+    const dim3 grid((uint32_t)((n_out + kRows - 1) / kRows));
     const size_t shm = (size_t)buf_words * 4 * kRowWaves;
-    hipLaunchKernelGGL((k_decode_rows<RUNS, UNI, NW, PACKED>), grid, dim3(kWave * kRowWaves), shm, s, t, geo,
+    hipLaunchKernelGGL((k_decode_rows<RUNS, UNI, NW, PACKED, kDecodeRowsPerWave>), grid, dim3(kWave * kRowWaves),
+                       shm, s, t, geo,
                        static_cast<const uint8_t*>(base), n_slots, bitmask, ids, n_out, static_cast<uint8_t*>(dst),
                        err, buf_words, items);
     return hipGetLastError();
