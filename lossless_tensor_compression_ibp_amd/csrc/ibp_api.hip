@@ -503,6 +503,7 @@ ibp_status ibp_compress(ibp_meta_t h, const void* src, uint64_t n_tensors, void*
     if (overlaps(src, n_tensors * L, dst_slots, n_tensors * L)) return IBP_ERR_INVALID_ARG;
     Geo geo = make_geo(h, aligned16(L, {src, dst_slots}), kLongTileWordsEncode);
     geo.src_in_hbm = pointer_kind(src, h->device) == Kind::Device;
+    geo.dst_in_hbm = pointer_kind(dst_slots, h->device) == Kind::Device;
     LookBack lb{};
     std::unique_lock<std::mutex> lock;
     if (geo.tiles_per_tensor > 1) {

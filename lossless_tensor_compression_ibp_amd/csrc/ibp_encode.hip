@@ -218,10 +218,31 @@ __global__ __launch_bounds__(256) void k_encode(Tables t, Geo geo, const uint8_t
 // registers.
 template <int RUNS, bool UNI>
 struct EncTabs {
+    static constexpr bool kRegs = false;
     const uint32_t* mrow;
     TabArrays ta;
     TabUniform<RUNS> tu;
     uint32_t mu;
+};
+
+// The same entries for one lane's NW consecutive positions (Mw a multiple of
+// 4, at most three runs), loaded once into registers.
+template <int RUNS, int NW>
+struct EncRegs {
+    static_assert(RUNS <= 3, "run shifts past the third live in the dx rows");
+    static constexpr bool kRegs = true;
+    using V = std::conditional_t<NW == 4, u32x4, u32x2>;
+    V m, b, kd;
+    V r[RUNS > 0 ? RUNS : 1];
+    TabUniform<RUNS> tu;  // unused
+    uint32_t mu = 0;      // unused
+    __device__ __forceinline__ void load(const Tables& t, uint32_t Mw, uint32_t pos0) {
+        m = *reinterpret_cast<const V*>(t.m + pos0);
+        b = *reinterpret_cast<const V*>(t.b + pos0);
+        kd = *reinterpret_cast<const V*>(t.kd + pos0);
+#pragma unroll
+        for (int j = 0; j < RUNS; ++j) r[j] = *reinterpret_cast<const V*>(t.r + (uint32_t)j * Mw + pos0);
+    }
 };
 
 template <int RUNS, bool UNI>
@@ -257,19 +278,26 @@ __device__ __forceinline__ void load_vec(const uint32_t* p, uint32_t (&v)[NW]) {
 // word's; each word's field goes to f and its width to size; returns the
 // widths' sum.  Every lane of the wave calls it (chunks longer than a lane's
 // words take a ballot).
-template <int NW, int RUNS, bool UNI, bool MW4, bool HDR>
-__device__ __forceinline__ uint32_t encode_lane(const EncTabs<RUNS, UNI>& et, uint32_t Mw, uint32_t lg, bool live,
+template <int NW, int RUNS, bool UNI, bool MW4, bool HDR, class ET = EncTabs<RUNS, UNI>>
+__device__ __forceinline__ uint32_t encode_lane(const ET& et, uint32_t Mw, uint32_t lg, bool live,
                                                 uint32_t pos0, const uint32_t (&x)[NW], uint32_t* hdr, uint32_t c0,
                                                 uint32_t (&f)[NW], uint32_t (&size)[NW]) {
     static_assert(NW == 2 || NW == 4, "two or four words per lane");
+    constexpr bool REGS = ET::kRegs;
     const uint32_t lane = lane_id();
     const uint32_t g = 1u << lg;
-    const uint32_t* mrow = et.mrow;
-    const TabArrays& ta = et.ta;
     const TabUniform<RUNS>& tu = et.tu;
     const uint32_t mu = et.mu;
     uint32_t m[NW], bv[NW], kd[NW], pos[NW];
-    if constexpr (UNI) {
+    if constexpr (REGS) {
+#pragma unroll
+        for (int j = 0; j < NW; ++j) {
+            pos[j] = pos0 + j;
+            m[j] = et.m[j];
+            bv[j] = et.b[j];
+            kd[j] = et.kd[j];
+        }
+    } else if constexpr (UNI) {
 #pragma unroll
         for (int j = 0; j < NW; ++j) {
             pos[j] = 0;
@@ -278,9 +306,9 @@ __device__ __forceinline__ uint32_t encode_lane(const EncTabs<RUNS, UNI>& et, ui
             kd[j] = tu.kdw(0);
         }
     } else if constexpr (MW4) {
-        load_vec<NW>(mrow + pos0, m);
-        load_vec<NW>(ta.b + pos0, bv);
-        load_vec<NW>(ta.kd + pos0, kd);
+        load_vec<NW>(et.mrow + pos0, m);
+        load_vec<NW>(et.ta.b + pos0, bv);
+        load_vec<NW>(et.ta.kd + pos0, kd);
 #pragma unroll
         for (int j = 0; j < NW; ++j) pos[j] = pos0 + j;
     } else {
@@ -289,9 +317,9 @@ __device__ __forceinline__ uint32_t encode_lane(const EncTabs<RUNS, UNI>& et, ui
         for (int j = 1; j < NW; ++j) pos[j] = (pos[j - 1] + 1 == Mw) ? 0u : pos[j - 1] + 1;
 #pragma unroll
         for (int j = 0; j < NW; ++j) {
-            m[j] = mrow[pos[j]];
-            bv[j] = ta.bw(pos[j]);
-            kd[j] = ta.kdw(pos[j]);
+            m[j] = et.mrow[pos[j]];
+            bv[j] = et.ta.bw(pos[j]);
+            kd[j] = et.ta.kdw(pos[j]);
         }
     }
     bool mis[NW];
@@ -329,22 +357,32 @@ __device__ __forceinline__ uint32_t encode_lane(const EncTabs<RUNS, UNI>& et, ui
     if (HDR && live && hbits) atomicOr(&hdr[c0 >> 5], hbits << (c0 & 31u));
     // run masks of the lane's positions: one vector read per run
     uint32_t rr[RUNS > 0 ? RUNS : 1][NW];
-    if constexpr (MW4 && !UNI) {
+    if constexpr (REGS) {
 #pragma unroll
-        for (int r = 0; r < RUNS; ++r) load_vec<NW>(ta.r + (uint32_t)r * Mw + pos0, rr[r]);
+        for (int r = 0; r < RUNS; ++r)
+#pragma unroll
+            for (int j = 0; j < NW; ++j) rr[r][j] = et.r[r][j];
+    } else if constexpr (MW4 && !UNI) {
+#pragma unroll
+        for (int r = 0; r < RUNS; ++r) load_vec<NW>(et.ta.r + (uint32_t)r * Mw + pos0, rr[r]);
     }
     uint32_t tot = 0;
 #pragma unroll
     for (int j = 0; j < NW; ++j) {
         uint32_t e;
-        if constexpr (UNI) {
+        if constexpr (REGS) {
+            // at most three runs: their shifts are kd's upper bytes
+            e = 0;
+#pragma unroll
+            for (int r = 0; r < RUNS; ++r) e |= (x[j] & rr[r][j]) >> ((kd[j] >> (8 * (r + 1))) & 31u);
+        } else if constexpr (UNI) {
             e = extract_t<RUNS>(tu, 0, kd[j], x[j]);
         } else if constexpr (MW4) {
             e = 0;
 #pragma unroll
-            for (int r = 0; r < RUNS; ++r) e |= (x[j] & rr[r][j]) >> (ta.dw(r, pos[j], kd[j]) & 31u);
+            for (int r = 0; r < RUNS; ++r) e |= (x[j] & rr[r][j]) >> (et.ta.dw(r, pos[j], kd[j]) & 31u);
         } else {
-            e = extract_t<RUNS>(ta, pos[j], kd[j], x[j]);
+            e = extract_t<RUNS>(et.ta, pos[j], kd[j], x[j]);
         }
         f[j] = p[j] ? e : x[j];
         size[j] = live ? (p[j] ? 32u - (kd[j] & 63u) : 32u) : 0u;
@@ -542,6 +580,106 @@ __global__ __launch_bounds__(1024) void k_encode_small(Tables t, Geo geo, const 
                 if (set) atomicOr(w, set);
                 if (touched & ~set) atomicAnd(w, ~(touched & ~set));
             }
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Short launches from GPU memory to GPU memory: tensors of at most 1 KiB
+// (one step of NW words per lane) and at most a few rows per CU.  A
+// workgroup of 16 waves takes 32 consecutive tensors, two per wave, so that
+// their bitmask bits fill exactly one bitmask word; nothing is staged: both
+// rows' source words are loaded at once (range-checked buffer loads), and
+// the table entries of the lanes' positions (or the wave-uniform words of
+// uniform metadata) straight into registers.  Each record is assembled in
+// its own LDS buffer as in k_encode_small and written with 16-byte stores;
+// an incompressible tensor is stored from the registers that hold it.
+// ---------------------------------------------------------------------------
+constexpr uint32_t kEncRowWaves = 16, kEncRowsPerWave = 2;
+
+template <int RUNS, bool UNI, int NW>
+__global__ __launch_bounds__(kWave * kEncRowWaves) void k_encode_rows(Tables t, Geo geo,
+                                                                     const uint8_t* __restrict__ src,
+                                                                     uint64_t n_tensors, uint8_t* __restrict__ slots,
+                                                                     uint32_t* __restrict__ bitmask,
+                                                                     uint64_t* __restrict__ stored,
+                                                                     uint32_t buf_words) {
+    extern __shared__ uint32_t smem[];
+    __shared__ uint32_t bm_set, bm_touched;
+    using Vec = std::conditional_t<NW == 4, u32x4, u32x2>;
+    const uint32_t lane = lane_id();
+    const uint32_t wib = uniform(threadIdx.x / kWave);
+    const uint64_t b0 = (uint64_t)blockIdx.x * (kEncRowWaves * kEncRowsPerWave);
+    const uint64_t t0 = b0 + (uint64_t)wib * kEncRowsPerWave;
+    const uint32_t nw = (uint32_t)geo.n_words;
+    const uint32_t Mw = geo.Mw;
+    if (threadIdx.x == 0) bm_set = bm_touched = 0u;
+    // both rows' words (lanes past a row, or a row past the launch, read zeros)
+    Vec xv[kEncRowsPerWave];
+    static_for<kEncRowsPerWave>([&](auto rc) {
+        constexpr int r = decltype(rc)::value;
+        const bool in = t0 + r < n_tensors;
+        const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+            (void*)(src + (in ? (t0 + r) * geo.L : 0)), (short)0, (int)(in ? geo.L : 0), 0x00020000);
+        if constexpr (NW == 4)
+            xv[r] = __builtin_amdgcn_raw_buffer_load_b128(rs, (int)(16 * lane), 0, 2);
+        else
+            xv[r] = __builtin_amdgcn_raw_buffer_load_b64(rs, (int)(8 * lane), 0, 2);
+    });
+    std::conditional_t<UNI, EncTabs<RUNS, true>, EncRegs<UNI ? 0 : RUNS, NW>> et;
+    if constexpr (UNI)
+        et = enc_tabs_global<RUNS, true>(t, Mw);
+    else
+        et.load(t, Mw, ((uint32_t)NW * lane) % Mw);
+    __syncthreads();
+    const uint32_t hw = (uint32_t)geo.hdr_words;
+    const uint32_t lw0 = (uint32_t)NW * lane;
+    const bool live = lw0 < nw;  // nw % 4 == 0: a live lane owns all its words
+    static_for<kEncRowsPerWave>([&](auto rc) {
+        constexpr int r = decltype(rc)::value;
+        const uint64_t ti = t0 + r;
+        if (ti >= n_tensors) return;
+        uint32_t* buf = smem + (wib * kEncRowsPerWave + r) * buf_words;
+        u32x4* b4 = reinterpret_cast<u32x4*>(buf);
+        for (uint32_t i = lane; i < (buf_words >> 2); i += kWave) b4[i] = u32x4{0u, 0u, 0u, 0u};
+        __builtin_amdgcn_wave_barrier();
+        uint32_t x[NW];
+#pragma unroll
+        for (int j = 0; j < NW; ++j) x[j] = xv[r][j];
+        uint32_t f[NW], size[NW];
+        const uint32_t tot = encode_lane<NW, RUNS, UNI, true, true>(et, Mw, geo.log2g, live, UNI ? 0u : lw0 % Mw, x,
+                                                                    buf, lw0 >> geo.log2g, f, size);
+        uint32_t carry = 0;
+        or_fields(buf + hw, carry, f, size, tot);
+        __builtin_amdgcn_wave_barrier();
+        const uint64_t R = 32ull * hw + carry;
+        const uint32_t words = (uint32_t)((R + 31) / 32);
+        const bool comp = 4ull * words < geo.L;
+        uint8_t* slot = slots + ti * geo.L;
+        if (comp) {
+            const uint32_t w4 = (words + 3) >> 2;
+            for (uint32_t i = lane; i < w4; i += kWave)
+                __builtin_nontemporal_store(b4[i], reinterpret_cast<u32x4*>(slot) + i);
+        } else if (live) {
+            __builtin_nontemporal_store(xv[r], reinterpret_cast<Vec*>(slot) + lane);
+        }
+        if (lane == 0) {
+            const uint32_t bit = 1u << (uint32_t)(ti - b0);
+            atomicOr(&bm_touched, bit);
+            if (comp) atomicOr(&bm_set, bit);
+            if (stored) stored[ti] = comp ? 4ull * words : geo.L;
+        }
+    });
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        // the workgroup's 32 tensors are one bitmask word (b0 is a multiple of 32)
+        const uint32_t set = bm_set, touched = bm_touched;
+        uint32_t* w = bitmask + (b0 >> 5);
+        if (touched == ~0u) {
+            *w = set;
+        } else {
+            if (set) atomicOr(w, set);
+            if (touched & ~set) atomicAnd(w, ~(touched & ~set));
         }
     }
 }
@@ -891,6 +1029,41 @@ static hipError_t launch_encode_small(const Tables& t, const Geo& geo, const voi
 #undef IBP_ENC_SMALL
 }
 
+// Single-tile tensors of at most 1 KiB encoded from GPU memory into GPU
+// memory, 16-byte aligned, at most three runs per position unless the
+// metadata is uniform, and at most 128 rows per CU: k_encode_rows.  0 sends
+// every call to the persistent kernel.
+#ifndef IBP_ENCODE_ROWS
+#define IBP_ENCODE_ROWS 1
+#endif
+
+static bool encode_rows(const Geo& geo, int runs, bool uni, uint64_t n_tensors, uint32_t cu_count) {
+    return IBP_ENCODE_ROWS && geo.src_in_hbm && geo.dst_in_hbm && geo.aligned16 && geo.n_words <= 4 * kWave &&
+           (uni || (runs <= 3 && geo.Mw % 4 == 0)) && n_tensors <= 128ull * cu_count;
+}
+
+template <int RUNS, bool UNI>
+static hipError_t launch_encode_rows(const Tables& t, const Geo& geo, const void* src, uint64_t n_tensors,
+                                     void* slots, uint32_t* bitmask, uint64_t* stored, uint32_t buf_words,
+                                     hipStream_t s) {
+    if constexpr (!UNI && RUNS > 3) {
+        return hipErrorInvalidValue;
+    } else {
+        constexpr uint32_t rows = kEncRowWaves * kEncRowsPerWave;
+        const dim3 grid((uint32_t)((n_tensors + rows - 1) / rows));
+        const size_t shm = (size_t)rows * buf_words * 4;
+        if (geo.n_words <= 2 * kWave)
+            hipLaunchKernelGGL((k_encode_rows<RUNS, UNI, 2>), grid, dim3(kWave * kEncRowWaves), shm, s, t, geo,
+                               static_cast<const uint8_t*>(src), n_tensors, static_cast<uint8_t*>(slots), bitmask,
+                               stored, buf_words);
+        else
+            hipLaunchKernelGGL((k_encode_rows<RUNS, UNI, 4>), grid, dim3(kWave * kEncRowWaves), shm, s, t, geo,
+                               static_cast<const uint8_t*>(src), n_tensors, static_cast<uint8_t*>(slots), bitmask,
+                               stored, buf_words);
+        return hipGetLastError();
+    }
+}
+
 template <int RUNS>
 static hipError_t launch_encode_r(const Tables& t, const Geo& geo, bool uniform_meta, const void* src,
                                   uint64_t n_tensors, void* slots, uint32_t* bitmask, uint64_t* stored,
@@ -900,6 +1073,11 @@ static hipError_t launch_encode_r(const Tables& t, const Geo& geo, bool uniform_
         uint32_t buf_words = 0;
         size_t head = 0, wave = 0;
         if (geo.aligned16 && small_encode_lds(geo, RUNS, uniform_meta, &buf_words, &head, &wave)) {
+            if (encode_rows(geo, RUNS, uniform_meta, n_tensors, cu_count))
+                return uniform_meta ? launch_encode_rows<RUNS, true>(t, geo, src, n_tensors, slots, bitmask, stored,
+                                                                     buf_words, s)
+                                    : launch_encode_rows<RUNS, false>(t, geo, src, n_tensors, slots, bitmask,
+                                                                      stored, buf_words, s);
             bool launched = false;
             const SmallArgs xa;
             const hipError_t e =

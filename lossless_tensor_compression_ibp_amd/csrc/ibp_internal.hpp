@@ -46,6 +46,7 @@ struct Geo {
     uint32_t spec_words;     // first-read words of a single-tile record (multiple of 4)
     uint32_t aligned16;      // slot base and L allow 16-byte vector access
     uint32_t src_in_hbm;     // what the launch reads (stored items, or the encode's source) is in device memory
+    uint32_t dst_in_hbm;     // the encode's slots are in device memory
 };
 
 // Decoupled look-back state for multi-tile tensors.  A status word packs

@@ -130,14 +130,16 @@ def test_llm_layer_multi_tile():
 
 
 @pytest.mark.parametrize("fill", [0, -1], ids=["zeroed", "all_ones"])
-def test_bitmask_words_rewritten(fill):
-    """Enough 512-byte rows (70,001) that each workgroup of the encode takes
-    whole bitmask words (written with one store) as well as words it shares
-    with its neighbours (atomics): every bit of the rows equals the oracle's
-    whatever the bitmask held, and the bits past the last row keep their
-    value."""
+@pytest.mark.parametrize("n", [70001, 3001], ids=["persistent", "rows"])
+def test_bitmask_words_rewritten(fill, n):
+    """512-byte rows encoded from HBM into HBM.  70,001 rows take the
+    persistent encode, whose workgroups write whole bitmask words with one
+    store and words shared with their neighbours with atomics; 3,001 rows take
+    the short-launch encode, one bitmask word per workgroup (the last one
+    partial).  Every bit of the rows equals the oracle's whatever the bitmask
+    held, and the bits past the last row keep their value."""
     w = WL.DENSE_GNN
-    raw = as_rows(WL.dense_gnn(70001))
+    raw = as_rows(WL.dense_gnn(n))
     n, L = raw.shape
     say(f"[parity] bitmask words n={n} L={L} fill={fill}")
     dev = device()
