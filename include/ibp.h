@@ -121,7 +121,9 @@ ibp_status ibp_meta_get_info(ibp_meta_t meta, ibp_meta_info* info);
  * metadata sample fits in them -- or the whole slot when the shortest
  * possible record spans all but at most 1/16 of the slot's 128-byte lines.
  * Rounded up to a multiple of 16 bytes and to at least the header; capped at
- * the slot.  Affects later decode calls on any stream. */
+ * the slot.  Affects later decode calls on any stream, except decodes of
+ * tensors of at most 1 KiB from slots in GPU memory in launches of at most
+ * 128 rows per compute unit, which read each slot whole in one pass. */
 ibp_status ibp_meta_set_first_read(ibp_meta_t meta, uint64_t bytes);
 
 /* Waits for all work on the handle's GPU, then frees the handle. */

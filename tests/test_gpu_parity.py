@@ -362,21 +362,26 @@ def test_mask_with_many_runs():
     assert ibp.ibp_meta_get_info(r.meta)["max_runs"] >= 9
 
 
-@pytest.mark.parametrize("wl", ["sparse_gnn", "dense_gnn", "kv_bf16"])
+@pytest.mark.parametrize("wl", ["sparse_gnn", "dense_gnn", "kv_bf16", "dense_gnn_hbm"])
 def test_first_read_sizes(wl):
     """Decode under every first-read split (the header-only read, reads cut
     mid-record, unaligned sizes that round up, the whole slot, beyond the
-    slot): the decoded bytes never depend on it."""
-    w = WL.ALL[wl]
+    slot): the decoded bytes never depend on it.  dense_gnn_hbm: 512-byte
+    rows in HBM slots, more than 128 per CU, so the persistent kernel (which
+    honours the split) rather than the one-wave-per-row kernel (which reads
+    whole slots) takes the decode and the gather."""
+    w = WL.ALL[wl.replace("_hbm", "")]
     if wl == "sparse_gnn":
         raw = as_rows(WL.sparse_gnn(900))
     elif wl == "dense_gnn":
         raw = as_rows(WL.dense_gnn(900))
+    elif wl == "dense_gnn_hbm":
+        raw = as_rows(WL.dense_gnn(128 * _cu_count() + 37))
     else:
         raw = WL.kv_cache(n_layers=1, n_heads=2, n_tokens=16 * 100).reshape(-1, 2048).view(np.uint8).reshape(-1, 4096)
     n, L = raw.shape
     dev = device()
-    pinned_slots = wl != "kv_bf16"
+    pinned_slots = wl in ("sparse_gnn", "dense_gnn")
     src = to_gpu(raw)
     meta = ibp.ibp_build_metadata(src, min(n, w.n_sample), L, w.chunk_bits, w.period_bits, w.threshold)
     slots = torch.empty((n, L), dtype=torch.uint8, pin_memory=True) if pinned_slots else torch.empty_like(src)
