@@ -8,6 +8,8 @@ produce (stored bytes, bitmask, records, raw slots, decoded tensors, gathers)
 is compared with the oracle's."""
 from __future__ import annotations
 
+import os
+
 import numpy as np
 import pytest
 import torch
@@ -18,7 +20,8 @@ from tests.gpu_util import bitmask_bits, device, empty_like_loc, say, to_gpu
 
 pytestmark = pytest.mark.gpu
 
-N_CASES = 150
+# seeds per layout; IBP_FUZZ_CASES raises it for a longer run
+N_CASES = int(os.environ.get("IBP_FUZZ_CASES", "150"))
 
 
 @pytest.fixture(scope="module", autouse=True)
