@@ -1100,10 +1100,16 @@ __global__ __launch_bounds__(256) void k_decode_rows(Tables t, Geo geo, const ui
     const uint32_t Mw = geo.Mw;
     TabUniform<RUNS> tu;
     TabRegs<UNI ? 0 : RUNS, NW> tr;
-    if constexpr (UNI)
+    if constexpr (UNI) {
         tu = load_uniform<RUNS>(t, Mw);
-    else
-        tr.load(t, Mw, ((uint32_t)NW * lane) % Mw);
+    } else {
+        // a period of at least a step's words needs no wrap (and no division)
+        const uint32_t p0 = (uint32_t)NW * lane;
+        if (Mw >= (uint32_t)NW * kWave)
+            tr.load(t, Mw, p0);
+        else
+            tr.load(t, Mw, p0 % Mw);
+    }
     const uint32_t nwords = (uint32_t)geo.n_words;
     const uint32_t hw = (uint32_t)geo.hdr_words;
     uint32_t* buf = smem + wib * buf_words;
@@ -1136,8 +1142,9 @@ __global__ __launch_bounds__(256) void k_decode_rows(Tables t, Geo geo, const ui
             pbits = decode_tile<RUNS, true, kMode>(tu, geo, buf, buf + hw, 0, 0, nwords, out, true);
         else
             pbits = decode_tile<RUNS, true, kMode>(tr, geo, buf, buf + hw, 0, 0, nwords, out, true);
-        const uint64_t words = hw + (pbits + 31) / 32;
-        if (bad_pad || 4ull * words >= geo.L || 4ull * words > len[r]) latch_error(err, kErrCorrupt);
+        // tensors of at most 1 KiB: 32-bit compares
+        const uint32_t words = hw + (pbits + 31) / 32;
+        if (bad_pad || 4 * words >= (uint32_t)geo.L || 4 * words > len[r]) latch_error(err, kErrCorrupt);
         __builtin_amdgcn_wave_barrier();
     });
 }

@@ -649,10 +649,16 @@ __global__ __launch_bounds__(kWave * kEncRowWaves) void k_encode_rows(Tables t, 
             xv[r] = __builtin_amdgcn_raw_buffer_load_b64(rs, (int)(8 * lane), 0, 2);
     });
     std::conditional_t<UNI, EncTabs<RUNS, true>, EncRegs<UNI ? 0 : RUNS, NW>> et;
-    if constexpr (UNI)
+    if constexpr (UNI) {
         et = enc_tabs_global<RUNS, true>(t, Mw);
-    else
-        et.load(t, Mw, ((uint32_t)NW * lane) % Mw);
+    } else {
+        // a period of at least a step's words needs no wrap (and no division)
+        const uint32_t p0 = (uint32_t)NW * lane;
+        if (Mw >= (uint32_t)NW * kWave)
+            et.load(t, Mw, p0);
+        else
+            et.load(t, Mw, p0 % Mw);
+    }
     __syncthreads();
     const uint32_t hw = (uint32_t)geo.hdr_words;
     const uint32_t lw0 = (uint32_t)NW * lane;
@@ -669,8 +675,9 @@ __global__ __launch_bounds__(kWave * kEncRowWaves) void k_encode_rows(Tables t, 
 #pragma unroll
         for (int j = 0; j < NW; ++j) x[j] = xv[r][j];
         uint32_t f[NW], size[NW];
-        const uint32_t tot = encode_lane<NW, RUNS, UNI, true, true>(et, Mw, geo.log2g, live, UNI ? 0u : lw0 % Mw, x,
-                                                                    buf, lw0 >> geo.log2g, f, size);
+        // (the positions only feed the table reads, which EncRegs has done)
+        const uint32_t tot = encode_lane<NW, RUNS, UNI, true, true>(et, Mw, geo.log2g, live, 0u, x, buf,
+                                                                    lw0 >> geo.log2g, f, size);
         uint32_t carry = 0;
         or_fields(buf + hw, carry, f, size, tot);
         __builtin_amdgcn_wave_barrier();
