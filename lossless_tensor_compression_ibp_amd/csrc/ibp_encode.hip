@@ -614,9 +614,10 @@ __global__ __launch_bounds__(1024) void k_encode_small(Tables t, Geo geo, const 
 // its own LDS buffer as in k_encode_small and written with 16-byte stores;
 // an incompressible tensor is stored from the registers that hold it.
 // ---------------------------------------------------------------------------
-// Measured on MI355X (16,384 rows of 512 bytes / of 1 KiB): 2 rows per wave
-// (16 waves) 7.8-7.9 / 8.3-8.4 us, 4 rows (8 waves) 7.9-8.2 / 9.5 us, 8 rows
-// (4 waves) 8.9-9.5 / 11.6 us.
+// Rows per wave, measured on MI355X (16,384 rows of 512 bytes / of 1 KiB,
+// header bits then still OR-ed one lane at a time): 2 rows (16 waves)
+// 7.8-7.9 / 8.3-8.4 us, 4 rows (8 waves) 7.9-8.2 / 9.5 us, 8 rows (4 waves)
+// 8.9-9.5 / 11.6 us.
 constexpr uint32_t kEncRowWaves = 16, kEncRowsPerWave = 2;
 
 template <int RUNS, bool UNI, int NW>
